@@ -1,0 +1,235 @@
+"""ctypes wrapper around the fp64 C oracle (``sda_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
+CPU-baseline leg use this module.  The HIP library never imports or calls it,
+and it imports nothing from the HIP package.
+
+Inputs are numpy arrays on the host.  bf16 tensors are passed as their uint16
+bit patterns and FP8 e4m3 tensors as their uint8 bytes; the oracle decodes
+both itself.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+from dataclasses import dataclass
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "sda_oracle.c")
+_LIB = os.path.join(_HERE, "libsda_oracle.so")
+
+KV_BF16 = 0
+KV_FP8_E4M3 = 1
+DIM = 192
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (plain -O2, no fast-math)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(
+            ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fno-fast-math",
+             "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+class _Problem(ctypes.Structure):
+    _fields_ = [
+        ("rows", ctypes.c_int32), ("heads", ctypes.c_int32), ("groups", ctypes.c_int32),
+        ("query_len", ctypes.c_int32), ("block", ctypes.c_int32), ("R", ctypes.c_int32),
+        ("region_tokens", ctypes.c_int32),
+        ("query", ctypes.c_void_p), ("q_row_stride", ctypes.c_int64),
+        ("q_head_stride", ctypes.c_int64),
+        ("cache", ctypes.c_void_p), ("kv_dtype", ctypes.c_int32),
+        ("c_page_stride", ctypes.c_int64), ("c_group_stride", ctypes.c_int64),
+        ("c_token_stride", ctypes.c_int64), ("num_pages", ctypes.c_int64),
+        ("regions", ctypes.c_void_p), ("regions_row_stride", ctypes.c_int64),
+        ("block_table", ctypes.c_void_p), ("table_row_stride", ctypes.c_int64),
+        ("table_cols", ctypes.c_int64),
+        ("positions", ctypes.c_void_p), ("active", ctypes.c_void_p),
+        ("scale", ctypes.c_float), ("clear_inactive", ctypes.c_int32),
+        ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float),
+        ("gate", ctypes.c_void_p), ("gate_row_stride", ctypes.c_int64),
+        ("gate_head_stride", ctypes.c_int64),
+    ]
+
+
+_lib = None
+_lib_lock = threading.Lock()
+
+
+def lib():
+    global _lib
+    with _lib_lock:
+        if _lib is None:
+            l = ctypes.CDLL(build())
+            l.sdo_bf16_to_double.restype = ctypes.c_double
+            l.sdo_bf16_to_double.argtypes = [ctypes.c_uint16]
+            l.sdo_e4m3_to_double.restype = ctypes.c_double
+            l.sdo_e4m3_to_double.argtypes = [ctypes.c_uint8]
+            l.sdo_f32_to_bf16_bits.restype = ctypes.c_uint16
+            l.sdo_f32_to_bf16_bits.argtypes = [ctypes.c_float]
+            l.sdo_gate_value.restype = ctypes.c_float
+            l.sdo_gate_value.argtypes = [ctypes.c_uint16]
+            l.sdo_splits_pages.restype = ctypes.c_int
+            l.sdo_splits_pages.argtypes = [ctypes.c_int]
+            l.sdo_decode.restype = ctypes.c_int
+            l.sdo_decode.argtypes = [ctypes.POINTER(_Problem), ctypes.c_void_p,
+                                     ctypes.c_int, ctypes.c_int]
+            l.sdo_decode_split.restype = ctypes.c_int
+            l.sdo_decode_split.argtypes = [ctypes.POINTER(_Problem), ctypes.c_int,
+                                           ctypes.c_void_p, ctypes.c_int, ctypes.c_int]
+            _lib = l
+    return _lib
+
+
+def bf16_to_double(bits: int) -> float:
+    return lib().sdo_bf16_to_double(bits)
+
+
+def e4m3_to_double(bits: int) -> float:
+    return lib().sdo_e4m3_to_double(bits)
+
+
+def f32_to_bf16_bits(x: float) -> int:
+    return lib().sdo_f32_to_bf16_bits(x)
+
+
+def gate_value(bits: int) -> float:
+    return lib().sdo_gate_value(bits)
+
+
+def splits_pages(rows: int) -> int:
+    return lib().sdo_splits_pages(rows)
+
+
+@dataclass
+class HostProblem:
+    """Host copies of every input, in the layouts the C ABI takes.
+
+    query: uint16 [rows, heads, 192] (bf16 bits, any strides with unit inner)
+    cache: uint16 (bf16 bits) or uint8 (e4m3) [pages, G, block, 384]
+    regions: int32 [rows, R]; block_table: int32 [requests, cols]
+    positions: int32 [rows]; active: uint8 [rows]; gate: uint16 or None
+    """
+    query: np.ndarray
+    cache: np.ndarray
+    regions: np.ndarray
+    block_table: np.ndarray
+    positions: np.ndarray
+    active: np.ndarray
+    scale: float
+    query_len: int = 1
+    region_tokens: int = 0
+    clear_inactive: bool = True
+    k_scale: float = 1.0
+    v_scale: float = 1.0
+    gate: np.ndarray | None = None
+
+
+def _strides(a: np.ndarray) -> tuple:
+    return tuple(s // a.itemsize for s in a.strides)
+
+
+def _problem(hp: HostProblem) -> _Problem:
+    q, c = hp.query, hp.cache
+    assert q.dtype == np.uint16 and q.ndim == 3 and q.shape[2] == DIM and q.strides[2] == 2
+    assert c.ndim == 4 and c.shape[3] == 2 * DIM and c.strides[3] == c.itemsize
+    assert c.dtype in (np.uint16, np.uint8)
+    assert hp.regions.dtype == np.int32 and hp.regions.strides[1] == 4
+    assert hp.block_table.dtype == np.int32 and hp.block_table.strides[1] == 4
+    assert hp.positions.dtype == np.int32 and hp.positions.flags.c_contiguous
+    assert hp.active.dtype == np.uint8 and hp.active.flags.c_contiguous
+    rows, heads, _ = q.shape
+    p = _Problem()
+    p.rows, p.heads, p.groups = rows, heads, c.shape[1]
+    p.query_len, p.block, p.R = hp.query_len, c.shape[2], hp.regions.shape[1]
+    p.region_tokens = hp.region_tokens
+    p.query = q.ctypes.data
+    p.q_row_stride, p.q_head_stride = _strides(q)[0], _strides(q)[1]
+    p.cache = c.ctypes.data
+    p.kv_dtype = KV_BF16 if c.dtype == np.uint16 else KV_FP8_E4M3
+    cs = _strides(c)
+    p.c_page_stride, p.c_group_stride, p.c_token_stride = cs[0], cs[1], cs[2]
+    p.num_pages = c.shape[0]
+    p.regions = hp.regions.ctypes.data
+    p.regions_row_stride = _strides(hp.regions)[0]
+    p.block_table = hp.block_table.ctypes.data
+    p.table_row_stride = _strides(hp.block_table)[0]
+    p.table_cols = hp.block_table.shape[1]
+    p.positions = hp.positions.ctypes.data
+    p.active = hp.active.ctypes.data
+    p.scale = hp.scale
+    p.clear_inactive = 1 if hp.clear_inactive else 0
+    p.k_scale, p.v_scale = hp.k_scale, hp.v_scale
+    if hp.gate is not None:
+        assert hp.gate.dtype == np.uint16
+        p.gate = hp.gate.ctypes.data
+        p.gate_row_stride, p.gate_head_stride = _strides(hp.gate)
+    else:
+        p.gate = None
+        p.gate_row_stride = p.gate_head_stride = 0
+    return p
+
+
+def _check_rc(rc: int) -> None:
+    if rc != 0:
+        raise RuntimeError({-1: "bad arguments", -2: "block-table column out of range",
+                            -3: "page id not present in the host cache",
+                            -4: "out of memory"}.get(rc, "error %d" % rc))
+
+
+def decode(hp: HostProblem, out: np.ndarray | None = None, rows=None,
+           splits: int | None = None, threads: int = 1) -> np.ndarray:
+    """fp64 reference output [rows, heads, 192].
+
+    ``out``: fp64 array to write into (rows left untouched by the semantics,
+    i.e. inactive rows with clear_inactive off, keep its contents); default is
+    a NaN-filled array.  ``rows``: optional iterable of row ids to compute
+    (others stay untouched).  ``splits``: use the split/merge organisation
+    with that many splits instead of the direct definition.  ``threads``:
+    host threads, each taking whole rows.
+    """
+    nrows, heads = hp.query.shape[0], hp.query.shape[1]
+    if out is None:
+        out = np.full((nrows, heads, DIM), np.nan)
+    assert out.dtype == np.float64 and out.shape == (nrows, heads, DIM) and out.flags.c_contiguous
+    p = _problem(hp)
+    l = lib()
+    row_list = list(range(nrows)) if rows is None else [int(r) for r in rows]
+    row_bytes = heads * DIM * 8
+
+    def run(rs):
+        for r in rs:
+            ptr = out.ctypes.data + r * row_bytes
+            if splits is None:
+                rc = l.sdo_decode(ctypes.byref(p), ptr, r, r + 1)
+            else:
+                rc = l.sdo_decode_split(ctypes.byref(p), splits, ptr, r, r + 1)
+            _check_rc(rc)
+
+    if threads <= 1 or len(row_list) < 2:
+        run(row_list)
+    else:
+        parts = [row_list[i::threads] for i in range(threads)]
+        errs = []
+
+        def worker(rs):
+            try:
+                run(rs)
+            except Exception as e:  # surfaced below
+                errs.append(e)
+
+        ts = [threading.Thread(target=worker, args=(rs,)) for rs in parts if rs]
+        for t in ts:
+            t.start()
+        for t in ts:
+            t.join()
+        if errs:
+            raise errs[0]
+    return out

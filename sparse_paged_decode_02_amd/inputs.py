@@ -1,0 +1,220 @@
+"""Seeded synthetic workloads for sparse paged decode attention.
+
+This module only draws inputs.  It holds none of the attention arithmetic: it
+does no region-to-page resolution and no masking, and it has no softmax.  The
+HIP path and the oracle both consume what it produces.  Index structures come
+from ``numpy.random.default_rng(seed)``, so they do not depend on the device.
+Bulk tensors (query, cache, gate) come from ``torch.Generator(device)`` seeded
+with the same seed.  They are drawn in fp32 and rounded to nearest: to bf16,
+or to float8_e4m3fn after division by the per-tensor scale.
+
+The five named workloads follow the decode shapes the pages describe.  Each
+row is a (token, KV group) pair, and the G*query_len rows of a request share
+one block-table row.  The cache is [pages, G, block, 384] with K then V.  A
+row selects a set of distinct region ids that always contains the region of
+its own position.  The ids are shuffled, and unused slots hold -1.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, replace
+
+import numpy as np
+import torch
+
+HEAD_DIM = 192
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    requests: int
+    query_len: int
+    groups: int
+    heads: int
+    block: int
+    pages_per_req: int
+    R: int
+    kv: str                      # "bf16" or "fp8"
+    pos_lo: int                  # first query token position ~ U[pos_lo, pos_hi]
+    pos_hi: int
+    live: tuple | None = None    # per-row live-slot count ~ U[lo, hi]; None: R
+    inactive_frac: float = 0.0   # round(frac * rows) rows inactive
+    inactive_rows: tuple = ()    # explicit inactive rows (overrides frac)
+    gated: bool = False
+    splits: int | None = None    # None: sda_splits(rows)
+    k_scale: float = 0.05
+    v_scale: float = 0.04
+    region_tokens: int = 0       # 0: one region per page
+    seed: int = 0
+
+    @property
+    def rows(self) -> int:
+        return self.requests * self.query_len * self.groups
+
+    @property
+    def tokens(self) -> int:
+        return self.requests * self.query_len
+
+    @property
+    def total_pages(self) -> int:
+        return self.requests * self.pages_per_req
+
+    @property
+    def rt(self) -> int:
+        return self.region_tokens or self.block
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(HEAD_DIM)
+
+
+def config_seed(k: int) -> int:
+    return 1000 * k + 7
+
+
+# The five decode workloads (1-based numbering).
+CONFIGS = {
+    1: Workload("tiny-bf16", requests=4, query_len=1, groups=1, heads=8, block=16,
+                pages_per_req=16, R=8, kv="bf16", pos_lo=1, pos_hi=127,
+                live=None, inactive_rows=(3,), gated=False, splits=1, seed=config_seed(1)),
+    2: Workload("bf16-gated", requests=64, query_len=1, groups=4, heads=16, block=64,
+                pages_per_req=512, R=32, kv="bf16", pos_lo=4096, pos_hi=32767,
+                inactive_frac=0.05, gated=True, splits=None, seed=config_seed(2)),
+    3: Workload("fp8-cache", requests=256, query_len=1, groups=2, heads=16, block=64,
+                pages_per_req=2048, R=64, kv="fp8", pos_lo=65536, pos_hi=131071,
+                gated=False, splits=None, seed=config_seed(3)),
+    4: Workload("multi-token", requests=128, query_len=2, groups=4, heads=8, block=32,
+                pages_per_req=512, R=64, kv="bf16", pos_lo=8192, pos_hi=16382,
+                live=(8, 64), inactive_frac=0.10, gated=True, splits=None,
+                seed=config_seed(4)),
+    5: Workload("large-batch-fp8", requests=1024, query_len=1, groups=4, heads=16, block=64,
+                pages_per_req=256, R=32, kv="fp8", pos_lo=8192, pos_hi=16383,
+                gated=True, splits=1, seed=config_seed(5)),
+}
+
+
+def scaled(w: Workload, **kw) -> Workload:
+    """A copy of ``w`` with some fields replaced (smaller parity cases)."""
+    return replace(w, **kw)
+
+
+@dataclass
+class Indices:
+    block_table: np.ndarray      # int32 [requests, pages_per_req]
+    positions: np.ndarray        # int32 [rows]
+    regions: np.ndarray          # int32 [rows, R]
+    active: np.ndarray           # uint8 [rows]
+
+
+def draw_indices(w: Workload, seed: int | None = None, block_table: np.ndarray | None = None
+                 ) -> Indices:
+    """Block table (a random permutation of all pages), positions, region
+    selections and the active mask."""
+    rng = np.random.default_rng(w.seed if seed is None else seed)
+    if block_table is None:
+        block_table = rng.permutation(w.total_pages).astype(np.int32).reshape(
+            w.requests, w.pages_per_req)
+    first = rng.integers(w.pos_lo, w.pos_hi + 1, size=w.requests)
+    # row r = (request * query_len + j) * G + g; token j of a request sits at first + j
+    req = np.repeat(np.arange(w.requests), w.query_len * w.groups)
+    j = np.tile(np.repeat(np.arange(w.query_len), w.groups), w.requests)
+    positions = (first[req] + j).astype(np.int32)
+    rt = w.rt
+    regions = np.full((w.rows, w.R), -1, dtype=np.int32)
+    for r in range(w.rows):
+        cur = int(positions[r]) // rt           # the region holding the row's own token
+        avail = cur + 1
+        want = w.R if w.live is None else int(rng.integers(w.live[0], w.live[1] + 1))
+        n = min(want, avail, w.R)
+        if n <= 0:
+            continue
+        others = rng.choice(cur, size=n - 1, replace=False) if n > 1 else np.zeros(0, np.int64)
+        ids = np.concatenate([others, [cur]]).astype(np.int32)
+        rng.shuffle(ids)
+        regions[r, :n] = ids
+    active = np.ones(w.rows, dtype=np.uint8)
+    if w.inactive_rows:
+        active[list(w.inactive_rows)] = 0
+    elif w.inactive_frac > 0:
+        k = int(round(w.inactive_frac * w.rows))
+        active[rng.choice(w.rows, size=k, replace=False)] = 0
+    return Indices(block_table, positions, regions, active)
+
+
+@dataclass
+class Inputs:
+    """Everything one decode call takes, on one device."""
+    w: Workload
+    query: torch.Tensor          # bf16 [rows, heads, 192]
+    cache: torch.Tensor          # bf16 or uint8 (e4m3 bytes) [pages, G, block, 384]
+    regions: torch.Tensor        # int32 [rows, R]
+    block_table: torch.Tensor    # int32 [requests, pages_per_req]
+    positions: torch.Tensor      # int32 [rows]
+    active: torch.Tensor         # bool [rows]
+    gate: torch.Tensor | None    # bf16 [tokens, G*heads]
+    k_scale: torch.Tensor | None  # fp32 [1] (FP8 only)
+    v_scale: torch.Tensor | None
+    scale: float
+    splits: int | None           # None: the library's sda_splits(rows)
+
+    @property
+    def fp8(self) -> bool:
+        return self.cache.dtype == torch.uint8
+
+
+def draw_cache(w: Workload, device, seed: int | None = None, pages_per_draw: int = 4096
+               ) -> torch.Tensor:
+    """bf16 ~ N(0,1), or FP8 e4m3 bytes of RN(N(0,1)/scale) (K: k_scale, V: v_scale).
+    Drawn in slices of ``pages_per_draw`` pages to bound temporaries."""
+    gen = torch.Generator(device=device)
+    gen.manual_seed((w.seed if seed is None else seed) * 2 + 1)
+    shape = (w.total_pages, w.groups, w.block, 2 * HEAD_DIM)
+    if w.kv == "bf16":
+        cache = torch.empty(shape, dtype=torch.bfloat16, device=device)
+    else:
+        cache = torch.empty(shape, dtype=torch.uint8, device=device)
+    for p0 in range(0, w.total_pages, pages_per_draw):
+        p1 = min(w.total_pages, p0 + pages_per_draw)
+        x = torch.randn((p1 - p0,) + shape[1:], generator=gen, device=device)
+        if w.kv == "bf16":
+            cache[p0:p1] = x.to(torch.bfloat16)
+        else:
+            x[..., :HEAD_DIM] /= w.k_scale
+            x[..., HEAD_DIM:] /= w.v_scale
+            cache[p0:p1] = x.to(torch.float8_e4m3fn).view(torch.uint8)
+        del x
+    return cache
+
+
+def make_inputs(w: Workload, device="cpu", seed: int | None = None,
+                cache: torch.Tensor | None = None, block_table: np.ndarray | None = None,
+                splits: int | None = None) -> Inputs:
+    """Draw a full input set.  Pass ``cache``/``block_table`` to draw another
+    query/selection set over an existing cache."""
+    seed = w.seed if seed is None else seed
+    idx = draw_indices(w, seed=seed, block_table=block_table)
+    if cache is None:
+        cache = draw_cache(w, device, seed=seed)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed * 2)
+    query = torch.randn((w.rows, w.heads, HEAD_DIM), generator=gen, device=device).to(
+        torch.bfloat16)
+    gate = None
+    if w.gated:
+        # N(0, 2): variance 2
+        g = torch.randn((w.tokens, w.groups * w.heads), generator=gen, device=device)
+        gate = (g * math.sqrt(2.0)).to(torch.bfloat16)
+    k_scale = v_scale = None
+    if w.kv == "fp8":
+        k_scale = torch.tensor([w.k_scale], dtype=torch.float32, device=device)
+        v_scale = torch.tensor([w.v_scale], dtype=torch.float32, device=device)
+    if splits is None:
+        splits = w.splits
+    return Inputs(
+        w=w, query=query, cache=cache,
+        regions=torch.from_numpy(idx.regions).to(device),
+        block_table=torch.from_numpy(idx.block_table).to(device),
+        positions=torch.from_numpy(idx.positions).to(device),
+        active=torch.from_numpy(idx.active.astype(bool)).to(device),
+        gate=gate, k_scale=k_scale, v_scale=v_scale, scale=w.scale, splits=splits)

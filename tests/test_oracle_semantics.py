@@ -1,0 +1,229 @@
+"""Pins of the oracle's row semantics (CPU): a dense brute force by another
+route (torch SDPA over the whole context with a multiplicity mask), closed
+forms and invariants."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle
+from oracle.hostprep import host_problem_from_inputs
+from sparse_paged_decode_02_amd import inputs as gen
+from _util import DIM, dense_reference, tiny_workload
+
+
+def _hp(w, **kw):
+    inp = gen.make_inputs(w, device="cpu")
+    return inp, host_problem_from_inputs(inp, **kw)
+
+
+def _random_case(seed):
+    rng = np.random.default_rng(seed)
+    block = int(rng.choice([4, 8, 16, 32]))
+    rts = [d for d in (block, block // 2, block // 4, 8, 4) if d >= 1 and block % d == 0]
+    rt = int(rng.choice(rts))
+    groups = int(rng.choice([1, 2, 3]))
+    qlen = int(rng.choice([1, 1, 2, 3]))
+    requests = int(rng.integers(1, 4))
+    R = int(rng.integers(1, 10))
+    pages = int(rng.integers(2, 6))
+    heads = int(rng.choice([1, 3, 8, 13, 16]))
+    kv = "fp8" if rng.random() < 0.4 else "bf16"
+    live = (1, R) if rng.random() < 0.5 else None
+    rows = requests * qlen * groups
+    inactive = tuple(rng.choice(rows, size=int(rng.integers(0, 2)), replace=False).tolist())
+    w = tiny_workload(seed, requests=requests, query_len=qlen, groups=groups, heads=heads,
+                      block=block, pages_per_req=pages, R=R, kv=kv, live=live,
+                      region_tokens=0 if rt == block else rt, inactive_rows=inactive)
+    return w, rng
+
+
+@pytest.mark.parametrize("seed", range(60))
+def test_oracle_matches_dense_sdpa(seed):
+    w, rng = _random_case(seed)
+    inp = gen.make_inputs(w, device="cpu")
+    # duplicate a live id into a free slot of some rows (a multiset)
+    reg = inp.regions.numpy()
+    for r in range(reg.shape[0]):
+        live = reg[r][reg[r] >= 0]
+        free = np.nonzero(reg[r] < 0)[0]
+        if len(live) and len(free) and rng.random() < 0.5:
+            reg[r, free[0]] = live[0]
+    hp = host_problem_from_inputs(inp)
+    got = oracle.decode(hp)
+    ref = dense_reference(hp)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    m = ~np.isnan(ref)
+    np.testing.assert_allclose(got[m], ref[m], rtol=0, atol=1e-10)
+
+
+def test_config1_matches_dense_sdpa():
+    inp = gen.make_inputs(gen.CONFIGS[1], device="cpu")
+    hp = host_problem_from_inputs(inp)
+    got = oracle.decode(hp)
+    ref = dense_reference(hp)
+    assert not np.isnan(got).any()
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-10)
+    assert (got[3] == 0).all()  # row 3 is inactive
+
+
+def test_zero_query_gives_mean_of_visible_values():
+    w = tiny_workload(11, requests=2, groups=2, heads=3, block=16, pages_per_req=4, R=3)
+    inp = gen.make_inputs(w, device="cpu")
+    inp.query.zero_()
+    hp = host_problem_from_inputs(inp)
+    got = oracle.decode(hp)
+    c = torch.from_numpy(hp.cache.view(np.int16)).view(torch.bfloat16).to(torch.float64)
+    for r in range(w.rows):
+        req, g, pos = r // w.groups, r % w.groups, int(hp.positions[r])
+        vals = []
+        for rid in hp.regions[r]:
+            if rid < 0:
+                continue
+            for t in range(int(rid) * 16, min(int(rid) * 16 + 16, pos + 1)):
+                vals.append(c[int(hp.block_table[req, t // 16]), g, t % 16, DIM:])
+        ref = torch.stack(vals).mean(0).numpy()
+        for h in range(3):
+            np.testing.assert_allclose(got[r, h], ref, rtol=0, atol=1e-14)
+
+
+def test_single_visible_token_returns_its_value_exactly():
+    """A row whose only live region starts at its position sees one token."""
+    w = tiny_workload(12, requests=2, groups=2, heads=5, block=8, pages_per_req=4, R=4, kv="fp8")
+    inp = gen.make_inputs(w, device="cpu")
+    reg = inp.regions.numpy()
+    pos = inp.positions.numpy()
+    reg[:] = -1
+    for r in range(w.rows):
+        pos[r] = 8 * (r % 3) + 8          # first token of region 1..3
+        reg[r, 2] = pos[r] // 8
+    hp = host_problem_from_inputs(inp)
+    got = oracle.decode(hp)
+    for r in range(w.rows):
+        req, g, t = r // w.groups, r % w.groups, int(pos[r])
+        page = int(hp.block_table[req, t // 8])
+        v = np.array([oracle.e4m3_to_double(int(b)) for b in hp.cache[page, g, t % 8, DIM:]])
+        v = v * float(np.float32(w.v_scale))
+        for h in range(5):
+            assert np.array_equal(got[r, h], v)
+
+
+def test_dominant_token_returns_its_value():
+    """One token whose logit beats all others by > 700 wins outright."""
+    w = tiny_workload(13, requests=1, groups=1, heads=2, block=16, pages_per_req=4, R=4,
+                      pos_lo=63, pos_hi=63)
+    inp = gen.make_inputs(w, device="cpu")
+    inp.query.fill_(0)
+    inp.query[:, :, 0] = 1.0
+    c = inp.cache
+    c[..., 0] = 0.0
+    bt = inp.block_table.numpy()
+    target = 37
+    c[bt[0, target // 16], 0, target % 16, 0] = 10000.0
+    inp.regions[0] = torch.tensor([0, 1, 2, 3], dtype=torch.int32)
+    hp = host_problem_from_inputs(inp)
+    got = oracle.decode(hp)
+    v = c[bt[0, target // 16], 0, target % 16, DIM:].to(torch.float64).numpy()
+    for h in range(2):
+        assert np.array_equal(got[0, h], v)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_invariants(seed):
+    w = tiny_workload(100 + seed, requests=3, query_len=2, groups=2, heads=6, block=16,
+                      pages_per_req=6, R=5, kv="fp8" if seed % 2 else "bf16", live=(1, 5),
+                      inactive_rows=(seed % 12,), gated=True)
+    inp = gen.make_inputs(w, device="cpu")
+    hp = host_problem_from_inputs(inp)
+    base = oracle.decode(hp)
+    rng = np.random.default_rng(seed)
+
+    # permuting slots: only the summation order changes
+    hp2 = host_problem_from_inputs(inp)
+    for r in range(w.rows):
+        hp2.regions[r] = hp2.regions[r][rng.permutation(w.R)]
+    np.testing.assert_allclose(oracle.decode(hp2), base, rtol=0, atol=1e-12)
+
+    # extra -1 slots and regions wholly past the position contribute nothing
+    hp3 = host_problem_from_inputs(inp)
+    extra = np.full((w.rows, 4), -1, dtype=np.int32)
+    for r in range(w.rows):
+        extra[r, 1] = hp3.positions[r] // 16 + 1   # starts past pos
+        extra[r, 3] = -7
+    hp3.regions = np.ascontiguousarray(np.concatenate([hp3.regions, extra], axis=1))
+    assert np.array_equal(oracle.decode(hp3), base)
+
+    # the split/merge organisation equals the definition
+    for splits in (1, 2, 3, 4, 5, 8, 33):
+        np.testing.assert_allclose(oracle.decode(hp, splits=splits), base, rtol=0, atol=1e-12)
+
+    # inactive rows: exact zeros when cleared, untouched otherwise
+    inactive = np.nonzero(hp.active == 0)[0]
+    assert (base[inactive] == 0).all() and not np.signbit(base[inactive]).any()
+    hp4 = host_problem_from_inputs(inp, clear_inactive=False)
+    sentinel = np.full_like(base, 7.25)
+    out4 = oracle.decode(hp4, out=sentinel.copy())
+    assert (out4[inactive] == 7.25).all()
+    act = hp.active == 1
+    assert np.array_equal(out4[act], base[act])
+
+
+def test_gate_off_equals_gate_one_and_half():
+    w = tiny_workload(21, requests=2, groups=2, heads=4, block=16, pages_per_req=4, R=4,
+                      gated=True)
+    inp = gen.make_inputs(w, device="cpu")
+    off = oracle.decode(host_problem_from_inputs(inp.__class__(**{**inp.__dict__, "gate": None})))
+    inp.gate.fill_(30.0)
+    one = oracle.decode(host_problem_from_inputs(inp))
+    assert np.array_equal(one, off)
+    inp.gate.fill_(0.0)
+    half = oracle.decode(host_problem_from_inputs(inp))
+    assert np.array_equal(half, off * 0.5)
+
+
+def test_gate_indexing_token_group_head():
+    """gate[token, g*heads + h] scales head h of row token*G + g only."""
+    w = tiny_workload(22, requests=2, query_len=2, groups=3, heads=4, block=16,
+                      pages_per_req=4, R=4, gated=True)
+    inp = gen.make_inputs(w, device="cpu")
+    inp.gate.fill_(30.0)
+    ones = oracle.decode(host_problem_from_inputs(inp))
+    token, g, h = 2, 1, 3
+    inp.gate[token, g * w.heads + h] = 0.0
+    got = oracle.decode(host_problem_from_inputs(inp))
+    r = token * w.groups + g
+    expect = ones.copy()
+    expect[r, h] *= 0.5
+    assert np.array_equal(got, expect)
+
+
+def test_page_renaming_is_invisible():
+    """Moving pages to other physical slots and updating the block table leaves
+    the output bit-identical: pages are reached only through the table."""
+    w = tiny_workload(31, requests=3, groups=2, heads=3, block=8, pages_per_req=5, R=5,
+                      kv="fp8")
+    inp = gen.make_inputs(w, device="cpu")
+    hp = host_problem_from_inputs(inp)
+    base = oracle.decode(hp)
+    perm = np.random.default_rng(0).permutation(hp.cache.shape[0])
+    inv = np.argsort(perm)
+    hp.cache = np.ascontiguousarray(hp.cache[perm])          # new slot i holds old page perm[i]
+    hp.block_table = np.ascontiguousarray(inv[hp.block_table].astype(np.int32))
+    assert np.array_equal(oracle.decode(hp), base)
+
+
+def test_missing_page_is_refused():
+    w = tiny_workload(32, requests=1, groups=1, heads=1, block=8, pages_per_req=4, R=4)
+    inp = gen.make_inputs(w, device="cpu")
+    hp = host_problem_from_inputs(inp)
+    hp.block_table[:] = -1
+    with pytest.raises(RuntimeError):
+        oracle.decode(hp)
+
+
+def test_no_visible_token_gives_zero():
+    w = tiny_workload(33, requests=2, groups=1, heads=2, block=8, pages_per_req=4, R=3)
+    inp = gen.make_inputs(w, device="cpu")
+    inp.regions[0] = torch.tensor([-1, -1, -1], dtype=torch.int32)
+    inp.regions[1] = torch.tensor([-1, int(inp.positions[1]) // 8 + 1, -5], dtype=torch.int32)
+    got = oracle.decode(host_problem_from_inputs(inp))
+    assert (got == 0).all()
