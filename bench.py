@@ -1,0 +1,227 @@
+#!/usr/bin/env python3
+"""Benchmark of sparse paged decode attention on one MI355X.
+
+A step is one ``sda_decode`` call (the split kernel, plus the combine kernel
+when splits > 1) over one batch of the workload.  Inputs are resident in HBM
+before timing.  The step rotates among ``--sets`` independently drawn
+query/selection sets over the same cache, so back-to-back calls do not reuse
+the last-level cache.
+
+Prints ONE JSON line.  ``value`` is the effective KV bandwidth in GB/s.  The
+algorithmic bytes of a call are the visible selected K|V rows plus Q of the
+active rows, plus the output of every row; each call's total is divided by
+its wall time.  ``roofline`` compares the per-launch algorithmic bytes with
+the launch duration from HIP events against the 8 TB/s HBM peak.
+``cpu_baseline`` times the fp64 oracle on a bounded sample of rows on the
+host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+HBM_PEAK_GBS = 8000.0
+METRIC = "effective KV GB/s (% of HBM peak) and rows/s for sparse decode attention"
+KERNEL_SRC = os.path.join(ROOT, "sparse_paged_decode_02_amd", "csrc", "sda_kernels.hip")
+
+
+def kernel_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def algorithmic_bytes(w, positions, regions, active) -> tuple:
+    """(bytes, visible tokens) of one call: visible selected K|V token rows
+    (384 elements each) and Q (heads x 192 bf16) of active rows, plus the
+    output (heads x 192 bf16) of every row."""
+    e = 1 if w.kv == "fp8" else 2
+    rt = w.rt
+    reg = regions.astype(np.int64)
+    pos = positions.astype(np.int64)[:, None]
+    t0 = reg * rt
+    vis = np.where(reg >= 0, np.clip(pos - t0 + 1, 0, rt), 0)
+    tokens = int((vis.sum(axis=1) * (active != 0)).sum())
+    nact = int((active != 0).sum())
+    q = nact * w.heads * 192 * 2
+    out = w.rows * w.heads * 192 * 2
+    return tokens * 384 * e + q + out, tokens
+
+
+def workload_desc(w) -> str:
+    return ("%s: %d rows = %d req x qlen %d x G %d, %d heads x 192, %s cache, block %d, "
+            "R %d, context %d" % (w.name, w.rows, w.requests, w.query_len, w.groups, w.heads,
+                                  w.kv, w.block, w.R, w.pages_per_req * w.block))
+
+
+def load_traffic(workload_name: str, splits: int):
+    """Counter-derived HBM bytes per launch, if measured on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s.json" % workload_name)
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+    except ValueError:
+        return None
+    if rec.get("kernel_hash") != kernel_hash() or rec.get("splits") != splits:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(inp, gpu_out, rows_sample: int, threads: int):
+    """Time the fp64 oracle (as it stands) on a sample of active rows."""
+    from oracle import oracle
+    from oracle.hostprep import host_problem_from_inputs
+
+    act = inp.active.cpu().numpy()
+    cand = np.nonzero(act)[0]
+    rng = np.random.default_rng(0)
+    rows = sorted(rng.choice(cand, size=min(rows_sample, len(cand)), replace=False).tolist())
+    hp = host_problem_from_inputs(inp, rows=rows)
+    out = np.full((inp.w.rows, inp.w.heads, 192), np.nan)
+    t0 = time.perf_counter()
+    oracle.decode(hp, out=out, rows=rows, threads=threads)
+    dt = time.perf_counter() - t0
+    sub_act = np.zeros_like(act)
+    sub_act[rows] = 1
+    nbytes, _ = algorithmic_bytes(inp.w, inp.positions.cpu().numpy()[rows],
+                                  inp.regions.cpu().numpy()[rows], sub_act[rows])
+    # the output term counts every row of a call; count only the sampled ones here
+    g = gpu_out.float().cpu().numpy().astype(np.float64)[rows]
+    err = np.abs(g - out[rows])
+    return {
+        "value": nbytes / dt / 1e9,
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": "%d active rows of the first input set (fp64 C oracle, %d threads), "
+                  "%.2f s wall; rows/s %.1f" % (len(rows), threads, dt, len(rows) / dt),
+        "parity_max_abs": float(err.max()),
+        "parity_mean_abs": float(err.mean()),
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2, help="workload number 1..5")
+    ap.add_argument("--sets", type=int, default=4, help="rotating input sets")
+    ap.add_argument("--splits", type=int, default=0, help="0: the workload's rule")
+    ap.add_argument("--cpu-rows", type=int, default=48)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(rows shard across GPUs with no exchange; see DESIGN.md). Run with --gpus 1.",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    from sparse_paged_decode_02_amd import binding as B
+    from sparse_paged_decode_02_amd import inputs as gen
+
+    if not os.path.exists(B.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+
+    dev = torch.device("cuda:0")
+    w = gen.CONFIGS[args.config]
+    splits = args.splits or w.splits or B.sda_splits(w.rows)
+
+    print("[bench] drawing %s" % workload_desc(w), file=sys.stderr, flush=True)
+    base = gen.make_inputs(w, device=dev, splits=splits)
+    sets = [base]
+    bt = base.block_table.cpu().numpy()
+    for i in range(1, args.sets):
+        sets.append(gen.make_inputs(w, device=dev, seed=w.seed + 100003 * i, cache=base.cache,
+                                    block_table=bt, splits=splits))
+    nbytes = []
+    for s in sets:
+        b, _ = algorithmic_bytes(w, s.positions.cpu().numpy(), s.regions.cpu().numpy(),
+                                 s.active.cpu().numpy())
+        nbytes.append(b)
+    outs = [torch.empty_like(s.query) for s in sets]
+    ws_bytes = B.sda_workspace_bytes(w.rows, w.heads, splits)
+    workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def call(i):
+        s = sets[i % len(sets)]
+        B.sda_decode(s.query, s.cache, s.regions, s.block_table, s.positions, s.active,
+                     outs[i % len(sets)], scale=s.scale, query_len=w.query_len, splits=splits,
+                     k_scale=s.k_scale, v_scale=s.v_scale, gate=s.gate,
+                     region_tokens=w.region_tokens, workspace=workspace, stream=stream)
+
+    for i in range(args.warmup):
+        call(i)
+    torch.cuda.synchronize()
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        call(i)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    launch_ms = np.array([starts[i].elapsed_time(ends[i]) for i in range(args.steps)])
+    total_bytes = sum(nbytes[i % len(sets)] for i in range(args.steps))
+    value = total_bytes / wall / 1e9
+    bytes_per_launch = float(np.mean([nbytes[i % len(sets)] for i in range(args.steps)]))
+    achieved = bytes_per_launch / (launch_ms.mean() * 1e-3) / 1e9
+    traffic = load_traffic(w.name, splits)
+
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.kv == "bf16" else "fp8-e4m3 cache, bf16 MFMA",
+        "data": "synthetic",
+        "config": {"workload": workload_desc(w), "rows": w.rows, "heads": w.heads,
+                   "splits": splits, "input_sets": len(sets), "seed": w.seed},
+        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "rows_per_s": round(w.rows * args.steps / wall, 1),
+        "us_per_call": {"median": round(float(np.median(launch_ms)) * 1e3, 2),
+                        "p10": round(float(np.percentile(launch_ms, 10)) * 1e3, 2),
+                        "p90": round(float(np.percentile(launch_ms, 90)) * 1e3, 2)},
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "sda split kernel" + (" + combine" if splits > 1 else " (combine fused)"),
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": int(bytes_per_launch),
+        },
+    }
+    if not args.no_cpu_baseline:
+        threads = max(1, min(16, os.cpu_count() or 1))
+        print("[bench] cpu baseline: oracle on %d rows, %d threads" % (args.cpu_rows, threads),
+              file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline(base, outs[0], args.cpu_rows, threads)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

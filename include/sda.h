@@ -1,0 +1,172 @@
+/*
+ * sda.h - DSA sparse decode attention over a paged KV cache, for MI355X
+ * (gfx950).  C ABI of libsda.so.
+ *
+ * The operation is the one the page "vllm.models.step5.nvidia.ops.
+ * sparse_decode_attention" documents: in its module docstring, in the
+ * `sparse_decode_attention` section (arguments, shapes and asserts) and in the
+ * `sparse_decode_splits` section (split heuristic).  Each row is one
+ * (token, KV group) pair.  It holds up to 16 GQA-packed query heads of dim 192,
+ * and it attends only over its selected regions, which are read in place from
+ * the paged cache.  The shape and stride eligibility rules follow
+ * `_direct_sparse_decode` on the page "vllm.models.step5.nvidia.
+ * flashinfer_sparse".
+ *
+ * All pointers in sda_decode_args are DEVICE pointers unless noted.  The
+ * caller owns every buffer, including the workspace.  The library allocates
+ * nothing and keeps no state, so every entry point is re-entrant.  sda_decode
+ * validates on the host and never reads device memory there; index contents
+ * (region ids, block-table entries, positions) are trusted, as on the page.
+ * On any error it returns before launching anything.
+ */
+#ifndef SDA_H_
+#define SDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SDA_ABI_VERSION 1
+#define SDA_HEAD_DIM 192     /* query / key / value head dim (fixed) */
+#define SDA_KV_ROW 384       /* one cache token row: K[0:192] then V[192:384] */
+#define SDA_MAX_HEADS 16     /* GQA-packed query heads per KV group */
+#define SDA_MAX_R 2048       /* region slots per row */
+#define SDA_MAX_SPLITS 256
+
+typedef enum {
+  SDA_OK = 0,
+  SDA_ERR_INVALID = -1,      /* an argument breaks the operation's contract */
+  SDA_ERR_UNSUPPORTED = -2,  /* legal, but outside what this build handles */
+  SDA_ERR_WORKSPACE = -3,    /* workspace missing or too small for splits > 1 */
+  SDA_ERR_LAUNCH = -4        /* the HIP launch reported an error */
+} sda_status;
+
+typedef enum {
+  SDA_KV_BF16 = 0,           /* cache elements are bfloat16 */
+  SDA_KV_FP8_E4M3 = 1        /* cache elements are OCP float8 e4m3fn bytes */
+} sda_kv_dtype;
+
+/*
+ * Arguments of one decode call.  Field meanings follow `sparse_decode_attention`
+ * (page "...ops.sparse_decode_attention").  Strides are in ELEMENTS of the
+ * pointed-to type.
+ *
+ *  rows         number of (token, KV group) rows; rows = tokens * groups.
+ *               Row r is group r % groups of token r / groups.  The
+ *               groups*query_len consecutive rows of one request share one
+ *               block-table row (request = r / (groups*query_len)).
+ *               rows == 0 returns SDA_OK without launching anything.
+ *  heads        query heads per row, 1..16.
+ *  groups       KV groups G (cache dim 1).
+ *  query_len    query tokens per request (1 for decode, >1 for MTP verify).
+ *  block        tokens per cache page (cache dim 2).
+ *  R            region slots per row (regions dim 1), 0..SDA_MAX_R.
+ *  region_tokens tokens per region; 0 means one region per page (= block).
+ *               It must divide block.  Region id i covers tokens
+ *               [i*region_tokens, (i+1)*region_tokens).
+ *  query        bf16 [rows, heads, 192]; dim stride 1; 16-byte aligned, with
+ *               row and head strides multiples of 8.
+ *  output       bf16 [rows, heads, 192], written in place; dim stride 1;
+ *               4-byte aligned, with even strides.
+ *  cache        [pages, groups, block, 384]: K in [0:192], V in [192:384].
+ *               Last-dim stride 1.  16-byte aligned, with the page, group
+ *               and token strides multiples of 16 bytes.  Addressing is
+ *               64-bit, so caches larger than 4 GiB are fine.
+ *  kv_dtype     sda_kv_dtype of the cache.
+ *  regions      int32 [rows, R], unit inner stride.  A negative id marks an
+ *               unused slot.  Slot order is irrelevant.  A region whose first
+ *               token lies past the row's position contributes nothing; its
+ *               block-table entry is never read.
+ *  block_table  int32 [requests, pages per request].  Token t of a request
+ *               lives at page block_table[request, t / block], slot
+ *               t % block.
+ *  positions    int32 [rows]: 0-based position of the row's query token.
+ *               Token t is visible iff t <= position (inclusive causal mask).
+ *  active       uint8 [rows]; 0 marks an inactive (padding) row.  For such a
+ *               row nothing else is read.
+ *  scale        softmax scale applied to q.k.
+ *  splits       >= 1: the row's visible regions are dealt to `splits`
+ *               workgroups, and their partials are merged by log-sum-exp.
+ *               Use sda_splits(rows).  The result does not depend on it
+ *               beyond rounding.
+ *  clear_inactive  nonzero: inactive rows are written as +0.0.  Zero: they
+ *               are left untouched.
+ *  k_scale, v_scale  device fp32 scalars, required for SDA_KV_FP8_E4M3 and
+ *               ignored for bf16.  Dequantized K = e4m3(byte) * k_scale, and
+ *               likewise for V.
+ *  gate         optional bf16 [tokens, groups*heads] headwise gate logits, or
+ *               NULL.  Head h of row r is scaled by the bf16-rounded
+ *               sigmoid(gate[r / groups, (r % groups)*heads + h]).  This is
+ *               the `_gate` helper on the same page.
+ *  workspace    device scratch of at least sda_workspace_bytes(rows, heads,
+ *               splits) bytes, 16-byte aligned.  May be NULL when splits == 1.
+ */
+typedef struct sda_decode_args {
+  int32_t rows, heads, groups, query_len, block, R, region_tokens;
+  const void *query;
+  int64_t q_row_stride, q_head_stride;
+  void *output;
+  int64_t o_row_stride, o_head_stride;
+  const void *cache;
+  int32_t kv_dtype;
+  int64_t c_page_stride, c_group_stride, c_token_stride;
+  const int32_t *regions;
+  int64_t regions_row_stride;
+  const int32_t *block_table;
+  int64_t table_row_stride;
+  const int32_t *positions;
+  const uint8_t *active;
+  float scale;
+  int32_t splits;
+  int32_t clear_inactive;
+  const float *k_scale;
+  const float *v_scale;
+  const void *gate;
+  int64_t gate_row_stride, gate_head_stride;
+  void *workspace;
+  size_t workspace_bytes;
+} sda_decode_args;
+
+/*
+ * Enqueue one sparse decode attention call on `stream`.  The call is
+ * asynchronous, performs no host synchronisation and no allocation, and may
+ * be captured in a HIP graph.  It launches the split kernel, a (rows, splits)
+ * grid.  When splits > 1 it also launches the combine kernel, which merges
+ * the partials and then applies the gate and the inactive-row clear.  When
+ * splits == 1 the combine is fused into the split kernel.
+ * Returns an sda_status.
+ */
+int sda_decode(const sda_decode_args *args, hipStream_t stream);
+
+/*
+ * Split count for `rows` rows.  This is the MI355X counterpart of
+ * `sparse_decode_splits` on page "...ops.sparse_decode_attention".  It depends
+ * on rows only, because graphs are captured per batch size.  Host-only and
+ * pure; returns 1 for rows <= 0.
+ */
+int sda_splits(int rows);
+
+/*
+ * Bytes of workspace sda_decode needs: 0 when splits == 1, else
+ * rows*splits*heads*(192+1)*4 rounded up to 256.  The workspace holds the
+ * fp32 partial outputs and log-sum-exps.  Returns 0 for invalid sizes.
+ */
+size_t sda_workspace_bytes(int rows, int heads, int splits);
+
+/* Static description of a status code (never NULL). */
+const char *sda_status_string(int status);
+
+/* SDA_ABI_VERSION of the built library, and sizeof(sda_decode_args), so a
+ * binding can check that its mirror of the struct matches. */
+int sda_abi_version(void);
+size_t sda_args_size(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SDA_H_ */

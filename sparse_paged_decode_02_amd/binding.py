@@ -1,0 +1,215 @@
+"""ctypes binding of libsda.so (see include/sda.h).
+
+Argument marshalling only: tensors become device pointers and element
+strides, and every step of the computation runs in the HIP library.  PyTorch
+supplies device memory and the stream.  If libsda.so is missing, the first call
+raises; nothing falls back to another implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libsda.so")
+
+SDA_OK = 0
+SDA_ERR_INVALID = -1
+SDA_ERR_UNSUPPORTED = -2
+SDA_ERR_WORKSPACE = -3
+SDA_ERR_LAUNCH = -4
+SDA_KV_BF16 = 0
+SDA_KV_FP8_E4M3 = 1
+ABI_VERSION = 1
+HEAD_DIM = 192
+
+
+class SdaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__("sda_decode failed (%d): %s" % (status, message))
+        self.status = status
+
+
+class DecodeArgs(ctypes.Structure):
+    """Mirror of ``sda_decode_args``; checked against sda_args_size()."""
+    _fields_ = [
+        ("rows", ctypes.c_int32), ("heads", ctypes.c_int32), ("groups", ctypes.c_int32),
+        ("query_len", ctypes.c_int32), ("block", ctypes.c_int32), ("R", ctypes.c_int32),
+        ("region_tokens", ctypes.c_int32),
+        ("query", ctypes.c_void_p), ("q_row_stride", ctypes.c_int64),
+        ("q_head_stride", ctypes.c_int64),
+        ("output", ctypes.c_void_p), ("o_row_stride", ctypes.c_int64),
+        ("o_head_stride", ctypes.c_int64),
+        ("cache", ctypes.c_void_p), ("kv_dtype", ctypes.c_int32),
+        ("c_page_stride", ctypes.c_int64), ("c_group_stride", ctypes.c_int64),
+        ("c_token_stride", ctypes.c_int64),
+        ("regions", ctypes.c_void_p), ("regions_row_stride", ctypes.c_int64),
+        ("block_table", ctypes.c_void_p), ("table_row_stride", ctypes.c_int64),
+        ("positions", ctypes.c_void_p), ("active", ctypes.c_void_p),
+        ("scale", ctypes.c_float), ("splits", ctypes.c_int32),
+        ("clear_inactive", ctypes.c_int32),
+        ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
+        ("gate", ctypes.c_void_p), ("gate_row_stride", ctypes.c_int64),
+        ("gate_head_stride", ctypes.c_int64),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+_lib = None
+_lock = threading.Lock()
+
+
+def lib() -> ctypes.CDLL:
+    """Load libsda.so once; raise if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(
+                    "libsda.so is not built (%s); run __graft_entry__.build() or "
+                    "python -m sparse_paged_decode_02_amd.build" % LIB_PATH)
+            l = ctypes.CDLL(LIB_PATH)
+            l.sda_decode.restype = ctypes.c_int
+            l.sda_decode.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.c_void_p]
+            l.sda_splits.restype = ctypes.c_int
+            l.sda_splits.argtypes = [ctypes.c_int]
+            l.sda_workspace_bytes.restype = ctypes.c_size_t
+            l.sda_workspace_bytes.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+            l.sda_status_string.restype = ctypes.c_char_p
+            l.sda_status_string.argtypes = [ctypes.c_int]
+            l.sda_abi_version.restype = ctypes.c_int
+            l.sda_abi_version.argtypes = []
+            l.sda_args_size.restype = ctypes.c_size_t
+            l.sda_args_size.argtypes = []
+            if l.sda_abi_version() != ABI_VERSION:
+                raise RuntimeError("libsda.so ABI version %d, binding expects %d"
+                                   % (l.sda_abi_version(), ABI_VERSION))
+            if l.sda_args_size() != ctypes.sizeof(DecodeArgs):
+                raise RuntimeError("sda_decode_args size mismatch: library %d, binding %d"
+                                   % (l.sda_args_size(), ctypes.sizeof(DecodeArgs)))
+            _lib = l
+    return _lib
+
+
+def sda_splits(rows: int) -> int:
+    return int(lib().sda_splits(int(rows)))
+
+
+def sda_workspace_bytes(rows: int, heads: int, splits: int) -> int:
+    return int(lib().sda_workspace_bytes(int(rows), int(heads), int(splits)))
+
+
+def status_string(status: int) -> str:
+    return lib().sda_status_string(int(status)).decode()
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def make_args(query, cache, regions, block_table, positions, active, output, *, scale,
+              query_len=1, splits, clear_inactive=True, k_scale=None, v_scale=None,
+              gate=None, region_tokens=0, workspace=None) -> DecodeArgs:
+    """Fill ``sda_decode_args`` from tensors (no validation beyond the C side)."""
+    a = DecodeArgs()
+    rows, heads = query.shape[0], query.shape[1]
+    a.rows, a.heads = rows, heads
+    a.groups, a.query_len, a.block = cache.shape[1], int(query_len), cache.shape[2]
+    a.R = regions.shape[1] if regions.dim() == 2 else 0
+    a.region_tokens = int(region_tokens)
+    a.query = _ptr(query)
+    a.q_row_stride, a.q_head_stride = query.stride(0), query.stride(1)
+    a.output = _ptr(output)
+    a.o_row_stride, a.o_head_stride = output.stride(0), output.stride(1)
+    a.cache = _ptr(cache)
+    fp8 = cache.dtype in (torch.uint8, torch.float8_e4m3fn)
+    a.kv_dtype = SDA_KV_FP8_E4M3 if fp8 else SDA_KV_BF16
+    a.c_page_stride, a.c_group_stride, a.c_token_stride = (
+        cache.stride(0), cache.stride(1), cache.stride(2))
+    a.regions = _ptr(regions)
+    a.regions_row_stride = regions.stride(0) if regions.dim() == 2 else 0
+    a.block_table = _ptr(block_table)
+    a.table_row_stride = block_table.stride(0)
+    a.positions = _ptr(positions)
+    a.active = _ptr(active)
+    a.scale = float(scale)
+    a.splits = int(splits)
+    a.clear_inactive = 1 if clear_inactive else 0
+    a.k_scale = _ptr(k_scale)
+    a.v_scale = _ptr(v_scale)
+    a.gate = _ptr(gate)
+    if gate is not None:
+        a.gate_row_stride, a.gate_head_stride = gate.stride(0), gate.stride(1)
+    a.workspace = _ptr(workspace)
+    a.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return a
+
+
+def _check_tensors(query, cache, regions, block_table, positions, active, output,
+                   k_scale, v_scale, gate):
+    """dtype checks the C ABI cannot make (it sees only pointers)."""
+    if query.dtype != torch.bfloat16 or output.dtype != torch.bfloat16:
+        raise SdaError(SDA_ERR_INVALID, "query and output must be bfloat16")
+    if query.dim() != 3 or output.shape != query.shape or query.shape[2] != HEAD_DIM:
+        raise SdaError(SDA_ERR_INVALID, "query/output must be [rows, heads, 192]")
+    if query.stride(2) != 1 or output.stride(2) != 1:
+        raise SdaError(SDA_ERR_INVALID, "query/output need unit stride in dim 2")
+    if cache.dim() != 4 or cache.shape[3] != 2 * HEAD_DIM or cache.stride(3) != 1:
+        raise SdaError(SDA_ERR_INVALID, "cache must be [pages, G, block, 384], unit last stride")
+    if cache.dtype not in (torch.bfloat16, torch.uint8, torch.float8_e4m3fn):
+        raise SdaError(SDA_ERR_INVALID, "cache must be bfloat16 or FP8 e4m3 (uint8 storage)")
+    if regions.dtype != torch.int32 or block_table.dtype != torch.int32:
+        raise SdaError(SDA_ERR_INVALID, "regions and block_table must be int32")
+    if regions.dim() != 2 or regions.shape[0] != query.shape[0] or (
+            regions.shape[1] > 0 and regions.stride(1) != 1):
+        raise SdaError(SDA_ERR_INVALID, "regions must be [rows, R] with unit inner stride")
+    if block_table.dim() != 2 or block_table.stride(1) != 1:
+        raise SdaError(SDA_ERR_INVALID, "block_table must be 2-D with unit inner stride")
+    if positions.dtype != torch.int32 or not positions.is_contiguous() or \
+            positions.numel() != query.shape[0]:
+        raise SdaError(SDA_ERR_INVALID, "positions must be contiguous int32 [rows]")
+    if active.dtype not in (torch.bool, torch.uint8) or not active.is_contiguous() or \
+            active.numel() != query.shape[0]:
+        raise SdaError(SDA_ERR_INVALID, "active must be contiguous bool/uint8 [rows]")
+    for s in (k_scale, v_scale):
+        if s is not None and (s.dtype != torch.float32 or s.numel() != 1):
+            raise SdaError(SDA_ERR_INVALID, "k_scale/v_scale must be fp32 scalars")
+    if gate is not None and (gate.dtype != torch.bfloat16 or gate.dim() != 2):
+        raise SdaError(SDA_ERR_INVALID, "gate must be bfloat16 [tokens, G*heads]")
+
+
+def sda_decode(query, cache, regions, block_table, positions, active, output, *, scale,
+               query_len=1, splits, clear_inactive=True, k_scale=None, v_scale=None,
+               gate=None, region_tokens=0, workspace=None, stream=None) -> None:
+    """Enqueue ``sda_decode`` on ``stream`` (default: torch's current stream).
+
+    Argument names follow ``sparse_decode_attention`` on the page
+    "vllm.models.step5.nvidia.ops.sparse_decode_attention".  ``workspace``: a
+    device tensor of at least sda_workspace_bytes(rows, heads, splits) bytes;
+    allocated here through torch when omitted and splits > 1.
+    """
+    _check_tensors(query, cache, regions, block_table, positions, active, output,
+                   k_scale, v_scale, gate)
+    rows, heads = query.shape[0], query.shape[1]
+    if workspace is None and splits > 1 and rows > 0:
+        nbytes = sda_workspace_bytes(rows, heads, splits)
+        if nbytes:
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=query.device)
+    a = make_args(query, cache, regions, block_table, positions, active, output, scale=scale,
+                  query_len=query_len, splits=splits, clear_inactive=clear_inactive,
+                  k_scale=k_scale, v_scale=v_scale, gate=gate, region_tokens=region_tokens,
+                  workspace=workspace)
+    if stream is None:
+        stream = torch.cuda.current_stream(query.device) if query.is_cuda else None
+    handle = None if stream is None else ctypes.c_void_p(stream.cuda_stream)
+    rc = lib().sda_decode(ctypes.byref(a), handle)
+    if rc != SDA_OK:
+        raise SdaError(rc, status_string(rc))
+
+
+def sda_decode_raw(args: DecodeArgs, stream_handle=None) -> int:
+    """Call the C entry point on a prepared struct; returns the status code."""
+    return int(lib().sda_decode(ctypes.byref(args), stream_handle))

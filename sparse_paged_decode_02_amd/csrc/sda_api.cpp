@@ -1,0 +1,138 @@
+// C-ABI layer of libsda.so: host-side validation, split heuristic, workspace
+// sizing and kernel launch.  Declarations and the full contract are in
+// include/sda.h.
+#include "sda.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include "sda_launch.h"
+
+static_assert(SDA_MAX_R == sda::kMaxRegions, "LDS region list must hold SDA_MAX_R slots");
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Split count for `rows` rows on MI355X.  The page "vllm.models.step5.nvidia.
+// ops.sparse_decode_attention" (`sparse_decode_splits`) doubles the split
+// count while rows*splits*2 <= 256, i.e. it sizes the grid for about 1.7 waves
+// of B300 programs, up to 32 splits.  The same rule with the target raised to
+// kTargetPrograms = 512 sizes the grid for 256 compute units.  One 256-thread
+// workgroup per (row, split) and two workgroups resident per CU give 512 slots.
+constexpr int kTargetPrograms = 512;
+constexpr int kMaxHeuristicSplits = 32;
+
+}  // namespace
+
+extern "C" {
+
+int sda_abi_version(void) { return SDA_ABI_VERSION; }
+
+size_t sda_args_size(void) { return sizeof(sda_decode_args); }
+
+int sda_splits(int rows) {
+  int splits = 1;
+  if (rows <= 0) return 1;
+  while (splits < kMaxHeuristicSplits && (int64_t)rows * splits * 2 <= kTargetPrograms) splits *= 2;
+  return splits;
+}
+
+size_t sda_workspace_bytes(int rows, int heads, int splits) {
+  if (rows < 0 || heads < 1 || heads > SDA_MAX_HEADS || splits < 1 || splits > SDA_MAX_SPLITS)
+    return 0;
+  if (splits == 1) return 0;
+  size_t n = (size_t)rows * (size_t)splits * (size_t)heads;
+  size_t bytes = n * (SDA_HEAD_DIM + 1) * sizeof(float);
+  return (bytes + 255) & ~(size_t)255;
+}
+
+const char* sda_status_string(int status) {
+  switch (status) {
+    case SDA_OK: return "ok";
+    case SDA_ERR_INVALID: return "invalid argument";
+    case SDA_ERR_UNSUPPORTED: return "unsupported argument (alignment, stride or size limit)";
+    case SDA_ERR_WORKSPACE: return "workspace missing or too small";
+    case SDA_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int sda_decode(const sda_decode_args* a, hipStream_t stream) {
+  if (!a) return SDA_ERR_INVALID;
+  // Shape contract: the asserts of `sparse_decode_attention` and the
+  // `_direct_sparse_decode` eligibility rule (dim 192, <= 16 heads, 384-wide
+  // unit-stride cache rows).
+  if (a->rows < 0 || a->heads < 1 || a->heads > SDA_MAX_HEADS || a->groups < 1 ||
+      a->query_len < 1 || a->block < 1 || a->R < 0 || a->splits < 1 || a->region_tokens < 0)
+    return SDA_ERR_INVALID;
+  if (a->kv_dtype != SDA_KV_BF16 && a->kv_dtype != SDA_KV_FP8_E4M3) return SDA_ERR_INVALID;
+  const int rt = a->region_tokens ? a->region_tokens : a->block;
+  if (a->block % rt) return SDA_ERR_INVALID;
+  const int64_t rows_per_req = (int64_t)a->groups * a->query_len;
+  if (a->rows % rows_per_req) return SDA_ERR_INVALID;
+  const bool fp8 = a->kv_dtype == SDA_KV_FP8_E4M3;
+  if (fp8 && (!a->k_scale || !a->v_scale)) return SDA_ERR_INVALID;
+  if (a->R > SDA_MAX_R || a->splits > SDA_MAX_SPLITS) return SDA_ERR_UNSUPPORTED;
+  if (a->rows == 0) return SDA_OK;  // nothing to do, nothing launched
+
+  if (!a->query || !a->output || !a->cache || !a->block_table || !a->positions || !a->active ||
+      (a->R > 0 && !a->regions))
+    return SDA_ERR_INVALID;
+
+  // Vector-load alignment: 16-byte Q and cache rows, 4-byte output pairs.
+  const int64_t esz = fp8 ? 1 : 2;
+  if (!aligned(a->query, 16) || a->q_row_stride % 8 || a->q_head_stride % 8)
+    return SDA_ERR_UNSUPPORTED;
+  if (!aligned(a->cache, 16) || (a->c_page_stride * esz) % 16 || (a->c_group_stride * esz) % 16 ||
+      (a->c_token_stride * esz) % 16)
+    return SDA_ERR_UNSUPPORTED;
+  if (!aligned(a->output, 4) || a->o_row_stride % 2 || a->o_head_stride % 2)
+    return SDA_ERR_UNSUPPORTED;
+
+  sda::Params p{};
+  p.q = static_cast<const uint16_t*>(a->query);
+  p.qrs = a->q_row_stride;
+  p.qhs = a->q_head_stride;
+  p.out = static_cast<uint16_t*>(a->output);
+  p.ors = a->o_row_stride;
+  p.ohs = a->o_head_stride;
+  p.cache = static_cast<const uint8_t*>(a->cache);
+  p.cps = a->c_page_stride;
+  p.cgs = a->c_group_stride;
+  p.cts = a->c_token_stride;
+  p.regions = a->regions;
+  p.rrs = a->regions_row_stride;
+  p.table = a->block_table;
+  p.trs = a->table_row_stride;
+  p.positions = a->positions;
+  p.active = a->active;
+  p.k_scale = a->k_scale;
+  p.v_scale = a->v_scale;
+  p.gate = static_cast<const uint16_t*>(a->gate);
+  p.grs = a->gate_row_stride;
+  p.ghs = a->gate_head_stride;
+  p.scale = a->scale;
+  p.rows = a->rows;
+  p.heads = a->heads;
+  p.groups = a->groups;
+  p.rows_per_req = (int32_t)rows_per_req;
+  p.block = a->block;
+  p.R = a->R;
+  p.rt = rt;
+  p.splits = a->splits;
+  p.clear = a->clear_inactive ? 1 : 0;
+  p.gated = a->gate ? 1 : 0;
+
+  if (a->splits > 1) {
+    size_t need = sda_workspace_bytes(a->rows, a->heads, a->splits);
+    if (!a->workspace || a->workspace_bytes < need || !aligned(a->workspace, 16))
+      return SDA_ERR_WORKSPACE;
+    p.partial = static_cast<float*>(a->workspace);
+    p.lse = p.partial + (size_t)a->rows * a->splits * a->heads * SDA_HEAD_DIM;
+  }
+
+  hipError_t e = sda::launch(p, fp8, stream);
+  return e == hipSuccess ? SDA_OK : SDA_ERR_LAUNCH;
+}
+
+}  // extern "C"

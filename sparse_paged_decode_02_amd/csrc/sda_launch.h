@@ -1,0 +1,38 @@
+// Internal interface between the C-ABI layer (sda_api.cpp) and the kernels
+// (sda_kernels.hip): the validated, kernel-ready argument block.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace sda {
+
+constexpr int kMaxRegions = 2048;  // LDS region list per workgroup (= SDA_MAX_R)
+
+struct Params {
+  const uint16_t* q;          // bf16 bits
+  int64_t qrs, qhs;           // query row / head strides (elements)
+  uint16_t* out;              // bf16 bits
+  int64_t ors, ohs;
+  const uint8_t* cache;       // byte view of the cache
+  int64_t cps, cgs, cts;      // cache page / group / token strides (elements)
+  const int32_t* regions;
+  int64_t rrs;
+  const int32_t* table;
+  int64_t trs;
+  const int32_t* positions;
+  const uint8_t* active;
+  const float* k_scale;
+  const float* v_scale;
+  const uint16_t* gate;       // bf16 bits or null
+  int64_t grs, ghs;
+  float* partial;             // [rows, splits, heads, 192] fp32 (splits > 1)
+  float* lse;                 // [rows, splits, heads] fp32, base-2 (splits > 1)
+  float scale;
+  int32_t rows, heads, groups, rows_per_req, block, R, rt, splits, clear, gated;
+};
+
+// Enqueue the split kernel (and the combine kernel when splits > 1).
+hipError_t launch(const Params& p, bool fp8, hipStream_t stream);
+
+}  // namespace sda

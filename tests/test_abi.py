@@ -1,0 +1,135 @@
+"""C-ABI contract of libsda.so, on the host (no kernel is launched here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_paged_decode_02_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "sda.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(sda_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_function():
+    names = _declared_functions()
+    assert {"sda_decode", "sda_splits", "sda_workspace_bytes", "sda_status_string",
+            "sda_abi_version", "sda_args_size"} <= set(names)
+    lib = B.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version_and_struct_size():
+    lib = B.lib()
+    assert lib.sda_abi_version() == B.ABI_VERSION
+    assert lib.sda_args_size() == ctypes.sizeof(B.DecodeArgs)
+
+
+def _table(name):
+    rows = []
+    for line in open(os.path.join(ROOT, "tests", "golden", name)):
+        line = line.split("#")[0].strip()
+        if line:
+            a, b = line.split()
+            rows.append((int(a), int(b)))
+    return rows
+
+
+@pytest.mark.parametrize("rows,splits", _table("splits_mi355x.txt"))
+def test_split_heuristic_table(rows, splits):
+    assert B.sda_splits(rows) == splits
+
+
+def test_workspace_bytes():
+    assert B.sda_workspace_bytes(256, 16, 1) == 0
+    n = 256 * 2 * 16 * 193 * 4
+    assert B.sda_workspace_bytes(256, 16, 2) == (n + 255) // 256 * 256
+    assert B.sda_workspace_bytes(3, 5, 7) == (3 * 7 * 5 * 193 * 4 + 255) // 256 * 256
+    assert B.sda_workspace_bytes(-1, 16, 2) == 0
+    assert B.sda_workspace_bytes(4, 17, 2) == 0
+    assert B.sda_workspace_bytes(4, 16, 0) == 0
+
+
+def test_status_strings():
+    for code in (0, -1, -2, -3, -4, 99):
+        assert isinstance(B.status_string(code), str) and B.status_string(code)
+
+
+# A fully valid argument block with fake (never dereferenced) device pointers.
+def _valid_args(**over):
+    a = B.DecodeArgs()
+    a.rows, a.heads, a.groups, a.query_len, a.block, a.R, a.region_tokens = 8, 16, 4, 1, 64, 32, 0
+    a.query, a.q_row_stride, a.q_head_stride = 0x100000, 16 * 192, 192
+    a.output, a.o_row_stride, a.o_head_stride = 0x200000, 16 * 192, 192
+    a.cache, a.kv_dtype = 0x300000, B.SDA_KV_BF16
+    a.c_page_stride, a.c_group_stride, a.c_token_stride = 4 * 64 * 384, 64 * 384, 384
+    a.regions, a.regions_row_stride = 0x400000, 32
+    a.block_table, a.table_row_stride = 0x500000, 512
+    a.positions, a.active = 0x600000, 0x700000
+    a.scale, a.splits, a.clear_inactive = 0.07, 1, 1
+    a.k_scale = a.v_scale = None
+    a.gate = None
+    a.workspace, a.workspace_bytes = None, 0
+    for k, v in over.items():
+        setattr(a, k, v)
+    return a
+
+
+INVALID = [
+    dict(heads=0), dict(heads=17), dict(groups=0), dict(query_len=0), dict(block=0),
+    dict(R=-1), dict(splits=0), dict(region_tokens=-1), dict(kv_dtype=2),
+    dict(region_tokens=48),                    # does not divide block 64
+    dict(rows=6),                              # not a multiple of groups * query_len
+    dict(kv_dtype=B.SDA_KV_FP8_E4M3),          # FP8 without scales
+    dict(kv_dtype=B.SDA_KV_FP8_E4M3, k_scale=0x800000),
+    dict(query=None), dict(output=None), dict(cache=None), dict(block_table=None),
+    dict(positions=None), dict(active=None), dict(regions=None),
+    dict(rows=-4),
+]
+
+UNSUPPORTED = [
+    dict(R=2049), dict(splits=257, workspace=0x900000, workspace_bytes=1 << 40),
+    dict(query=0x100008), dict(q_head_stride=196), dict(q_row_stride=16 * 192 + 4),
+    dict(cache=0x300008), dict(c_token_stride=388), dict(c_page_stride=4 * 64 * 384 + 4),
+    dict(output=0x200002), dict(o_head_stride=193),
+]
+
+
+@pytest.mark.parametrize("over", INVALID, ids=[str(o) for o in INVALID])
+def test_invalid_arguments_are_rejected(over):
+    assert B.sda_decode_raw(_valid_args(**over)) == B.SDA_ERR_INVALID
+
+
+@pytest.mark.parametrize("over", UNSUPPORTED, ids=[str(o) for o in UNSUPPORTED])
+def test_unsupported_arguments_are_rejected(over):
+    assert B.sda_decode_raw(_valid_args(**over)) == B.SDA_ERR_UNSUPPORTED
+
+
+def test_workspace_checks():
+    need = B.sda_workspace_bytes(8, 16, 4)
+    assert B.sda_decode_raw(_valid_args(splits=4)) == B.SDA_ERR_WORKSPACE
+    assert B.sda_decode_raw(_valid_args(splits=4, workspace=0x900000,
+                                        workspace_bytes=need - 1)) == B.SDA_ERR_WORKSPACE
+    assert B.sda_decode_raw(_valid_args(splits=4, workspace=0x900004,
+                                        workspace_bytes=need)) == B.SDA_ERR_WORKSPACE
+
+
+def test_null_args_and_zero_rows():
+    assert B.lib().sda_decode(None, None) == B.SDA_ERR_INVALID
+    # rows == 0 returns OK without launching, even with null buffers
+    a = _valid_args(rows=0, query=None, output=None, regions=None, positions=None, active=None)
+    assert B.sda_decode_raw(a) == B.SDA_OK
+    # ... but the shape contract is still checked first
+    assert B.sda_decode_raw(_valid_args(rows=0, heads=17)) == B.SDA_ERR_INVALID
+
+
+def test_fp8_scale_pointers_required_only_for_fp8():
+    # bf16 with no scales is fine up to the launch; FP8 needs both (checked above).
+    a = _valid_args(kv_dtype=B.SDA_KV_FP8_E4M3, k_scale=0x800000, v_scale=None)
+    assert B.sda_decode_raw(a) == B.SDA_ERR_INVALID
