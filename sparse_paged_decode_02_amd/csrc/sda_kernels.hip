@@ -15,31 +15,39 @@
 //    balanced share of them, and resolves each region to a cache offset
 //    through the block table.  Only that share's block-table entries are
 //    read.  The offsets go into LDS.
-//  * Main loop: each wave owns chunks of 32 token slots.  For every chunk it
-//    issues the next chunk's K|V loads before computing on the current one.
-//    The loads are 16-byte global loads into registers, in MFMA operand
-//    layout, so K never touches LDS.
-//      S^T[tok, head] = K[tok, :] . Q^T[:, head]
-//          12 x v_mfma_f32_16x16x32_bf16 (2 token tiles x 6 dim slices)
+//  * Main loop: every wave runs its own kStages-deep pipeline over chunks of
+//    token slots (16 tokens for a bf16 cache, 32 for FP8: 6 KiB of V either
+//    way).  For each chunk the wave issues 6 global loads of 16 bytes per
+//    lane, which put K straight into registers in MFMA A-operand layout.
+//    It also issues 6 LDS-DMA loads (global_load_lds_dwordx4), which put V
+//    into a wave-private LDS stage without passing through registers.  Chunk
+//    c is computed while chunks c+1 .. c+kStages-1 are in flight.
+//      S^T[tok, head] = K[tok, :] . Q^T[:, head]   v_mfma_f32_16x16x32_bf16
 //      online softmax per head, in the exp2 domain
 //      O^T[dim, head] += V^T[dim, tok] . P^T[tok, head]
-//          12 x MFMA (12 dim tiles).  V^T is read from a wave-private,
-//          padded LDS tile, and P^T comes straight from the S^T accumulators:
-//          the S^T tile already has the B-operand layout.
-//    FP8 K and V are converted exactly to bf16 (e4m3 is a subset of bf16).
-//    k_scale is folded into the logit scale and v_scale into the final
-//    normalisation.
+//    V^T comes from transposing LDS reads (ds_read_b64_tr_b16 for bf16,
+//    ds_read_b64_tr_b8 for FP8).  P^T is the S^T accumulator itself,
+//    because the C layout of S^T is the B-operand layout of the second
+//    product.  bf16 uses v_mfma_f32_16x16x16_bf16 for P.V; FP8 uses the x32
+//    form.  FP8 K and V are converted exactly to bf16 (e4m3 is a subset of
+//    bf16).  k_scale is folded into the logit scale and v_scale into the
+//    final normalisation.
 //  * Epilogue: the 4 waves' (max, sum, acc) states are merged through LDS.
 //    With one split, the gate is applied and the result is written as bf16
 //    (combine fused).  Otherwise the fp32 partial output and its base-2
 //    log-sum-exp go to the workspace.
-// Combine kernel (splits > 1): one workgroup per row merges the partials,
-// applies the gate and writes bf16, or clears an inactive row.
+// Combine kernel (splits > 1): one 64-thread workgroup per (row, head) merges
+// the partials, applies the gate and writes bf16, or clears an inactive row.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 #include "sda_launch.h"
+
+#define SDA_LDS __attribute__((address_space(3)))
 
 namespace sda {
 namespace {
@@ -47,17 +55,28 @@ namespace {
 constexpr int kDim = 192;
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kChunk = 32;       // token slots per wave iteration (2 MFMA tiles)
-constexpr int kVStride = 208;    // bf16 per LDS V row: 192 + 16 pad; 104 dwords,
-                                 // so the 4 token rows one V^T read touches
-                                 // land 8 banks apart
-constexpr int kAccStride = 196;  // floats per head row in the wave-merge area
+constexpr int kStages = 3;          // LDS stages per wave: 1 computed, 2 in flight
+constexpr int kStageBytes = 6144;   // K (or V) bytes of one chunk (16 bf16 / 32 FP8 tokens)
+constexpr int kChunkBytes = 2 * kStageBytes;  // one stage: K then V
+constexpr int kAccStride = 196;     // floats per head row in the wave-merge area
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
+
+// Per cache dtype: tokens per chunk, V bytes per token, 16-byte V pieces per token.
+template <bool kFp8>
+struct Cfg {
+  static constexpr int kTok = kFp8 ? 32 : 16;
+  static constexpr int kEsz = kFp8 ? 1 : 2;
+  static constexpr int kVBytes = kDim * kEsz;
+  static constexpr int kPieces = kVBytes / 16;
+  static_assert(kTok * kVBytes == kStageBytes, "one chunk of V fills one stage");
+};
 
 __device__ __forceinline__ float bf16_bits_to_float(uint32_t b) {
   return __uint_as_float(b << 16);
@@ -81,188 +100,251 @@ __device__ __forceinline__ float gate_value(const uint16_t* gate, int64_t idx) {
   return bf16_bits_to_float(float_to_bf16_bits(sig));
 }
 
-__device__ __forceinline__ u32x4 load16(const uint8_t* p) {
-  return *reinterpret_cast<const u32x4*>(p);
-}
-
-// 4 e4m3 bytes -> 4 bf16 (exact): {bytes 0,1 ; bytes 2,3} as two packed pairs.
+// 4 e4m3 bytes -> 4 bf16 (exact), as two packed pairs {bytes 0,1} {bytes 2,3}.
 __device__ __forceinline__ u32x2 fp8x4_to_bf16(uint32_t w) {
   bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
   bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
   return u32x2{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b)};
 }
 
-// Dim offset of the 8 elements lane group g4 supplies to MFMA k-slice cc.
-// bf16 loads 8 elements per 16-byte load: slice cc covers [32cc, 32cc+32).
-// FP8 loads 16 elements per load, feeding slices 2pp and 2pp+1.
+// LDS swizzles.  A stage holds one chunk's V rows, one per token, as 16-byte
+// pieces.  Piece p of token row r is stored at piece position p ^ swz(r).
+// The XOR keeps a piece inside its aligned 8-piece (bf16) or 4-piece (FP8)
+// block.  The swizzle makes the transposing reads of one 16-lane group hit 32
+// distinct banks:
+//  bf16: lanes 4y+q of group g read row 4g+y, pieces 2nt+(q>>1);
+//  FP8:  lanes 2y+h of group g read row 16(y>>2)+4g+(y&3), piece nt.
 template <bool kFp8>
-__device__ __forceinline__ int slice_dim(int cc, int g4) {
-  return kFp8 ? 64 * (cc >> 1) + 16 * g4 + 8 * (cc & 1) : 32 * cc + 8 * g4;
+__device__ __forceinline__ int swz(int row) {
+  return kFp8 ? 2 * ((row >> 4) & 1) + ((row >> 1) & 1) : 2 * (row & 3) + ((row >> 2) & 1);
+}
+// K pieces: the A-operand reads of 8 consecutive lanes (rows i..i+7 of one
+// tile, one piece) hit 32 distinct banks.
+template <bool kFp8>
+__device__ __forceinline__ int swz_k(int row) {
+  return kFp8 ? (row >> 1) & 3 : row & 7;
 }
 
-template <bool kFp8>
-struct ChunkRegs {
-  static constexpr int kLoads = kFp8 ? 3 : 6;  // 16-byte loads per token half-row
-  u32x4 k[2][kLoads];
-  u32x4 v[2][kLoads];
-  bool valid[2];
+// One 16-byte LDS-DMA per lane: global src -> LDS (lds_addr + 16 * lane).
+// Issued from inline assembly so that the compiler does not tie later LDS
+// reads to it; completion is awaited explicitly with wait_vmcnt.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_addr) {
+  __asm__ __volatile__("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                       :
+                       : "v"(src), "s"(lds_addr)
+                       : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __asm__ __volatile__("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const SDA_LDS void*)p;
+}
+
+// Where one token slot of a chunk lives.  Masked slots are redirected to the
+// first token of a region of the split (always visible), so every load stays
+// in bounds and every V row in LDS is finite data whose weight is exactly 0.
+struct ChunkCtx {
+  int c;                       // chunk index within this split
+  // uniform-region chunks (region_tokens a multiple of the chunk size):
+  int64_t rbase;               // element offset of the region's first token
+  int off0;                    // slot offset of the chunk within the region
+  int nval;                    // visible tokens of the region
 };
 
-struct RowState {
-  f32x4 acc[12];   // O^T tiles: lane holds head (lane&15), dims 16nt+4*(lane>>4)+v
-  float m;         // running max (base-2 logit units), same in the 4 lanes of a head
-  float l;         // this lane's part of the running sum
-};
-
-// Token slot of MFMA row i of tile t within a chunk.  The interleave makes the
-// 4 tokens that one V^T read touches (fixed t and v, lane groups g4 = 0..3)
-// consecutive LDS rows.
-__device__ __forceinline__ int chunk_token(int t, int i) { return 16 * t + 4 * (i & 3) + (i >> 2); }
-
-template <bool kFp8>
-__device__ __forceinline__ void issue_chunk(const Params& p, int c, int nreg,
-                                            const int64_t* s_base, const int* s_n,
-                                            int lane, ChunkRegs<kFp8>& cr) {
-  const int i16 = lane & 15, g4 = lane >> 4;
-  constexpr int kEsz = kFp8 ? 1 : 2;
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    int slot = c * kChunk + chunk_token(t, i16);
+template <bool kFp8, bool kUni>
+__device__ __forceinline__ int64_t token_elem(const Params& p, const ChunkCtx& cx, int tau,
+                                              const int64_t* s_base, const int* s_n, int nreg,
+                                              bool& valid) {
+  if (kUni) {
+    int off = cx.off0 + tau;
+    valid = off < cx.nval;
+    return cx.rbase + (int64_t)(valid ? off : 0) * p.cts;
+  } else {
+    int slot = cx.c * Cfg<kFp8>::kTok + tau;
     int k = slot / p.rt;
     int off = slot - k * p.rt;
-    bool valid = k < nreg && off < s_n[k < nreg ? k : 0];
-    cr.valid[t] = valid;
-    if (valid) {
-      const uint8_t* row = p.cache + (s_base[k] + (int64_t)off * p.cts) * kEsz;
-#pragma unroll
-      for (int u = 0; u < ChunkRegs<kFp8>::kLoads; ++u) {
-        int d = kFp8 ? 64 * u + 16 * g4 : 32 * u + 8 * g4;
-        cr.k[t][u] = load16(row + d * kEsz);
-        cr.v[t][u] = load16(row + (kDim + d) * kEsz);
-      }
-    } else {
-#pragma unroll
-      for (int u = 0; u < ChunkRegs<kFp8>::kLoads; ++u) {
-        cr.k[t][u] = u32x4{0, 0, 0, 0};
-        cr.v[t][u] = u32x4{0, 0, 0, 0};
-      }
-    }
+    int kk = k < nreg ? k : nreg - 1;
+    valid = k < nreg && off < s_n[kk];
+    return s_base[kk] + (int64_t)(valid ? off : 0) * p.cts;
   }
 }
 
-template <bool kFp8>
-__device__ __forceinline__ void compute_chunk(const ChunkRegs<kFp8>& cr, const u32x4 (&qreg)[6],
-                                              float qk_scale_log2, uint16_t (*s_vw)[kVStride],
-                                              int lane, RowState& st) {
-  const int i16 = lane & 15, g4 = lane >> 4;
-
-  // V rows of this lane's two tokens -> wave-private LDS tile (bf16, row = token slot).
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    uint16_t* vrow = s_vw[chunk_token(t, i16)];
-#pragma unroll
-    for (int u = 0; u < ChunkRegs<kFp8>::kLoads; ++u) {
-      if (kFp8) {
-        u32x4 w = cr.v[t][u];
-        u32x2 w0 = fp8x4_to_bf16(w[0]), w1 = fp8x4_to_bf16(w[1]);
-        u32x2 w2 = fp8x4_to_bf16(w[2]), w3 = fp8x4_to_bf16(w[3]);
-        u32x4 a = {w0[0], w0[1], w1[0], w1[1]};
-        u32x4 b = {w2[0], w2[1], w3[0], w3[1]};
-        int d = 64 * u + 16 * g4;
-        *reinterpret_cast<u32x4*>(vrow + d) = a;
-        *reinterpret_cast<u32x4*>(vrow + d + 8) = b;
-      } else {
-        *reinterpret_cast<u32x4*>(vrow + 32 * u + 8 * g4) = cr.v[t][u];
-      }
-    }
+template <bool kFp8, bool kUni>
+__device__ __forceinline__ ChunkCtx chunk_ctx(const Params& p, int c, const int64_t* s_base,
+                                              const int* s_n) {
+  ChunkCtx cx;
+  cx.c = c;
+  if (kUni) {
+    int slot0 = c * Cfg<kFp8>::kTok;
+    int k = slot0 / p.rt;
+    cx.off0 = slot0 - k * p.rt;
+    cx.rbase = s_base[k];
+    cx.nval = s_n[k];
+  } else {
+    cx.off0 = 0;
+    cx.rbase = 0;
+    cx.nval = 0;
   }
+  return cx;
+}
 
-  // S^T tiles: rows = token slots chunk_token(t, 4*g4 + v), columns = heads.
-  f32x4 s[2];
+// Issue chunk c into one LDS stage: 6 K and 6 V DMAs of 16 bytes per lane.
+// Stage slot 64j + lane (j = 0..5) is token row r = slot / kPieces, piece
+// position slot % kPieces, which holds global piece (position ^ swizzle(r)).
+// Returns the visibility of this lane's S^T rows (token slots 16t + i16).
+template <bool kFp8, bool kUni>
+__device__ __forceinline__ uint32_t issue_chunk(const Params& p, int c, int nreg,
+                                                const int64_t* s_base, const int* s_n, int lane,
+                                                uint32_t stage) {
+  using C = Cfg<kFp8>;
+  const int i16 = lane & 15;
+  const ChunkCtx cx = chunk_ctx<kFp8, kUni>(p, c, s_base, s_n);
+  uint32_t vbits = 0;
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    f32x4 a = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int cc = 0; cc < 6; ++cc) {
-      u32x4 kb;
-      if (kFp8) {
-        uint32_t w0 = cr.k[t][cc >> 1][(cc & 1) * 2 + 0];
-        uint32_t w1 = cr.k[t][cc >> 1][(cc & 1) * 2 + 1];
-        u32x2 c0 = fp8x4_to_bf16(w0), c1 = fp8x4_to_bf16(w1);
-        kb = u32x4{c0[0], c0[1], c1[0], c1[1]};
-      } else {
-        kb = cr.k[t][cc];
-      }
-      a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kb),
-                                                  __builtin_bit_cast(bf16x8, qreg[cc]), a, 0, 0, 0);
-    }
-    s[t] = a;
+  for (int t = 0; t < (kFp8 ? 2 : 1); ++t) {
+    bool valid;
+    (void)token_elem<kFp8, kUni>(p, cx, 16 * t + i16, s_base, s_n, nreg, valid);
+    vbits |= (valid ? 1u : 0u) << t;
   }
+  const uint32_t st = __builtin_amdgcn_readfirstlane(stage);
+#pragma unroll
+  for (int j = 0; j < 6; ++j) {
+    const int slot = 64 * j + lane;
+    const int r = slot / C::kPieces;
+    const int pos = slot - r * C::kPieces;
+    bool valid;
+    const int64_t e = token_elem<kFp8, kUni>(p, cx, r, s_base, s_n, nreg, valid);
+    const uint8_t* row = p.cache + e * C::kEsz;
+    dma16(row + 16 * (pos ^ swz_k<kFp8>(r)), st + 1024 * j);
+    dma16(row + C::kVBytes + 16 * (pos ^ swz<kFp8>(r)), st + kStageBytes + 1024 * j);
+  }
+  return vbits;
+}
 
-  // Which token rows are real: lanes 0..15 loaded rows 0..15 of each tile.
-  uint64_t vb0 = __ballot(cr.valid[0]);
-  uint64_t vb1 = __ballot(cr.valid[1]);
+struct RowState {
+  f32x4 acc[12];  // O^T tiles: lane holds head (lane&15), dims 16nt+4*(lane>>4)+v
+  float m;        // running max (base-2 logit units), same in the 4 lanes of a head
+  float l;        // this lane's part of the running sum
+};
 
-  float x[2][4];
+// Online-softmax update from this lane's logits x[] (already scaled, masked
+// to -inf); returns the rescale factor and writes p (bf16-rounded) into pb.
+template <int N>
+__device__ __forceinline__ void softmax_step(float (&x)[N], RowState& st, uint32_t (&pb)[N / 2]) {
   float mloc = -INFINITY;
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    int bit = 4 * g4 + v;
-    x[0][v] = ((vb0 >> bit) & 1) ? s[0][v] * qk_scale_log2 : -INFINITY;
-    x[1][v] = ((vb1 >> bit) & 1) ? s[1][v] * qk_scale_log2 : -INFINITY;
-    mloc = fmaxf(mloc, fmaxf(x[0][v], x[1][v]));
-  }
+  for (int i = 0; i < N; ++i) mloc = fmaxf(mloc, x[i]);
   mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
   mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-  float m_new = fmaxf(st.m, mloc);
-  float m_use = m_new == -INFINITY ? 0.f : m_new;
-  float alpha = __builtin_amdgcn_exp2f(st.m - m_use);
+  const float m_new = fmaxf(st.m, mloc);
+  const float m_use = m_new == -INFINITY ? 0.f : m_new;
+  const float alpha = __builtin_amdgcn_exp2f(st.m - m_use);
   st.m = m_new;
-
-  // P^T B-operand: element e = 4t + v <-> token chunk_token(t, 4*g4 + v).
-  u32x4 pb;
   float psum = 0.f;
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-#pragma unroll
-    for (int v = 0; v < 4; v += 2) {
-      float p0 = __builtin_amdgcn_exp2f(x[t][v] - m_use);
-      float p1 = __builtin_amdgcn_exp2f(x[t][v + 1] - m_use);
-      uint32_t b0 = float_to_bf16_bits(p0), b1 = float_to_bf16_bits(p1);
-      psum += bf16_bits_to_float(b0) + bf16_bits_to_float(b1);
-      pb[2 * t + v / 2] = b0 | (b1 << 16);
-    }
+  for (int i = 0; i < N; i += 2) {
+    uint32_t b0 = float_to_bf16_bits(__builtin_amdgcn_exp2f(x[i] - m_use));
+    uint32_t b1 = float_to_bf16_bits(__builtin_amdgcn_exp2f(x[i + 1] - m_use));
+    psum += bf16_bits_to_float(b0) + bf16_bits_to_float(b1);
+    pb[i / 2] = b0 | (b1 << 16);
   }
   st.l = st.l * alpha + psum;
 #pragma unroll
   for (int nt = 0; nt < 12; ++nt) st.acc[nt] *= alpha;
+}
 
-  // LDS writes above are from other lanes of this wave; LDS executes a wave's
-  // operations in order, so only compiler reordering must be prevented.
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-  const bf16x8 pbv = __builtin_bit_cast(bf16x8, pb);
+// Compute one chunk from its LDS stage (K at +0, V at +kStageBytes).
+template <bool kFp8>
+__device__ __forceinline__ void compute_chunk(const uint8_t* stage, uint32_t vbits,
+                                              const u32x4 (&qreg)[6], float qk_scale_log2,
+                                              int lane, RowState& st) {
+  using C = Cfg<kFp8>;
+  const int i16 = lane & 15, g4 = lane >> 4;
+  const SDA_LDS uint8_t* kl = (const SDA_LDS uint8_t*)stage;
+  // S^T: rows = token slots 16t + 4*g4 + v, columns = heads.  Lane (i16, g4)
+  // reads K of token slot 16t + i16, pieces 4u + g4 (8 bf16 dims per k-slice,
+  // or 16 FP8 dims feeding two k-slices).
+  constexpr int kT = kFp8 ? 2 : 1;
+  f32x4 s[kT];
 #pragma unroll
-  for (int nt = 0; nt < 12; ++nt) {
-    const uint16_t* col = &s_vw[0][16 * nt + i16];
-    u32x4 a;
+  for (int t = 0; t < kT; ++t) {
+    const int row = 16 * t + i16;
+    const int f = swz_k<kFp8>(row);
+    const SDA_LDS uint8_t* kr = kl + row * C::kVBytes;
+    u32x4 kw[kFp8 ? 3 : 6];
 #pragma unroll
-    for (int e = 0; e < 8; e += 2) {
-      int t = e >> 2, v = e & 3;
-      uint32_t lo = col[(size_t)(16 * t + 4 * v + g4) * kVStride];
-      uint32_t hi = col[(size_t)(16 * t + 4 * (v + 1) + g4) * kVStride];
-      a[e >> 1] = lo | (hi << 16);
+    for (int u = 0; u < (kFp8 ? 3 : 6); ++u)
+      kw[u] = *(const SDA_LDS u32x4*)(kr + 16 * ((4 * u + g4) ^ f));
+    f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int cc = 0; cc < 6; ++cc) {
+      u32x4 k;
+      if (kFp8) {
+        u32x4 w = kw[cc >> 1];
+        u32x2 c0 = fp8x4_to_bf16(w[(cc & 1) * 2 + 0]);
+        u32x2 c1 = fp8x4_to_bf16(w[(cc & 1) * 2 + 1]);
+        k = u32x4{c0[0], c0[1], c1[0], c1[1]};
+      } else {
+        k = kw[cc];
+      }
+      a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k),
+                                                  __builtin_bit_cast(bf16x8, qreg[cc]), a, 0, 0,
+                                                  0);
     }
-    st.acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), pbv,
-                                                         st.acc[nt], 0, 0, 0);
+    s[t] = a;
   }
+  // Validity of token rows: lanes 0..15 loaded rows 0..15 of each tile.
+  float x[4 * kT];
+#pragma unroll
+  for (int t = 0; t < kT; ++t) {
+    const uint64_t vb = __ballot((vbits >> t) & 1u);
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+      x[4 * t + v] = ((vb >> (4 * g4 + v)) & 1) ? s[t][v] * qk_scale_log2 : -INFINITY;
+  }
+  uint32_t pb[2 * kT];
+  softmax_step<4 * kT>(x, st, pb);
 
-  // The next chunk's LDS writes must not move above these reads.
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // O^T += V^T . P^T over the 12 dim tiles.
+  const SDA_LDS uint8_t* lds = kl + kStageBytes;
+  if (kFp8) {
+    // tr8: lane 16*g4 + m reads 8 bytes of token row 16*(y>>2)+4*g4+(y&3), y = m>>1,
+    // at V byte 16*nt + 8*(m&1); it receives byte (lane&15) of 8 rows.
+    const int m = lane & 15, y = m >> 1, h = m & 1;
+    const int row = 16 * (y >> 2) + 4 * g4 + (y & 3);
+    const int f = swz<true>(row);
+    const SDA_LDS uint8_t* base = lds + row * Cfg<true>::kVBytes + 8 * h;
+    const bf16x8 pv = __builtin_bit_cast(bf16x8, u32x4{pb[0], pb[1], pb[2], pb[3]});
+#pragma unroll
+    for (int nt = 0; nt < 12; ++nt) {
+      const int piece = (nt & ~3) | ((nt & 3) ^ f);
+      i32x2 raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32((SDA_LDS i32x2*)(base + 16 * piece));
+      u32x2 c0 = fp8x4_to_bf16((uint32_t)raw[0]);
+      u32x2 c1 = fp8x4_to_bf16((uint32_t)raw[1]);
+      u32x4 a = u32x4{c0[0], c0[1], c1[0], c1[1]};
+      st.acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), pv,
+                                                           st.acc[nt], 0, 0, 0);
+    }
+  } else {
+    // tr16: lane 16*g4 + 4y + q reads 4 bf16 of token row 4*g4 + y at dims
+    // 16*nt + 4q; it receives dim 16*nt + (lane&15) of the 4 rows.
+    const int y = (lane >> 2) & 3, q = lane & 3;
+    const int row = 4 * g4 + y;
+    const int f = swz<false>(row) ^ (q >> 1);
+    const SDA_LDS uint8_t* base = lds + row * Cfg<false>::kVBytes + 8 * (q & 1);
+    const bf16x4 pv = __builtin_bit_cast(bf16x4, u32x2{pb[0], pb[1]});
+#pragma unroll
+    for (int nt = 0; nt < 12; ++nt) {
+      const int piece = ((2 * nt) & ~7) | (((2 * nt) & 7) ^ f);
+      bf16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SDA_LDS bf16x4*)(base + 16 * piece));
+      st.acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pv, st.acc[nt], 0, 0, 0);
+    }
+  }
 }
 
 __device__ __forceinline__ void store_row_pair(const Params& p, int r, int h, int d, float o0,
@@ -271,29 +353,37 @@ __device__ __forceinline__ void store_row_pair(const Params& p, int r, int h, in
   *reinterpret_cast<uint32_t*>(p.out + (int64_t)r * p.ors + (int64_t)h * p.ohs + d) = v;
 }
 
-__device__ __forceinline__ void clear_row(const Params& p, int r) {
-  for (int e = threadIdx.x; e < p.heads * (kDim / 2); e += kThreads) {
+__device__ __forceinline__ void clear_row(const Params& p, int r, int tid, int nthreads) {
+  for (int e = tid; e < p.heads * (kDim / 2); e += nthreads) {
     int h = e / (kDim / 2), d = 2 * (e - h * (kDim / 2));
     *reinterpret_cast<uint32_t*>(p.out + (int64_t)r * p.ors + (int64_t)h * p.ohs + d) = 0u;
   }
 }
 
-template <bool kFp8, bool kFused>
+// Runs step(i0, 0), step(i0, 1), ... with compile-time stage indices while
+// they return true.
+template <typename F, int... Ss>
+__device__ __forceinline__ bool run_steps(F& step, int i0, std::integer_sequence<int, Ss...>) {
+  return (step(i0, std::integral_constant<int, Ss>{}) && ...);
+}
+
+template <bool kFp8, bool kFused, bool kUni>
 __global__ __launch_bounds__(kThreads) void split_kernel(const Params p) {
+  using C = Cfg<kFp8>;
   const int r = blockIdx.x;
   const int split = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
   __shared__ int64_t s_base[kMaxRegions];
   __shared__ int s_n[kMaxRegions];
-  __shared__ __attribute__((aligned(16))) uint16_t s_v[kWaves][kChunk][kVStride];
+  __shared__ __attribute__((aligned(1024))) uint8_t s_stage[kWaves][kStages][kChunkBytes];
   __shared__ int s_cnt[kWaves];
   __shared__ float s_m[kWaves][16];
   __shared__ float s_l[kWaves][16];
 
   if (!p.active[r]) {
     // Inactive rows read nothing else.  With splits > 1 the combine clears.
-    if (kFused && p.clear) clear_row(p, r);
+    if (kFused && p.clear) clear_row(p, r, tid, kThreads);
     return;
   }
 
@@ -353,18 +443,21 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const Params p) {
   }
   __syncthreads();
 
-  // Q^T B-operand: lane holds head (lane & 15), 8 dims per k-slice.
+  // Q^T B-operand: lane holds head (lane & 15), 8 dims per k-slice, in the
+  // same dim order as the K loads.
   const int i16 = lane & 15, g4 = lane >> 4;
   u32x4 qreg[6];
   {
     const uint16_t* qrow = p.q + (int64_t)r * p.qrs + (int64_t)i16 * p.qhs;
 #pragma unroll
     for (int cc = 0; cc < 6; ++cc) {
-      if (i16 < p.heads)
-        qreg[cc] = *reinterpret_cast<const u32x4*>(qrow + slice_dim<kFp8>(cc, g4));
-      else
-        qreg[cc] = u32x4{0, 0, 0, 0};
+      int d = kFp8 ? 64 * (cc >> 1) + 16 * g4 + 8 * (cc & 1) : 32 * cc + 8 * g4;
+      qreg[cc] = i16 < p.heads ? *reinterpret_cast<const u32x4*>(qrow + d) : u32x4{0, 0, 0, 0};
     }
+    // Consume Q here, so the compiler's wait for these loads sits before the
+    // pipeline rather than inside it.
+#pragma unroll
+    for (int cc = 0; cc < 6; ++cc) __asm__ __volatile__("" : "+v"(qreg[cc]));
   }
   const float kscale = kFp8 ? *p.k_scale : 1.0f;
   const float qk_scale_log2 = p.scale * kscale * 1.4426950408889634f;
@@ -375,32 +468,50 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const Params p) {
   st.m = -INFINITY;
   st.l = 0.f;
 
-  const int nchunks = (int)(((int64_t)nreg * rt + kChunk - 1) / kChunk);
-  uint16_t(*s_vw)[kVStride] = s_v[wave];
+  const int nchunks = (int)(((int64_t)nreg * rt + C::kTok - 1) / C::kTok);
+  const uint8_t* my_stage = &s_stage[wave][0][0];
+  const uint32_t my_stage_lds = lds_addr(my_stage);
 
-  // Software pipeline: chunk c+kWaves is in flight while chunk c is computed.
-  ChunkRegs<kFp8> ra, rb;
-  int c = wave;
-  if (c < nchunks) issue_chunk<kFp8>(p, c, nreg, s_base, s_n, lane, ra);
-  while (c < nchunks) {
-    int cn = c + kWaves;
-    if (cn < nchunks) issue_chunk<kFp8>(p, cn, nreg, s_base, s_n, lane, rb);
-    compute_chunk<kFp8>(ra, qreg, qk_scale_log2, s_vw, lane, st);
-    c = cn;
-    if (c >= nchunks) break;
-    cn = c + kWaves;
-    if (cn < nchunks) issue_chunk<kFp8>(p, cn, nreg, s_base, s_n, lane, ra);
-    compute_chunk<kFp8>(rb, qreg, qk_scale_log2, s_vw, lane, st);
-    c = cn;
+  // kStages-deep per-wave pipeline over LDS stages: iteration i (chunk
+  // c = wave + 4i) computes stage i % kStages while the next kStages-1 chunks
+  // are in flight.  Every iteration issues exactly one chunk (12 DMA
+  // instructions), so chunk i has landed once at most 12*(kStages-1) are
+  // outstanding.  Past the last chunk the issue repeats the last one
+  // (clamped, in bounds, never computed).
+  if (wave < nchunks) {
+    const int last = nchunks - 1;
+    uint32_t vb[kStages];
+#pragma unroll
+    for (int s = 0; s < kStages - 1; ++s)
+      vb[s] = issue_chunk<kFp8, kUni>(p, min(wave + kWaves * s, last), nreg, s_base, s_n, lane,
+                                      my_stage_lds + s * kChunkBytes);
+    auto step = [&](int i0, auto stage_c) -> bool {
+      constexpr int S = decltype(stage_c)::value;
+      constexpr int SN = (S + kStages - 1) % kStages;
+      const int c = wave + kWaves * (i0 + S);
+      if (c >= nchunks) return false;
+      // Stage SN was last read by the previous iteration, whose reads all
+      // completed before its MFMAs; the asm below keeps them above the DMA.
+      vb[SN] = issue_chunk<kFp8, kUni>(p, min(c + kWaves * (kStages - 1), last), nreg, s_base,
+                                       s_n, lane, my_stage_lds + SN * kChunkBytes);
+      wait_vmcnt<12 * (kStages - 1)>();
+      compute_chunk<kFp8>(my_stage + S * kChunkBytes, vb[S], qreg, qk_scale_log2, lane, st);
+      return true;
+    };
+    for (int i0 = 0;; i0 += kStages)
+      if (!run_steps(step, i0, std::make_integer_sequence<int, kStages>{})) break;
+    // Repeated issues past the end may still be in flight: drain them before
+    // the stage memory is reused below.
+    wait_vmcnt<0>();
   }
 
   // Merge the 4 waves.  The per-lane sums of a head live in its 4 lane groups.
   float l = st.l;
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
-  __syncthreads();  // every wave is done with s_v
-  float* s_acc = reinterpret_cast<float*>(&s_v[0][0][0]);  // [kWaves][16][kAccStride]
-  static_assert(sizeof(s_v) >= sizeof(float) * kWaves * 16 * kAccStride, "merge area");
+  __syncthreads();  // every wave is done with its stages
+  float* s_acc = reinterpret_cast<float*>(&s_stage[0][0][0]);  // [kWaves][16][kAccStride]
+  static_assert(sizeof(s_stage) >= sizeof(float) * kWaves * 16 * kAccStride, "merge area");
 #pragma unroll
   for (int nt = 0; nt < 12; ++nt) {
     float* dst = s_acc + ((size_t)wave * 16 + i16) * kAccStride + 16 * nt + 4 * g4;
@@ -448,62 +559,68 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const Params p) {
   }
 }
 
-__global__ __launch_bounds__(kThreads) void combine_kernel(const Params p) {
-  const int r = blockIdx.x;
+// One 64-thread workgroup per (row, head): 3 dims per thread.
+__global__ __launch_bounds__(64) void combine_kernel(const Params p) {
+  const int r = blockIdx.x / p.heads;
+  const int h = blockIdx.x - r * p.heads;
+  const int tid = threadIdx.x;
+  uint16_t* orow = p.out + (int64_t)r * p.ors + (int64_t)h * p.ohs;
   if (!p.active[r]) {
-    if (p.clear) clear_row(p, r);
+    if (p.clear)
+      for (int d = tid; d < kDim; d += 64) orow[d] = 0;
     return;
   }
-  const int g = r % p.groups;
-  for (int e = threadIdx.x; e < p.heads * (kDim / 2); e += kThreads) {
-    int h = e / (kDim / 2), d = 2 * (e - h * (kDim / 2));
-    const int64_t ph0 = (int64_t)r * p.splits * p.heads + h;
-    float M = -INFINITY;
-    for (int s = 0; s < p.splits; ++s) M = fmaxf(M, p.lse[ph0 + (int64_t)s * p.heads]);
-    float o0 = 0.f, o1 = 0.f;
-    if (M != -INFINITY) {
-      float W = 0.f;
-      for (int s = 0; s < p.splits; ++s) {
-        int64_t ph = ph0 + (int64_t)s * p.heads;
-        float w = __builtin_amdgcn_exp2f(p.lse[ph] - M);
-        float2 v = *reinterpret_cast<const float2*>(p.partial + ph * kDim + d);
-        W += w;
-        o0 += w * v.x;
-        o1 += w * v.y;
-      }
-      o0 /= W;
-      o1 /= W;
+  const int64_t ph0 = (int64_t)r * p.splits * p.heads + h;
+  float M = -INFINITY;
+  for (int s = 0; s < p.splits; ++s) M = fmaxf(M, p.lse[ph0 + (int64_t)s * p.heads]);
+  float o[3] = {0.f, 0.f, 0.f};
+  if (M != -INFINITY) {
+    float W = 0.f;
+    for (int s = 0; s < p.splits; ++s) {
+      const int64_t ph = ph0 + (int64_t)s * p.heads;
+      const float w = __builtin_amdgcn_exp2f(p.lse[ph] - M);
+      const float* src = p.partial + ph * kDim;
+      W += w;
+#pragma unroll
+      for (int u = 0; u < 3; ++u) o[u] += w * src[tid + 64 * u];
     }
-    if (p.gated) {
-      float gv = gate_value(p.gate, (int64_t)(r / p.groups) * p.grs +
-                                        (int64_t)(g * p.heads + h) * p.ghs);
-      o0 *= gv;
-      o1 *= gv;
-    }
-    store_row_pair(p, r, h, d, o0, o1);
+#pragma unroll
+    for (int u = 0; u < 3; ++u) o[u] /= W;
   }
+  float gv = 1.0f;
+  if (p.gated)
+    gv = gate_value(p.gate, (int64_t)(r / p.groups) * p.grs +
+                                (int64_t)((r % p.groups) * p.heads + h) * p.ghs);
+#pragma unroll
+  for (int u = 0; u < 3; ++u) orow[tid + 64 * u] = (uint16_t)float_to_bf16_bits(o[u] * gv);
+}
+
+template <bool kFp8, bool kFused, bool kUni>
+void launch_split(const Params& p, hipStream_t stream) {
+  hipLaunchKernelGGL((split_kernel<kFp8, kFused, kUni>), dim3((unsigned)p.rows, (unsigned)p.splits),
+                     dim3(kThreads), 0, stream, p);
+}
+
+template <bool kFp8>
+void launch_dtype(const Params& p, hipStream_t stream) {
+  const bool fused = p.splits == 1;
+  const bool uni = p.rt % Cfg<kFp8>::kTok == 0;
+  if (fused)
+    uni ? launch_split<kFp8, true, true>(p, stream) : launch_split<kFp8, true, false>(p, stream);
+  else
+    uni ? launch_split<kFp8, false, true>(p, stream) : launch_split<kFp8, false, false>(p, stream);
 }
 
 }  // namespace
 
 hipError_t launch(const Params& p, bool fp8, hipStream_t stream) {
-  dim3 grid((unsigned)p.rows, (unsigned)p.splits);
-  dim3 block(kThreads);
-  const bool fused = p.splits == 1;
-  if (fp8) {
-    if (fused)
-      hipLaunchKernelGGL((split_kernel<true, true>), grid, block, 0, stream, p);
-    else
-      hipLaunchKernelGGL((split_kernel<true, false>), grid, block, 0, stream, p);
-  } else {
-    if (fused)
-      hipLaunchKernelGGL((split_kernel<false, true>), grid, block, 0, stream, p);
-    else
-      hipLaunchKernelGGL((split_kernel<false, false>), grid, block, 0, stream, p);
-  }
+  if (fp8)
+    launch_dtype<true>(p, stream);
+  else
+    launch_dtype<false>(p, stream);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || fused) return e;
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)p.rows), block, 0, stream, p);
+  if (e != hipSuccess || p.splits == 1) return e;
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)(p.rows * p.heads)), dim3(64), 0, stream, p);
   return hipGetLastError();
 }
 
