@@ -28,6 +28,9 @@ HIPCC_FLAGS = [
     # The gate's fp32 division must be correctly rounded.
     "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-fno-fast-math",
+    # MFMA accumulators stay in arch VGPRs: the online-softmax state is loop
+    # carried and rescaled by VALU, so AGPR accumulators cost a copy per chunk.
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I" + INCLUDE,
     "-I" + CSRC,
 ]

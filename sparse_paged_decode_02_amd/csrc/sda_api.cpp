@@ -15,11 +15,14 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 // Split count for `rows` rows on MI355X.  The page "vllm.models.step5.nvidia.
 // ops.sparse_decode_attention" (`sparse_decode_splits`) doubles the split
-// count while rows*splits*2 <= 256, i.e. it sizes the grid for about 1.7 waves
-// of B300 programs, up to 32 splits.  The same rule with the target raised to
-// kTargetPrograms = 512 sizes the grid for 256 compute units.  One 256-thread
-// workgroup per (row, split) and two workgroups resident per CU give 512 slots.
-constexpr int kTargetPrograms = 512;
+// count while rows*splits*2 <= 256, up to 32 splits.  On B300 that sizes the
+// grid for about 1.7 waves of programs.  Here one split workgroup (256
+// threads, ~157 KiB of LDS) occupies a whole compute unit, so the target is
+// one workgroup per CU: double while the doubled grid rows*splits*2 still
+// fits the 256 CUs.  That is the page's rule and bound, for a different
+// reason.  Measured on the bf16 gated workload (256 rows): 1 split 75 us,
+// 2 splits 86 us.
+constexpr int kComputeUnits = 256;
 constexpr int kMaxHeuristicSplits = 32;
 
 }  // namespace
@@ -33,7 +36,7 @@ size_t sda_args_size(void) { return sizeof(sda_decode_args); }
 int sda_splits(int rows) {
   int splits = 1;
   if (rows <= 0) return 1;
-  while (splits < kMaxHeuristicSplits && (int64_t)rows * splits * 2 <= kTargetPrograms) splits *= 2;
+  while (splits < kMaxHeuristicSplits && (int64_t)rows * splits * 2 <= kComputeUnits) splits *= 2;
   return splits;
 }
 
@@ -87,6 +90,9 @@ int sda_decode(const sda_decode_args* a, hipStream_t stream) {
       (a->c_token_stride * esz) % 16)
     return SDA_ERR_UNSUPPORTED;
   if (!aligned(a->output, 4) || a->o_row_stride % 2 || a->o_head_stride % 2)
+    return SDA_ERR_UNSUPPORTED;
+  // Token rows of one page are addressed with 32-bit byte offsets.
+  if (a->c_token_stride < 0 || (int64_t)a->block * a->c_token_stride * esz + 2 * SDA_KV_ROW > 0xFFFFFFFFll)
     return SDA_ERR_UNSUPPORTED;
 
   sda::Params p{};

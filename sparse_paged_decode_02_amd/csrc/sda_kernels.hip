@@ -125,14 +125,88 @@ __device__ __forceinline__ int swz_k(int row) {
   return kFp8 ? (row >> 1) & 3 : row & 7;
 }
 
-// One 16-byte LDS-DMA per lane: global src -> LDS (lds_addr + 16 * lane).
-// Issued from inline assembly so that the compiler does not tie later LDS
-// reads to it; completion is awaited explicitly with wait_vmcnt.
-__device__ __forceinline__ void dma16(const void* src, uint32_t lds_addr) {
-  __asm__ __volatile__("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-                       :
-                       : "v"(src), "s"(lds_addr)
-                       : "memory", "m0");
+// One chunk's 12 LDS-DMAs (global_load_lds_dwordx4: each lane moves 16 bytes
+// to LDS address M0 + 16 * lane).  K pieces land at stage + 1024*j, V pieces
+// at stage + 6144 + 1024*j, j = 0..5.  Issued from inline assembly so that
+// the compiler does not tie later LDS reads to them; completion is awaited
+// with wait_vmcnt.  M0 is saved and restored around the block.
+//
+// dma_chunk_sbase: one uniform 64-bit base (SGPRs) plus 32-bit per-lane
+// byte offsets (kUni chunks, all tokens in one region).
+__device__ __forceinline__ void dma_chunk_sbase(const uint8_t* base, uint32_t stage,
+                                                const uint32_t (&ko)[6],
+                                                const uint32_t (&vo)[6]) {
+  uint32_t saved;
+  __asm__ __volatile__(
+      "s_mov_b32 %[sv], m0\n\t"
+      "s_mov_b32 m0, %[st]\n\t"
+      "global_load_lds_dwordx4 %[k0], %[b]\n\t"
+      "s_add_u32 m0, m0, 0x400\n\t"
+      "global_load_lds_dwordx4 %[k1], %[b]\n\t"
+      "s_add_u32 m0, m0, 0x400\n\t"
+      "global_load_lds_dwordx4 %[k2], %[b]\n\t"
+      "s_add_u32 m0, m0, 0x400\n\t"
+      "global_load_lds_dwordx4 %[k3], %[b]\n\t"
+      "s_add_u32 m0, m0, 0x400\n\t"
+      "global_load_lds_dwordx4 %[k4], %[b]\n\t"
+      "s_add_u32 m0, m0, 0x400\n\t"
+      "global_load_lds_dwordx4 %[k5], %[b]\n\t"
+      "s_add_u32 m0, m0, 0x400\n\t"
+      "global_load_lds_dwordx4 %[v0], %[b]\n\t"
+      "s_add_u32 m0, m0, 0x400\n\t"
+      "global_load_lds_dwordx4 %[v1], %[b]\n\t"
+      "s_add_u32 m0, m0, 0x400\n\t"
+      "global_load_lds_dwordx4 %[v2], %[b]\n\t"
+      "s_add_u32 m0, m0, 0x400\n\t"
+      "global_load_lds_dwordx4 %[v3], %[b]\n\t"
+      "s_add_u32 m0, m0, 0x400\n\t"
+      "global_load_lds_dwordx4 %[v4], %[b]\n\t"
+      "s_add_u32 m0, m0, 0x400\n\t"
+      "global_load_lds_dwordx4 %[v5], %[b]\n\t"
+      "s_mov_b32 m0, %[sv]"
+      : [sv] "=&s"(saved)
+      : [st] "s"(stage), [b] "s"(base), [k0] "v"(ko[0]), [k1] "v"(ko[1]), [k2] "v"(ko[2]),
+        [k3] "v"(ko[3]), [k4] "v"(ko[4]), [k5] "v"(ko[5]), [v0] "v"(vo[0]), [v1] "v"(vo[1]),
+        [v2] "v"(vo[2]), [v3] "v"(vo[3]), [v4] "v"(vo[4]), [v5] "v"(vo[5])
+      : "memory");
+}
+
+// dma_chunk_vaddr: per-lane 64-bit addresses (chunks spanning regions).
+__device__ __forceinline__ void dma_chunk_vaddr(uint32_t stage, const uint8_t* const (&ka)[6],
+                                                const uint8_t* const (&va)[6]) {
+  uint32_t saved;
+  __asm__ __volatile__(
+      "s_mov_b32 %[sv], m0\n\t"
+      "s_mov_b32 m0, %[st]\n\t"
+      "global_load_lds_dwordx4 %[k0], off\n\t"
+      "s_add_u32 m0, m0, 0x400\n\t"
+      "global_load_lds_dwordx4 %[k1], off\n\t"
+      "s_add_u32 m0, m0, 0x400\n\t"
+      "global_load_lds_dwordx4 %[k2], off\n\t"
+      "s_add_u32 m0, m0, 0x400\n\t"
+      "global_load_lds_dwordx4 %[k3], off\n\t"
+      "s_add_u32 m0, m0, 0x400\n\t"
+      "global_load_lds_dwordx4 %[k4], off\n\t"
+      "s_add_u32 m0, m0, 0x400\n\t"
+      "global_load_lds_dwordx4 %[k5], off\n\t"
+      "s_add_u32 m0, m0, 0x400\n\t"
+      "global_load_lds_dwordx4 %[v0], off\n\t"
+      "s_add_u32 m0, m0, 0x400\n\t"
+      "global_load_lds_dwordx4 %[v1], off\n\t"
+      "s_add_u32 m0, m0, 0x400\n\t"
+      "global_load_lds_dwordx4 %[v2], off\n\t"
+      "s_add_u32 m0, m0, 0x400\n\t"
+      "global_load_lds_dwordx4 %[v3], off\n\t"
+      "s_add_u32 m0, m0, 0x400\n\t"
+      "global_load_lds_dwordx4 %[v4], off\n\t"
+      "s_add_u32 m0, m0, 0x400\n\t"
+      "global_load_lds_dwordx4 %[v5], off\n\t"
+      "s_mov_b32 m0, %[sv]"
+      : [sv] "=&s"(saved)
+      : [st] "s"(stage), [k0] "v"(ka[0]), [k1] "v"(ka[1]), [k2] "v"(ka[2]), [k3] "v"(ka[3]),
+        [k4] "v"(ka[4]), [k5] "v"(ka[5]), [v0] "v"(va[0]), [v1] "v"(va[1]), [v2] "v"(va[2]),
+        [v3] "v"(va[3]), [v4] "v"(va[4]), [v5] "v"(va[5])
+      : "memory");
 }
 
 template <int N>
@@ -193,35 +267,86 @@ __device__ __forceinline__ ChunkCtx chunk_ctx(const Params& p, int c, const int6
   return cx;
 }
 
-// Issue chunk c into one LDS stage: 6 K and 6 V DMAs of 16 bytes per lane.
-// Stage slot 64j + lane (j = 0..5) is token row r = slot / kPieces, piece
-// position slot % kPieces, which holds global piece (position ^ swizzle(r)).
-// Returns the visibility of this lane's S^T rows (token slots 16t + i16).
-template <bool kFp8, bool kUni>
-__device__ __forceinline__ uint32_t issue_chunk(const Params& p, int c, int nreg,
-                                                const int64_t* s_base, const int* s_n, int lane,
-                                                uint32_t stage) {
+// Loop-invariant DMA geometry of one lane.  Stage slot 64j + lane (j = 0..5)
+// is token row r = slot / kPieces, piece position slot % kPieces, which holds
+// global piece (position ^ swizzle(r)).  koff/voff are that piece's byte
+// offsets within the token's cache row (V after the 192 K elements).
+struct LaneDma {
+  int row[6];
+  uint32_t koff[6], voff[6];
+};
+
+template <bool kFp8>
+__device__ __forceinline__ LaneDma lane_dma(int lane) {
   using C = Cfg<kFp8>;
-  const int i16 = lane & 15;
-  const ChunkCtx cx = chunk_ctx<kFp8, kUni>(p, c, s_base, s_n);
-  uint32_t vbits = 0;
-#pragma unroll
-  for (int t = 0; t < (kFp8 ? 2 : 1); ++t) {
-    bool valid;
-    (void)token_elem<kFp8, kUni>(p, cx, 16 * t + i16, s_base, s_n, nreg, valid);
-    vbits |= (valid ? 1u : 0u) << t;
-  }
-  const uint32_t st = __builtin_amdgcn_readfirstlane(stage);
+  LaneDma d;
 #pragma unroll
   for (int j = 0; j < 6; ++j) {
     const int slot = 64 * j + lane;
     const int r = slot / C::kPieces;
     const int pos = slot - r * C::kPieces;
-    bool valid;
-    const int64_t e = token_elem<kFp8, kUni>(p, cx, r, s_base, s_n, nreg, valid);
-    const uint8_t* row = p.cache + e * C::kEsz;
-    dma16(row + 16 * (pos ^ swz_k<kFp8>(r)), st + 1024 * j);
-    dma16(row + C::kVBytes + 16 * (pos ^ swz<kFp8>(r)), st + kStageBytes + 1024 * j);
+    d.row[j] = r;
+    d.koff[j] = 16u * (uint32_t)(pos ^ swz_k<kFp8>(r));
+    d.voff[j] = (uint32_t)C::kVBytes + 16u * (uint32_t)(pos ^ swz<kFp8>(r));
+  }
+  return d;
+}
+
+// Issue chunk c into LDS stage `stage`.  Returns the visibility of this
+// lane's S^T rows (bit t: token slot 16t + i16).  Masked slots load the first
+// token of their region instead (visible, in bounds, weight 0).
+template <bool kFp8, bool kUni>
+__device__ __forceinline__ uint32_t issue_chunk(const Params& p, int c, int nreg,
+                                                const int64_t* s_base, const int* s_n, int lane,
+                                                uint32_t stage, const LaneDma& ld,
+                                                uint32_t cts_bytes) {
+  using C = Cfg<kFp8>;
+  const int i16 = lane & 15;
+  const uint32_t st = (uint32_t)__builtin_amdgcn_readfirstlane(stage);
+  uint32_t vbits = 0;
+  if (kUni) {
+    // The chunk lies inside one region: uniform base, 32-bit lane offsets.
+    const int slot0 = c * C::kTok;
+    const int k = slot0 / p.rt;
+    const int off0 = slot0 - k * p.rt;
+    const int64_t rb = s_base[k];
+    const int nval = __builtin_amdgcn_readfirstlane(s_n[k]);
+    // readfirstlane returns int: go through uint32_t so the low half is
+    // zero-extended, never sign-extended into the high half.
+    const uint64_t b64 = (uint64_t)(uintptr_t)(p.cache + rb * C::kEsz);
+    const uint32_t b_lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b64);
+    const uint32_t b_hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b64 >> 32));
+    const uint64_t base = ((uint64_t)b_hi << 32) | (uint64_t)b_lo;
+#pragma unroll
+    for (int t = 0; t < (kFp8 ? 2 : 1); ++t) vbits |= (off0 + 16 * t + i16 < nval ? 1u : 0u) << t;
+    uint32_t ko[6], vo[6];
+#pragma unroll
+    for (int j = 0; j < 6; ++j) {
+      const int tok = off0 + ld.row[j];
+      const uint32_t roff = tok < nval ? (uint32_t)tok * cts_bytes : 0u;
+      ko[j] = roff + ld.koff[j];
+      vo[j] = roff + ld.voff[j];
+    }
+    dma_chunk_sbase((const uint8_t*)(uintptr_t)base, st, ko, vo);
+  } else {
+    const ChunkCtx cx = chunk_ctx<kFp8, false>(p, c, s_base, s_n);
+#pragma unroll
+    for (int t = 0; t < (kFp8 ? 2 : 1); ++t) {
+      bool valid;
+      (void)token_elem<kFp8, false>(p, cx, 16 * t + i16, s_base, s_n, nreg, valid);
+      vbits |= (valid ? 1u : 0u) << t;
+    }
+    const uint8_t* ka[6];
+    const uint8_t* va[6];
+#pragma unroll
+    for (int j = 0; j < 6; ++j) {
+      bool valid;
+      const int64_t e = token_elem<kFp8, false>(p, cx, ld.row[j], s_base, s_n, nreg, valid);
+      const uint8_t* row = p.cache + e * C::kEsz;
+      ka[j] = row + ld.koff[j];
+      va[j] = row + ld.voff[j];
+    }
+    dma_chunk_vaddr(st, ka, va);
   }
   return vbits;
 }
@@ -232,8 +357,15 @@ struct RowState {
   float l;        // this lane's part of the running sum
 };
 
-// Online-softmax update from this lane's logits x[] (already scaled, masked
-// to -inf); returns the rescale factor and writes p (bf16-rounded) into pb.
+// Online-softmax update from this lane's logits x[] (already scaled to base-2
+// units and masked to -inf).  The running max is raised only when some head
+// of the wave sees a logit more than kLazyRescale above it.  Otherwise the
+// stale max is kept, which only means p <= 2^kLazyRescale (exact up to
+// rounding), and the rescale of the 48 accumulators is skipped.  p is
+// rounded to bf16 for the P.V product, and the running sum adds the rounded
+// values.
+constexpr float kLazyRescale = 8.0f;
+
 template <int N>
 __device__ __forceinline__ void softmax_step(float (&x)[N], RowState& st, uint32_t (&pb)[N / 2]) {
   float mloc = -INFINITY;
@@ -241,21 +373,25 @@ __device__ __forceinline__ void softmax_step(float (&x)[N], RowState& st, uint32
   for (int i = 0; i < N; ++i) mloc = fmaxf(mloc, x[i]);
   mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
   mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-  const float m_new = fmaxf(st.m, mloc);
-  const float m_use = m_new == -INFINITY ? 0.f : m_new;
-  const float alpha = __builtin_amdgcn_exp2f(st.m - m_use);
-  st.m = m_new;
+  if (__ballot(mloc > st.m + kLazyRescale) != 0) {
+    const float m_new = fmaxf(st.m, mloc);
+    const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
+    st.m = m_new;
+    st.l *= alpha;
+#pragma unroll
+    for (int nt = 0; nt < 12; ++nt) st.acc[nt] *= alpha;
+  }
+  const float m_use = st.m == -INFINITY ? 0.f : st.m;
   float psum = 0.f;
 #pragma unroll
   for (int i = 0; i < N; i += 2) {
-    uint32_t b0 = float_to_bf16_bits(__builtin_amdgcn_exp2f(x[i] - m_use));
-    uint32_t b1 = float_to_bf16_bits(__builtin_amdgcn_exp2f(x[i + 1] - m_use));
-    psum += bf16_bits_to_float(b0) + bf16_bits_to_float(b1);
-    pb[i / 2] = b0 | (b1 << 16);
+    bf16x2 pk = {(__bf16)__builtin_amdgcn_exp2f(x[i] - m_use),
+                 (__bf16)__builtin_amdgcn_exp2f(x[i + 1] - m_use)};
+    const uint32_t w = __builtin_bit_cast(uint32_t, pk);
+    psum += __uint_as_float(w << 16) + __uint_as_float(w & 0xFFFF0000u);
+    pb[i / 2] = w;
   }
-  st.l = st.l * alpha + psum;
-#pragma unroll
-  for (int nt = 0; nt < 12; ++nt) st.acc[nt] *= alpha;
+  st.l += psum;
 }
 
 // Compute one chunk from its LDS stage (K at +0, V at +kStageBytes).
@@ -368,7 +504,9 @@ __device__ __forceinline__ bool run_steps(F& step, int i0, std::integer_sequence
 }
 
 template <bool kFp8, bool kFused, bool kUni>
-__global__ __launch_bounds__(kThreads) void split_kernel(const Params p) {
+// LDS use (stages + region list) allows one workgroup, i.e. one wave per SIMD.
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void split_kernel(
+    const Params p) {
   using C = Cfg<kFp8>;
   const int r = blockIdx.x;
   const int split = blockIdx.y;
@@ -480,11 +618,13 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const Params p) {
   // (clamped, in bounds, never computed).
   if (wave < nchunks) {
     const int last = nchunks - 1;
+    const LaneDma ld = lane_dma<kFp8>(lane);
+    const uint32_t cts_bytes = (uint32_t)(p.cts * C::kEsz);
     uint32_t vb[kStages];
 #pragma unroll
     for (int s = 0; s < kStages - 1; ++s)
       vb[s] = issue_chunk<kFp8, kUni>(p, min(wave + kWaves * s, last), nreg, s_base, s_n, lane,
-                                      my_stage_lds + s * kChunkBytes);
+                                      my_stage_lds + s * kChunkBytes, ld, cts_bytes);
     auto step = [&](int i0, auto stage_c) -> bool {
       constexpr int S = decltype(stage_c)::value;
       constexpr int SN = (S + kStages - 1) % kStages;
@@ -493,7 +633,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const Params p) {
       // Stage SN was last read by the previous iteration, whose reads all
       // completed before its MFMAs; the asm below keeps them above the DMA.
       vb[SN] = issue_chunk<kFp8, kUni>(p, min(c + kWaves * (kStages - 1), last), nreg, s_base,
-                                       s_n, lane, my_stage_lds + SN * kChunkBytes);
+                                       s_n, lane, my_stage_lds + SN * kChunkBytes, ld, cts_bytes);
       wait_vmcnt<12 * (kStages - 1)>();
       compute_chunk<kFp8>(my_stage + S * kChunkBytes, vb[S], qreg, qk_scale_log2, lane, st);
       return true;
