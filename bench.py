@@ -33,6 +33,7 @@ KERNEL_SRC = os.path.join(ROOT, "sparse_paged_decode_02_amd", "csrc", "sda_kerne
 
 
 def kernel_hash() -> str:
+    """First 16 hex digits of the kernel source's SHA-256 (ties counters to code)."""
     with open(KERNEL_SRC, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
@@ -61,17 +62,22 @@ def workload_desc(w) -> str:
 
 
 def load_traffic(workload_name: str, splits: int):
-    """Counter-derived HBM bytes per launch, if measured on the current kernel source."""
-    path = os.path.join(ROOT, "profiles", "traffic_%s.json" % workload_name)
+    """Counter-derived HBM bytes per launch from the committed profile summary,
+    or None unless it was measured on the current kernel source and split count."""
+    path = os.path.join(ROOT, "profiles", "split_kernel_%s.md" % workload_name)
     if not os.path.exists(path):
         return None
+    fields = {}
+    for line in open(path):
+        parts = line.strip().split("=")
+        if len(parts) == 2:
+            fields[parts[0].strip()] = parts[1].strip()
+    if fields.get("kernel_sha256_16") != kernel_hash() or fields.get("splits") != str(splits):
+        return None
     try:
-        rec = json.load(open(path))
-    except ValueError:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
         return None
-    if rec.get("kernel_hash") != kernel_hash() or rec.get("splits") != splits:
-        return None
-    return rec.get("bytes_per_launch")
 
 
 def cpu_baseline(inp, gpu_out, rows_sample: int, threads: int):
@@ -117,6 +123,8 @@ def main() -> int:
     ap.add_argument("--splits", type=int, default=0, help="0: the workload's rule")
     ap.add_argument("--cpu-rows", type=int, default=48)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -134,6 +142,17 @@ def main() -> int:
         __graft_entry__.build()
 
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        # A copy of known size: its FETCH_SIZE / WRITE_SIZE counters give the
+        # scale between counter readings and bytes moved.
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "calls": args.steps}), flush=True)
+        return 0
     w = gen.CONFIGS[args.config]
     splits = args.splits or w.splits or B.sda_splits(w.rows)
 
