@@ -515,7 +515,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   __shared__ int64_t s_base[kMaxRegions];
   __shared__ int s_n[kMaxRegions];
   __shared__ __attribute__((aligned(1024))) uint8_t s_stage[kWaves][kStages][kChunkBytes];
-  __shared__ int s_cnt[kWaves];
   __shared__ float s_m[kWaves][16];
   __shared__ float s_l[kWaves][16];
 
@@ -531,58 +530,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   const int rt = p.rt;
   const int32_t* reg = p.regions + (int64_t)r * p.rrs;
 
-  // Pass 1: how many slots are visible (id >= 0 and first token <= pos).
-  int nvis = 0;
-  for (int j0 = 0; j0 < p.R; j0 += kThreads) {
-    int j = j0 + tid;
-    bool vis = false;
-    if (j < p.R) {
-      int id = reg[j];
-      vis = id >= 0 && (int64_t)id * rt <= pos;
-    }
-    nvis += __syncthreads_count(vis);
-  }
-  // Balanced share: split s takes visible ranks [ceil(s*V/S), ceil((s+1)*V/S)).
-  const int lo = (int)(((int64_t)split * nvis + p.splits - 1) / p.splits);
-  const int hi = (int)(((int64_t)(split + 1) * nvis + p.splits - 1) / p.splits);
-  const int nreg = hi - lo;
-
-  // Pass 2: rank the visible slots in slot order; resolve this split's share.
-  int base_rank = 0;
-  for (int j0 = 0; j0 < p.R; j0 += kThreads) {
-    int j = j0 + tid;
-    int id = -1;
-    bool vis = false;
-    if (j < p.R) {
-      id = reg[j];
-      vis = id >= 0 && (int64_t)id * rt <= pos;
-    }
-    uint64_t m = __ballot(vis);
-    __syncthreads();
-    if (lane == 0) s_cnt[wave] = __popcll(m);
-    __syncthreads();
-    int before = base_rank, total = 0;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      int cw = s_cnt[w];
-      before += w < wave ? cw : 0;
-      total += cw;
-    }
-    int k = before + __popcll(m & ((1ull << lane) - 1ull));
-    if (vis && k >= lo && k < hi) {
-      int64_t t0 = (int64_t)id * rt;
-      int64_t col = t0 / p.block;
-      int off0 = (int)(t0 - col * p.block);
-      int64_t page = p.table[(int64_t)req * p.trs + col];
-      s_base[k - lo] = page * p.cps + (int64_t)g * p.cgs + (int64_t)off0 * p.cts;
-      s_n[k - lo] = (int)min((int64_t)rt, (int64_t)pos - t0 + 1);
-    }
-    base_rank += total;
-  }
-  __syncthreads();
-
   // Q^T B-operand: lane holds head (lane & 15), 8 dims per k-slice, in the
-  // same dim order as the K loads.
+  // same dim order as the K loads.  Issued first so that its latency overlaps
+  // the region resolution below.
   const int i16 = lane & 15, g4 = lane >> 4;
   u32x4 qreg[6];
   {
@@ -592,11 +542,51 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       int d = kFp8 ? 64 * (cc >> 1) + 16 * g4 + 8 * (cc & 1) : 32 * cc + 8 * g4;
       qreg[cc] = i16 < p.heads ? *reinterpret_cast<const u32x4*>(qrow + d) : u32x4{0, 0, 0, 0};
     }
-    // Consume Q here, so the compiler's wait for these loads sits before the
-    // pipeline rather than inside it.
-#pragma unroll
-    for (int cc = 0; cc < 6; ++cc) __asm__ __volatile__("" : "+v"(qreg[cc]));
   }
+
+  // Region resolution, done by every wave on its own with no workgroup
+  // barrier.  Each wave ranks the visible slots (id >= 0, first token <= pos)
+  // in slot order, 64 at a time.  It takes this split's balanced share,
+  // ranks [ceil(s*V/S), ceil((s+1)*V/S)), and writes the share's cache
+  // offsets and visible counts to the shared LDS list.  All waves write
+  // identical values, and a wave only ever reads entries after its own
+  // writes (LDS executes a wave's operations in order), so the list is
+  // consistent without synchronisation.
+  int nvis = 0;
+  int id0 = -1;  // the first 64 slots stay in registers for the second pass
+  for (int j0 = 0; j0 < p.R; j0 += 64) {
+    const int j = j0 + lane;
+    const int id = j < p.R ? reg[j] : -1;
+    if (j0 == 0) id0 = id;
+    nvis += __popcll(__ballot(id >= 0 && (int64_t)id * rt <= pos));
+  }
+  const int lo = (int)(((int64_t)split * nvis + p.splits - 1) / p.splits);
+  const int hi = (int)(((int64_t)(split + 1) * nvis + p.splits - 1) / p.splits);
+  const int nreg = hi - lo;
+  int base_rank = 0;
+  for (int j0 = 0; j0 < p.R; j0 += 64) {
+    const int j = j0 + lane;
+    const int id = j0 == 0 ? id0 : (j < p.R ? reg[j] : -1);
+    const bool vis = id >= 0 && (int64_t)id * rt <= pos;
+    const uint64_t m = __ballot(vis);
+    const int k = base_rank + __popcll(m & ((1ull << lane) - 1ull));
+    if (vis && k >= lo && k < hi) {
+      const int64_t t0 = (int64_t)id * rt;
+      const int64_t col = t0 / p.block;
+      const int off0 = (int)(t0 - col * p.block);
+      const int64_t page = p.table[(int64_t)req * p.trs + col];
+      s_base[k - lo] = page * p.cps + (int64_t)g * p.cgs + (int64_t)off0 * p.cts;
+      s_n[k - lo] = (int)min((int64_t)rt, (int64_t)pos - t0 + 1);
+    }
+    base_rank += __popcll(m);
+  }
+  // The list reads below must follow this wave's own list writes.
+  __asm__ __volatile__("" ::: "memory");
+  // Consume Q here, so the compiler's wait for these loads sits before the
+  // pipeline rather than inside it.
+#pragma unroll
+  for (int cc = 0; cc < 6; ++cc) __asm__ __volatile__("" : "+v"(qreg[cc]));
+
   const float kscale = kFp8 ? *p.k_scale : 1.0f;
   const float qk_scale_log2 = p.scale * kscale * 1.4426950408889634f;
 
@@ -646,15 +636,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   }
 
   // Merge the 4 waves.  The per-lane sums of a head live in its 4 lane groups.
+  // Each wave parks its state in its own (drained) stage memory, so a single
+  // barrier separates the writes from the cross-wave reads.
   float l = st.l;
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
-  __syncthreads();  // every wave is done with its stages
-  float* s_acc = reinterpret_cast<float*>(&s_stage[0][0][0]);  // [kWaves][16][kAccStride]
-  static_assert(sizeof(s_stage) >= sizeof(float) * kWaves * 16 * kAccStride, "merge area");
+  constexpr int kWaveStride = kStages * kChunkBytes / sizeof(float);  // floats between waves
+  static_assert(16 * kAccStride <= kWaveStride, "merge area fits a wave's stages");
+  float* s_acc = reinterpret_cast<float*>(&s_stage[0][0][0]);
 #pragma unroll
   for (int nt = 0; nt < 12; ++nt) {
-    float* dst = s_acc + ((size_t)wave * 16 + i16) * kAccStride + 16 * nt + 4 * g4;
+    float* dst = s_acc + (size_t)wave * kWaveStride + i16 * kAccStride + 16 * nt + 4 * g4;
     *reinterpret_cast<f32x4*>(dst) = st.acc[nt];
   }
   if (g4 == 0) {
@@ -674,7 +666,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) {
         float f = __builtin_amdgcn_exp2f(s_m[w][h] - M);
-        const float* src = s_acc + ((size_t)w * 16 + h) * kAccStride + d;
+        const float* src = s_acc + (size_t)w * kWaveStride + h * kAccStride + d;
         L += s_l[w][h] * f;
         o0 += src[0] * f;
         o1 += src[1] * f;
