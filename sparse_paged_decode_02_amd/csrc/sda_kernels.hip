@@ -11,19 +11,19 @@
 // inactive-row clear.
 //
 // Split kernel: one 256-thread workgroup (4 waves of 64) per (row, split).
-//  * Prologue: the workgroup ranks the row's visible region slots, takes its
-//    balanced share of them, and resolves each region to a cache offset
-//    through the block table.  Only that share's block-table entries are
-//    read.  The offsets go into LDS.
-//  * Main loop: every wave runs its own kStages-deep pipeline over chunks of
-//    token slots (16 tokens for a bf16 cache, 32 for FP8: 6 KiB of V either
-//    way).  For each chunk the wave issues 6 global loads of 16 bytes per
-//    lane, which put K straight into registers in MFMA A-operand layout.
-//    It also issues 6 LDS-DMA loads (global_load_lds_dwordx4), which put V
-//    into a wave-private LDS stage without passing through registers.  Chunk
-//    c is computed while chunks c+1 .. c+kStages-1 are in flight.
+//  * Prologue, per wave and without workgroup barriers: rank the row's
+//    visible region slots with ballots, take the split's balanced share, and
+//    resolve each region to a cache offset through the block table (only the
+//    share's entries are read).  The list goes into LDS.
+//  * Main loop: every wave runs its own 2-stage pipeline over chunks of token
+//    slots (16 tokens for a bf16 cache, 32 for FP8: 6 KiB of K and 6 KiB of
+//    V either way).  A chunk is 12 LDS-DMAs (global_load_lds_dwordx4) into a
+//    wave-private stage.  They are issued from inline assembly and marked
+//    non-temporal (the bytes are read once), and their completion is awaited
+//    with an explicit vmcnt.  Chunk c+4 is in flight while chunk c is
+//    computed:
 //      S^T[tok, head] = K[tok, :] . Q^T[:, head]   v_mfma_f32_16x16x32_bf16
-//      online softmax per head, in the exp2 domain
+//      online softmax per head, in the exp2 domain, with lazy rescaling
 //      O^T[dim, head] += V^T[dim, tok] . P^T[tok, head]
 //    V^T comes from transposing LDS reads (ds_read_b64_tr_b16 for bf16,
 //    ds_read_b64_tr_b8 for FP8).  P^T is the S^T accumulator itself,
@@ -55,7 +55,14 @@ namespace {
 constexpr int kDim = 192;
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kStages = 3;          // LDS stages per wave: 1 computed, 2 in flight
+constexpr int kStages = 2;          // LDS stages per wave: 1 computed, 1 in flight
+#ifndef SDA_PREFETCH_D
+#define SDA_PREFETCH_D 0
+#endif
+// Line-touch prefetch distance (in the wave's chunk sequence) beyond the DMA
+// stages; 0 disables it.
+constexpr int kPrefetchD = SDA_PREFETCH_D;
+constexpr int kOpsPerChunk = 12 + (kPrefetchD > 0 ? 2 : 0);  // vector-memory ops per issue
 constexpr int kStageBytes = 6144;   // K (or V) bytes of one chunk (16 bf16 / 32 FP8 tokens)
 constexpr int kChunkBytes = 2 * kStageBytes;  // one stage: K then V
 constexpr int kAccStride = 196;     // floats per head row in the wave-merge area
@@ -131,81 +138,91 @@ __device__ __forceinline__ int swz_k(int row) {
 // the compiler does not tie later LDS reads to them; completion is awaited
 // with wait_vmcnt.  M0 is saved and restored around the block.
 //
+// Cache policy: K|V bytes are read exactly once, so the DMAs are
+// non-temporal (`nt`).  The exception is FP8 K.  A 384-byte FP8 token row
+// puts K[128:192] and V[0:64] in one 128-byte line, so K keeps the default
+// policy and the line stays cached for the V DMA that follows.  Measured on
+// MI355X: bf16 gated 72.4 -> 64.3 us with nt; FP8 large batch 629 us with
+// every DMA nt vs 601 us with V only.
+#define SDA_LDDMA(op, addr, suf) "global_load_lds_dwordx4 %[" op "], " addr suf "\n\t"
+#define SDA_NEXT "s_add_u32 m0, m0, 0x400\n\t"
+#define SDA_CHUNK_ASM(addr, ksuf, vsuf)                                                      \
+  "s_mov_b32 %[sv], m0\n\t"                                                                  \
+  "s_mov_b32 m0, %[st]\n\t" SDA_LDDMA("k0", addr, ksuf) SDA_NEXT SDA_LDDMA("k1", addr, ksuf) \
+      SDA_NEXT SDA_LDDMA("k2", addr, ksuf) SDA_NEXT SDA_LDDMA("k3", addr, ksuf) SDA_NEXT     \
+      SDA_LDDMA("k4", addr, ksuf) SDA_NEXT SDA_LDDMA("k5", addr, ksuf) SDA_NEXT              \
+      SDA_LDDMA("v0", addr, vsuf) SDA_NEXT SDA_LDDMA("v1", addr, vsuf) SDA_NEXT              \
+      SDA_LDDMA("v2", addr, vsuf) SDA_NEXT SDA_LDDMA("v3", addr, vsuf) SDA_NEXT              \
+      SDA_LDDMA("v4", addr, vsuf) SDA_NEXT SDA_LDDMA("v5", addr, vsuf)                       \
+  "s_mov_b32 m0, %[sv]"
+
 // dma_chunk_sbase: one uniform 64-bit base (SGPRs) plus 32-bit per-lane
 // byte offsets (kUni chunks, all tokens in one region).
+template <bool kFp8>
 __device__ __forceinline__ void dma_chunk_sbase(const uint8_t* base, uint32_t stage,
                                                 const uint32_t (&ko)[6],
                                                 const uint32_t (&vo)[6]) {
   uint32_t saved;
-  __asm__ __volatile__(
-      "s_mov_b32 %[sv], m0\n\t"
-      "s_mov_b32 m0, %[st]\n\t"
-      "global_load_lds_dwordx4 %[k0], %[b]\n\t"
-      "s_add_u32 m0, m0, 0x400\n\t"
-      "global_load_lds_dwordx4 %[k1], %[b]\n\t"
-      "s_add_u32 m0, m0, 0x400\n\t"
-      "global_load_lds_dwordx4 %[k2], %[b]\n\t"
-      "s_add_u32 m0, m0, 0x400\n\t"
-      "global_load_lds_dwordx4 %[k3], %[b]\n\t"
-      "s_add_u32 m0, m0, 0x400\n\t"
-      "global_load_lds_dwordx4 %[k4], %[b]\n\t"
-      "s_add_u32 m0, m0, 0x400\n\t"
-      "global_load_lds_dwordx4 %[k5], %[b]\n\t"
-      "s_add_u32 m0, m0, 0x400\n\t"
-      "global_load_lds_dwordx4 %[v0], %[b]\n\t"
-      "s_add_u32 m0, m0, 0x400\n\t"
-      "global_load_lds_dwordx4 %[v1], %[b]\n\t"
-      "s_add_u32 m0, m0, 0x400\n\t"
-      "global_load_lds_dwordx4 %[v2], %[b]\n\t"
-      "s_add_u32 m0, m0, 0x400\n\t"
-      "global_load_lds_dwordx4 %[v3], %[b]\n\t"
-      "s_add_u32 m0, m0, 0x400\n\t"
-      "global_load_lds_dwordx4 %[v4], %[b]\n\t"
-      "s_add_u32 m0, m0, 0x400\n\t"
-      "global_load_lds_dwordx4 %[v5], %[b]\n\t"
-      "s_mov_b32 m0, %[sv]"
-      : [sv] "=&s"(saved)
-      : [st] "s"(stage), [b] "s"(base), [k0] "v"(ko[0]), [k1] "v"(ko[1]), [k2] "v"(ko[2]),
-        [k3] "v"(ko[3]), [k4] "v"(ko[4]), [k5] "v"(ko[5]), [v0] "v"(vo[0]), [v1] "v"(vo[1]),
-        [v2] "v"(vo[2]), [v3] "v"(vo[3]), [v4] "v"(vo[4]), [v5] "v"(vo[5])
-      : "memory");
+#define SDA_SBASE_OPERANDS                                                                      \
+  : [sv] "=&s"(saved)                                                                           \
+  : [st] "s"(stage), [b] "s"(base), [k0] "v"(ko[0]), [k1] "v"(ko[1]), [k2] "v"(ko[2]),          \
+    [k3] "v"(ko[3]), [k4] "v"(ko[4]), [k5] "v"(ko[5]), [v0] "v"(vo[0]), [v1] "v"(vo[1]),        \
+    [v2] "v"(vo[2]), [v3] "v"(vo[3]), [v4] "v"(vo[4]), [v5] "v"(vo[5])                          \
+  : "memory"
+  if constexpr (kFp8)
+    __asm__ __volatile__(SDA_CHUNK_ASM("%[b]", "", " nt") SDA_SBASE_OPERANDS);
+  else
+    __asm__ __volatile__(SDA_CHUNK_ASM("%[b]", " nt", " nt") SDA_SBASE_OPERANDS);
+#undef SDA_SBASE_OPERANDS
 }
 
 // dma_chunk_vaddr: per-lane 64-bit addresses (chunks spanning regions).
+template <bool kFp8>
 __device__ __forceinline__ void dma_chunk_vaddr(uint32_t stage, const uint8_t* const (&ka)[6],
                                                 const uint8_t* const (&va)[6]) {
+  uint32_t saved;
+#define SDA_VADDR_OPERANDS                                                                     \
+  : [sv] "=&s"(saved)                                                                          \
+  : [st] "s"(stage), [k0] "v"(ka[0]), [k1] "v"(ka[1]), [k2] "v"(ka[2]), [k3] "v"(ka[3]),       \
+    [k4] "v"(ka[4]), [k5] "v"(ka[5]), [v0] "v"(va[0]), [v1] "v"(va[1]), [v2] "v"(va[2]),       \
+    [v3] "v"(va[3]), [v4] "v"(va[4]), [v5] "v"(va[5])                                          \
+  : "memory"
+  if constexpr (kFp8)
+    __asm__ __volatile__(SDA_CHUNK_ASM("off", "", " nt") SDA_VADDR_OPERANDS);
+  else
+    __asm__ __volatile__(SDA_CHUNK_ASM("off", " nt", " nt") SDA_VADDR_OPERANDS);
+#undef SDA_VADDR_OPERANDS
+}
+
+// Two 4-byte LDS-DMAs per lane that touch one 128-byte line each of a later
+// chunk, pulling it into the caches ahead of its real DMA.  They land in a
+// wave-private dummy LDS slot.
+__device__ __forceinline__ void touch_lines(const uint8_t* base, uint32_t dummy, uint32_t o0,
+                                            uint32_t o1) {
   uint32_t saved;
   __asm__ __volatile__(
       "s_mov_b32 %[sv], m0\n\t"
       "s_mov_b32 m0, %[st]\n\t"
-      "global_load_lds_dwordx4 %[k0], off\n\t"
-      "s_add_u32 m0, m0, 0x400\n\t"
-      "global_load_lds_dwordx4 %[k1], off\n\t"
-      "s_add_u32 m0, m0, 0x400\n\t"
-      "global_load_lds_dwordx4 %[k2], off\n\t"
-      "s_add_u32 m0, m0, 0x400\n\t"
-      "global_load_lds_dwordx4 %[k3], off\n\t"
-      "s_add_u32 m0, m0, 0x400\n\t"
-      "global_load_lds_dwordx4 %[k4], off\n\t"
-      "s_add_u32 m0, m0, 0x400\n\t"
-      "global_load_lds_dwordx4 %[k5], off\n\t"
-      "s_add_u32 m0, m0, 0x400\n\t"
-      "global_load_lds_dwordx4 %[v0], off\n\t"
-      "s_add_u32 m0, m0, 0x400\n\t"
-      "global_load_lds_dwordx4 %[v1], off\n\t"
-      "s_add_u32 m0, m0, 0x400\n\t"
-      "global_load_lds_dwordx4 %[v2], off\n\t"
-      "s_add_u32 m0, m0, 0x400\n\t"
-      "global_load_lds_dwordx4 %[v3], off\n\t"
-      "s_add_u32 m0, m0, 0x400\n\t"
-      "global_load_lds_dwordx4 %[v4], off\n\t"
-      "s_add_u32 m0, m0, 0x400\n\t"
-      "global_load_lds_dwordx4 %[v5], off\n\t"
+      "global_load_lds_dword %[a], %[b]\n\t"
+      "global_load_lds_dword %[c], %[b]\n\t"
       "s_mov_b32 m0, %[sv]"
       : [sv] "=&s"(saved)
-      : [st] "s"(stage), [k0] "v"(ka[0]), [k1] "v"(ka[1]), [k2] "v"(ka[2]), [k3] "v"(ka[3]),
-        [k4] "v"(ka[4]), [k5] "v"(ka[5]), [v0] "v"(va[0]), [v1] "v"(va[1]), [v2] "v"(va[2]),
-        [v3] "v"(va[3]), [v4] "v"(va[4]), [v5] "v"(va[5])
+      : [st] "s"(dummy), [b] "s"(base), [a] "v"(o0), [c] "v"(o1)
+      : "memory");
+}
+
+// touch_lines with per-lane 64-bit addresses.
+__device__ __forceinline__ void touch_lines_vaddr(uint32_t dummy, const uint8_t* a0,
+                                                  const uint8_t* a1) {
+  uint32_t saved;
+  __asm__ __volatile__(
+      "s_mov_b32 %[sv], m0\n\t"
+      "s_mov_b32 m0, %[st]\n\t"
+      "global_load_lds_dword %[a], off\n\t"
+      "global_load_lds_dword %[c], off\n\t"
+      "s_mov_b32 m0, %[sv]"
+      : [sv] "=&s"(saved)
+      : [st] "s"(dummy), [a] "v"(a0), [c] "v"(a1)
       : "memory");
 }
 
@@ -299,7 +316,7 @@ template <bool kFp8, bool kUni>
 __device__ __forceinline__ uint32_t issue_chunk(const Params& p, int c, int nreg,
                                                 const int64_t* s_base, const int* s_n, int lane,
                                                 uint32_t stage, const LaneDma& ld,
-                                                uint32_t cts_bytes) {
+                                                uint32_t cts_bytes, int cpf, uint32_t dummy) {
   using C = Cfg<kFp8>;
   const int i16 = lane & 15;
   const uint32_t st = (uint32_t)__builtin_amdgcn_readfirstlane(stage);
@@ -327,7 +344,30 @@ __device__ __forceinline__ uint32_t issue_chunk(const Params& p, int c, int nreg
       ko[j] = roff + ld.koff[j];
       vo[j] = roff + ld.voff[j];
     }
-    dma_chunk_sbase((const uint8_t*)(uintptr_t)base, st, ko, vo);
+    dma_chunk_sbase<kFp8>((const uint8_t*)(uintptr_t)base, st, ko, vo);
+    if (kPrefetchD > 0) {
+      // 96 lines per chunk (16 rows x 6 or 32 rows x 3); lanes past 95 repeat.
+      constexpr int kLinesPerRow = 2 * C::kVBytes / 128;
+      const int pslot0 = cpf * C::kTok;
+      const int pk = pslot0 / p.rt;
+      const int poff0 = pslot0 - pk * p.rt;
+      const int pnval = __builtin_amdgcn_readfirstlane(s_n[pk]);
+      const uint64_t pb64 = (uint64_t)(uintptr_t)(p.cache + s_base[pk] * C::kEsz);
+      const uint32_t pb_lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)pb64);
+      const uint32_t pb_hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(pb64 >> 32));
+      const uint64_t pbase = ((uint64_t)pb_hi << 32) | (uint64_t)pb_lo;
+      uint32_t po[2];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int L = min(64 * q + lane, 95);
+        const int row = L / kLinesPerRow;
+        const int tok = poff0 + row;
+        po[q] = (tok < pnval ? (uint32_t)tok * cts_bytes : 0u) +
+                128u * (uint32_t)(L - row * kLinesPerRow);
+      }
+      touch_lines((const uint8_t*)(uintptr_t)pbase, (uint32_t)__builtin_amdgcn_readfirstlane(dummy),
+                  po[0], po[1]);
+    }
   } else {
     const ChunkCtx cx = chunk_ctx<kFp8, false>(p, c, s_base, s_n);
 #pragma unroll
@@ -346,7 +386,11 @@ __device__ __forceinline__ uint32_t issue_chunk(const Params& p, int c, int nreg
       ka[j] = row + ld.koff[j];
       va[j] = row + ld.voff[j];
     }
-    dma_chunk_vaddr(st, ka, va);
+    dma_chunk_vaddr<kFp8>(st, ka, va);
+    if (kPrefetchD > 0) {
+      // Keep the per-issue op count uniform: touch this chunk's own first lines.
+      touch_lines_vaddr((uint32_t)__builtin_amdgcn_readfirstlane(dummy), ka[0], va[0]);
+    }
   }
   return vbits;
 }
@@ -515,6 +559,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   __shared__ int64_t s_base[kMaxRegions];
   __shared__ int s_n[kMaxRegions];
   __shared__ __attribute__((aligned(1024))) uint8_t s_stage[kWaves][kStages][kChunkBytes];
+  __shared__ __attribute__((aligned(256))) uint8_t s_dummy[kWaves][kPrefetchD > 0 ? 256 : 4];
   __shared__ float s_m[kWaves][16];
   __shared__ float s_l[kWaves][16];
 
@@ -599,6 +644,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   const int nchunks = (int)(((int64_t)nreg * rt + C::kTok - 1) / C::kTok);
   const uint8_t* my_stage = &s_stage[wave][0][0];
   const uint32_t my_stage_lds = lds_addr(my_stage);
+  const uint32_t dummy_lds = lds_addr(&s_dummy[wave][0]);
 
   // kStages-deep per-wave pipeline over LDS stages: iteration i (chunk
   // c = wave + 4i) computes stage i % kStages while the next kStages-1 chunks
@@ -614,7 +660,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
     for (int s = 0; s < kStages - 1; ++s)
       vb[s] = issue_chunk<kFp8, kUni>(p, min(wave + kWaves * s, last), nreg, s_base, s_n, lane,
-                                      my_stage_lds + s * kChunkBytes, ld, cts_bytes);
+                                      my_stage_lds + s * kChunkBytes, ld, cts_bytes,
+                                      min(wave + kWaves * (s + kPrefetchD), last), dummy_lds);
     auto step = [&](int i0, auto stage_c) -> bool {
       constexpr int S = decltype(stage_c)::value;
       constexpr int SN = (S + kStages - 1) % kStages;
@@ -623,8 +670,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       // Stage SN was last read by the previous iteration, whose reads all
       // completed before its MFMAs; the asm below keeps them above the DMA.
       vb[SN] = issue_chunk<kFp8, kUni>(p, min(c + kWaves * (kStages - 1), last), nreg, s_base,
-                                       s_n, lane, my_stage_lds + SN * kChunkBytes, ld, cts_bytes);
-      wait_vmcnt<12 * (kStages - 1)>();
+                                       s_n, lane, my_stage_lds + SN * kChunkBytes, ld, cts_bytes,
+                                       min(c + kWaves * (kStages - 1 + kPrefetchD), last),
+                                       dummy_lds);
+      wait_vmcnt<kOpsPerChunk * (kStages - 1)>();
       compute_chunk<kFp8>(my_stage + S * kChunkBytes, vb[S], qreg, qk_scale_log2, lane, st);
       return true;
     };
