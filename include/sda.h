@@ -34,7 +34,7 @@ extern "C" {
 #define SDA_HEAD_DIM 192     /* query / key / value head dim (fixed) */
 #define SDA_KV_ROW 384       /* one cache token row: K[0:192] then V[192:384] */
 #define SDA_MAX_HEADS 16     /* GQA-packed query heads per KV group */
-#define SDA_MAX_R 1024       /* region slots per row */
+#define SDA_MAX_R 2048       /* region slots per row */
 #define SDA_MAX_SPLITS 256
 
 typedef enum {

@@ -148,8 +148,8 @@ def make_args(query, cache, regions, block_table, positions, active, output, *, 
     return a
 
 
-def _check_tensors(query, cache, regions, block_table, positions, active, output,
-                   k_scale, v_scale, gate):
+def check_tensors(query, cache, regions, block_table, positions, active, output,
+                  k_scale, v_scale, gate):
     """dtype checks the C ABI cannot make (it sees only pointers)."""
     if query.dtype != torch.bfloat16 or output.dtype != torch.bfloat16:
         raise SdaError(SDA_ERR_INVALID, "query and output must be bfloat16")
@@ -191,8 +191,8 @@ def sda_decode(query, cache, regions, block_table, positions, active, output, *,
     device tensor of at least sda_workspace_bytes(rows, heads, splits) bytes;
     allocated here through torch when omitted and splits > 1.
     """
-    _check_tensors(query, cache, regions, block_table, positions, active, output,
-                   k_scale, v_scale, gate)
+    check_tensors(query, cache, regions, block_table, positions, active, output,
+                  k_scale, v_scale, gate)
     rows, heads = query.shape[0], query.shape[1]
     if workspace is None and splits > 1 and rows > 0:
         nbytes = sda_workspace_bytes(rows, heads, splits)

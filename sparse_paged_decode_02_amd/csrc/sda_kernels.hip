@@ -56,13 +56,7 @@ constexpr int kDim = 192;
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kStages = 2;          // LDS stages per wave: 1 computed, 1 in flight
-#ifndef SDA_PREFETCH_D
-#define SDA_PREFETCH_D 0
-#endif
-// Line-touch prefetch distance (in the wave's chunk sequence) beyond the DMA
-// stages; 0 disables it.
-constexpr int kPrefetchD = SDA_PREFETCH_D;
-constexpr int kOpsPerChunk = 12 + (kPrefetchD > 0 ? 2 : 0);  // vector-memory ops per issue
+constexpr int kOpsPerChunk = 12;    // vector-memory instructions per chunk issue
 constexpr int kStageBytes = 6144;   // K (or V) bytes of one chunk (16 bf16 / 32 FP8 tokens)
 constexpr int kChunkBytes = 2 * kStageBytes;  // one stage: K then V
 constexpr int kAccStride = 196;     // floats per head row in the wave-merge area
@@ -194,38 +188,6 @@ __device__ __forceinline__ void dma_chunk_vaddr(uint32_t stage, const uint8_t* c
 #undef SDA_VADDR_OPERANDS
 }
 
-// Two 4-byte LDS-DMAs per lane that touch one 128-byte line each of a later
-// chunk, pulling it into the caches ahead of its real DMA.  They land in a
-// wave-private dummy LDS slot.
-__device__ __forceinline__ void touch_lines(const uint8_t* base, uint32_t dummy, uint32_t o0,
-                                            uint32_t o1) {
-  uint32_t saved;
-  __asm__ __volatile__(
-      "s_mov_b32 %[sv], m0\n\t"
-      "s_mov_b32 m0, %[st]\n\t"
-      "global_load_lds_dword %[a], %[b]\n\t"
-      "global_load_lds_dword %[c], %[b]\n\t"
-      "s_mov_b32 m0, %[sv]"
-      : [sv] "=&s"(saved)
-      : [st] "s"(dummy), [b] "s"(base), [a] "v"(o0), [c] "v"(o1)
-      : "memory");
-}
-
-// touch_lines with per-lane 64-bit addresses.
-__device__ __forceinline__ void touch_lines_vaddr(uint32_t dummy, const uint8_t* a0,
-                                                  const uint8_t* a1) {
-  uint32_t saved;
-  __asm__ __volatile__(
-      "s_mov_b32 %[sv], m0\n\t"
-      "s_mov_b32 m0, %[st]\n\t"
-      "global_load_lds_dword %[a], off\n\t"
-      "global_load_lds_dword %[c], off\n\t"
-      "s_mov_b32 m0, %[sv]"
-      : [sv] "=&s"(saved)
-      : [st] "s"(dummy), [a] "v"(a0), [c] "v"(a1)
-      : "memory");
-}
-
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
@@ -316,7 +278,7 @@ template <bool kFp8, bool kUni>
 __device__ __forceinline__ uint32_t issue_chunk(const Params& p, int c, int nreg,
                                                 const int64_t* s_base, const int* s_n, int lane,
                                                 uint32_t stage, const LaneDma& ld,
-                                                uint32_t cts_bytes, int cpf, uint32_t dummy) {
+                                                uint32_t cts_bytes) {
   using C = Cfg<kFp8>;
   const int i16 = lane & 15;
   const uint32_t st = (uint32_t)__builtin_amdgcn_readfirstlane(stage);
@@ -345,29 +307,6 @@ __device__ __forceinline__ uint32_t issue_chunk(const Params& p, int c, int nreg
       vo[j] = roff + ld.voff[j];
     }
     dma_chunk_sbase<kFp8>((const uint8_t*)(uintptr_t)base, st, ko, vo);
-    if (kPrefetchD > 0) {
-      // 96 lines per chunk (16 rows x 6 or 32 rows x 3); lanes past 95 repeat.
-      constexpr int kLinesPerRow = 2 * C::kVBytes / 128;
-      const int pslot0 = cpf * C::kTok;
-      const int pk = pslot0 / p.rt;
-      const int poff0 = pslot0 - pk * p.rt;
-      const int pnval = __builtin_amdgcn_readfirstlane(s_n[pk]);
-      const uint64_t pb64 = (uint64_t)(uintptr_t)(p.cache + s_base[pk] * C::kEsz);
-      const uint32_t pb_lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)pb64);
-      const uint32_t pb_hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(pb64 >> 32));
-      const uint64_t pbase = ((uint64_t)pb_hi << 32) | (uint64_t)pb_lo;
-      uint32_t po[2];
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int L = min(64 * q + lane, 95);
-        const int row = L / kLinesPerRow;
-        const int tok = poff0 + row;
-        po[q] = (tok < pnval ? (uint32_t)tok * cts_bytes : 0u) +
-                128u * (uint32_t)(L - row * kLinesPerRow);
-      }
-      touch_lines((const uint8_t*)(uintptr_t)pbase, (uint32_t)__builtin_amdgcn_readfirstlane(dummy),
-                  po[0], po[1]);
-    }
   } else {
     const ChunkCtx cx = chunk_ctx<kFp8, false>(p, c, s_base, s_n);
 #pragma unroll
@@ -387,10 +326,6 @@ __device__ __forceinline__ uint32_t issue_chunk(const Params& p, int c, int nreg
       va[j] = row + ld.voff[j];
     }
     dma_chunk_vaddr<kFp8>(st, ka, va);
-    if (kPrefetchD > 0) {
-      // Keep the per-issue op count uniform: touch this chunk's own first lines.
-      touch_lines_vaddr((uint32_t)__builtin_amdgcn_readfirstlane(dummy), ka[0], va[0]);
-    }
   }
   return vbits;
 }
@@ -559,7 +494,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   __shared__ int64_t s_base[kMaxRegions];
   __shared__ int s_n[kMaxRegions];
   __shared__ __attribute__((aligned(1024))) uint8_t s_stage[kWaves][kStages][kChunkBytes];
-  __shared__ __attribute__((aligned(256))) uint8_t s_dummy[kWaves][kPrefetchD > 0 ? 256 : 4];
   __shared__ float s_m[kWaves][16];
   __shared__ float s_l[kWaves][16];
 
@@ -644,7 +578,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   const int nchunks = (int)(((int64_t)nreg * rt + C::kTok - 1) / C::kTok);
   const uint8_t* my_stage = &s_stage[wave][0][0];
   const uint32_t my_stage_lds = lds_addr(my_stage);
-  const uint32_t dummy_lds = lds_addr(&s_dummy[wave][0]);
 
   // kStages-deep per-wave pipeline over LDS stages: iteration i (chunk
   // c = wave + 4i) computes stage i % kStages while the next kStages-1 chunks
@@ -660,8 +593,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
     for (int s = 0; s < kStages - 1; ++s)
       vb[s] = issue_chunk<kFp8, kUni>(p, min(wave + kWaves * s, last), nreg, s_base, s_n, lane,
-                                      my_stage_lds + s * kChunkBytes, ld, cts_bytes,
-                                      min(wave + kWaves * (s + kPrefetchD), last), dummy_lds);
+                                      my_stage_lds + s * kChunkBytes, ld, cts_bytes);
     auto step = [&](int i0, auto stage_c) -> bool {
       constexpr int S = decltype(stage_c)::value;
       constexpr int SN = (S + kStages - 1) % kStages;
@@ -670,9 +602,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       // Stage SN was last read by the previous iteration, whose reads all
       // completed before its MFMAs; the asm below keeps them above the DMA.
       vb[SN] = issue_chunk<kFp8, kUni>(p, min(c + kWaves * (kStages - 1), last), nreg, s_base,
-                                       s_n, lane, my_stage_lds + SN * kChunkBytes, ld, cts_bytes,
-                                       min(c + kWaves * (kStages - 1 + kPrefetchD), last),
-                                       dummy_lds);
+                                       s_n, lane, my_stage_lds + SN * kChunkBytes, ld, cts_bytes);
       wait_vmcnt<kOpsPerChunk * (kStages - 1)>();
       compute_chunk<kFp8>(my_stage + S * kChunkBytes, vb[S], qreg, qk_scale_log2, lane, st);
       return true;

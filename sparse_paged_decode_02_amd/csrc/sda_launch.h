@@ -7,7 +7,7 @@
 
 namespace sda {
 
-constexpr int kMaxRegions = 1024;  // LDS region list per workgroup (= SDA_MAX_R)
+constexpr int kMaxRegions = 2048;  // LDS region list per workgroup (= SDA_MAX_R)
 
 struct Params {
   const uint16_t* q;          // bf16 bits

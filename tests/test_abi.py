@@ -94,7 +94,7 @@ INVALID = [
 ]
 
 UNSUPPORTED = [
-    dict(R=1025), dict(splits=257, workspace=0x900000, workspace_bytes=1 << 40),
+    dict(R=2049), dict(splits=257, workspace=0x900000, workspace_bytes=1 << 40),
     dict(query=0x100008), dict(q_head_stride=196), dict(q_row_stride=16 * 192 + 4),
     dict(cache=0x300008), dict(c_token_stride=388), dict(c_page_stride=4 * 64 * 384 + 4),
     dict(output=0x200002), dict(o_head_stride=193),

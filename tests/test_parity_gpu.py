@@ -133,6 +133,17 @@ def test_sub_page_regions(rt):
         check_close(out, oracle_out(inp), what="rt=%d splits=%d" % (rt, s))
 
 
+@pytest.mark.parametrize("splits", [1, 3])
+def test_maximum_region_slots(splits):
+    """R at the library maximum (2048 slots of 8-token regions, 16K tokens)."""
+    w = gen.scaled(gen.CONFIGS[2], name="max-R", requests=2, groups=1, heads=4,
+                   pages_per_req=256, pos_lo=12000, pos_hi=16383, R=2048,
+                   region_tokens=8, inactive_frac=0.0, gated=False)
+    inp = gen.make_inputs(w, device=DEV)
+    assert (inp.regions >= 0).sum().item() > 2 * 1400
+    check_close(run(inp, splits=splits), oracle_out(inp), what="R=2048 splits=%d" % splits)
+
+
 def test_query_len_three_and_duplicates():
     w = small(4, requests=4, query_len=3, pages_per_req=24, pos_lo=200, pos_hi=700,
               live=(1, 20), R=24)
