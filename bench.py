@@ -122,7 +122,8 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=2, help="workload number 1..5")
+    ap.add_argument("--config", type=int, default=2,
+                    help="workload: 1..5, or 6 = bf16-gated shape at 8-token regions")
     ap.add_argument("--sets", type=int, default=4, help="rotating input sets")
     ap.add_argument("--splits", type=int, default=0, help="0: the workload's rule")
     ap.add_argument("--cpu-rows", type=int, default=48)

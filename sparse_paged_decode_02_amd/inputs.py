@@ -73,7 +73,7 @@ def config_seed(k: int) -> int:
     return 1000 * k + 7
 
 
-# The five decode workloads (1-based numbering).
+# The five decode workloads (1-based numbering), and one at 8-token regions.
 CONFIGS = {
     1: Workload("tiny-bf16", requests=4, query_len=1, groups=1, heads=8, block=16,
                 pages_per_req=16, R=8, kv="bf16", pos_lo=1, pos_hi=127,
@@ -91,6 +91,12 @@ CONFIGS = {
     5: Workload("large-batch-fp8", requests=1024, query_len=1, groups=4, heads=16, block=64,
                 pages_per_req=256, R=32, kv="fp8", pos_lo=8192, pos_hi=16383,
                 gated=True, splits=1, seed=config_seed(5)),
+    # The pages' own region granularity (8 tokens, many regions per page) at the
+    # bf16-gated shape: 256 slots of 8 tokens = the same 2048 tokens per row.
+    6: Workload("bf16-gated-8tok", requests=64, query_len=1, groups=4, heads=16, block=64,
+                pages_per_req=512, R=256, kv="bf16", pos_lo=4096, pos_hi=32767,
+                inactive_frac=0.05, gated=True, splits=None, region_tokens=8,
+                seed=config_seed(6)),
 }
 
 

@@ -353,7 +353,7 @@ def test_fp8_all_codes_through_the_kernel():
 
 
 # --- full-size workloads: sampled rows + properties ---------------------------
-@pytest.mark.parametrize("k", [2, 3, 4, 5])
+@pytest.mark.parametrize("k", [2, 3, 4, 5, 6])
 def test_full_size_sampled(k):
     w = gen.CONFIGS[k]
     _say("drawing full workload %d (%s)" % (k, w.name))
