@@ -13,7 +13,7 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from .oracle import HostProblem
+from .oracle import HostProblem, SwaHostProblem
 
 _WHOLE_CACHE_BYTES = 256 << 20
 
@@ -107,3 +107,45 @@ def host_problem_from_inputs(inp, rows=None, clear_inactive=True) -> HostProblem
                         inp.active, scale=inp.scale, query_len=inp.w.query_len,
                         region_tokens=inp.w.region_tokens, clear_inactive=clear_inactive,
                         k_scale=inp.k_scale, v_scale=inp.v_scale, gate=inp.gate, rows=rows)
+
+
+def swa_host_problem(query, cache, block_table, seq_lens, *, scale, window, query_len=1,
+                     gate=None, rows=None) -> SwaHostProblem:
+    """The oracle's sliding-window problem.  ``query`` is [tokens, G*heads,
+    192] as the attention layer holds it; the host copy is its row view
+    [tokens*G, heads, 192].  With a large cache only the window pages of the
+    ``rows`` to be evaluated are copied (block table renumbered, the rest -1)."""
+    groups, block = cache.shape[1], cache.shape[2]
+    tokens = query.shape[0]
+    heads = query.shape[1] // groups
+    table = np.array(block_table.detach().cpu().numpy(), dtype=np.int32, copy=True)
+    lens = np.array(seq_lens.detach().cpu().numpy(), dtype=np.int32, copy=True)
+    q = _bits16(query).reshape(tokens * groups, heads, query.shape[2])
+    row_list = range(tokens * groups) if rows is None else [int(r) for r in rows]
+    if cache.numel() * cache.element_size() <= _WHOLE_CACHE_BYTES:
+        host_cache = _bits16(cache)
+        host_table = np.ascontiguousarray(table)
+    else:
+        need = set()
+        for r in row_list:
+            t = r // groups
+            req, j = t // query_len, t % query_len
+            pos = int(lens[req]) - query_len + j
+            if pos < 0:
+                continue
+            first = max(0, pos - window + 1)
+            for col in range(first // block, pos // block + 1):
+                need.add((req, col))
+        pages = sorted({int(table[q_, c]) for q_, c in need})
+        remap = {p: i for i, p in enumerate(pages)}
+        idx = torch.tensor(pages if pages else [0], dtype=torch.long, device=cache.device)
+        host_cache = _bits16(cache.index_select(0, idx))
+        if not pages:
+            host_cache = host_cache[:0]
+        host_table = np.full(table.shape, -1, dtype=np.int32)
+        for q_, c in need:
+            host_table[q_, c] = remap[int(table[q_, c])]
+    return SwaHostProblem(query=q, cache=host_cache, block_table=host_table,
+                          seq_lens=np.ascontiguousarray(lens), scale=float(scale),
+                          window=int(window), query_len=int(query_len),
+                          gate=None if gate is None else _bits16(gate))

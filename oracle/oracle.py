@@ -59,6 +59,24 @@ class _Problem(ctypes.Structure):
     ]
 
 
+class _SwaProblem(ctypes.Structure):
+    _fields_ = [
+        ("tokens", ctypes.c_int32), ("heads", ctypes.c_int32), ("groups", ctypes.c_int32),
+        ("query_len", ctypes.c_int32), ("block", ctypes.c_int32), ("window", ctypes.c_int32),
+        ("query", ctypes.c_void_p), ("q_row_stride", ctypes.c_int64),
+        ("q_head_stride", ctypes.c_int64),
+        ("cache", ctypes.c_void_p),
+        ("c_page_stride", ctypes.c_int64), ("c_group_stride", ctypes.c_int64),
+        ("c_token_stride", ctypes.c_int64), ("num_pages", ctypes.c_int64),
+        ("block_table", ctypes.c_void_p), ("table_row_stride", ctypes.c_int64),
+        ("table_cols", ctypes.c_int64),
+        ("seq_lens", ctypes.c_void_p),
+        ("scale", ctypes.c_float),
+        ("gate", ctypes.c_void_p), ("gate_row_stride", ctypes.c_int64),
+        ("gate_head_stride", ctypes.c_int64),
+    ]
+
+
 _lib = None
 _lib_lock = threading.Lock()
 
@@ -84,6 +102,9 @@ def lib():
             l.sdo_decode_split.restype = ctypes.c_int
             l.sdo_decode_split.argtypes = [ctypes.POINTER(_Problem), ctypes.c_int,
                                            ctypes.c_void_p, ctypes.c_int, ctypes.c_int]
+            l.sdo_swa_decode.restype = ctypes.c_int
+            l.sdo_swa_decode.argtypes = [ctypes.POINTER(_SwaProblem), ctypes.c_void_p,
+                                         ctypes.c_int, ctypes.c_int]
             _lib = l
     return _lib
 
@@ -226,6 +247,93 @@ def decode(hp: HostProblem, out: np.ndarray | None = None, rows=None,
                 errs.append(e)
 
         ts = [threading.Thread(target=worker, args=(rs,)) for rs in parts if rs]
+        for t in ts:
+            t.start()
+        for t in ts:
+            t.join()
+        if errs:
+            raise errs[0]
+    return out
+
+
+@dataclass
+class SwaHostProblem:
+    """Host copies of the gated sliding-window decode inputs.
+
+    query: uint16 [tokens*G, heads, 192], the row view (row r is group r % G
+    of token r // G); cache: uint16 [pages, G, block, 384] (bf16 bits);
+    block_table: int32 [requests, cols]; seq_lens: int32 [requests];
+    gate: uint16 [tokens, G*heads] or None.
+    """
+    query: np.ndarray
+    cache: np.ndarray
+    block_table: np.ndarray
+    seq_lens: np.ndarray
+    scale: float
+    window: int
+    query_len: int = 1
+    gate: np.ndarray | None = None
+
+
+def _swa_problem(hp: SwaHostProblem) -> _SwaProblem:
+    q, c = hp.query, hp.cache
+    assert q.dtype == np.uint16 and q.ndim == 3 and q.shape[2] == DIM and q.strides[2] == 2
+    assert c.dtype == np.uint16 and c.ndim == 4 and c.shape[3] == 2 * DIM and c.strides[3] == 2
+    assert hp.block_table.dtype == np.int32 and hp.block_table.strides[1] == 4
+    assert hp.seq_lens.dtype == np.int32 and hp.seq_lens.flags.c_contiguous
+    groups = c.shape[1]
+    assert q.shape[0] % groups == 0
+    p = _SwaProblem()
+    p.tokens, p.heads, p.groups = q.shape[0] // groups, q.shape[1], groups
+    p.query_len, p.block, p.window = hp.query_len, c.shape[2], hp.window
+    p.query = q.ctypes.data
+    p.q_row_stride, p.q_head_stride = _strides(q)[0], _strides(q)[1]
+    p.cache = c.ctypes.data
+    cs = _strides(c)
+    p.c_page_stride, p.c_group_stride, p.c_token_stride = cs[0], cs[1], cs[2]
+    p.num_pages = c.shape[0]
+    p.block_table = hp.block_table.ctypes.data
+    p.table_row_stride = _strides(hp.block_table)[0]
+    p.table_cols = hp.block_table.shape[1]
+    p.seq_lens = hp.seq_lens.ctypes.data
+    p.scale = hp.scale
+    if hp.gate is not None:
+        assert hp.gate.dtype == np.uint16
+        p.gate = hp.gate.ctypes.data
+        p.gate_row_stride, p.gate_head_stride = _strides(hp.gate)
+    else:
+        p.gate = None
+        p.gate_row_stride = p.gate_head_stride = 0
+    return p
+
+
+def swa_decode(hp: SwaHostProblem, rows=None, threads: int = 1) -> np.ndarray:
+    """fp64 reference output [tokens*G, heads, 192] of the gated
+    sliding-window decode (rows not listed in ``rows`` stay NaN)."""
+    nrows, heads = hp.query.shape[0], hp.query.shape[1]
+    out = np.full((nrows, heads, DIM), np.nan)
+    p = _swa_problem(hp)
+    l = lib()
+    row_list = list(range(nrows)) if rows is None else [int(r) for r in rows]
+    row_bytes = heads * DIM * 8
+
+    def run(rs):
+        for r in rs:
+            _check_rc(l.sdo_swa_decode(ctypes.byref(p), out.ctypes.data + r * row_bytes, r, r + 1))
+
+    if threads <= 1 or len(row_list) < 2:
+        run(row_list)
+    else:
+        errs = []
+
+        def worker(rs):
+            try:
+                run(rs)
+            except Exception as e:  # surfaced below
+                errs.append(e)
+
+        ts = [threading.Thread(target=worker, args=(row_list[i::threads],))
+              for i in range(threads) if row_list[i::threads]]
         for t in ts:
             t.start()
         for t in ts:

@@ -329,3 +329,93 @@ int sdo_decode_split(const sdo_problem *p, int splits, double *out, int row_begi
   free(toks); free(logit); free(part); free(lse); free(live);
   return rc;
 }
+
+/* ---- gated sliding-window decode ------------------------------------------
+ * [P2] `Step5SplitKVFlashAttentionImpl.forward_with_headwise_gate`: the
+ * non-DSA layers attend, per decode token, over a causal sliding window of
+ * `window` tokens (window = sliding_window[0] + 1, right edge 0), reading the
+ * same packed [pages, G, block, 384] cache through K and V views
+ * (`_split_kv_cache`), with the query heads of each KV group packed together
+ * (GQA), and apply the headwise sigmoid gate to the result.  The batch is
+ * uniform: requests * query_len tokens, query_len tokens per request.
+ * Readings: token j (0-based) of a request whose sequence length is L sits at
+ * position L - query_len + j, the convention [P3] `decode_logits` writes out
+ * for query_len > 1; it sees tokens max(0, pos - window + 1) .. pos.  Rows
+ * fold (token, KV group) as in the sparse path: row r is group r % G of
+ * token r / G. */
+typedef struct {
+  int32_t tokens, heads, groups, query_len, block, window;
+  const uint16_t *query;            /* bf16 bits, row view [tokens*G, heads, 192] */
+  int64_t q_row_stride, q_head_stride;
+  const uint16_t *cache;            /* bf16 bits [pages, G, block, 384] */
+  int64_t c_page_stride, c_group_stride, c_token_stride;
+  int64_t num_pages;
+  const int32_t *block_table;       /* [requests, table_cols] */
+  int64_t table_row_stride, table_cols;
+  const int32_t *seq_lens;          /* [requests] */
+  float scale;
+  const uint16_t *gate;             /* bf16 bits [tokens, G*heads] or NULL */
+  int64_t gate_row_stride, gate_head_stride;
+} sdo_swa_problem;
+
+/* Rows [row_begin, row_end) into out (contiguous fp64 [n, heads, 192]): the
+ * exact softmax attention of each head over its window, gated if a gate is
+ * given.  A row whose window holds no token (position < 0) outputs zero. */
+int sdo_swa_decode(const sdo_swa_problem *s, double *out, int row_begin, int row_end) {
+  if (!s || s->heads < 1 || s->groups < 1 || s->query_len < 1 || s->block < 1 || s->window < 1 ||
+      s->tokens < 0 || s->tokens % s->query_len)
+    return SDO_ERR_ARGS;
+  int rows = s->tokens * s->groups;
+  if (row_begin < 0 || row_end > rows || row_begin > row_end) return SDO_ERR_ARGS;
+  /* the fields `attend` and `apply_gate` read */
+  sdo_problem p;
+  memset(&p, 0, sizeof(p));
+  p.rows = rows;
+  p.heads = s->heads;
+  p.groups = s->groups;
+  p.query_len = s->query_len;
+  p.block = s->block;
+  p.query = s->query;
+  p.q_row_stride = s->q_row_stride;
+  p.q_head_stride = s->q_head_stride;
+  p.cache = s->cache;
+  p.kv_dtype = SDO_KV_BF16;
+  p.c_page_stride = s->c_page_stride;
+  p.c_group_stride = s->c_group_stride;
+  p.c_token_stride = s->c_token_stride;
+  p.scale = s->scale;
+  p.gate = s->gate;
+  p.gate_row_stride = s->gate_row_stride;
+  p.gate_head_stride = s->gate_head_stride;
+  sdo_tok *toks = (sdo_tok *)malloc(sizeof(sdo_tok) * (size_t)s->window);
+  double *logit = (double *)malloc(sizeof(double) * (size_t)s->window);
+  if (!toks || !logit) { free(toks); free(logit); return SDO_ERR_NOMEM; }
+  int rc = SDO_OK;
+  for (int r = row_begin; r < row_end && rc == SDO_OK; ++r) {
+    int token = r / s->groups;
+    int req = token / s->query_len, j = token % s->query_len;
+    int64_t pos = (int64_t)s->seq_lens[req] - s->query_len + j;
+    int64_t first = pos - s->window + 1;
+    if (first < 0) first = 0;
+    int n = 0;
+    for (int64_t t = first; t <= pos; ++t) {
+      int64_t col = t / s->block;
+      if (col >= s->table_cols) { rc = SDO_ERR_TABLE; break; }
+      int64_t page = s->block_table[(int64_t)req * s->table_row_stride + col];
+      if (page < 0 || page >= s->num_pages) { rc = SDO_ERR_PAGE; break; }
+      toks[n].page = page;
+      toks[n].off = (int32_t)(t % s->block);
+      ++n;
+    }
+    if (rc) break;
+    double *orow = out + (int64_t)(r - row_begin) * s->heads * SDO_DIM;
+    for (int h = 0; h < s->heads; ++h) {
+      double *o = orow + (int64_t)h * SDO_DIM;
+      attend(&p, r, h, toks, n, logit, o);
+      apply_gate(&p, r, h, o);
+    }
+  }
+  free(toks);
+  free(logit);
+  return rc;
+}

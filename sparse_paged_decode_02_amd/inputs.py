@@ -224,3 +224,97 @@ def make_inputs(w: Workload, device="cpu", seed: int | None = None,
         positions=torch.from_numpy(idx.positions).to(device),
         active=torch.from_numpy(idx.active.astype(bool)).to(device),
         gate=gate, k_scale=k_scale, v_scale=v_scale, scale=w.scale, splits=splits)
+
+
+# ---- gated sliding-window decode -------------------------------------------
+# The non-DSA layers' decode: a uniform batch of requests*query_len tokens, each
+# attending over the last `window` tokens of its request in the same packed
+# cache.  The pages leave the window length open; 1024 tokens is used here.
+
+@dataclass(frozen=True)
+class SwaWorkload:
+    name: str
+    requests: int
+    query_len: int
+    groups: int
+    heads: int                   # query heads per KV group
+    block: int
+    pages_per_req: int
+    window: int
+    seq_lo: int                  # sequence length ~ U[seq_lo, seq_hi]
+    seq_hi: int
+    gated: bool = True
+    splits: int | None = None    # None: sda_swa_splits(...)
+    seed: int = 0
+
+    @property
+    def tokens(self) -> int:
+        return self.requests * self.query_len
+
+    @property
+    def rows(self) -> int:
+        return self.tokens * self.groups
+
+    @property
+    def total_pages(self) -> int:
+        return self.requests * self.pages_per_req
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(HEAD_DIM)
+
+
+SWA_CONFIGS = {
+    # decode, 16 heads per KV group, full 1024-token windows in 8K contexts
+    "swa-gated": SwaWorkload("swa-gated", requests=256, query_len=1, groups=4, heads=16,
+                             block=64, pages_per_req=128, window=1024, seq_lo=1024,
+                             seq_hi=8192, seed=config_seed(11)),
+    # MTP verify: 4 query tokens per request, 4 heads per KV group
+    "swa-mtp": SwaWorkload("swa-mtp", requests=128, query_len=4, groups=4, heads=4,
+                           block=64, pages_per_req=128, window=1024, seq_lo=4,
+                           seq_hi=8192, seed=config_seed(12)),
+}
+
+
+@dataclass
+class SwaInputs:
+    w: SwaWorkload
+    query: torch.Tensor          # bf16 [tokens, G*heads, 192]
+    cache: torch.Tensor          # bf16 [pages, G, block, 384]
+    block_table: torch.Tensor    # int32 [requests, pages_per_req]
+    seq_lens: torch.Tensor       # int32 [requests]
+    gate: torch.Tensor | None    # bf16 [tokens, G*heads]
+    scale: float
+    splits: int | None
+
+
+def make_swa_inputs(w: SwaWorkload, device="cpu", seed: int | None = None,
+                    cache: torch.Tensor | None = None, seq_lens=None,
+                    splits: int | None = None) -> SwaInputs:
+    """Block table = random permutation of all pages; seq_lens ~ U[seq_lo,
+    seq_hi] (or as given); query, cache ~ N(0,1) bf16; gate ~ N(0,2) bf16."""
+    seed = w.seed if seed is None else seed
+    rng = np.random.default_rng(seed)
+    table = rng.permutation(w.total_pages).astype(np.int32).reshape(w.requests, w.pages_per_req)
+    if seq_lens is None:
+        seq_lens = rng.integers(w.seq_lo, w.seq_hi + 1, size=w.requests)
+    seq_lens = np.asarray(seq_lens, dtype=np.int32)
+    assert seq_lens.shape == (w.requests,)
+    assert int(seq_lens.max(initial=0)) <= w.pages_per_req * w.block
+    if cache is None:
+        cache = draw_cache(Workload(w.name, requests=w.requests, query_len=w.query_len,
+                                    groups=w.groups, heads=w.heads, block=w.block,
+                                    pages_per_req=w.pages_per_req, R=0, kv="bf16", pos_lo=0,
+                                    pos_hi=0, seed=seed), device, seed=seed)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed * 2)
+    query = torch.randn((w.tokens, w.groups * w.heads, HEAD_DIM), generator=gen,
+                        device=device).to(torch.bfloat16)
+    gate = None
+    if w.gated:
+        g = torch.randn((w.tokens, w.groups * w.heads), generator=gen, device=device)
+        gate = (g * math.sqrt(2.0)).to(torch.bfloat16)
+    return SwaInputs(w=w, query=query, cache=cache,
+                     block_table=torch.from_numpy(table).to(device),
+                     seq_lens=torch.from_numpy(seq_lens).to(device), gate=gate, scale=w.scale,
+                     splits=w.splits if splits is None else splits)

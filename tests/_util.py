@@ -89,3 +89,48 @@ def dense_reference(hp: oracle.HostProblem, gate_values=None) -> np.ndarray:
 
 def run_oracle(hp, **kw) -> np.ndarray:
     return oracle.decode(hp, **kw)
+
+
+def swa_dense_reference(hp: oracle.SwaHostProblem, gate_values=None) -> np.ndarray:
+    """Sliding-window brute force by another route: the request's context up
+    to the row's position is laid out densely through the block table and
+    torch's scaled_dot_product_attention (float64) runs over it with a band
+    mask that keeps tokens pos-window+1 .. pos.  Rows without a token give 0."""
+    q = torch.from_numpy(hp.query.astype(np.int16)).view(torch.bfloat16).to(torch.float64)
+    c = torch.from_numpy(hp.cache.view(np.int16)).view(torch.bfloat16).to(torch.float64)
+    K, V = c[..., :DIM], c[..., DIM:]
+    rows, heads = q.shape[0], q.shape[1]
+    G, block = hp.cache.shape[1], hp.cache.shape[2]
+    out = np.zeros((rows, heads, DIM))
+    for r in range(rows):
+        tok, g = r // G, r % G
+        req, j = tok // hp.query_len, tok % hp.query_len
+        pos = int(hp.seq_lens[req]) - hp.query_len + j
+        if pos < 0:
+            continue
+        t = torch.arange(pos + 1)
+        pages = torch.from_numpy(hp.block_table[req].astype(np.int64))[t // block]
+        Kd, Vd = K[pages, g, t % block], V[pages, g, t % block]
+        keep = t >= pos - hp.window + 1
+        bias = torch.where(keep, torch.tensor(0.0, dtype=torch.float64),
+                           torch.tensor(-math.inf, dtype=torch.float64))
+        o = F.scaled_dot_product_attention(q[r][None, :, None, :], Kd[None, None],
+                                           Vd[None, None], attn_mask=bias[None, None, None, :],
+                                           scale=float(np.float32(hp.scale)))[0, :, 0, :].numpy()
+        if gate_values is not None:
+            o = o * gate_values[r][:, None]
+        out[r] = o
+    return out
+
+
+def swa_gate_values(hp: oracle.SwaHostProblem) -> np.ndarray:
+    """[rows, heads] gate factors from the (separately pinned) oracle gate."""
+    G = hp.cache.shape[1]
+    rows, heads = hp.query.shape[0], hp.query.shape[1]
+    gv = np.ones((rows, heads))
+    if hp.gate is None:
+        return gv
+    for r in range(rows):
+        for h in range(heads):
+            gv[r, h] = oracle.gate_value(int(hp.gate[r // G, (r % G) * heads + h]))
+    return gv
