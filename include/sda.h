@@ -30,12 +30,13 @@
 extern "C" {
 #endif
 
-#define SDA_ABI_VERSION 1
+#define SDA_ABI_VERSION 2
 #define SDA_HEAD_DIM 192     /* query / key / value head dim (fixed) */
 #define SDA_KV_ROW 384       /* one cache token row: K[0:192] then V[192:384] */
 #define SDA_MAX_HEADS 16     /* GQA-packed query heads per KV group */
 #define SDA_MAX_R 2048       /* region slots per row */
 #define SDA_MAX_SPLITS 256
+#define SDA_MAX_ROWS 16777215 /* rows per call: grid limit (rows * 256 threads < 2^32) */
 
 typedef enum {
   SDA_OK = 0,
@@ -55,7 +56,8 @@ typedef enum {
  * (page "...ops.sparse_decode_attention").  Strides are in ELEMENTS of the
  * pointed-to type.
  *
- *  rows         number of (token, KV group) rows; rows = tokens * groups.
+ *  rows         number of (token, KV group) rows; rows = tokens * groups,
+ *               at most SDA_MAX_ROWS.
  *               Row r is group r % groups of token r / groups.  The
  *               groups*query_len consecutive rows of one request share one
  *               block-table row (request = r / (groups*query_len)).
@@ -157,13 +159,93 @@ int sda_splits(int rows);
  */
 size_t sda_workspace_bytes(int rows, int heads, int splits);
 
+/*
+ * Gated sliding-window decode: the fused decode of the non-DSA layers, page
+ * "vllm.models.step5.nvidia.sparse_attention", section
+ * `Step5SplitKVFlashAttentionImpl` (`forward_with_headwise_gate`, which
+ * calls `swa_decode_gated`, and `_split_kv_cache`, which views the same
+ * packed cache as K and V).  A uniform batch of tokens = requests *
+ * query_len query tokens; token j (0-based) of request q has position
+ * seq_lens[q] - query_len + j and attends, head by head, over the tokens at
+ * positions max(0, pos - window + 1) .. pos of its request (a causal window
+ * of `window` tokens, i.e. sliding_window[0] + 1).  The query heads of a KV
+ * group are packed into one workgroup (GQA), as in sda_decode, and the
+ * headwise sigmoid gate (the `_gate` helper of page "...ops.
+ * sparse_decode_attention") scales each head.  A token whose position is
+ * negative (seq_len < query_len) outputs zeros.  Strides are in ELEMENTS.
+ *
+ *  tokens       query tokens, a multiple of query_len; 0 returns SDA_OK.
+ *               tokens * groups must not exceed SDA_MAX_ROWS.
+ *  heads        query heads per KV group, 1..16.
+ *  groups       KV groups G (cache dim 1).
+ *  query_len    query tokens per request (1 decode, 2..4 MTP verify; any
+ *               value >= 1 is accepted).
+ *  block        tokens per page; a multiple of 16 (else UNSUPPORTED).
+ *  window       tokens attended, >= 1.  (window + 15) / block + 2 must not
+ *               exceed SDA_MAX_R (else UNSUPPORTED).
+ *  query        bf16 [tokens, groups*heads, 192]; head g*heads + h belongs
+ *               to KV group g.  Dim stride 1; 16-byte aligned; token and
+ *               head strides multiples of 8.
+ *  output       bf16 [tokens, groups*heads, 192], written in place; dim
+ *               stride 1; 4-byte aligned; even strides.
+ *  cache        bf16 [pages, groups, block, 384], K then V; same alignment
+ *               and 32-bit in-page offset rules as sda_decode.
+ *  block_table  int32 [requests, pages per request], unit inner stride.
+ *               Only the columns covering each window are read.
+ *  seq_lens     int32 [requests]: tokens of the request, the new ones
+ *               included.
+ *  scale        softmax scale applied to q.k.
+ *  splits       >= 1 (sda_swa_splits): each row's window is cut into
+ *               `splits` contiguous runs whose partials are merged by
+ *               log-sum-exp.  The result does not depend on it beyond
+ *               rounding.
+ *  gate         bf16 [tokens, groups*heads] gate logits, or NULL for none.
+ *  workspace    as for sda_decode, sda_workspace_bytes(tokens*groups,
+ *               heads, splits) bytes; may be NULL when splits == 1.
+ */
+typedef struct sda_swa_args {
+  int32_t tokens, heads, groups, query_len, block, window;
+  const void *query;
+  int64_t q_token_stride, q_head_stride;
+  void *output;
+  int64_t o_token_stride, o_head_stride;
+  const void *cache;
+  int64_t c_page_stride, c_group_stride, c_token_stride;
+  const int32_t *block_table;
+  int64_t table_row_stride;
+  const int32_t *seq_lens;
+  float scale;
+  int32_t splits;
+  const void *gate;
+  int64_t gate_token_stride, gate_head_stride;
+  void *workspace;
+  size_t workspace_bytes;
+} sda_swa_args;
+
+/*
+ * Enqueue one gated sliding-window decode call on `stream`: the split kernel
+ * of sda_decode in its window mode over a (tokens*groups, splits) grid, and
+ * the combine kernel when splits > 1.  Asynchronous, no allocation, no host
+ * synchronisation.  Returns an sda_status; on error nothing is launched.
+ */
+int sda_swa_decode(const sda_swa_args *args, hipStream_t stream);
+
+/*
+ * Split count for a sliding-window call: the rule of sda_splits on
+ * tokens*groups rows, further capped so that every split keeps at least 8
+ * chunks of 16 window tokens.  Host-only and pure; 1 for empty sizes.
+ */
+int sda_swa_splits(int tokens, int groups, int window);
+
 /* Static description of a status code (never NULL). */
 const char *sda_status_string(int status);
 
-/* SDA_ABI_VERSION of the built library, and sizeof(sda_decode_args), so a
- * binding can check that its mirror of the struct matches. */
+/* SDA_ABI_VERSION of the built library, and sizeof(sda_decode_args) and
+ * sizeof(sda_swa_args), so a binding can check that its mirrors of the
+ * structs match. */
 int sda_abi_version(void);
 size_t sda_args_size(void);
+size_t sda_swa_args_size(void);
 
 #ifdef __cplusplus
 }

@@ -23,7 +23,7 @@ SDA_ERR_WORKSPACE = -3
 SDA_ERR_LAUNCH = -4
 SDA_KV_BF16 = 0
 SDA_KV_FP8_E4M3 = 1
-ABI_VERSION = 1
+ABI_VERSION = 2
 HEAD_DIM = 192
 
 
@@ -58,6 +58,27 @@ class DecodeArgs(ctypes.Structure):
     ]
 
 
+class SwaArgs(ctypes.Structure):
+    """Mirror of ``sda_swa_args``; checked against sda_swa_args_size()."""
+    _fields_ = [
+        ("tokens", ctypes.c_int32), ("heads", ctypes.c_int32), ("groups", ctypes.c_int32),
+        ("query_len", ctypes.c_int32), ("block", ctypes.c_int32), ("window", ctypes.c_int32),
+        ("query", ctypes.c_void_p), ("q_token_stride", ctypes.c_int64),
+        ("q_head_stride", ctypes.c_int64),
+        ("output", ctypes.c_void_p), ("o_token_stride", ctypes.c_int64),
+        ("o_head_stride", ctypes.c_int64),
+        ("cache", ctypes.c_void_p),
+        ("c_page_stride", ctypes.c_int64), ("c_group_stride", ctypes.c_int64),
+        ("c_token_stride", ctypes.c_int64),
+        ("block_table", ctypes.c_void_p), ("table_row_stride", ctypes.c_int64),
+        ("seq_lens", ctypes.c_void_p),
+        ("scale", ctypes.c_float), ("splits", ctypes.c_int32),
+        ("gate", ctypes.c_void_p), ("gate_token_stride", ctypes.c_int64),
+        ("gate_head_stride", ctypes.c_int64),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
 _lib = None
 _lock = threading.Lock()
 
@@ -84,12 +105,21 @@ def lib() -> ctypes.CDLL:
             l.sda_abi_version.argtypes = []
             l.sda_args_size.restype = ctypes.c_size_t
             l.sda_args_size.argtypes = []
+            l.sda_swa_decode.restype = ctypes.c_int
+            l.sda_swa_decode.argtypes = [ctypes.POINTER(SwaArgs), ctypes.c_void_p]
+            l.sda_swa_splits.restype = ctypes.c_int
+            l.sda_swa_splits.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+            l.sda_swa_args_size.restype = ctypes.c_size_t
+            l.sda_swa_args_size.argtypes = []
             if l.sda_abi_version() != ABI_VERSION:
                 raise RuntimeError("libsda.so ABI version %d, binding expects %d"
                                    % (l.sda_abi_version(), ABI_VERSION))
             if l.sda_args_size() != ctypes.sizeof(DecodeArgs):
                 raise RuntimeError("sda_decode_args size mismatch: library %d, binding %d"
                                    % (l.sda_args_size(), ctypes.sizeof(DecodeArgs)))
+            if l.sda_swa_args_size() != ctypes.sizeof(SwaArgs):
+                raise RuntimeError("sda_swa_args size mismatch: library %d, binding %d"
+                                   % (l.sda_swa_args_size(), ctypes.sizeof(SwaArgs)))
             _lib = l
     return _lib
 
@@ -213,3 +243,90 @@ def sda_decode(query, cache, regions, block_table, positions, active, output, *,
 def sda_decode_raw(args: DecodeArgs, stream_handle=None) -> int:
     """Call the C entry point on a prepared struct; returns the status code."""
     return int(lib().sda_decode(ctypes.byref(args), stream_handle))
+
+
+def sda_swa_splits(tokens: int, groups: int, window: int) -> int:
+    return int(lib().sda_swa_splits(int(tokens), int(groups), int(window)))
+
+
+def make_swa_args(query, cache, block_table, seq_lens, output, *, scale, window, query_len=1,
+                  splits, gate=None, workspace=None) -> SwaArgs:
+    """Fill ``sda_swa_args`` from tensors (no validation beyond the C side).
+    ``query``/``output``: [tokens, groups*heads, 192]; ``cache``: [pages,
+    groups, block, 384]."""
+    a = SwaArgs()
+    groups = cache.shape[1]
+    a.tokens, a.heads, a.groups = query.shape[0], query.shape[1] // groups, groups
+    a.query_len, a.block, a.window = int(query_len), cache.shape[2], int(window)
+    a.query = _ptr(query)
+    a.q_token_stride, a.q_head_stride = query.stride(0), query.stride(1)
+    a.output = _ptr(output)
+    a.o_token_stride, a.o_head_stride = output.stride(0), output.stride(1)
+    a.cache = _ptr(cache)
+    a.c_page_stride, a.c_group_stride, a.c_token_stride = (
+        cache.stride(0), cache.stride(1), cache.stride(2))
+    a.block_table = _ptr(block_table)
+    a.table_row_stride = block_table.stride(0)
+    a.seq_lens = _ptr(seq_lens)
+    a.scale = float(scale)
+    a.splits = int(splits)
+    a.gate = _ptr(gate)
+    if gate is not None:
+        a.gate_token_stride, a.gate_head_stride = gate.stride(0), gate.stride(1)
+    a.workspace = _ptr(workspace)
+    a.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return a
+
+
+def check_swa_tensors(query, cache, block_table, seq_lens, output, gate):
+    """dtype and shape checks the C ABI cannot make (it sees only pointers)."""
+    if query.dtype != torch.bfloat16 or output.dtype != torch.bfloat16:
+        raise SdaError(SDA_ERR_INVALID, "query and output must be bfloat16")
+    if query.dim() != 3 or output.shape != query.shape or query.shape[2] != HEAD_DIM:
+        raise SdaError(SDA_ERR_INVALID, "query/output must be [tokens, heads, 192]")
+    if query.stride(2) != 1 or output.stride(2) != 1:
+        raise SdaError(SDA_ERR_INVALID, "query/output need unit stride in dim 2")
+    if cache.dtype != torch.bfloat16 or cache.dim() != 4 or cache.shape[3] != 2 * HEAD_DIM \
+            or cache.stride(3) != 1:
+        raise SdaError(SDA_ERR_INVALID, "cache must be bfloat16 [pages, G, block, 384]")
+    if query.shape[1] % cache.shape[1]:
+        raise SdaError(SDA_ERR_INVALID, "query heads must be a multiple of the KV groups")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.stride(1) != 1:
+        raise SdaError(SDA_ERR_INVALID, "block_table must be int32 2-D, unit inner stride")
+    if seq_lens.dtype != torch.int32 or not seq_lens.is_contiguous() or \
+            seq_lens.numel() != block_table.shape[0]:
+        raise SdaError(SDA_ERR_INVALID, "seq_lens must be contiguous int32 [requests]")
+    if gate is not None and (gate.dtype != torch.bfloat16 or gate.dim() != 2 or
+                             gate.shape != query.shape[:2]):
+        raise SdaError(SDA_ERR_INVALID, "gate must be bfloat16 [tokens, heads]")
+
+
+def sda_swa_decode(query, cache, block_table, seq_lens, output, *, scale, window,
+                   query_len=1, splits, gate=None, workspace=None, stream=None) -> None:
+    """Enqueue ``sda_swa_decode`` (gated sliding-window decode) on ``stream``.
+
+    Argument names follow ``swa_decode_gated`` as ``forward_with_headwise_gate``
+    calls it on the page "vllm.models.step5.nvidia.sparse_attention", with the
+    packed cache in place of its K and V views.  The workspace is allocated
+    here through torch when omitted and splits > 1.
+    """
+    check_swa_tensors(query, cache, block_table, seq_lens, output, gate)
+    groups = cache.shape[1]
+    rows, heads = query.shape[0] * groups, query.shape[1] // groups
+    if workspace is None and splits > 1 and rows > 0:
+        nbytes = sda_workspace_bytes(rows, heads, splits)
+        if nbytes:
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=query.device)
+    a = make_swa_args(query, cache, block_table, seq_lens, output, scale=scale, window=window,
+                      query_len=query_len, splits=splits, gate=gate, workspace=workspace)
+    if stream is None:
+        stream = torch.cuda.current_stream(query.device) if query.is_cuda else None
+    handle = None if stream is None else ctypes.c_void_p(stream.cuda_stream)
+    rc = lib().sda_swa_decode(ctypes.byref(a), handle)
+    if rc != SDA_OK:
+        raise SdaError(rc, status_string(rc))
+
+
+def sda_swa_decode_raw(args: SwaArgs, stream_handle=None) -> int:
+    """Call sda_swa_decode on a prepared struct; returns the status code."""
+    return int(lib().sda_swa_decode(ctypes.byref(args), stream_handle))

@@ -24,6 +24,7 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 // 2 splits 86 us.
 constexpr int kComputeUnits = 256;
 constexpr int kMaxHeuristicSplits = 32;
+constexpr int kSwaMinChunksPerSplit = 8;
 
 }  // namespace
 
@@ -75,7 +76,8 @@ int sda_decode(const sda_decode_args* a, hipStream_t stream) {
   if (a->rows % rows_per_req) return SDA_ERR_INVALID;
   const bool fp8 = a->kv_dtype == SDA_KV_FP8_E4M3;
   if (fp8 && (!a->k_scale || !a->v_scale)) return SDA_ERR_INVALID;
-  if (a->R > SDA_MAX_R || a->splits > SDA_MAX_SPLITS) return SDA_ERR_UNSUPPORTED;
+  if (a->R > SDA_MAX_R || a->splits > SDA_MAX_SPLITS || a->rows > SDA_MAX_ROWS)
+    return SDA_ERR_UNSUPPORTED;
   if (a->rows == 0) return SDA_OK;  // nothing to do, nothing launched
 
   if (!a->query || !a->output || !a->cache || !a->block_table || !a->positions || !a->active ||
@@ -96,11 +98,14 @@ int sda_decode(const sda_decode_args* a, hipStream_t stream) {
     return SDA_ERR_UNSUPPORTED;
 
   sda::Params p{};
+  // row r = token r / groups, group r % groups: row stride per group
   p.q = static_cast<const uint16_t*>(a->query);
-  p.qrs = a->q_row_stride;
+  p.qts = a->q_row_stride * a->groups;
+  p.qgs = a->q_row_stride;
   p.qhs = a->q_head_stride;
   p.out = static_cast<uint16_t*>(a->output);
-  p.ors = a->o_row_stride;
+  p.ots = a->o_row_stride * a->groups;
+  p.ogs = a->o_row_stride;
   p.ohs = a->o_head_stride;
   p.cache = static_cast<const uint8_t*>(a->cache);
   p.cps = a->c_page_stride;
@@ -138,6 +143,92 @@ int sda_decode(const sda_decode_args* a, hipStream_t stream) {
   }
 
   hipError_t e = sda::launch(p, fp8, stream);
+  return e == hipSuccess ? SDA_OK : SDA_ERR_LAUNCH;
+}
+
+size_t sda_swa_args_size(void) { return sizeof(sda_swa_args); }
+
+int sda_swa_splits(int tokens, int groups, int window) {
+  if (tokens <= 0 || groups <= 0 || window <= 0) return 1;
+  // The row-count rule of sda_splits, and at least kSwaMinChunksPerSplit
+  // 16-token chunks per split so that each of the 4 waves keeps its pipeline.
+  const int64_t rows = (int64_t)tokens * groups;
+  const int64_t chunks = ((int64_t)window + 15) / 16;
+  int splits = 1;
+  while (splits < kMaxHeuristicSplits && rows * splits * 2 <= kComputeUnits &&
+         chunks >= (int64_t)kSwaMinChunksPerSplit * splits * 2)
+    splits *= 2;
+  return splits;
+}
+
+int sda_swa_decode(const sda_swa_args* a, hipStream_t stream) {
+  if (!a) return SDA_ERR_INVALID;
+  // Shape contract of the fused path of `forward_with_headwise_gate`: a
+  // uniform batch (tokens = requests * query_len), head dim 192, <= 16 query
+  // heads per KV group, a causal window of >= 1 token.
+  if (a->tokens < 0 || a->heads < 1 || a->heads > SDA_MAX_HEADS || a->groups < 1 ||
+      a->query_len < 1 || a->block < 1 || a->window < 1 || a->splits < 1)
+    return SDA_ERR_INVALID;
+  if (a->tokens % a->query_len) return SDA_ERR_INVALID;
+  if (a->splits > SDA_MAX_SPLITS || a->block % 16) return SDA_ERR_UNSUPPORTED;
+  // LDS page list: a split's run of chunks spans at most window + 15 tokens.
+  if (((int64_t)a->window + 15) / a->block + 2 > sda::kMaxRegions) return SDA_ERR_UNSUPPORTED;
+  const int64_t rows = (int64_t)a->tokens * a->groups;
+  if (rows > SDA_MAX_ROWS) return SDA_ERR_UNSUPPORTED;
+  if (a->tokens == 0) return SDA_OK;
+
+  if (!a->query || !a->output || !a->cache || !a->block_table || !a->seq_lens)
+    return SDA_ERR_INVALID;
+  if (!aligned(a->query, 16) || a->q_token_stride % 8 || a->q_head_stride % 8)
+    return SDA_ERR_UNSUPPORTED;
+  if (!aligned(a->cache, 16) || (a->c_page_stride * 2) % 16 || (a->c_group_stride * 2) % 16 ||
+      (a->c_token_stride * 2) % 16)
+    return SDA_ERR_UNSUPPORTED;
+  if (!aligned(a->output, 4) || a->o_token_stride % 2 || a->o_head_stride % 2)
+    return SDA_ERR_UNSUPPORTED;
+  if (a->c_token_stride < 0 || (int64_t)a->block * a->c_token_stride * 2 + 2 * SDA_KV_ROW > 0xFFFFFFFFll)
+    return SDA_ERR_UNSUPPORTED;
+
+  sda::Params p{};
+  p.q = static_cast<const uint16_t*>(a->query);
+  p.qts = a->q_token_stride;
+  p.qgs = a->q_head_stride * a->heads;  // group g's heads start at head g*heads
+  p.qhs = a->q_head_stride;
+  p.out = static_cast<uint16_t*>(a->output);
+  p.ots = a->o_token_stride;
+  p.ogs = a->o_head_stride * a->heads;
+  p.ohs = a->o_head_stride;
+  p.cache = static_cast<const uint8_t*>(a->cache);
+  p.cps = a->c_page_stride;
+  p.cgs = a->c_group_stride;
+  p.cts = a->c_token_stride;
+  p.table = a->block_table;
+  p.trs = a->table_row_stride;
+  p.seq_lens = a->seq_lens;
+  p.gate = static_cast<const uint16_t*>(a->gate);
+  p.grs = a->gate_token_stride;
+  p.ghs = a->gate_head_stride;
+  p.scale = a->scale;
+  p.rows = (int32_t)rows;
+  p.heads = a->heads;
+  p.groups = a->groups;
+  p.rows_per_req = a->groups * a->query_len;
+  p.block = a->block;
+  p.rt = a->block;
+  p.splits = a->splits;
+  p.gated = a->gate ? 1 : 0;
+  p.query_len = a->query_len;
+  p.window = a->window;
+
+  if (a->splits > 1) {
+    size_t need = sda_workspace_bytes(p.rows, a->heads, a->splits);
+    if (!a->workspace || a->workspace_bytes < need || !aligned(a->workspace, 16))
+      return SDA_ERR_WORKSPACE;
+    p.partial = static_cast<float*>(a->workspace);
+    p.lse = p.partial + (size_t)p.rows * a->splits * a->heads * SDA_HEAD_DIM;
+  }
+
+  hipError_t e = sda::launch_window(p, stream);
   return e == hipSuccess ? SDA_OK : SDA_ERR_LAUNCH;
 }
 

@@ -69,6 +69,13 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
 
+// How a split finds the cache rows of its token slots.
+enum Addr : int {
+  kGeneral = 0,  // region list; a chunk may span regions (per-lane 64-bit addresses)
+  kUniform = 1,  // region list; every chunk lies inside one region
+  kWindow = 2,   // a contiguous sliding window of tokens, 16-token chunks
+};
+
 // Per cache dtype: tokens per chunk, V bytes per token, 16-byte V pieces per token.
 template <bool kFp8>
 struct Cfg {
@@ -151,7 +158,7 @@ __device__ __forceinline__ int swz_k(int row) {
   "s_mov_b32 m0, %[sv]"
 
 // dma_chunk_sbase: one uniform 64-bit base (SGPRs) plus 32-bit per-lane
-// byte offsets (kUni chunks, all tokens in one region).
+// byte offsets (chunks inside one region or one page).
 template <bool kFp8>
 __device__ __forceinline__ void dma_chunk_sbase(const uint8_t* base, uint32_t stage,
                                                 const uint32_t (&ko)[6],
@@ -198,52 +205,17 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const SDA_LDS void*)p;
 }
 
-// Where one token slot of a chunk lives.  Masked slots are redirected to the
-// first token of a region of the split (always visible), so every load stays
-// in bounds and every V row in LDS is finite data whose weight is exactly 0.
-struct ChunkCtx {
-  int c;                       // chunk index within this split
-  // uniform-region chunks (region_tokens a multiple of the chunk size):
-  int64_t rbase;               // element offset of the region's first token
-  int off0;                    // slot offset of the chunk within the region
-  int nval;                    // visible tokens of the region
-};
-
-template <bool kFp8, bool kUni>
-__device__ __forceinline__ int64_t token_elem(const Params& p, const ChunkCtx& cx, int tau,
-                                              const int64_t* s_base, const int* s_n, int nreg,
-                                              bool& valid) {
-  if (kUni) {
-    int off = cx.off0 + tau;
-    valid = off < cx.nval;
-    return cx.rbase + (int64_t)(valid ? off : 0) * p.cts;
-  } else {
-    int slot = cx.c * Cfg<kFp8>::kTok + tau;
-    int k = slot / p.rt;
-    int off = slot - k * p.rt;
-    int kk = k < nreg ? k : nreg - 1;
-    valid = k < nreg && off < s_n[kk];
-    return s_base[kk] + (int64_t)(valid ? off : 0) * p.cts;
-  }
-}
-
-template <bool kFp8, bool kUni>
-__device__ __forceinline__ ChunkCtx chunk_ctx(const Params& p, int c, const int64_t* s_base,
-                                              const int* s_n) {
-  ChunkCtx cx;
-  cx.c = c;
-  if (kUni) {
-    int slot0 = c * Cfg<kFp8>::kTok;
-    int k = slot0 / p.rt;
-    cx.off0 = slot0 - k * p.rt;
-    cx.rbase = s_base[k];
-    cx.nval = s_n[k];
-  } else {
-    cx.off0 = 0;
-    cx.rbase = 0;
-    cx.nval = 0;
-  }
-  return cx;
+// Where token slot `slot` of a split lives (general addressing: a chunk may
+// span regions).  A masked slot is redirected to the first token of a region
+// of the split (always visible), so every load stays in bounds and every V
+// row in LDS is finite data whose weight is exactly 0.
+__device__ __forceinline__ int64_t token_elem(const Params& p, int slot, const int64_t* s_base,
+                                              const int* s_n, int nreg, bool& valid) {
+  int k = slot / p.rt;
+  int off = slot - k * p.rt;
+  int kk = k < nreg ? k : nreg - 1;
+  valid = k < nreg && off < s_n[kk];
+  return s_base[kk] + (int64_t)(valid ? off : 0) * p.cts;
 }
 
 // Loop-invariant DMA geometry of one lane.  Stage slot 64j + lane (j = 0..5)
@@ -271,31 +243,63 @@ __device__ __forceinline__ LaneDma lane_dma(int lane) {
   return d;
 }
 
+// A split's sliding window: visible positions w0..pos; chunk c starts at
+// token t_base + 16c; s_base[k] is the cache offset of block-table column
+// col_lo + k (page and KV group).
+struct Win {
+  int w0, pos, t_base, col_lo;
+};
+
+// Wave-uniform 64-bit address from a per-lane value that is uniform in fact.
+// readfirstlane returns int: go through uint32_t so the low half is
+// zero-extended, never sign-extended into the high half.
+__device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* ptr) {
+  const uint64_t b64 = (uint64_t)(uintptr_t)ptr;
+  const uint32_t b_lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b64);
+  const uint32_t b_hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b64 >> 32));
+  return (const uint8_t*)(uintptr_t)(((uint64_t)b_hi << 32) | (uint64_t)b_lo);
+}
+
 // Issue chunk c into LDS stage `stage`.  Returns the visibility of this
-// lane's S^T rows (bit t: token slot 16t + i16).  Masked slots load the first
-// token of their region instead (visible, in bounds, weight 0).
-template <bool kFp8, bool kUni>
+// lane's S^T rows (bit t: token slot 16t + i16).  Masked slots load a visible
+// token of the same chunk instead (in bounds, finite, weight 0): the first
+// token of their region, or the nearest window token.
+template <bool kFp8, int kAddr>
 __device__ __forceinline__ uint32_t issue_chunk(const Params& p, int c, int nreg,
                                                 const int64_t* s_base, const int* s_n, int lane,
                                                 uint32_t stage, const LaneDma& ld,
-                                                uint32_t cts_bytes) {
+                                                uint32_t cts_bytes, const Win& win) {
   using C = Cfg<kFp8>;
   const int i16 = lane & 15;
   const uint32_t st = (uint32_t)__builtin_amdgcn_readfirstlane(stage);
   uint32_t vbits = 0;
-  if (kUni) {
+  if (kAddr == kWindow) {
+    // 16 consecutive tokens of one page (block is a multiple of 16): uniform
+    // base at the chunk's first token, 32-bit lane offsets.
+    static_assert(!kFp8 || kAddr != kWindow, "window chunks are 16 bf16 tokens");
+    const int t0 = win.t_base + 16 * c;
+    const int col = t0 / p.block;
+    const int64_t rb = s_base[col - win.col_lo] + (int64_t)(t0 - col * p.block) * p.cts;
+    const uint8_t* base = uniform_ptr(p.cache + rb * C::kEsz);
+    const int tok = t0 + i16;
+    vbits = (tok >= win.w0 && tok <= win.pos) ? 1u : 0u;
+    uint32_t ko[6], vo[6];
+#pragma unroll
+    for (int j = 0; j < 6; ++j) {
+      const int tc = min(max(t0 + ld.row[j], win.w0), win.pos);
+      const uint32_t roff = (uint32_t)(tc - t0) * cts_bytes;
+      ko[j] = roff + ld.koff[j];
+      vo[j] = roff + ld.voff[j];
+    }
+    dma_chunk_sbase<kFp8>(base, st, ko, vo);
+  } else if (kAddr == kUniform) {
     // The chunk lies inside one region: uniform base, 32-bit lane offsets.
     const int slot0 = c * C::kTok;
     const int k = slot0 / p.rt;
     const int off0 = slot0 - k * p.rt;
     const int64_t rb = s_base[k];
     const int nval = __builtin_amdgcn_readfirstlane(s_n[k]);
-    // readfirstlane returns int: go through uint32_t so the low half is
-    // zero-extended, never sign-extended into the high half.
-    const uint64_t b64 = (uint64_t)(uintptr_t)(p.cache + rb * C::kEsz);
-    const uint32_t b_lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b64);
-    const uint32_t b_hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b64 >> 32));
-    const uint64_t base = ((uint64_t)b_hi << 32) | (uint64_t)b_lo;
+    const uint8_t* base = uniform_ptr(p.cache + rb * C::kEsz);
 #pragma unroll
     for (int t = 0; t < (kFp8 ? 2 : 1); ++t) vbits |= (off0 + 16 * t + i16 < nval ? 1u : 0u) << t;
     uint32_t ko[6], vo[6];
@@ -306,13 +310,13 @@ __device__ __forceinline__ uint32_t issue_chunk(const Params& p, int c, int nreg
       ko[j] = roff + ld.koff[j];
       vo[j] = roff + ld.voff[j];
     }
-    dma_chunk_sbase<kFp8>((const uint8_t*)(uintptr_t)base, st, ko, vo);
+    dma_chunk_sbase<kFp8>(base, st, ko, vo);
   } else {
-    const ChunkCtx cx = chunk_ctx<kFp8, false>(p, c, s_base, s_n);
+    const int slot0 = c * C::kTok;
 #pragma unroll
     for (int t = 0; t < (kFp8 ? 2 : 1); ++t) {
       bool valid;
-      (void)token_elem<kFp8, false>(p, cx, 16 * t + i16, s_base, s_n, nreg, valid);
+      (void)token_elem(p, slot0 + 16 * t + i16, s_base, s_n, nreg, valid);
       vbits |= (valid ? 1u : 0u) << t;
     }
     const uint8_t* ka[6];
@@ -320,7 +324,7 @@ __device__ __forceinline__ uint32_t issue_chunk(const Params& p, int c, int nreg
 #pragma unroll
     for (int j = 0; j < 6; ++j) {
       bool valid;
-      const int64_t e = token_elem<kFp8, false>(p, cx, ld.row[j], s_base, s_n, nreg, valid);
+      const int64_t e = token_elem(p, slot0 + ld.row[j], s_base, s_n, nreg, valid);
       const uint8_t* row = p.cache + e * C::kEsz;
       ka[j] = row + ld.koff[j];
       va[j] = row + ld.voff[j];
@@ -462,16 +466,22 @@ __device__ __forceinline__ void compute_chunk(const uint8_t* stage, uint32_t vbi
   }
 }
 
-__device__ __forceinline__ void store_row_pair(const Params& p, int r, int h, int d, float o0,
-                                               float o1) {
+__device__ __forceinline__ uint16_t* out_row(const Params& p, int r) {
+  const int t = r / p.groups;
+  return p.out + (int64_t)t * p.ots + (int64_t)(r - t * p.groups) * p.ogs;
+}
+
+__device__ __forceinline__ void store_row_pair(uint16_t* orow, const Params& p, int h, int d,
+                                               float o0, float o1) {
   uint32_t v = float_to_bf16_bits(o0) | (float_to_bf16_bits(o1) << 16);
-  *reinterpret_cast<uint32_t*>(p.out + (int64_t)r * p.ors + (int64_t)h * p.ohs + d) = v;
+  *reinterpret_cast<uint32_t*>(orow + (int64_t)h * p.ohs + d) = v;
 }
 
 __device__ __forceinline__ void clear_row(const Params& p, int r, int tid, int nthreads) {
+  uint16_t* orow = out_row(p, r);
   for (int e = tid; e < p.heads * (kDim / 2); e += nthreads) {
     int h = e / (kDim / 2), d = 2 * (e - h * (kDim / 2));
-    *reinterpret_cast<uint32_t*>(p.out + (int64_t)r * p.ors + (int64_t)h * p.ohs + d) = 0u;
+    *reinterpret_cast<uint32_t*>(orow + (int64_t)h * p.ohs + d) = 0u;
   }
 }
 
@@ -482,7 +492,7 @@ __device__ __forceinline__ bool run_steps(F& step, int i0, std::integer_sequence
   return (step(i0, std::integral_constant<int, Ss>{}) && ...);
 }
 
-template <bool kFp8, bool kFused, bool kUni>
+template <bool kFp8, bool kFused, int kAddr>
 // LDS use (stages + region list) allows one workgroup, i.e. one wave per SIMD.
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void split_kernel(
     const Params p) {
@@ -497,17 +507,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   __shared__ float s_m[kWaves][16];
   __shared__ float s_l[kWaves][16];
 
-  if (!p.active[r]) {
+  if (kAddr != kWindow && !p.active[r]) {
     // Inactive rows read nothing else.  With splits > 1 the combine clears.
     if (kFused && p.clear) clear_row(p, r, tid, kThreads);
     return;
   }
 
-  const int pos = p.positions[r];
-  const int g = r % p.groups;
+  const int token = r / p.groups;
+  const int g = r - token * p.groups;
   const int req = r / p.rows_per_req;
-  const int rt = p.rt;
-  const int32_t* reg = p.regions + (int64_t)r * p.rrs;
+  // Window mode: token j of a request of length L sits at L - query_len + j.
+  const int pos = kAddr == kWindow
+                      ? p.seq_lens[req] - p.query_len + (token - req * p.query_len)
+                      : p.positions[r];
 
   // Q^T B-operand: lane holds head (lane & 15), 8 dims per k-slice, in the
   // same dim order as the K loads.  Issued first so that its latency overlaps
@@ -515,7 +527,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   const int i16 = lane & 15, g4 = lane >> 4;
   u32x4 qreg[6];
   {
-    const uint16_t* qrow = p.q + (int64_t)r * p.qrs + (int64_t)i16 * p.qhs;
+    const uint16_t* qrow =
+        p.q + (int64_t)token * p.qts + (int64_t)g * p.qgs + (int64_t)i16 * p.qhs;
 #pragma unroll
     for (int cc = 0; cc < 6; ++cc) {
       int d = kFp8 ? 64 * (cc >> 1) + 16 * g4 + 8 * (cc & 1) : 32 * cc + 8 * g4;
@@ -523,41 +536,69 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     }
   }
 
-  // Region resolution, done by every wave on its own with no workgroup
-  // barrier.  Each wave ranks the visible slots (id >= 0, first token <= pos)
-  // in slot order, 64 at a time.  It takes this split's balanced share,
-  // ranks [ceil(s*V/S), ceil((s+1)*V/S)), and writes the share's cache
-  // offsets and visible counts to the shared LDS list.  All waves write
-  // identical values, and a wave only ever reads entries after its own
-  // writes (LDS executes a wave's operations in order), so the list is
-  // consistent without synchronisation.
-  int nvis = 0;
-  int id0 = -1;  // the first 64 slots stay in registers for the second pass
-  for (int j0 = 0; j0 < p.R; j0 += 64) {
-    const int j = j0 + lane;
-    const int id = j < p.R ? reg[j] : -1;
-    if (j0 == 0) id0 = id;
-    nvis += __popcll(__ballot(id >= 0 && (int64_t)id * rt <= pos));
-  }
-  const int lo = (int)(((int64_t)split * nvis + p.splits - 1) / p.splits);
-  const int hi = (int)(((int64_t)(split + 1) * nvis + p.splits - 1) / p.splits);
-  const int nreg = hi - lo;
-  int base_rank = 0;
-  for (int j0 = 0; j0 < p.R; j0 += 64) {
-    const int j = j0 + lane;
-    const int id = j0 == 0 ? id0 : (j < p.R ? reg[j] : -1);
-    const bool vis = id >= 0 && (int64_t)id * rt <= pos;
-    const uint64_t m = __ballot(vis);
-    const int k = base_rank + __popcll(m & ((1ull << lane) - 1ull));
-    if (vis && k >= lo && k < hi) {
-      const int64_t t0 = (int64_t)id * rt;
-      const int64_t col = t0 / p.block;
-      const int off0 = (int)(t0 - col * p.block);
-      const int64_t page = p.table[(int64_t)req * p.trs + col];
-      s_base[k - lo] = page * p.cps + (int64_t)g * p.cgs + (int64_t)off0 * p.cts;
-      s_n[k - lo] = (int)min((int64_t)rt, (int64_t)pos - t0 + 1);
+  // Row extent, resolved by every wave on its own with no workgroup barrier.
+  // All waves write identical values to the shared LDS list, and a wave only
+  // ever reads entries after its own writes (LDS executes a wave's
+  // operations in order), so the list is consistent without synchronisation.
+  int nreg = 0, nchunks = 0;
+  Win win{0, 0, 0, 0};
+  if (kAddr == kWindow) {
+    // The window's 16-token chunks, aligned down to a multiple of 16 so that
+    // a chunk never straddles a page, are dealt to the splits in balanced
+    // contiguous runs.  s_base gets the pages this split's run touches.
+    const int w0 = max(0, pos - p.window + 1);
+    const int a = w0 & ~15;
+    const int total = pos < 0 ? 0 : (pos + 1 - a + 15) >> 4;
+    const int clo = (int)(((int64_t)split * total + p.splits - 1) / p.splits);
+    const int chi = (int)(((int64_t)(split + 1) * total + p.splits - 1) / p.splits);
+    nchunks = chi - clo;
+    win.w0 = w0;
+    win.pos = pos;
+    win.t_base = a + 16 * clo;
+    if (nchunks > 0) {
+      const int tb = min(a + 16 * chi, pos + 1) - 1;
+      win.col_lo = win.t_base / p.block;
+      const int npages = tb / p.block - win.col_lo + 1;
+      const int32_t* trow = p.table + (int64_t)req * p.trs + win.col_lo;
+      for (int k = lane; k < npages; k += 64)
+        s_base[k] = (int64_t)trow[k] * p.cps + (int64_t)g * p.cgs;
     }
-    base_rank += __popcll(m);
+  } else {
+    const int rt = p.rt;
+    const int32_t* reg = p.regions + (int64_t)r * p.rrs;
+    // Each wave ranks the visible slots (id >= 0, first token <= pos) in
+    // slot order, 64 at a time.  It takes this split's balanced share, ranks
+    // [ceil(s*V/S), ceil((s+1)*V/S)), and writes the share's cache offsets
+    // and visible counts to the LDS list.
+    int nvis = 0;
+    int id0 = -1;  // the first 64 slots stay in registers for the second pass
+    for (int j0 = 0; j0 < p.R; j0 += 64) {
+      const int j = j0 + lane;
+      const int id = j < p.R ? reg[j] : -1;
+      if (j0 == 0) id0 = id;
+      nvis += __popcll(__ballot(id >= 0 && (int64_t)id * rt <= pos));
+    }
+    const int lo = (int)(((int64_t)split * nvis + p.splits - 1) / p.splits);
+    const int hi = (int)(((int64_t)(split + 1) * nvis + p.splits - 1) / p.splits);
+    nreg = hi - lo;
+    int base_rank = 0;
+    for (int j0 = 0; j0 < p.R; j0 += 64) {
+      const int j = j0 + lane;
+      const int id = j0 == 0 ? id0 : (j < p.R ? reg[j] : -1);
+      const bool vis = id >= 0 && (int64_t)id * rt <= pos;
+      const uint64_t m = __ballot(vis);
+      const int k = base_rank + __popcll(m & ((1ull << lane) - 1ull));
+      if (vis && k >= lo && k < hi) {
+        const int64_t t0 = (int64_t)id * rt;
+        const int64_t col = t0 / p.block;
+        const int off0 = (int)(t0 - col * p.block);
+        const int64_t page = p.table[(int64_t)req * p.trs + col];
+        s_base[k - lo] = page * p.cps + (int64_t)g * p.cgs + (int64_t)off0 * p.cts;
+        s_n[k - lo] = (int)min((int64_t)rt, (int64_t)pos - t0 + 1);
+      }
+      base_rank += __popcll(m);
+    }
+    nchunks = (int)(((int64_t)nreg * rt + C::kTok - 1) / C::kTok);
   }
   // The list reads below must follow this wave's own list writes.
   __asm__ __volatile__("" ::: "memory");
@@ -575,7 +616,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   st.m = -INFINITY;
   st.l = 0.f;
 
-  const int nchunks = (int)(((int64_t)nreg * rt + C::kTok - 1) / C::kTok);
   const uint8_t* my_stage = &s_stage[wave][0][0];
   const uint32_t my_stage_lds = lds_addr(my_stage);
 
@@ -592,8 +632,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     uint32_t vb[kStages];
 #pragma unroll
     for (int s = 0; s < kStages - 1; ++s)
-      vb[s] = issue_chunk<kFp8, kUni>(p, min(wave + kWaves * s, last), nreg, s_base, s_n, lane,
-                                      my_stage_lds + s * kChunkBytes, ld, cts_bytes);
+      vb[s] = issue_chunk<kFp8, kAddr>(p, min(wave + kWaves * s, last), nreg, s_base, s_n, lane,
+                                       my_stage_lds + s * kChunkBytes, ld, cts_bytes, win);
     auto step = [&](int i0, auto stage_c) -> bool {
       constexpr int S = decltype(stage_c)::value;
       constexpr int SN = (S + kStages - 1) % kStages;
@@ -601,8 +641,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       if (c >= nchunks) return false;
       // Stage SN was last read by the previous iteration, whose reads all
       // completed before its MFMAs; the asm below keeps them above the DMA.
-      vb[SN] = issue_chunk<kFp8, kUni>(p, min(c + kWaves * (kStages - 1), last), nreg, s_base,
-                                       s_n, lane, my_stage_lds + SN * kChunkBytes, ld, cts_bytes);
+      vb[SN] = issue_chunk<kFp8, kAddr>(p, min(c + kWaves * (kStages - 1), last), nreg, s_base,
+                                        s_n, lane, my_stage_lds + SN * kChunkBytes, ld, cts_bytes,
+                                        win);
       wait_vmcnt<kOpsPerChunk * (kStages - 1)>();
       compute_chunk<kFp8>(my_stage + S * kChunkBytes, vb[S], qreg, qk_scale_log2, lane, st);
       return true;
@@ -635,6 +676,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   __syncthreads();
 
   const float vscale = kFp8 ? *p.v_scale : 1.0f;
+  uint16_t* orow = out_row(p, r);
   for (int e = tid; e < p.heads * (kDim / 2); e += kThreads) {
     int h = e / (kDim / 2), d = 2 * (e - h * (kDim / 2));
     float M = -INFINITY;
@@ -656,12 +698,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     }
     if (kFused) {
       if (p.gated) {
-        float gv = gate_value(p.gate, (int64_t)(r / p.groups) * p.grs +
-                                          (int64_t)(g * p.heads + h) * p.ghs);
+        float gv = gate_value(p.gate, (int64_t)token * p.grs + (int64_t)(g * p.heads + h) * p.ghs);
         o0 *= gv;
         o1 *= gv;
       }
-      store_row_pair(p, r, h, d, o0, o1);
+      store_row_pair(orow, p, h, d, o0, o1);
     } else {
       int64_t ph = ((int64_t)r * p.splits + split) * p.heads + h;
       *reinterpret_cast<float2*>(p.partial + ph * kDim + d) = make_float2(o0, o1);
@@ -675,8 +716,8 @@ __global__ __launch_bounds__(64) void combine_kernel(const Params p) {
   const int r = blockIdx.x / p.heads;
   const int h = blockIdx.x - r * p.heads;
   const int tid = threadIdx.x;
-  uint16_t* orow = p.out + (int64_t)r * p.ors + (int64_t)h * p.ohs;
-  if (!p.active[r]) {
+  uint16_t* orow = out_row(p, r) + (int64_t)h * p.ohs;
+  if (p.active && !p.active[r]) {
     if (p.clear)
       for (int d = tid; d < kDim; d += 64) orow[d] = 0;
     return;
@@ -706,9 +747,9 @@ __global__ __launch_bounds__(64) void combine_kernel(const Params p) {
   for (int u = 0; u < 3; ++u) orow[tid + 64 * u] = (uint16_t)float_to_bf16_bits(o[u] * gv);
 }
 
-template <bool kFp8, bool kFused, bool kUni>
+template <bool kFp8, bool kFused, int kAddr>
 void launch_split(const Params& p, hipStream_t stream) {
-  hipLaunchKernelGGL((split_kernel<kFp8, kFused, kUni>), dim3((unsigned)p.rows, (unsigned)p.splits),
+  hipLaunchKernelGGL((split_kernel<kFp8, kFused, kAddr>), dim3((unsigned)p.rows, (unsigned)p.splits),
                      dim3(kThreads), 0, stream, p);
 }
 
@@ -717,9 +758,18 @@ void launch_dtype(const Params& p, hipStream_t stream) {
   const bool fused = p.splits == 1;
   const bool uni = p.rt % Cfg<kFp8>::kTok == 0;
   if (fused)
-    uni ? launch_split<kFp8, true, true>(p, stream) : launch_split<kFp8, true, false>(p, stream);
+    uni ? launch_split<kFp8, true, kUniform>(p, stream)
+        : launch_split<kFp8, true, kGeneral>(p, stream);
   else
-    uni ? launch_split<kFp8, false, true>(p, stream) : launch_split<kFp8, false, false>(p, stream);
+    uni ? launch_split<kFp8, false, kUniform>(p, stream)
+        : launch_split<kFp8, false, kGeneral>(p, stream);
+}
+
+hipError_t launch_combine(const Params& p, hipStream_t stream) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.splits == 1) return e;
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)(p.rows * p.heads)), dim3(64), 0, stream, p);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -729,10 +779,15 @@ hipError_t launch(const Params& p, bool fp8, hipStream_t stream) {
     launch_dtype<true>(p, stream);
   else
     launch_dtype<false>(p, stream);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.splits == 1) return e;
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)(p.rows * p.heads)), dim3(64), 0, stream, p);
-  return hipGetLastError();
+  return launch_combine(p, stream);
+}
+
+hipError_t launch_window(const Params& p, hipStream_t stream) {
+  if (p.splits == 1)
+    launch_split<false, true, kWindow>(p, stream);
+  else
+    launch_split<false, false, kWindow>(p, stream);
+  return launch_combine(p, stream);
 }
 
 }  // namespace sda

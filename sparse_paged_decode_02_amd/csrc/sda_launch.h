@@ -10,18 +10,21 @@ namespace sda {
 constexpr int kMaxRegions = 2048;  // LDS region list per workgroup (= SDA_MAX_R)
 
 struct Params {
+  // Row r is group r % groups of token r / groups; its head h sits at
+  // q + (r / groups) * qts + (r % groups) * qgs + h * qhs (likewise out).
   const uint16_t* q;          // bf16 bits
-  int64_t qrs, qhs;           // query row / head strides (elements)
+  int64_t qts, qgs, qhs;      // query token / group / head strides (elements)
   uint16_t* out;              // bf16 bits
-  int64_t ors, ohs;
+  int64_t ots, ogs, ohs;
   const uint8_t* cache;       // byte view of the cache
   int64_t cps, cgs, cts;      // cache page / group / token strides (elements)
   const int32_t* regions;
   int64_t rrs;
   const int32_t* table;
   int64_t trs;
-  const int32_t* positions;
-  const uint8_t* active;
+  const int32_t* positions;   // sparse: [rows]
+  const uint8_t* active;      // sparse: [rows]; null means every row is active
+  const int32_t* seq_lens;    // window: [requests]
   const float* k_scale;
   const float* v_scale;
   const uint16_t* gate;       // bf16 bits or null
@@ -30,9 +33,16 @@ struct Params {
   float* lse;                 // [rows, splits, heads] fp32, base-2 (splits > 1)
   float scale;
   int32_t rows, heads, groups, rows_per_req, block, R, rt, splits, clear, gated;
+  int32_t query_len, window;  // window mode
 };
 
-// Enqueue the split kernel (and the combine kernel when splits > 1).
+// Enqueue the split kernel (and the combine kernel when splits > 1) over
+// region lists (sparse decode).
 hipError_t launch(const Params& p, bool fp8, hipStream_t stream);
+
+// The same kernels over each row's sliding window (bf16 cache): token j of a
+// request of length L sits at position L - query_len + j and attends over
+// positions max(0, pos - window + 1) .. pos.  Requires block % 16 == 0.
+hipError_t launch_window(const Params& p, hipStream_t stream);
 
 }  // namespace sda

@@ -19,7 +19,8 @@ def _declared_functions():
 def test_library_exports_every_declared_function():
     names = _declared_functions()
     assert {"sda_decode", "sda_splits", "sda_workspace_bytes", "sda_status_string",
-            "sda_abi_version", "sda_args_size"} <= set(names)
+            "sda_abi_version", "sda_args_size", "sda_swa_decode", "sda_swa_splits",
+            "sda_swa_args_size"} <= set(names)
     lib = B.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -29,6 +30,7 @@ def test_abi_version_and_struct_size():
     lib = B.lib()
     assert lib.sda_abi_version() == B.ABI_VERSION
     assert lib.sda_args_size() == ctypes.sizeof(B.DecodeArgs)
+    assert lib.sda_swa_args_size() == ctypes.sizeof(B.SwaArgs)
 
 
 def _table(name):
@@ -36,8 +38,7 @@ def _table(name):
     for line in open(os.path.join(ROOT, "tests", "golden", name)):
         line = line.split("#")[0].strip()
         if line:
-            a, b = line.split()
-            rows.append((int(a), int(b)))
+            rows.append(tuple(int(x) for x in line.split()))
     return rows
 
 
@@ -133,3 +134,70 @@ def test_fp8_scale_pointers_required_only_for_fp8():
     # bf16 with no scales is fine up to the launch; FP8 needs both (checked above).
     a = _valid_args(kv_dtype=B.SDA_KV_FP8_E4M3, k_scale=0x800000, v_scale=None)
     assert B.sda_decode_raw(a) == B.SDA_ERR_INVALID
+
+
+def test_rows_limit():
+    assert B.sda_decode_raw(_valid_args(rows=16777216, groups=1)) == B.SDA_ERR_UNSUPPORTED
+
+
+# ---- sliding-window entry point ---------------------------------------------
+
+@pytest.mark.parametrize("tokens,groups,window,splits", _table("swa_splits_mi355x.txt"))
+def test_swa_split_heuristic_table(tokens, groups, window, splits):
+    assert B.sda_swa_splits(tokens, groups, window) == splits
+
+
+def _valid_swa(**over):
+    a = B.SwaArgs()
+    a.tokens, a.heads, a.groups, a.query_len, a.block, a.window = 8, 16, 4, 2, 64, 1024
+    a.query, a.q_token_stride, a.q_head_stride = 0x100000, 64 * 192, 192
+    a.output, a.o_token_stride, a.o_head_stride = 0x200000, 64 * 192, 192
+    a.cache = 0x300000
+    a.c_page_stride, a.c_group_stride, a.c_token_stride = 4 * 64 * 384, 64 * 384, 384
+    a.block_table, a.table_row_stride = 0x500000, 128
+    a.seq_lens = 0x600000
+    a.scale, a.splits = 0.07, 1
+    a.gate, a.gate_token_stride, a.gate_head_stride = 0x700000, 64, 1
+    a.workspace, a.workspace_bytes = None, 0
+    for k, v in over.items():
+        setattr(a, k, v)
+    return a
+
+
+SWA_INVALID = [
+    dict(heads=0), dict(heads=17), dict(groups=0), dict(query_len=0), dict(block=0),
+    dict(window=0), dict(splits=0), dict(tokens=-2), dict(tokens=7),   # 7 % query_len 2
+    dict(query=None), dict(output=None), dict(cache=None), dict(block_table=None),
+    dict(seq_lens=None),
+]
+
+SWA_UNSUPPORTED = [
+    dict(block=24),                                   # not a multiple of 16
+    dict(block=16, window=2048 * 16),                 # page list beyond SDA_MAX_R
+    dict(splits=257, workspace=0x900000, workspace_bytes=1 << 40),
+    dict(tokens=4194304, groups=4, query_len=1),      # rows beyond SDA_MAX_ROWS
+    dict(query=0x100008), dict(q_head_stride=196), dict(q_token_stride=64 * 192 + 4),
+    dict(cache=0x300008), dict(c_token_stride=388), dict(c_group_stride=64 * 384 + 4),
+    dict(output=0x200002), dict(o_head_stride=193), dict(o_token_stride=64 * 192 + 1),
+]
+
+
+@pytest.mark.parametrize("over", SWA_INVALID, ids=[str(o) for o in SWA_INVALID])
+def test_swa_invalid_arguments_are_rejected(over):
+    assert B.sda_swa_decode_raw(_valid_swa(**over)) == B.SDA_ERR_INVALID
+
+
+@pytest.mark.parametrize("over", SWA_UNSUPPORTED, ids=[str(o) for o in SWA_UNSUPPORTED])
+def test_swa_unsupported_arguments_are_rejected(over):
+    assert B.sda_swa_decode_raw(_valid_swa(**over)) == B.SDA_ERR_UNSUPPORTED
+
+
+def test_swa_workspace_and_empty_batch():
+    assert B.lib().sda_swa_decode(None, None) == B.SDA_ERR_INVALID
+    need = B.sda_workspace_bytes(32, 16, 4)
+    assert B.sda_swa_decode_raw(_valid_swa(splits=4)) == B.SDA_ERR_WORKSPACE
+    assert B.sda_swa_decode_raw(_valid_swa(splits=4, workspace=0x900000,
+                                           workspace_bytes=need - 1)) == B.SDA_ERR_WORKSPACE
+    a = _valid_swa(tokens=0, query=None, output=None, seq_lens=None)
+    assert B.sda_swa_decode_raw(a) == B.SDA_OK
+    assert B.sda_swa_decode_raw(_valid_swa(tokens=0, heads=17)) == B.SDA_ERR_INVALID
