@@ -17,6 +17,10 @@ events on the launch stream around the timed region) against the 8 TB/s HBM
 peak.
 ``cpu_baseline`` times the fp64 oracle on a bounded sample of rows on the
 host cores.
+
+``--swa NAME`` measures the gated sliding-window decode (``sda_swa_decode``)
+on one of its workloads instead; its algorithmic bytes are each row's window
+of K|V rows, plus Q and the output.
 """
 from __future__ import annotations
 
@@ -63,6 +67,184 @@ def workload_desc(w) -> str:
     return ("%s: %d rows = %d req x qlen %d x G %d, %d heads x 192, %s cache, block %d, "
             "R %d, context %d" % (w.name, w.rows, w.requests, w.query_len, w.groups, w.heads,
                                   w.kv, w.block, w.R, w.pages_per_req * w.block))
+
+
+def swa_algorithmic_bytes(w, seq_lens) -> tuple:
+    """(bytes, K|V tokens) of one sliding-window call: for every request and
+    KV group, the K|V token rows (384 bf16) of the union of its query tokens'
+    windows, each read once; plus Q and output (heads x 192 bf16) of every
+    row."""
+    lens = np.asarray(seq_lens, dtype=np.int64)
+    last = lens - 1
+    first = np.maximum(0, lens - w.query_len - w.window + 1)
+    ntok = np.clip(last - first + 1, 0, None)
+    tokens = int(ntok.sum()) * w.groups
+    return tokens * 384 * 2 + 2 * w.rows * w.heads * 192 * 2, tokens
+
+
+def swa_workload_desc(w) -> str:
+    return ("%s: %d rows = %d req x qlen %d x G %d, %d heads x 192, bf16 cache, block %d, "
+            "window %d, seq_len U[%d,%d]" % (w.name, w.rows, w.requests, w.query_len, w.groups,
+                                            w.heads, w.block, w.window, w.seq_lo, w.seq_hi))
+
+
+def time_calls(call, steps: int, warmup: int, stream):
+    """Warm up, then time `steps` back-to-back calls: wall seconds (between
+    synchronisations), average launch ms (two HIP events on the launch stream
+    around the timed region) and a second pass of per-launch durations."""
+    import torch
+    for i in range(warmup):
+        call(i)
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(steps):
+        call(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_avg_ms = ev0.elapsed_time(ev1) / steps
+    # Distribution of single-launch durations: a second pass over the same K
+    # calls with events around each launch (kept out of the timed region).
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for i in range(steps):
+        starts[i].record(stream)
+        call(i)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    launch_ms = np.array([starts[i].elapsed_time(ends[i]) for i in range(steps)])
+    return wall, launch_avg_ms, launch_ms
+
+
+def record(args, *, value, wall, launch_avg_ms, launch_ms, bytes_per_launch, rows, dtype,
+           config, kernel, traffic, metric=METRIC):
+    achieved = bytes_per_launch / (launch_avg_ms * 1e-3) / 1e9
+    return {
+        "metric": metric,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic",
+        "config": config,
+        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "rows_per_s": round(rows * args.steps / wall, 1),
+        "us_per_call": {"median": round(float(np.median(launch_ms)) * 1e3, 2),
+                        "p10": round(float(np.percentile(launch_ms, 10)) * 1e3, 2),
+                        "p90": round(float(np.percentile(launch_ms, 90)) * 1e3, 2)},
+        "roofline": {
+            "bound": "hbm",
+            "kernel": kernel,
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": int(bytes_per_launch),
+            "avg_launch_us": round(launch_avg_ms * 1e3, 3),
+        },
+    }
+
+
+def swa_cpu_baseline(inp, gpu_out, rows_sample: int, threads: int):
+    """Time the fp64 oracle (as it stands) on a sample of sliding-window rows."""
+    from oracle import oracle
+    from oracle.hostprep import swa_host_problem
+
+    w = inp.w
+    rng = np.random.default_rng(0)
+    rows = sorted(rng.choice(w.rows, size=min(rows_sample, w.rows), replace=False).tolist())
+    hp = swa_host_problem(inp.query, inp.cache, inp.block_table, inp.seq_lens, scale=inp.scale,
+                          window=w.window, query_len=w.query_len, gate=inp.gate, rows=rows)
+    t0 = time.perf_counter()
+    out = oracle.swa_decode(hp, rows=rows, threads=threads)
+    dt = time.perf_counter() - t0
+    lens = inp.seq_lens.cpu().numpy().astype(np.int64)
+    ntok = 0
+    for r in rows:
+        tok = r // w.groups
+        req, j = tok // w.query_len, tok % w.query_len
+        ntok += max(0, min(int(lens[req]) - w.query_len + j + 1, w.window))
+    nbytes = ntok * 384 * 2 + 2 * len(rows) * w.heads * 192 * 2
+    g = gpu_out.float().cpu().numpy().astype(np.float64).reshape(w.rows, w.heads, 192)[rows]
+    err = np.abs(g - out[rows])
+    return {
+        "value": nbytes / dt / 1e9,
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": "%d rows of the first input set (fp64 C oracle, %d threads), %.2f s wall; "
+                  "rows/s %.1f" % (len(rows), threads, dt, len(rows) / dt),
+        "parity_max_abs": float(err.max()),
+        "parity_mean_abs": float(err.mean()),
+    }
+
+
+def run_swa(args, dev) -> int:
+    import torch
+    from sparse_paged_decode_02_amd import binding as B
+    from sparse_paged_decode_02_amd import inputs as gen
+
+    w = gen.SWA_CONFIGS[args.swa]
+    pack, plan_splits = B.sda_swa_plan(w.tokens, w.groups, w.heads, w.query_len, w.window)
+    pack = args.pack or pack
+    splits = args.splits or w.splits or plan_splits
+    print("[bench] drawing %s" % swa_workload_desc(w), file=sys.stderr, flush=True)
+    base = gen.make_swa_inputs(w, device=dev, splits=splits)
+    sets = [base] + [gen.make_swa_inputs(w, device=dev, seed=w.seed + 100003 * i,
+                                         cache=base.cache, splits=splits)
+                     for i in range(1, args.sets)]
+    nbytes = [swa_algorithmic_bytes(w, s.seq_lens.cpu().numpy())[0] for s in sets]
+    outs = [torch.empty_like(s.query) for s in sets]
+    ws_bytes = B.sda_workspace_bytes(w.rows, w.heads, splits)
+    workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    handle = ctypes.c_void_p(stream.cuda_stream)
+    prepared = []
+    for s, o in zip(sets, outs):
+        B.check_swa_tensors(s.query, s.cache, s.block_table, s.seq_lens, o, s.gate)
+        prepared.append(B.make_swa_args(
+            s.query, s.cache, s.block_table, s.seq_lens, o, scale=s.scale, window=w.window,
+            query_len=w.query_len, splits=splits, pack=pack, gate=s.gate,
+            workspace=workspace if ws_bytes else None))
+
+    def call(i):
+        rc = B.sda_swa_decode_raw(prepared[i % len(prepared)], handle)
+        if rc != B.SDA_OK:
+            raise B.SdaError(rc, B.status_string(rc))
+
+    wall, launch_avg_ms, launch_ms = time_calls(call, args.steps, args.warmup, stream)
+    total_bytes = sum(nbytes[i % len(sets)] for i in range(args.steps))
+    bytes_per_launch = float(np.mean([nbytes[i % len(sets)] for i in range(args.steps)]))
+    rec = record(args, value=total_bytes / wall / 1e9, wall=wall, launch_avg_ms=launch_avg_ms,
+                 launch_ms=launch_ms, bytes_per_launch=bytes_per_launch, rows=w.rows,
+                 dtype="bf16",
+                 config={"workload": swa_workload_desc(w), "rows": w.rows, "heads": w.heads,
+                         "splits": splits, "pack": pack, "input_sets": len(sets),
+                         "seed": w.seed},
+                 kernel="sda split kernel, window mode" + (
+                     " + combine" if splits > 1 else " (combine fused)"),
+                 traffic=load_traffic(w.name, splits) if pack == B.sda_swa_plan(
+                     w.tokens, w.groups, w.heads, w.query_len, w.window)[0] else None,
+                 metric="effective KV GB/s (% of HBM peak) and rows/s for gated "
+                        "sliding-window decode")
+    if not args.no_cpu_baseline:
+        threads = max(1, min(16, os.cpu_count() or 1))
+        print("[bench] cpu baseline: oracle on %d rows, %d threads" % (args.cpu_rows, threads),
+              file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = swa_cpu_baseline(base, outs[0], args.cpu_rows, threads)
+    print(json.dumps(rec), flush=True)
+    return 0
 
 
 def load_traffic(workload_name: str, splits: int):
@@ -124,6 +306,11 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=2,
                     help="workload: 1..5, or 6 = bf16-gated shape at 8-token regions")
+    ap.add_argument("--swa", default="", metavar="NAME",
+                    help="measure the gated sliding-window decode on workload NAME "
+                         "(swa-gated, swa-mtp) instead")
+    ap.add_argument("--pack", type=int, default=0,
+                    help="with --swa: query tokens per workgroup (0: the library's plan)")
     ap.add_argument("--sets", type=int, default=4, help="rotating input sets")
     ap.add_argument("--splits", type=int, default=0, help="0: the workload's rule")
     ap.add_argument("--cpu-rows", type=int, default=48)
@@ -158,6 +345,8 @@ def main() -> int:
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": n, "calls": args.steps}), flush=True)
         return 0
+    if args.swa:
+        return run_swa(args, dev)
     w = gen.CONFIGS[args.config]
     splits = args.splits or w.splits or B.sda_splits(w.rows)
 
@@ -196,74 +385,16 @@ def main() -> int:
         if rc != B.SDA_OK:
             raise B.SdaError(rc, B.status_string(rc))
 
-    for i in range(args.warmup):
-        call(i)
-    torch.cuda.synchronize()
-
-    # Timed region: K calls back to back, bracketed by synchronisations, with
-    # two HIP events on the launch stream around it.  The launches run back
-    # to back, so the event span / K is the average launch duration.
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for i in range(args.steps):
-        call(i)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    launch_avg_ms = ev0.elapsed_time(ev1) / args.steps
-
-    # Distribution of single-launch durations: a second pass over the same K
-    # calls with events around each launch (kept out of the timed region).
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    for i in range(args.steps):
-        starts[i].record(stream)
-        call(i)
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-
-    launch_ms = np.array([starts[i].elapsed_time(ends[i]) for i in range(args.steps)])
+    wall, launch_avg_ms, launch_ms = time_calls(call, args.steps, args.warmup, stream)
     total_bytes = sum(nbytes[i % len(sets)] for i in range(args.steps))
-    value = total_bytes / wall / 1e9
     bytes_per_launch = float(np.mean([nbytes[i % len(sets)] for i in range(args.steps)]))
-    achieved = bytes_per_launch / (launch_avg_ms * 1e-3) / 1e9
-    traffic = load_traffic(w.name, splits)
-
-    rec = {
-        "metric": METRIC,
-        "value": round(value, 2),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(wall / args.steps * 1e3, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16" if w.kv == "bf16" else "fp8-e4m3 cache, bf16 MFMA",
-        "data": "synthetic",
-        "config": {"workload": workload_desc(w), "rows": w.rows, "heads": w.heads,
-                   "splits": splits, "input_sets": len(sets), "seed": w.seed},
-        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
-        "rows_per_s": round(w.rows * args.steps / wall, 1),
-        "us_per_call": {"median": round(float(np.median(launch_ms)) * 1e3, 2),
-                        "p10": round(float(np.percentile(launch_ms, 10)) * 1e3, 2),
-                        "p90": round(float(np.percentile(launch_ms, 90)) * 1e3, 2)},
-        "roofline": {
-            "bound": "hbm",
-            "kernel": "sda split kernel" + (" + combine" if splits > 1 else " (combine fused)"),
-            "achieved": round(achieved, 2),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": traffic,
-            "algorithmic_bytes_per_launch": int(bytes_per_launch),
-            "avg_launch_us": round(launch_avg_ms * 1e3, 3),
-        },
-    }
+    rec = record(args, value=total_bytes / wall / 1e9, wall=wall, launch_avg_ms=launch_avg_ms,
+                 launch_ms=launch_ms, bytes_per_launch=bytes_per_launch, rows=w.rows,
+                 dtype="bf16" if w.kv == "bf16" else "fp8-e4m3 cache, bf16 MFMA",
+                 config={"workload": workload_desc(w), "rows": w.rows, "heads": w.heads,
+                         "splits": splits, "input_sets": len(sets), "seed": w.seed},
+                 kernel="sda split kernel" + (" + combine" if splits > 1 else " (combine fused)"),
+                 traffic=load_traffic(w.name, splits))
     if not args.no_cpu_baseline:
         threads = max(1, min(16, os.cpu_count() or 1))
         print("[bench] cpu baseline: oracle on %d rows, %d threads" % (args.cpu_rows, threads),

@@ -169,8 +169,10 @@ size_t sda_workspace_bytes(int rows, int heads, int splits);
  * seq_lens[q] - query_len + j and attends, head by head, over the tokens at
  * positions max(0, pos - window + 1) .. pos of its request (a causal window
  * of `window` tokens, i.e. sliding_window[0] + 1).  The query heads of a KV
- * group are packed into one workgroup (GQA), as in sda_decode, and the
- * headwise sigmoid gate (the `_gate` helper of page "...ops.
+ * group are packed into one workgroup (GQA), as in sda_decode, together
+ * with up to `pack` consecutive query tokens of the request, whose windows
+ * overlap (`swa_decode_plan` returns such a pack), and the headwise sigmoid
+ * gate (the `_gate` helper of page "...ops.
  * sparse_decode_attention") scales each head.  A token whose position is
  * negative (seq_len < query_len) outputs zeros.  Strides are in ELEMENTS.
  *
@@ -181,8 +183,13 @@ size_t sda_workspace_bytes(int rows, int heads, int splits);
  *  query_len    query tokens per request (1 decode, 2..4 MTP verify; any
  *               value >= 1 is accepted).
  *  block        tokens per page; a multiple of 16 (else UNSUPPORTED).
- *  window       tokens attended, >= 1.  (window + 15) / block + 2 must not
- *               exceed SDA_MAX_R (else UNSUPPORTED).
+ *  window       tokens attended, >= 1.  (window + pack + 14) / block + 2
+ *               must not exceed SDA_MAX_R (else UNSUPPORTED).
+ *  pack         query tokens per workgroup, 1..min(query_len, 16 / heads),
+ *               or 0 for that maximum (sda_swa_plan).  Each token's heads
+ *               are separate MFMA columns with their own window mask; the
+ *               union of the windows is read once.  The result does not
+ *               depend on it beyond rounding.
  *  query        bf16 [tokens, groups*heads, 192]; head g*heads + h belongs
  *               to KV group g.  Dim stride 1; 16-byte aligned; token and
  *               head strides multiples of 8.
@@ -204,7 +211,7 @@ size_t sda_workspace_bytes(int rows, int heads, int splits);
  *               heads, splits) bytes; may be NULL when splits == 1.
  */
 typedef struct sda_swa_args {
-  int32_t tokens, heads, groups, query_len, block, window;
+  int32_t tokens, heads, groups, query_len, block, window, pack;
   const void *query;
   int64_t q_token_stride, q_head_stride;
   void *output;
@@ -224,18 +231,23 @@ typedef struct sda_swa_args {
 
 /*
  * Enqueue one gated sliding-window decode call on `stream`: the split kernel
- * of sda_decode in its window mode over a (tokens*groups, splits) grid, and
- * the combine kernel when splits > 1.  Asynchronous, no allocation, no host
+ * of sda_decode in its window mode over a (requests * ceil(query_len / pack)
+ * * groups, splits) grid, and the combine kernel (per row) when splits > 1.  Asynchronous, no allocation, no host
  * synchronisation.  Returns an sda_status; on error nothing is launched.
  */
 int sda_swa_decode(const sda_swa_args *args, hipStream_t stream);
 
 /*
- * Split count for a sliding-window call: the rule of sda_splits on
- * tokens*groups rows, further capped so that every split keeps at least 8
- * chunks of 16 window tokens.  Host-only and pure; 1 for empty sizes.
+ * Plan of a sliding-window call, the MI355X counterpart of `swa_decode_plan`
+ * (named on page "vllm.models.step5.nvidia.sparse_attention"): writes the
+ * pack (the largest, min(query_len, 16 / heads)) to *pack if pack is not NULL
+ * and returns the split count: the rule of sda_splits applied to the
+ * workgroup count requests * ceil(query_len / pack) * groups, further capped
+ * so that every split keeps at least 8 chunks of 16 tokens of the packed
+ * tokens' union window.  Host-only and pure; returns 1 (and pack 1) for
+ * invalid sizes.
  */
-int sda_swa_splits(int tokens, int groups, int window);
+int sda_swa_plan(int tokens, int groups, int heads, int query_len, int window, int *pack);
 
 /* Static description of a status code (never NULL). */
 const char *sda_status_string(int status);

@@ -11,7 +11,7 @@ from .binding import (  # noqa: F401
     sda_decode,
     sda_splits,
     sda_swa_decode,
-    sda_swa_splits,
+    sda_swa_plan,
     sda_workspace_bytes,
     status_string,
 )

@@ -63,6 +63,7 @@ class SwaArgs(ctypes.Structure):
     _fields_ = [
         ("tokens", ctypes.c_int32), ("heads", ctypes.c_int32), ("groups", ctypes.c_int32),
         ("query_len", ctypes.c_int32), ("block", ctypes.c_int32), ("window", ctypes.c_int32),
+        ("pack", ctypes.c_int32),
         ("query", ctypes.c_void_p), ("q_token_stride", ctypes.c_int64),
         ("q_head_stride", ctypes.c_int64),
         ("output", ctypes.c_void_p), ("o_token_stride", ctypes.c_int64),
@@ -107,8 +108,8 @@ def lib() -> ctypes.CDLL:
             l.sda_args_size.argtypes = []
             l.sda_swa_decode.restype = ctypes.c_int
             l.sda_swa_decode.argtypes = [ctypes.POINTER(SwaArgs), ctypes.c_void_p]
-            l.sda_swa_splits.restype = ctypes.c_int
-            l.sda_swa_splits.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+            l.sda_swa_plan.restype = ctypes.c_int
+            l.sda_swa_plan.argtypes = [ctypes.c_int] * 5 + [ctypes.POINTER(ctypes.c_int)]
             l.sda_swa_args_size.restype = ctypes.c_size_t
             l.sda_swa_args_size.argtypes = []
             if l.sda_abi_version() != ABI_VERSION:
@@ -245,12 +246,16 @@ def sda_decode_raw(args: DecodeArgs, stream_handle=None) -> int:
     return int(lib().sda_decode(ctypes.byref(args), stream_handle))
 
 
-def sda_swa_splits(tokens: int, groups: int, window: int) -> int:
-    return int(lib().sda_swa_splits(int(tokens), int(groups), int(window)))
+def sda_swa_plan(tokens: int, groups: int, heads: int, query_len: int, window: int) -> tuple:
+    """(pack, splits) the library picks for a sliding-window call."""
+    pack = ctypes.c_int(0)
+    splits = lib().sda_swa_plan(int(tokens), int(groups), int(heads), int(query_len),
+                                int(window), ctypes.byref(pack))
+    return int(pack.value), int(splits)
 
 
 def make_swa_args(query, cache, block_table, seq_lens, output, *, scale, window, query_len=1,
-                  splits, gate=None, workspace=None) -> SwaArgs:
+                  splits, pack=0, gate=None, workspace=None) -> SwaArgs:
     """Fill ``sda_swa_args`` from tensors (no validation beyond the C side).
     ``query``/``output``: [tokens, groups*heads, 192]; ``cache``: [pages,
     groups, block, 384]."""
@@ -258,6 +263,7 @@ def make_swa_args(query, cache, block_table, seq_lens, output, *, scale, window,
     groups = cache.shape[1]
     a.tokens, a.heads, a.groups = query.shape[0], query.shape[1] // groups, groups
     a.query_len, a.block, a.window = int(query_len), cache.shape[2], int(window)
+    a.pack = int(pack)
     a.query = _ptr(query)
     a.q_token_stride, a.q_head_stride = query.stride(0), query.stride(1)
     a.output = _ptr(output)
@@ -302,7 +308,8 @@ def check_swa_tensors(query, cache, block_table, seq_lens, output, gate):
 
 
 def sda_swa_decode(query, cache, block_table, seq_lens, output, *, scale, window,
-                   query_len=1, splits, gate=None, workspace=None, stream=None) -> None:
+                   query_len=1, splits, pack=0, gate=None, workspace=None,
+                   stream=None) -> None:
     """Enqueue ``sda_swa_decode`` (gated sliding-window decode) on ``stream``.
 
     Argument names follow ``swa_decode_gated`` as ``forward_with_headwise_gate``
@@ -318,7 +325,8 @@ def sda_swa_decode(query, cache, block_table, seq_lens, output, *, scale, window
         if nbytes:
             workspace = torch.empty(nbytes, dtype=torch.uint8, device=query.device)
     a = make_swa_args(query, cache, block_table, seq_lens, output, scale=scale, window=window,
-                      query_len=query_len, splits=splits, gate=gate, workspace=workspace)
+                      query_len=query_len, splits=splits, pack=pack, gate=gate,
+                      workspace=workspace)
     if stream is None:
         stream = torch.cuda.current_stream(query.device) if query.is_cuda else None
     handle = None if stream is None else ctypes.c_void_p(stream.cuda_stream)

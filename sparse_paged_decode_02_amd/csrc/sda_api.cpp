@@ -26,6 +26,13 @@ constexpr int kComputeUnits = 256;
 constexpr int kMaxHeuristicSplits = 32;
 constexpr int kSwaMinChunksPerSplit = 8;
 
+// Query tokens of one request that share a window workgroup: as many as fit
+// the 16 MFMA columns next to the heads of one KV group.
+int max_pack(int heads, int query_len) {
+  const int fit = SDA_MAX_HEADS / heads;
+  return fit < query_len ? fit : query_len;
+}
+
 }  // namespace
 
 extern "C" {
@@ -148,14 +155,20 @@ int sda_decode(const sda_decode_args* a, hipStream_t stream) {
 
 size_t sda_swa_args_size(void) { return sizeof(sda_swa_args); }
 
-int sda_swa_splits(int tokens, int groups, int window) {
-  if (tokens <= 0 || groups <= 0 || window <= 0) return 1;
-  // The row-count rule of sda_splits, and at least kSwaMinChunksPerSplit
-  // 16-token chunks per split so that each of the 4 waves keeps its pipeline.
-  const int64_t rows = (int64_t)tokens * groups;
-  const int64_t chunks = ((int64_t)window + 15) / 16;
+int sda_swa_plan(int tokens, int groups, int heads, int query_len, int window, int* pack) {
+  if (pack) *pack = 1;
+  if (tokens <= 0 || groups <= 0 || window <= 0 || heads < 1 || heads > SDA_MAX_HEADS ||
+      query_len < 1 || tokens % query_len)
+    return 1;
+  const int pk = max_pack(heads, query_len);
+  if (pack) *pack = pk;
+  // The row-count rule of sda_splits on workgroups, and at least
+  // kSwaMinChunksPerSplit 16-token chunks per split so that each of the 4
+  // waves keeps its pipeline.
+  const int64_t wgs = (int64_t)(tokens / query_len) * ((query_len + pk - 1) / pk) * groups;
+  const int64_t chunks = ((int64_t)window + pk - 1 + 15) / 16;
   int splits = 1;
-  while (splits < kMaxHeuristicSplits && rows * splits * 2 <= kComputeUnits &&
+  while (splits < kMaxHeuristicSplits && wgs * splits * 2 <= kComputeUnits &&
          chunks >= (int64_t)kSwaMinChunksPerSplit * splits * 2)
     splits *= 2;
   return splits;
@@ -170,9 +183,14 @@ int sda_swa_decode(const sda_swa_args* a, hipStream_t stream) {
       a->query_len < 1 || a->block < 1 || a->window < 1 || a->splits < 1)
     return SDA_ERR_INVALID;
   if (a->tokens % a->query_len) return SDA_ERR_INVALID;
+  const int pmax = max_pack(a->heads, a->query_len);
+  if (a->pack < 0 || a->pack > pmax) return SDA_ERR_INVALID;
+  const int pack = a->pack ? a->pack : pmax;
   if (a->splits > SDA_MAX_SPLITS || a->block % 16) return SDA_ERR_UNSUPPORTED;
-  // LDS page list: a split's run of chunks spans at most window + 15 tokens.
-  if (((int64_t)a->window + 15) / a->block + 2 > sda::kMaxRegions) return SDA_ERR_UNSUPPORTED;
+  // LDS page list: a split's run of chunks spans at most the union window
+  // (window + pack - 1 tokens) plus 15 tokens of alignment.
+  if (((int64_t)a->window + pack - 1 + 15) / a->block + 2 > sda::kMaxRegions)
+    return SDA_ERR_UNSUPPORTED;
   const int64_t rows = (int64_t)a->tokens * a->groups;
   if (rows > SDA_MAX_ROWS) return SDA_ERR_UNSUPPORTED;
   if (a->tokens == 0) return SDA_OK;
@@ -219,6 +237,8 @@ int sda_swa_decode(const sda_swa_args* a, hipStream_t stream) {
   p.gated = a->gate ? 1 : 0;
   p.query_len = a->query_len;
   p.window = a->window;
+  p.pack = pack;
+  p.ntg = (a->query_len + pack - 1) / pack;
 
   if (a->splits > 1) {
     size_t need = sda_workspace_bytes(p.rows, a->heads, a->splits);

@@ -243,9 +243,9 @@ __device__ __forceinline__ LaneDma lane_dma(int lane) {
   return d;
 }
 
-// A split's sliding window: visible positions w0..pos; chunk c starts at
-// token t_base + 16c; s_base[k] is the cache offset of block-table column
-// col_lo + k (page and KV group).
+// A split's sliding window: w0..pos is the union of the windows of the
+// workgroup's query tokens; chunk c starts at token t_base + 16c; s_base[k]
+// is the cache offset of block-table column col_lo + k (page and KV group).
 struct Win {
   int w0, pos, t_base, col_lo;
 };
@@ -270,7 +270,6 @@ __device__ __forceinline__ uint32_t issue_chunk(const Params& p, int c, int nreg
                                                 uint32_t stage, const LaneDma& ld,
                                                 uint32_t cts_bytes, const Win& win) {
   using C = Cfg<kFp8>;
-  const int i16 = lane & 15;
   const uint32_t st = (uint32_t)__builtin_amdgcn_readfirstlane(stage);
   uint32_t vbits = 0;
   if (kAddr == kWindow) {
@@ -281,8 +280,6 @@ __device__ __forceinline__ uint32_t issue_chunk(const Params& p, int c, int nreg
     const int col = t0 / p.block;
     const int64_t rb = s_base[col - win.col_lo] + (int64_t)(t0 - col * p.block) * p.cts;
     const uint8_t* base = uniform_ptr(p.cache + rb * C::kEsz);
-    const int tok = t0 + i16;
-    vbits = (tok >= win.w0 && tok <= win.pos) ? 1u : 0u;
     uint32_t ko[6], vo[6];
 #pragma unroll
     for (int j = 0; j < 6; ++j) {
@@ -293,6 +290,7 @@ __device__ __forceinline__ uint32_t issue_chunk(const Params& p, int c, int nreg
     }
     dma_chunk_sbase<kFp8>(base, st, ko, vo);
   } else if (kAddr == kUniform) {
+    const int i16 = lane & 15;
     // The chunk lies inside one region: uniform base, 32-bit lane offsets.
     const int slot0 = c * C::kTok;
     const int k = slot0 / p.rt;
@@ -312,6 +310,7 @@ __device__ __forceinline__ uint32_t issue_chunk(const Params& p, int c, int nreg
     }
     dma_chunk_sbase<kFp8>(base, st, ko, vo);
   } else {
+    const int i16 = lane & 15;
     const int slot0 = c * C::kTok;
 #pragma unroll
     for (int t = 0; t < (kFp8 ? 2 : 1); ++t) {
@@ -358,7 +357,9 @@ __device__ __forceinline__ void softmax_step(float (&x)[N], RowState& st, uint32
   mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
   if (__ballot(mloc > st.m + kLazyRescale) != 0) {
     const float m_new = fmaxf(st.m, mloc);
-    const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
+    // A column that has seen no visible token yet keeps max -inf (its
+    // accumulators are 0): scale it by 1, not by exp2(-inf - -inf) = NaN.
+    const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(st.m - m_new);
     st.m = m_new;
     st.l *= alpha;
 #pragma unroll
@@ -377,11 +378,20 @@ __device__ __forceinline__ void softmax_step(float (&x)[N], RowState& st, uint32
   st.l += psum;
 }
 
+// Window-mode visibility of this lane's S^T column: token t of the chunk
+// starting at t0 is visible iff lo <= t <= hi (an empty range for unused
+// columns).
+struct ColWin {
+  int t0, lo, hi;
+};
+
 // Compute one chunk from its LDS stage (K at +0, V at +kStageBytes).
-template <bool kFp8>
+// Visibility comes from the issue's per-token bits (region modes) or from the
+// lane's column window (window mode).
+template <bool kFp8, bool kWin>
 __device__ __forceinline__ void compute_chunk(const uint8_t* stage, uint32_t vbits,
-                                              const u32x4 (&qreg)[6], float qk_scale_log2,
-                                              int lane, RowState& st) {
+                                              const ColWin& cw, const u32x4 (&qreg)[6],
+                                              float qk_scale_log2, int lane, RowState& st) {
   using C = Cfg<kFp8>;
   const int i16 = lane & 15, g4 = lane >> 4;
   const SDA_LDS uint8_t* kl = (const SDA_LDS uint8_t*)stage;
@@ -417,14 +427,23 @@ __device__ __forceinline__ void compute_chunk(const uint8_t* stage, uint32_t vbi
     }
     s[t] = a;
   }
-  // Validity of token rows: lanes 0..15 loaded rows 0..15 of each tile.
   float x[4 * kT];
+  if (kWin) {
+    static_assert(!kWin || kT == 1, "window chunks are one 16-token tile");
 #pragma unroll
-  for (int t = 0; t < kT; ++t) {
-    const uint64_t vb = __ballot((vbits >> t) & 1u);
+    for (int v = 0; v < 4; ++v) {
+      const int t = cw.t0 + 4 * g4 + v;
+      x[v] = (t >= cw.lo && t <= cw.hi) ? s[0][v] * qk_scale_log2 : -INFINITY;
+    }
+  } else {
+    // Validity of token rows: lanes 0..15 loaded rows 0..15 of each tile.
 #pragma unroll
-    for (int v = 0; v < 4; ++v)
-      x[4 * t + v] = ((vb >> (4 * g4 + v)) & 1) ? s[t][v] * qk_scale_log2 : -INFINITY;
+    for (int t = 0; t < kT; ++t) {
+      const uint64_t vb = __ballot((vbits >> t) & 1u);
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        x[4 * t + v] = ((vb >> (4 * g4 + v)) & 1) ? s[t][v] * qk_scale_log2 : -INFINITY;
+    }
   }
   uint32_t pb[2 * kT];
   softmax_step<4 * kT>(x, st, pb);
@@ -497,9 +516,9 @@ template <bool kFp8, bool kFused, int kAddr>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void split_kernel(
     const Params p) {
   using C = Cfg<kFp8>;
-  const int r = blockIdx.x;
   const int split = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int i16 = lane & 15, g4 = lane >> 4;
 
   __shared__ int64_t s_base[kMaxRegions];
   __shared__ int s_n[kMaxRegions];
@@ -507,33 +526,59 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   __shared__ float s_m[kWaves][16];
   __shared__ float s_l[kWaves][16];
 
-  if (kAddr != kWindow && !p.active[r]) {
-    // Inactive rows read nothing else.  With splits > 1 the combine clears.
-    if (kFused && p.clear) clear_row(p, r, tid, kThreads);
-    return;
+  // The workgroup's query columns (the 16 columns of the MFMA tiles).
+  //  * region modes: row r = blockIdx.x (token r / groups, group r % groups);
+  //    column = head.
+  //  * window mode: blockIdx.x = (request, token group, KV group), group
+  //    fastest.  A token group is `pack` consecutive query tokens of the
+  //    request (GQA and token packing: column = token-in-group * heads + head).
+  int r = 0, tok0, g, req, pos, ncols;
+  ColWin cw{0, 1, 0};
+  const uint16_t* qcol;
+  if (kAddr == kWindow) {
+    const int wg = blockIdx.x;
+    const int rest = wg / p.groups;
+    g = wg - rest * p.groups;
+    req = rest / p.ntg;
+    const int jj0 = (rest - req * p.ntg) * p.pack;
+    const int np = min(p.pack, p.query_len - jj0);
+    tok0 = req * p.query_len + jj0;
+    ncols = np * p.heads;
+    // Token j of a request of length L sits at L - query_len + j; `pos` is
+    // the last token of the group, and the group's windows span
+    // [max(0, pos_first - window + 1), pos].
+    const int pos_first = p.seq_lens[req] - p.query_len + jj0;
+    pos = pos_first + np - 1;
+    const int jl = i16 / p.heads;
+    const int h = i16 - jl * p.heads;
+    qcol = p.q + (int64_t)(tok0 + jl) * p.qts + (int64_t)g * p.qgs + (int64_t)h * p.qhs;
+    if (i16 < ncols) {
+      cw.hi = pos_first + jl;
+      cw.lo = (int)max((int64_t)0, (int64_t)cw.hi - p.window + 1);
+    }
+  } else {
+    r = blockIdx.x;
+    if (!p.active[r]) {
+      // Inactive rows read nothing else.  With splits > 1 the combine clears.
+      if (kFused && p.clear) clear_row(p, r, tid, kThreads);
+      return;
+    }
+    tok0 = r / p.groups;
+    g = r - tok0 * p.groups;
+    req = r / p.rows_per_req;
+    pos = p.positions[r];
+    ncols = p.heads;
+    qcol = p.q + (int64_t)tok0 * p.qts + (int64_t)g * p.qgs + (int64_t)i16 * p.qhs;
   }
 
-  const int token = r / p.groups;
-  const int g = r - token * p.groups;
-  const int req = r / p.rows_per_req;
-  // Window mode: token j of a request of length L sits at L - query_len + j.
-  const int pos = kAddr == kWindow
-                      ? p.seq_lens[req] - p.query_len + (token - req * p.query_len)
-                      : p.positions[r];
-
-  // Q^T B-operand: lane holds head (lane & 15), 8 dims per k-slice, in the
+  // Q^T B-operand: lane holds column (lane & 15), 8 dims per k-slice, in the
   // same dim order as the K loads.  Issued first so that its latency overlaps
   // the region resolution below.
-  const int i16 = lane & 15, g4 = lane >> 4;
   u32x4 qreg[6];
-  {
-    const uint16_t* qrow =
-        p.q + (int64_t)token * p.qts + (int64_t)g * p.qgs + (int64_t)i16 * p.qhs;
 #pragma unroll
-    for (int cc = 0; cc < 6; ++cc) {
-      int d = kFp8 ? 64 * (cc >> 1) + 16 * g4 + 8 * (cc & 1) : 32 * cc + 8 * g4;
-      qreg[cc] = i16 < p.heads ? *reinterpret_cast<const u32x4*>(qrow + d) : u32x4{0, 0, 0, 0};
-    }
+  for (int cc = 0; cc < 6; ++cc) {
+    int d = kFp8 ? 64 * (cc >> 1) + 16 * g4 + 8 * (cc & 1) : 32 * cc + 8 * g4;
+    qreg[cc] = i16 < ncols ? *reinterpret_cast<const u32x4*>(qcol + d) : u32x4{0, 0, 0, 0};
   }
 
   // Row extent, resolved by every wave on its own with no workgroup barrier.
@@ -543,10 +588,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   int nreg = 0, nchunks = 0;
   Win win{0, 0, 0, 0};
   if (kAddr == kWindow) {
-    // The window's 16-token chunks, aligned down to a multiple of 16 so that
-    // a chunk never straddles a page, are dealt to the splits in balanced
-    // contiguous runs.  s_base gets the pages this split's run touches.
-    const int w0 = max(0, pos - p.window + 1);
+    // The union window's 16-token chunks, aligned down to a multiple of 16
+    // so that a chunk never straddles a page, are dealt to the splits in
+    // balanced contiguous runs.  s_base gets the pages this split's run
+    // touches.
+    const int w0 = (int)max((int64_t)0, (int64_t)pos - (ncols / p.heads - 1) - p.window + 1);
     const int a = w0 & ~15;
     const int total = pos < 0 ? 0 : (pos + 1 - a + 15) >> 4;
     const int clo = (int)(((int64_t)split * total + p.splits - 1) / p.splits);
@@ -645,7 +691,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                                         s_n, lane, my_stage_lds + SN * kChunkBytes, ld, cts_bytes,
                                         win);
       wait_vmcnt<kOpsPerChunk * (kStages - 1)>();
-      compute_chunk<kFp8>(my_stage + S * kChunkBytes, vb[S], qreg, qk_scale_log2, lane, st);
+      if (kAddr == kWindow) cw.t0 = win.t_base + 16 * c;
+      compute_chunk<kFp8, kAddr == kWindow>(my_stage + S * kChunkBytes, vb[S], cw, qreg,
+                                            qk_scale_log2, lane, st);
       return true;
     };
     for (int i0 = 0;; i0 += kStages)
@@ -676,19 +724,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   __syncthreads();
 
   const float vscale = kFp8 ? *p.v_scale : 1.0f;
-  uint16_t* orow = out_row(p, r);
-  for (int e = tid; e < p.heads * (kDim / 2); e += kThreads) {
-    int h = e / (kDim / 2), d = 2 * (e - h * (kDim / 2));
+  for (int e = tid; e < ncols * (kDim / 2); e += kThreads) {
+    const int c = e / (kDim / 2), d = 2 * (e - c * (kDim / 2));
+    // column c -> (token, head) and its output row
+    int token = tok0, h = c;
+    if (kAddr == kWindow) {
+      const int jl = c / p.heads;
+      token += jl;
+      h = c - jl * p.heads;
+    }
+    const int row = kAddr == kWindow ? token * p.groups + g : r;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w][h]);
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w][c]);
     float o0 = 0.f, o1 = 0.f, L = 0.f;
     if (M != -INFINITY) {
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) {
-        float f = __builtin_amdgcn_exp2f(s_m[w][h] - M);
-        const float* src = s_acc + (size_t)w * kWaveStride + h * kAccStride + d;
-        L += s_l[w][h] * f;
+        float f = __builtin_amdgcn_exp2f(s_m[w][c] - M);
+        const float* src = s_acc + (size_t)w * kWaveStride + c * kAccStride + d;
+        L += s_l[w][c] * f;
         o0 += src[0] * f;
         o1 += src[1] * f;
       }
@@ -702,9 +757,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         o0 *= gv;
         o1 *= gv;
       }
+      uint16_t* orow = p.out + (int64_t)token * p.ots + (int64_t)g * p.ogs;
       store_row_pair(orow, p, h, d, o0, o1);
     } else {
-      int64_t ph = ((int64_t)r * p.splits + split) * p.heads + h;
+      int64_t ph = ((int64_t)row * p.splits + split) * p.heads + h;
       *reinterpret_cast<float2*>(p.partial + ph * kDim + d) = make_float2(o0, o1);
       if (d == 0) p.lse[ph] = M == -INFINITY ? -INFINITY : M + __log2f(L);
     }
@@ -783,10 +839,14 @@ hipError_t launch(const Params& p, bool fp8, hipStream_t stream) {
 }
 
 hipError_t launch_window(const Params& p, hipStream_t stream) {
+  // grid.x = requests * token groups * KV groups; the combine runs per row.
+  const unsigned wgs = (unsigned)(p.rows / p.rows_per_req * p.ntg * p.groups);
   if (p.splits == 1)
-    launch_split<false, true, kWindow>(p, stream);
+    hipLaunchKernelGGL((split_kernel<false, true, kWindow>), dim3(wgs, (unsigned)p.splits),
+                       dim3(kThreads), 0, stream, p);
   else
-    launch_split<false, false, kWindow>(p, stream);
+    hipLaunchKernelGGL((split_kernel<false, false, kWindow>), dim3(wgs, (unsigned)p.splits),
+                       dim3(kThreads), 0, stream, p);
   return launch_combine(p, stream);
 }
 

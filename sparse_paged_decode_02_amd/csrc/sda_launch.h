@@ -34,6 +34,7 @@ struct Params {
   float scale;
   int32_t rows, heads, groups, rows_per_req, block, R, rt, splits, clear, gated;
   int32_t query_len, window;  // window mode
+  int32_t pack, ntg;          // window mode: tokens per workgroup, token groups per request
 };
 
 // Enqueue the split kernel (and the combine kernel when splits > 1) over
@@ -42,7 +43,9 @@ hipError_t launch(const Params& p, bool fp8, hipStream_t stream);
 
 // The same kernels over each row's sliding window (bf16 cache): token j of a
 // request of length L sits at position L - query_len + j and attends over
-// positions max(0, pos - window + 1) .. pos.  Requires block % 16 == 0.
+// positions max(0, pos - window + 1) .. pos.  One split workgroup serves
+// `pack` consecutive tokens of a request and KV group (pack * heads <= 16).
+// Requires block % 16 == 0.
 hipError_t launch_window(const Params& p, hipStream_t stream);
 
 }  // namespace sda

@@ -19,7 +19,7 @@ def _declared_functions():
 def test_library_exports_every_declared_function():
     names = _declared_functions()
     assert {"sda_decode", "sda_splits", "sda_workspace_bytes", "sda_status_string",
-            "sda_abi_version", "sda_args_size", "sda_swa_decode", "sda_swa_splits",
+            "sda_abi_version", "sda_args_size", "sda_swa_decode", "sda_swa_plan",
             "sda_swa_args_size"} <= set(names)
     lib = B.lib()
     for n in names:
@@ -142,9 +142,11 @@ def test_rows_limit():
 
 # ---- sliding-window entry point ---------------------------------------------
 
-@pytest.mark.parametrize("tokens,groups,window,splits", _table("swa_splits_mi355x.txt"))
-def test_swa_split_heuristic_table(tokens, groups, window, splits):
-    assert B.sda_swa_splits(tokens, groups, window) == splits
+@pytest.mark.parametrize("tokens,groups,heads,qlen,window,pack,splits",
+                         _table("swa_plan_mi355x.txt"))
+def test_swa_plan_table(tokens, groups, heads, qlen, window, pack, splits):
+    assert B.sda_swa_plan(tokens, groups, heads, qlen, window) == (pack, splits)
+    assert B.lib().sda_swa_plan(tokens, groups, heads, qlen, window, None) == splits
 
 
 def _valid_swa(**over):
@@ -169,11 +171,14 @@ SWA_INVALID = [
     dict(window=0), dict(splits=0), dict(tokens=-2), dict(tokens=7),   # 7 % query_len 2
     dict(query=None), dict(output=None), dict(cache=None), dict(block_table=None),
     dict(seq_lens=None),
+    dict(pack=-1), dict(pack=3),                      # max pack is min(2, 16 // 16) = 1
+    dict(heads=4, pack=3),                            # > query_len 2
 ]
 
 SWA_UNSUPPORTED = [
     dict(block=24),                                   # not a multiple of 16
     dict(block=16, window=2048 * 16),                 # page list beyond SDA_MAX_R
+    dict(block=16, heads=8, pack=2, window=32736),    # + pack - 1 crosses the limit
     dict(splits=257, workspace=0x900000, workspace_bytes=1 << 40),
     dict(tokens=4194304, groups=4, query_len=1),      # rows beyond SDA_MAX_ROWS
     dict(query=0x100008), dict(q_head_stride=196), dict(q_token_stride=64 * 192 + 4),
@@ -201,3 +206,14 @@ def test_swa_workspace_and_empty_batch():
     a = _valid_swa(tokens=0, query=None, output=None, seq_lens=None)
     assert B.sda_swa_decode_raw(a) == B.SDA_OK
     assert B.sda_swa_decode_raw(_valid_swa(tokens=0, heads=17)) == B.SDA_ERR_INVALID
+
+
+def test_swa_pack_limit_edges():
+    # (window + pack + 14) // block + 2 <= 2048 with block 16: the largest
+    # window is 32736 at pack 1 and 32735 at pack 2.  splits = 2 with no
+    # workspace makes an accepted shape stop at the workspace check, so no
+    # kernel is ever launched on the fake pointers.
+    for pack, window in ((1, 32736), (2, 32735)):
+        rc = B.sda_swa_decode_raw(_valid_swa(block=16, heads=8, pack=pack, window=window,
+                                             splits=2))
+        assert rc == B.SDA_ERR_WORKSPACE, (pack, window, rc)

@@ -38,20 +38,20 @@ def case(seed, **kw):
     return gen.SwaWorkload(**base)
 
 
-def run(inp, splits=None, query=None, out=None, gate="inp", label=""):
+def run(inp, splits=None, query=None, out=None, gate="inp", label="", pack=0):
     w = inp.w
     if splits is None:
-        splits = inp.splits if inp.splits is not None else B.sda_swa_splits(
-            w.tokens, w.groups, w.window)
+        splits = inp.splits if inp.splits is not None else B.sda_swa_plan(
+            w.tokens, w.groups, w.heads, w.query_len, w.window)[1]
     q = inp.query if query is None else query
     if out is None:
         out = torch.empty_like(inp.query)
     g = inp.gate if gate == "inp" else gate
-    _say("sda_swa_decode %s tokens=%d G=%d heads=%d block=%d window=%d qlen=%d splits=%d gate=%s"
-         % (label or w.name, w.tokens, w.groups, w.heads, w.block, w.window, w.query_len,
-            splits, g is not None))
+    _say("sda_swa_decode %s tokens=%d G=%d heads=%d block=%d window=%d qlen=%d splits=%d "
+         "pack=%d gate=%s" % (label or w.name, w.tokens, w.groups, w.heads, w.block, w.window,
+                              w.query_len, splits, pack, g is not None))
     B.sda_swa_decode(q, inp.cache, inp.block_table, inp.seq_lens, out, scale=inp.scale,
-                     window=w.window, query_len=w.query_len, splits=splits, gate=g)
+                     window=w.window, query_len=w.query_len, splits=splits, pack=pack, gate=g)
     torch.cuda.synchronize()
     return out
 
@@ -98,7 +98,9 @@ def test_random_cases_match_oracle(seed):
     w = _random_case(seed)
     inp = gen.make_swa_inputs(w, device=DEV)
     splits = [1, 2, 3, 5][seed % 4]
-    out = run(inp, splits=splits, label="random%d" % seed)
+    pack = int(np.random.default_rng(seed + 1000).integers(0, min(w.query_len,
+                                                                  16 // w.heads) + 1))
+    out = run(inp, splits=splits, label="random%d" % seed, pack=pack)
     check_close(out, oracle_out(inp), w, what="random%d" % seed)
 
 
@@ -110,12 +112,41 @@ def test_split_sweep(splits):
     check_close(out, oracle_out(inp), w, what="splits%d" % splits)
 
 
+@pytest.mark.parametrize("heads,pack", [(4, 1), (4, 2), (4, 3), (4, 4), (3, 0), (8, 2),
+                                        (16, 1)])
 @pytest.mark.parametrize("splits", [1, 3])
-def test_window_extent_exact(splits):
+def test_token_packing(heads, pack, splits):
+    # the query tokens of a request share one workgroup, each with its own
+    # window mask; windows straddle page and chunk edges
+    w = case(31 + heads, requests=3, query_len=4, groups=2, heads=heads, block=32,
+             pages_per_req=20, window=70, gated=True)
+    inp = gen.make_swa_inputs(w, device=DEV, seq_lens=[4, 75, 640])
+    out = run(inp, splits=splits, pack=pack, label="pack%d" % pack)
+    check_close(out, oracle_out(inp), w, what="heads%d pack%d splits%d" % (heads, pack, splits))
+
+
+@pytest.mark.parametrize("splits", [1, 2])
+def test_packed_column_empty_in_one_wave(splits):
+    # seq_len 33, query_len 2, window 16: token 0 sees 16..31 and token 1
+    # sees 17..32.  The union's second chunk (32..47) holds a visible token
+    # for token 1 only, so the wave computing it has token 0's columns still
+    # empty while token 1's columns raise the running max.
+    w = case(41, requests=2, query_len=2, groups=2, heads=8, block=16, pages_per_req=4,
+             window=16, gated=True)
+    inp = gen.make_swa_inputs(w, device=DEV, seq_lens=[33, 49])
+    out = run(inp, splits=splits, pack=2, label="empty column")
+    assert torch.isfinite(out.float()).all()
+    check_close(out, oracle_out(inp), w, what="empty column splits%d" % splits)
+
+
+@pytest.mark.parametrize("pack", [1, 4])
+@pytest.mark.parametrize("splits", [1, 3])
+def test_window_extent_exact(splits, pack):
     # q = 0: uniform weights; V[t] = 1 at dim t % 192, so the output's support
     # is exactly the set of window positions mod 192 (window <= 192).
     w = case(7, requests=4, query_len=4, groups=2, heads=3, block=16, pages_per_req=24,
              window=37, gated=False)
+    assert pack <= 16 // w.heads
     inp = gen.make_swa_inputs(w, device=DEV, seq_lens=[4, 37, 40, 384])
     inp.query.zero_()
     cache = torch.zeros_like(inp.cache)
@@ -124,7 +155,7 @@ def test_window_extent_exact(splits):
         for t in range(w.pages_per_req * w.block):
             cache[table[req, t // w.block], :, t % w.block, DIM + t % DIM] = 1.0
     inp.cache = cache
-    out = as_rows(run(inp, splits=splits), w)
+    out = as_rows(run(inp, splits=splits, pack=pack), w)
     lens = [4, 37, 40, 384]
     for r in range(w.rows):
         tok = r // w.groups
@@ -144,7 +175,7 @@ def test_tokens_before_the_first_position_are_zero():
     w = case(9, requests=3, query_len=4, groups=2, heads=4, block=16, pages_per_req=4,
              window=20)
     inp = gen.make_swa_inputs(w, device=DEV, seq_lens=[1, 2, 50])
-    out = run(inp, splits=2)
+    out = run(inp, splits=2, pack=3)
     ref = oracle_out(inp)
     check_close(out, ref, w, what="short requests")
     o = as_rows(out, w)
