@@ -137,6 +137,7 @@ int sda_decode(const sda_decode_args* a, hipStream_t stream) {
   p.block = a->block;
   p.R = a->R;
   p.rt = rt;
+  p.rt_shift = (rt & (rt - 1)) == 0 ? __builtin_ctz((unsigned)rt) : -1;
   p.splits = a->splits;
   p.clear = a->clear_inactive ? 1 : 0;
   p.gated = a->gate ? 1 : 0;
@@ -233,6 +234,7 @@ int sda_swa_decode(const sda_swa_args* a, hipStream_t stream) {
   p.rows_per_req = a->groups * a->query_len;
   p.block = a->block;
   p.rt = a->block;
+  p.rt_shift = -1;
   p.splits = a->splits;
   p.gated = a->gate ? 1 : 0;
   p.query_len = a->query_len;

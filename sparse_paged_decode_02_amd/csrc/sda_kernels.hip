@@ -53,8 +53,12 @@ namespace sda {
 namespace {
 
 constexpr int kDim = 192;
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
+// Waves per split workgroup: 4 (one workgroup per CU, ~121 KiB of LDS) when
+// the grid is at most one workgroup per CU, else 2 (~72 KiB, two per CU, so
+// that one workgroup's prologue and epilogue overlap the other's streaming).
+constexpr int kWavesSmallGrid = 4;
+constexpr int kWavesLargeGrid = 2;
+constexpr int kComputeUnits = 256;
 constexpr int kStages = 2;          // LDS stages per wave: 1 computed, 1 in flight
 constexpr int kOpsPerChunk = 12;    // vector-memory instructions per chunk issue
 constexpr int kStageBytes = 6144;   // K (or V) bytes of one chunk (16 bf16 / 32 FP8 tokens)
@@ -101,11 +105,15 @@ __device__ __forceinline__ uint32_t float_to_bf16_bits(float f) {
 // Headwise sigmoid gate of the `_gate` section: the bf16 logit widened to fp32,
 // 1 / (1 + exp(-g)) with a correctly rounded fp32 division (this file is built
 // with -fhip-fp32-correctly-rounded-divide-sqrt), rounded to bf16, widened.
-__device__ __forceinline__ float gate_value(const uint16_t* gate, int64_t idx) {
-  float g = bf16_bits_to_float(gate[idx]);
+__device__ __forceinline__ float gate_sigmoid(uint32_t bits) {
+  float g = bf16_bits_to_float(bits);
   float den = 1.0f + expf(-g);
   float sig = 1.0f / den;
   return bf16_bits_to_float(float_to_bf16_bits(sig));
+}
+
+__device__ __forceinline__ float gate_value(const uint16_t* gate, int64_t idx) {
+  return gate_sigmoid(gate[idx]);
 }
 
 // 4 e4m3 bytes -> 4 bf16 (exact), as two packed pairs {bytes 0,1} {bytes 2,3}.
@@ -211,8 +219,9 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // row in LDS is finite data whose weight is exactly 0.
 __device__ __forceinline__ int64_t token_elem(const Params& p, int slot, const int64_t* s_base,
                                               const int* s_n, int nreg, bool& valid) {
-  int k = slot / p.rt;
-  int off = slot - k * p.rt;
+  // region_tokens is almost always a power of two: shift, not divide
+  const int k = p.rt_shift >= 0 ? slot >> p.rt_shift : slot / p.rt;
+  const int off = slot - k * p.rt;
   int kk = k < nreg ? k : nreg - 1;
   valid = k < nreg && off < s_n[kk];
   return s_base[kk] + (int64_t)(valid ? off : 0) * p.cts;
@@ -511,11 +520,13 @@ __device__ __forceinline__ bool run_steps(F& step, int i0, std::integer_sequence
   return (step(i0, std::integral_constant<int, Ss>{}) && ...);
 }
 
-template <bool kFp8, bool kFused, int kAddr>
-// LDS use (stages + region list) allows one workgroup, i.e. one wave per SIMD.
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void split_kernel(
-    const Params p) {
+// LDS use (stages + region list) allows one 4-wave or two 2-wave workgroups
+// per CU, i.e. one wave per SIMD.
+template <bool kFp8, bool kFused, int kAddr, int kWaves>
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(1, 1))) void
+split_kernel(const Params p) {
   using C = Cfg<kFp8>;
+  constexpr int kThreads = 64 * kWaves;
   const int split = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int i16 = lane & 15, g4 = lane >> 4;
@@ -525,6 +536,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   __shared__ __attribute__((aligned(1024))) uint8_t s_stage[kWaves][kStages][kChunkBytes];
   __shared__ float s_m[kWaves][16];
   __shared__ float s_l[kWaves][16];
+  __shared__ float s_fac[kWaves][16];
 
   // The workgroup's query columns (the 16 columns of the MFMA tiles).
   //  * region modes: row r = blockIdx.x (token r / groups, group r % groups);
@@ -532,7 +544,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   //  * window mode: blockIdx.x = (request, token group, KV group), group
   //    fastest.  A token group is `pack` consecutive query tokens of the
   //    request (GQA and token packing: column = token-in-group * heads + head).
-  int r = 0, tok0, g, req, pos, ncols;
+  int r = 0, tok0, g, req, pos, ncols, id_first = -1;
+  int col_token, col_head;  // this lane's column
   ColWin cw{0, 1, 0};
   const uint16_t* qcol;
   if (kAddr == kWindow) {
@@ -551,6 +564,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     pos = pos_first + np - 1;
     const int jl = i16 / p.heads;
     const int h = i16 - jl * p.heads;
+    col_token = tok0 + jl;
+    col_head = h;
     qcol = p.q + (int64_t)(tok0 + jl) * p.qts + (int64_t)g * p.qgs + (int64_t)h * p.qhs;
     if (i16 < ncols) {
       cw.hi = pos_first + jl;
@@ -558,7 +573,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     }
   } else {
     r = blockIdx.x;
-    if (!p.active[r]) {
+    // The active flag, the position and the first 64 region ids do not
+    // depend on each other: one round trip for all three.
+    const int act = p.active[r];
+    pos = p.positions[r];
+    id_first = lane < p.R ? p.regions[(int64_t)r * p.rrs + lane] : -1;
+    __asm__ __volatile__("" : "+v"(pos), "+v"(id_first));
+    if (!act) {
       // Inactive rows read nothing else.  With splits > 1 the combine clears.
       if (kFused && p.clear) clear_row(p, r, tid, kThreads);
       return;
@@ -566,8 +587,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     tok0 = r / p.groups;
     g = r - tok0 * p.groups;
     req = r / p.rows_per_req;
-    pos = p.positions[r];
     ncols = p.heads;
+    col_token = tok0;
+    col_head = i16;
     qcol = p.q + (int64_t)tok0 * p.qts + (int64_t)g * p.qgs + (int64_t)i16 * p.qhs;
   }
 
@@ -580,6 +602,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     int d = kFp8 ? 64 * (cc >> 1) + 16 * g4 + 8 * (cc & 1) : 32 * cc + 8 * g4;
     qreg[cc] = i16 < ncols ? *reinterpret_cast<const u32x4*>(qcol + d) : u32x4{0, 0, 0, 0};
   }
+  // The column's gate logit travels with Q, so that the epilogue does no
+  // dependent global load.
+  uint32_t gbits = 0;
+  if (kFused && p.gated && i16 < ncols)
+    gbits = p.gate[(int64_t)col_token * p.grs + (int64_t)(g * p.heads + col_head) * p.ghs];
 
   // Row extent, resolved by every wave on its own with no workgroup barrier.
   // All waves write identical values to the shared LDS list, and a wave only
@@ -616,12 +643,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     // slot order, 64 at a time.  It takes this split's balanced share, ranks
     // [ceil(s*V/S), ceil((s+1)*V/S)), and writes the share's cache offsets
     // and visible counts to the LDS list.
+    // The first 64 slots (id_first) stay in registers for the second pass.
     int nvis = 0;
-    int id0 = -1;  // the first 64 slots stay in registers for the second pass
     for (int j0 = 0; j0 < p.R; j0 += 64) {
       const int j = j0 + lane;
-      const int id = j < p.R ? reg[j] : -1;
-      if (j0 == 0) id0 = id;
+      const int id = j0 == 0 ? id_first : (j < p.R ? reg[j] : -1);
       nvis += __popcll(__ballot(id >= 0 && (int64_t)id * rt <= pos));
     }
     const int lo = (int)(((int64_t)split * nvis + p.splits - 1) / p.splits);
@@ -630,7 +656,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     int base_rank = 0;
     for (int j0 = 0; j0 < p.R; j0 += 64) {
       const int j = j0 + lane;
-      const int id = j0 == 0 ? id0 : (j < p.R ? reg[j] : -1);
+      const int id = j0 == 0 ? id_first : (j < p.R ? reg[j] : -1);
       const bool vis = id >= 0 && (int64_t)id * rt <= pos;
       const uint64_t m = __ballot(vis);
       const int k = base_rank + __popcll(m & ((1ull << lane) - 1ull));
@@ -652,6 +678,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   // pipeline rather than inside it.
 #pragma unroll
   for (int cc = 0; cc < 6; ++cc) __asm__ __volatile__("" : "+v"(qreg[cc]));
+  __asm__ __volatile__("" : "+v"(gbits));
 
   const float kscale = kFp8 ? *p.k_scale : 1.0f;
   const float qk_scale_log2 = p.scale * kscale * 1.4426950408889634f;
@@ -723,7 +750,33 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   }
   __syncthreads();
 
-  const float vscale = kFp8 ? *p.v_scale : 1.0f;
+  // Per column, once: the merged max and sum, the weight of each wave's
+  // partial state, 1/L, v_scale and (combine fused) the gate, folded into one
+  // factor per wave.  Lanes 0..15 of wave 0 hold columns 0..15.
+  if (tid < 16) {
+    const int c = tid;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w][c]);
+    float f[kWaves];
+    float L = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      f[w] = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s_m[w][c] - M);
+      L += s_l[w][c] * f[w];
+    }
+    float scale = M == -INFINITY ? 0.f : (kFp8 ? *p.v_scale : 1.0f) / L;
+    if (kFused && p.gated) scale *= gate_sigmoid(gbits);
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) s_fac[w][c] = f[w] * scale;
+    if (!kFused && c < ncols) {
+      const int row = kAddr == kWindow ? col_token * p.groups + g : r;
+      p.lse[((int64_t)row * p.splits + split) * p.heads + col_head] =
+          M == -INFINITY ? -INFINITY : M + __log2f(L);
+    }
+  }
+  __syncthreads();
+
   for (int e = tid; e < ncols * (kDim / 2); e += kThreads) {
     const int c = e / (kDim / 2), d = 2 * (e - c * (kDim / 2));
     // column c -> (token, head) and its output row
@@ -733,36 +786,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       token += jl;
       h = c - jl * p.heads;
     }
-    const int row = kAddr == kWindow ? token * p.groups + g : r;
-    float M = -INFINITY;
+    float o0 = 0.f, o1 = 0.f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w][c]);
-    float o0 = 0.f, o1 = 0.f, L = 0.f;
-    if (M != -INFINITY) {
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        float f = __builtin_amdgcn_exp2f(s_m[w][c] - M);
-        const float* src = s_acc + (size_t)w * kWaveStride + c * kAccStride + d;
-        L += s_l[w][c] * f;
-        o0 += src[0] * f;
-        o1 += src[1] * f;
-      }
-      float inv = vscale / L;
-      o0 *= inv;
-      o1 *= inv;
+    for (int w = 0; w < kWaves; ++w) {
+      const float fw = s_fac[w][c];
+      const float* src = s_acc + (size_t)w * kWaveStride + c * kAccStride + d;
+      o0 += src[0] * fw;
+      o1 += src[1] * fw;
     }
     if (kFused) {
-      if (p.gated) {
-        float gv = gate_value(p.gate, (int64_t)token * p.grs + (int64_t)(g * p.heads + h) * p.ghs);
-        o0 *= gv;
-        o1 *= gv;
-      }
       uint16_t* orow = p.out + (int64_t)token * p.ots + (int64_t)g * p.ogs;
       store_row_pair(orow, p, h, d, o0, o1);
     } else {
+      const int row = kAddr == kWindow ? token * p.groups + g : r;
       int64_t ph = ((int64_t)row * p.splits + split) * p.heads + h;
       *reinterpret_cast<float2*>(p.partial + ph * kDim + d) = make_float2(o0, o1);
-      if (d == 0) p.lse[ph] = M == -INFINITY ? -INFINITY : M + __log2f(L);
     }
   }
 }
@@ -804,21 +842,27 @@ __global__ __launch_bounds__(64) void combine_kernel(const Params p) {
 }
 
 template <bool kFp8, bool kFused, int kAddr>
-void launch_split(const Params& p, hipStream_t stream) {
-  hipLaunchKernelGGL((split_kernel<kFp8, kFused, kAddr>), dim3((unsigned)p.rows, (unsigned)p.splits),
-                     dim3(kThreads), 0, stream, p);
+void launch_split(const Params& p, unsigned wgs, hipStream_t stream) {
+  const dim3 grid(wgs, (unsigned)p.splits);
+  if ((int64_t)wgs * p.splits >= 2 * kComputeUnits)
+    hipLaunchKernelGGL((split_kernel<kFp8, kFused, kAddr, kWavesLargeGrid>), grid,
+                       dim3(64 * kWavesLargeGrid), 0, stream, p);
+  else
+    hipLaunchKernelGGL((split_kernel<kFp8, kFused, kAddr, kWavesSmallGrid>), grid,
+                       dim3(64 * kWavesSmallGrid), 0, stream, p);
 }
 
 template <bool kFp8>
 void launch_dtype(const Params& p, hipStream_t stream) {
   const bool fused = p.splits == 1;
   const bool uni = p.rt % Cfg<kFp8>::kTok == 0;
+  const unsigned wgs = (unsigned)p.rows;
   if (fused)
-    uni ? launch_split<kFp8, true, kUniform>(p, stream)
-        : launch_split<kFp8, true, kGeneral>(p, stream);
+    uni ? launch_split<kFp8, true, kUniform>(p, wgs, stream)
+        : launch_split<kFp8, true, kGeneral>(p, wgs, stream);
   else
-    uni ? launch_split<kFp8, false, kUniform>(p, stream)
-        : launch_split<kFp8, false, kGeneral>(p, stream);
+    uni ? launch_split<kFp8, false, kUniform>(p, wgs, stream)
+        : launch_split<kFp8, false, kGeneral>(p, wgs, stream);
 }
 
 hipError_t launch_combine(const Params& p, hipStream_t stream) {
@@ -842,11 +886,9 @@ hipError_t launch_window(const Params& p, hipStream_t stream) {
   // grid.x = requests * token groups * KV groups; the combine runs per row.
   const unsigned wgs = (unsigned)(p.rows / p.rows_per_req * p.ntg * p.groups);
   if (p.splits == 1)
-    hipLaunchKernelGGL((split_kernel<false, true, kWindow>), dim3(wgs, (unsigned)p.splits),
-                       dim3(kThreads), 0, stream, p);
+    launch_split<false, true, kWindow>(p, wgs, stream);
   else
-    hipLaunchKernelGGL((split_kernel<false, false, kWindow>), dim3(wgs, (unsigned)p.splits),
-                       dim3(kThreads), 0, stream, p);
+    launch_split<false, false, kWindow>(p, wgs, stream);
   return launch_combine(p, stream);
 }
 

@@ -33,6 +33,7 @@ struct Params {
   float* lse;                 // [rows, splits, heads] fp32, base-2 (splits > 1)
   float scale;
   int32_t rows, heads, groups, rows_per_req, block, R, rt, splits, clear, gated;
+  int32_t rt_shift;           // log2(rt) when rt is a power of two, else -1
   int32_t query_len, window;  // window mode
   int32_t pack, ntg;          // window mode: tokens per workgroup, token groups per request
 };

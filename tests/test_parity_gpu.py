@@ -352,6 +352,21 @@ def test_fp8_all_codes_through_the_kernel():
             assert torch.equal(out[r, h].cpu(), ref)
 
 
+# --- grids of >= 2 workgroups per CU take the 2-wave kernel variant ----------
+@pytest.mark.parametrize("kv,rt,splits", [("bf16", 0, 1), ("fp8", 0, 1), ("bf16", 8, 1),
+                                          ("fp8", 16, 2), ("bf16", 0, 3)])
+def test_large_grid_variant(kv, rt, splits):
+    w = gen.Workload("large-grid", requests=128, query_len=1, groups=4, heads=16, block=32,
+                     pages_per_req=8, R=6 if rt == 0 else 24, kv=kv, pos_lo=16, pos_hi=255,
+                     inactive_frac=0.05, gated=True, splits=splits, region_tokens=rt,
+                     seed=500 + splits + rt)
+    assert w.rows * splits >= 512
+    inp = gen.make_inputs(w, device=DEV)
+    out = run(inp, label="large grid %s rt%d" % (kv, rt))
+    check_close(out, oracle_out(inp), what="large grid %s rt%d splits%d" % (kv, rt, splits))
+    check_inactive_zero(out, inp)
+
+
 # --- full-size workloads: sampled rows + properties ---------------------------
 @pytest.mark.parametrize("k", [2, 3, 4, 5, 6])
 def test_full_size_sampled(k):

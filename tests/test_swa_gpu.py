@@ -237,6 +237,16 @@ def test_empty_batch_is_noop():
     torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("qlen,heads,splits", [(1, 16, 1), (4, 4, 2), (2, 16, 1)])
+def test_large_grid_variant(qlen, heads, splits):
+    # >= 512 workgroups: the 2-wave kernel variant
+    w = case(61, requests=160, query_len=qlen, groups=4, heads=heads, block=16,
+             pages_per_req=8, window=50, seq_lo=qlen, seq_hi=128)
+    inp = gen.make_swa_inputs(w, device=DEV)
+    out = run(inp, splits=splits, label="large grid")
+    check_close(out, oracle_out(inp), w, what="large grid q%d h%d s%d" % (qlen, heads, splits))
+
+
 # --- full-size workloads: sampled rows + properties ---------------------------
 @pytest.mark.parametrize("name", ["swa-gated", "swa-mtp"])
 def test_full_size_sampled(name):
