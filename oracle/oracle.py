@@ -102,6 +102,10 @@ def lib():
             l.sdo_decode_split.restype = ctypes.c_int
             l.sdo_decode_split.argtypes = [ctypes.POINTER(_Problem), ctypes.c_int,
                                            ctypes.c_void_p, ctypes.c_int, ctypes.c_int]
+            l.sdo_select_regions.restype = ctypes.c_int
+            l.sdo_select_regions.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                             ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64]
             l.sdo_swa_decode.restype = ctypes.c_int
             l.sdo_swa_decode.argtypes = [ctypes.POINTER(_SwaProblem), ctypes.c_void_p,
                                          ctypes.c_int, ctypes.c_int]
@@ -340,4 +344,23 @@ def swa_decode(hp: SwaHostProblem, rows=None, threads: int = 1) -> np.ndarray:
             t.join()
         if errs:
             raise errs[0]
+    return out
+
+
+def select_regions(scores: np.ndarray, current: np.ndarray, topk: int,
+                   topk_lengths: np.ndarray | None = None) -> np.ndarray:
+    """int32 [rows, topk]: the selected region ids of each row in ascending
+    order, then -1 (see ``sdo_select_regions``).  ``scores``: float32
+    [rows, S] (any row stride, unit inner stride)."""
+    assert scores.dtype == np.float32 and scores.ndim == 2
+    assert scores.strides[1] == 4 or scores.shape[1] <= 1
+    rows, S = scores.shape
+    cur = np.ascontiguousarray(current, dtype=np.int32)
+    assert cur.shape == (rows,)
+    lens = None if topk_lengths is None else np.ascontiguousarray(topk_lengths, dtype=np.int32)
+    out = np.full((rows, topk), -7, dtype=np.int32)
+    rs = scores.strides[0] // 4 if rows > 1 else S
+    _check_rc(lib().sdo_select_regions(rows, S, topk, scores.ctypes.data, rs, cur.ctypes.data,
+                                       None if lens is None else lens.ctypes.data,
+                                       out.ctypes.data, topk))
     return out

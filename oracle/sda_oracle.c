@@ -419,3 +419,63 @@ int sdo_swa_decode(const sdo_swa_problem *s, double *out, int row_begin, int row
   free(logit);
   return rc;
 }
+
+/* ---- region selection ------------------------------------------------------
+ * [P3] `select_regions` as `select_and_run_decode_attention` and the prefill
+ * loop call it (`sort=False`): per row, the `topk` regions to attend.  The
+ * body is not on the pages.  Reading: the candidates of row r are regions
+ * 0 .. n_r - 1 with n_r = topk_lengths[r] clamped to [0, S] (S = score
+ * columns; all S without lengths); the current region is forced in when it is
+ * a candidate; the other slots take the highest-scoring remaining
+ * candidates, equal scores going to the lower region id (-0.0 ranks below
+ * +0.0); the selected ids are written in ascending order, then -1 up to topk.
+ * NaN scores are outside the contract. */
+typedef struct { float s; int32_t j; } sdo_cand;
+
+static int cand_order(const void *pa, const void *pb) {
+  const sdo_cand *a = (const sdo_cand *)pa, *b = (const sdo_cand *)pb;
+  if (a->s != b->s) return a->s > b->s ? -1 : 1;            /* higher score first */
+  if (signbit(a->s) != signbit(b->s)) return signbit(a->s) ? 1 : -1;  /* +0 before -0 */
+  return a->j < b->j ? -1 : (a->j > b->j ? 1 : 0);          /* lower id first */
+}
+
+static int id_order(const void *pa, const void *pb) {
+  int32_t a = *(const int32_t *)pa, b = *(const int32_t *)pb;
+  return a < b ? -1 : (a > b ? 1 : 0);
+}
+
+int sdo_select_regions(int32_t rows, int32_t S, int32_t topk, const float *scores,
+                       int64_t scores_row_stride, const int32_t *current,
+                       const int32_t *topk_lengths, int32_t *out, int64_t out_row_stride) {
+  if (rows < 0 || S < 0 || topk < 0 || (rows > 0 && (!scores || !current || !out)))
+    return SDO_ERR_ARGS;
+  sdo_cand *cand = (sdo_cand *)malloc(sizeof(sdo_cand) * (size_t)(S + 1));
+  int32_t *sel = (int32_t *)malloc(sizeof(int32_t) * (size_t)(topk + 1));
+  if (!cand || !sel) { free(cand); free(sel); return SDO_ERR_NOMEM; }
+  for (int32_t r = 0; r < rows; ++r) {
+    int64_t n = topk_lengths ? topk_lengths[r] : S;
+    if (n < 0) n = 0;
+    if (n > S) n = S;
+    int32_t cur = current[r];
+    int forced = cur >= 0 && cur < n && topk > 0;
+    int m = 0;
+    for (int32_t j = 0; j < n; ++j) {
+      if (forced && j == cur) continue;
+      cand[m].s = scores[(int64_t)r * scores_row_stride + j];
+      cand[m].j = j;
+      ++m;
+    }
+    qsort(cand, (size_t)m, sizeof(sdo_cand), cand_order);
+    int take = topk - forced;
+    if (take > m) take = m;
+    int k = 0;
+    if (forced) sel[k++] = cur;
+    for (int i = 0; i < take; ++i) sel[k++] = cand[i].j;
+    qsort(sel, (size_t)k, sizeof(int32_t), id_order);
+    int32_t *o = out + (int64_t)r * out_row_stride;
+    for (int i = 0; i < topk; ++i) o[i] = i < k ? sel[i] : -1;
+  }
+  free(cand);
+  free(sel);
+  return SDO_OK;
+}
