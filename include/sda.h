@@ -30,7 +30,7 @@
 extern "C" {
 #endif
 
-#define SDA_ABI_VERSION 2
+#define SDA_ABI_VERSION 3
 #define SDA_HEAD_DIM 192     /* query / key / value head dim (fixed) */
 #define SDA_KV_ROW 384       /* one cache token row: K[0:192] then V[192:384] */
 #define SDA_MAX_HEADS 16     /* GQA-packed query heads per KV group */
@@ -249,15 +249,60 @@ int sda_swa_decode(const sda_swa_args *args, hipStream_t stream);
  */
 int sda_swa_plan(int tokens, int groups, int heads, int query_len, int window, int *pack);
 
+/*
+ * Region selection: `select_regions` on page "vllm.models.step5.nvidia.
+ * flashinfer_sparse" as `select_and_run_decode_attention` calls it before the
+ * sparse decode (`sort=False`).  For each row: the candidates are regions
+ * 0 .. n_r - 1, n_r = topk_lengths[r] clamped to [0, num_regions] (all
+ * num_regions score columns when topk_lengths is NULL).  The current region is
+ * selected whenever it is a candidate; the other topk - 1 slots take the
+ * highest-scoring remaining candidates.  Equal scores go to the lower region
+ * id (-0.0 ranks below +0.0).  The selected ids are written in ascending
+ * order, followed by -1 up to topk: exactly the `regions` input of
+ * sda_decode (with region_tokens = the indexer's region size).  NaN scores
+ * are outside the contract.  All pointers are device pointers; strides in
+ * elements.
+ *
+ *  rows          rows (token, KV group), at most SDA_MAX_ROWS; 0 returns OK.
+ *  num_regions   score columns S, 0..SDA_MAX_SCORE_COLUMNS.
+ *  topk          output slots per row; 0 returns OK.
+ *  scores        fp32 [rows, S], unit inner stride, 4-byte aligned.
+ *  current       int32 [rows]: the region holding the row's own token
+ *                (position / region_tokens); a value outside [0, n_r) forces
+ *                nothing.
+ *  topk_lengths  int32 [rows] or NULL.
+ *  regions       int32 [rows, topk] output; row stride >= topk.
+ */
+#define SDA_MAX_SCORE_COLUMNS 32768
+
+typedef struct sda_select_args {
+  int32_t rows, num_regions, topk;
+  const float *scores;
+  int64_t scores_row_stride;
+  const int32_t *current;
+  const int32_t *topk_lengths;
+  int32_t *regions;
+  int64_t regions_row_stride;
+} sda_select_args;
+
+/*
+ * Enqueue one selection call: one 256-thread workgroup per row (radix select
+ * of the threshold score in registers and LDS, then an ordered compaction).
+ * Asynchronous, no allocation.  Returns an sda_status; on error nothing is
+ * launched.
+ */
+int sda_select_regions(const sda_select_args *args, hipStream_t stream);
+
 /* Static description of a status code (never NULL). */
 const char *sda_status_string(int status);
 
-/* SDA_ABI_VERSION of the built library, and sizeof(sda_decode_args) and
- * sizeof(sda_swa_args), so a binding can check that its mirrors of the
- * structs match. */
+/* SDA_ABI_VERSION of the built library, and the sizes of sda_decode_args,
+ * sda_swa_args and sda_select_args, so a binding can check that its mirrors
+ * of the structs match. */
 int sda_abi_version(void);
 size_t sda_args_size(void);
 size_t sda_swa_args_size(void);
+size_t sda_select_args_size(void);
 
 #ifdef __cplusplus
 }

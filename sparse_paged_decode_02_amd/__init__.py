@@ -2,13 +2,15 @@
 
 The compute path is libsda.so (HIP kernels behind a C ABI, include/sda.h);
 this package is its thin ctypes binding.  ``sda_decode`` is the sparse decode
-of the DSA layers; ``sda_swa_decode`` the gated sliding-window decode of the
-other layers over the same cache.  Seeded synthetic workloads live in
+of the DSA layers, ``sda_select_regions`` the region selection upstream of it,
+and ``sda_swa_decode`` the gated sliding-window decode of the other layers over
+the same cache.  Seeded synthetic workloads live in
 ``inputs``.
 """
 from .binding import (  # noqa: F401
     SdaError,
     sda_decode,
+    sda_select_regions,
     sda_splits,
     sda_swa_decode,
     sda_swa_plan,

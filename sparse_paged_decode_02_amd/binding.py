@@ -23,7 +23,7 @@ SDA_ERR_WORKSPACE = -3
 SDA_ERR_LAUNCH = -4
 SDA_KV_BF16 = 0
 SDA_KV_FP8_E4M3 = 1
-ABI_VERSION = 2
+ABI_VERSION = 3
 HEAD_DIM = 192
 
 
@@ -80,6 +80,16 @@ class SwaArgs(ctypes.Structure):
     ]
 
 
+class SelectArgs(ctypes.Structure):
+    """Mirror of ``sda_select_args``; checked against sda_select_args_size()."""
+    _fields_ = [
+        ("rows", ctypes.c_int32), ("num_regions", ctypes.c_int32), ("topk", ctypes.c_int32),
+        ("scores", ctypes.c_void_p), ("scores_row_stride", ctypes.c_int64),
+        ("current", ctypes.c_void_p), ("topk_lengths", ctypes.c_void_p),
+        ("regions", ctypes.c_void_p), ("regions_row_stride", ctypes.c_int64),
+    ]
+
+
 _lib = None
 _lock = threading.Lock()
 
@@ -112,12 +122,19 @@ def lib() -> ctypes.CDLL:
             l.sda_swa_plan.argtypes = [ctypes.c_int] * 5 + [ctypes.POINTER(ctypes.c_int)]
             l.sda_swa_args_size.restype = ctypes.c_size_t
             l.sda_swa_args_size.argtypes = []
+            l.sda_select_regions.restype = ctypes.c_int
+            l.sda_select_regions.argtypes = [ctypes.POINTER(SelectArgs), ctypes.c_void_p]
+            l.sda_select_args_size.restype = ctypes.c_size_t
+            l.sda_select_args_size.argtypes = []
             if l.sda_abi_version() != ABI_VERSION:
                 raise RuntimeError("libsda.so ABI version %d, binding expects %d"
                                    % (l.sda_abi_version(), ABI_VERSION))
             if l.sda_args_size() != ctypes.sizeof(DecodeArgs):
                 raise RuntimeError("sda_decode_args size mismatch: library %d, binding %d"
                                    % (l.sda_args_size(), ctypes.sizeof(DecodeArgs)))
+            if l.sda_select_args_size() != ctypes.sizeof(SelectArgs):
+                raise RuntimeError("sda_select_args size mismatch: library %d, binding %d"
+                                   % (l.sda_select_args_size(), ctypes.sizeof(SelectArgs)))
             if l.sda_swa_args_size() != ctypes.sizeof(SwaArgs):
                 raise RuntimeError("sda_swa_args size mismatch: library %d, binding %d"
                                    % (l.sda_swa_args_size(), ctypes.sizeof(SwaArgs)))
@@ -338,3 +355,50 @@ def sda_swa_decode(query, cache, block_table, seq_lens, output, *, scale, window
 def sda_swa_decode_raw(args: SwaArgs, stream_handle=None) -> int:
     """Call sda_swa_decode on a prepared struct; returns the status code."""
     return int(lib().sda_swa_decode(ctypes.byref(args), stream_handle))
+
+
+def make_select_args(scores, current, topk, out, topk_lengths=None) -> SelectArgs:
+    """Fill ``sda_select_args`` from tensors (no validation beyond the C side)."""
+    a = SelectArgs()
+    a.rows, a.num_regions, a.topk = scores.shape[0], scores.shape[1], int(topk)
+    a.scores = _ptr(scores)
+    a.scores_row_stride = scores.stride(0)
+    a.current = _ptr(current)
+    a.topk_lengths = _ptr(topk_lengths)
+    a.regions = _ptr(out)
+    a.regions_row_stride = out.stride(0) if out.dim() == 2 else 0
+    return a
+
+
+def sda_select_regions(scores, current, topk, *, topk_lengths=None, out=None,
+                       stream=None):
+    """Enqueue ``sda_select_regions``; returns the int32 [rows, topk] regions.
+
+    Argument names follow ``select_regions`` on the page "vllm.models.step5.
+    nvidia.flashinfer_sparse" (``sort=False``)."""
+    if scores.dtype != torch.float32 or scores.dim() != 2 or (
+            scores.shape[1] > 1 and scores.stride(1) != 1):
+        raise SdaError(SDA_ERR_INVALID, "scores must be float32 [rows, regions], unit inner stride")
+    rows = scores.shape[0]
+    for t, name in ((current, "current"), (topk_lengths, "topk_lengths")):
+        if t is not None and (t.dtype != torch.int32 or not t.is_contiguous() or
+                              t.numel() != rows):
+            raise SdaError(SDA_ERR_INVALID, "%s must be contiguous int32 [rows]" % name)
+    if out is None:
+        out = torch.empty((rows, int(topk)), dtype=torch.int32, device=scores.device)
+    if out.dtype != torch.int32 or out.dim() != 2 or out.shape != (rows, int(topk)) or (
+            topk > 1 and out.stride(1) != 1):
+        raise SdaError(SDA_ERR_INVALID, "out must be int32 [rows, topk], unit inner stride")
+    a = make_select_args(scores, current, topk, out, topk_lengths)
+    if stream is None:
+        stream = torch.cuda.current_stream(scores.device) if scores.is_cuda else None
+    handle = None if stream is None else ctypes.c_void_p(stream.cuda_stream)
+    rc = lib().sda_select_regions(ctypes.byref(a), handle)
+    if rc != SDA_OK:
+        raise SdaError(rc, status_string(rc))
+    return out
+
+
+def sda_select_regions_raw(args: SelectArgs, stream_handle=None) -> int:
+    """Call sda_select_regions on a prepared struct; returns the status code."""
+    return int(lib().sda_select_regions(ctypes.byref(args), stream_handle))

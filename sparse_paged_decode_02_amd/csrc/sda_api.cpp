@@ -254,4 +254,30 @@ int sda_swa_decode(const sda_swa_args* a, hipStream_t stream) {
   return e == hipSuccess ? SDA_OK : SDA_ERR_LAUNCH;
 }
 
+size_t sda_select_args_size(void) { return sizeof(sda_select_args); }
+
+int sda_select_regions(const sda_select_args* a, hipStream_t stream) {
+  if (!a) return SDA_ERR_INVALID;
+  if (a->rows < 0 || a->num_regions < 0 || a->topk < 0) return SDA_ERR_INVALID;
+  if (a->rows > 1 && a->regions_row_stride < a->topk) return SDA_ERR_INVALID;
+  if (a->num_regions > SDA_MAX_SCORE_COLUMNS || a->rows > SDA_MAX_ROWS) return SDA_ERR_UNSUPPORTED;
+  if (a->rows == 0 || a->topk == 0) return SDA_OK;
+  if (!a->current || !a->regions || (a->num_regions > 0 && !a->scores)) return SDA_ERR_INVALID;
+  if (!aligned(a->scores, 4) || !aligned(a->current, 4) || !aligned(a->topk_lengths, 4) ||
+      !aligned(a->regions, 4))
+    return SDA_ERR_INVALID;
+  sda::SelParams p{};
+  p.scores = a->scores;
+  p.srs = a->scores_row_stride;
+  p.current = a->current;
+  p.lengths = a->topk_lengths;
+  p.out = a->regions;
+  p.ors = a->regions_row_stride;
+  p.rows = a->rows;
+  p.S = a->num_regions;
+  p.topk = a->topk;
+  hipError_t e = sda::launch_select(p, stream);
+  return e == hipSuccess ? SDA_OK : SDA_ERR_LAUNCH;
+}
+
 }  // extern "C"

@@ -49,4 +49,17 @@ hipError_t launch(const Params& p, bool fp8, hipStream_t stream);
 // Requires block % 16 == 0.
 hipError_t launch_window(const Params& p, hipStream_t stream);
 
+// Region selection (sda_select.hip).
+struct SelParams {
+  const float* scores;        // [rows, S]
+  int64_t srs;
+  const int32_t* current;     // [rows]
+  const int32_t* lengths;     // [rows] or null (all S columns are candidates)
+  int32_t* out;               // [rows, topk]
+  int64_t ors;
+  int32_t rows, S, topk;
+};
+
+hipError_t launch_select(const SelParams& p, hipStream_t stream);
+
 }  // namespace sda

@@ -318,3 +318,58 @@ def make_swa_inputs(w: SwaWorkload, device="cpu", seed: int | None = None,
                      block_table=torch.from_numpy(table).to(device),
                      seq_lens=torch.from_numpy(seq_lens).to(device), gate=gate, scale=w.scale,
                      splits=w.splits if splits is None else splits)
+
+
+# ---- region selection -------------------------------------------------------
+# Scores of 8-token regions for decode rows: row r's current region is
+# position // 8 and its candidates are regions 0 .. position // 8.
+
+@dataclass(frozen=True)
+class SelectWorkload:
+    name: str
+    rows: int
+    num_regions: int             # score columns S
+    topk: int
+    pos_lo: int                  # row position ~ U[pos_lo, pos_hi]
+    pos_hi: int
+    region_tokens: int = 8
+    seed: int = 0
+
+
+SELECT_CONFIGS = {
+    # the bf16-gated decode batch (64 requests x G 4) over 32K contexts
+    "select-decode": SelectWorkload("select-decode", rows=256, num_regions=4096, topk=512,
+                                    pos_lo=4096, pos_hi=32767, seed=config_seed(21)),
+    # the large batch (1024 requests x G 4) over 128K contexts
+    "select-large": SelectWorkload("select-large", rows=4096, num_regions=16384, topk=512,
+                                   pos_lo=65536, pos_hi=131071, seed=config_seed(22)),
+}
+
+
+@dataclass
+class SelectInputs:
+    w: SelectWorkload
+    scores: torch.Tensor         # fp32 [rows, S]
+    current: torch.Tensor        # int32 [rows]
+    topk_lengths: torch.Tensor   # int32 [rows]
+
+
+def make_select_inputs(w: SelectWorkload, device="cpu", seed: int | None = None,
+                       dist: str = "normal") -> SelectInputs:
+    """scores ~ N(0,1) fp32 ("normal"), or small integers with many ties
+    ("ties"); positions ~ U[pos_lo, pos_hi]; current = position // region_tokens,
+    topk_lengths = current + 1."""
+    seed = w.seed if seed is None else seed
+    rng = np.random.default_rng(seed)
+    pos = rng.integers(w.pos_lo, w.pos_hi + 1, size=w.rows)
+    cur = (pos // w.region_tokens).astype(np.int32)
+    lens = np.minimum(cur + 1, w.num_regions).astype(np.int32)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed * 2 + 1)
+    if dist == "normal":
+        scores = torch.randn((w.rows, w.num_regions), generator=gen, device=device)
+    else:
+        scores = torch.randint(0, 8, (w.rows, w.num_regions), generator=gen,
+                               device=device).to(torch.float32)
+    return SelectInputs(w=w, scores=scores, current=torch.from_numpy(cur).to(device),
+                        topk_lengths=torch.from_numpy(lens).to(device))

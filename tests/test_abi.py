@@ -20,6 +20,7 @@ def test_library_exports_every_declared_function():
     names = _declared_functions()
     assert {"sda_decode", "sda_splits", "sda_workspace_bytes", "sda_status_string",
             "sda_abi_version", "sda_args_size", "sda_swa_decode", "sda_swa_plan",
+            "sda_select_regions", "sda_select_args_size",
             "sda_swa_args_size"} <= set(names)
     lib = B.lib()
     for n in names:
@@ -31,6 +32,7 @@ def test_abi_version_and_struct_size():
     assert lib.sda_abi_version() == B.ABI_VERSION
     assert lib.sda_args_size() == ctypes.sizeof(B.DecodeArgs)
     assert lib.sda_swa_args_size() == ctypes.sizeof(B.SwaArgs)
+    assert lib.sda_select_args_size() == ctypes.sizeof(B.SelectArgs)
 
 
 def _table(name):
@@ -217,3 +219,43 @@ def test_swa_pack_limit_edges():
         rc = B.sda_swa_decode_raw(_valid_swa(block=16, heads=8, pack=pack, window=window,
                                              splits=2))
         assert rc == B.SDA_ERR_WORKSPACE, (pack, window, rc)
+
+
+# ---- region selection entry point --------------------------------------------
+
+def _valid_select(**over):
+    a = B.SelectArgs()
+    a.rows, a.num_regions, a.topk = 8, 4096, 512
+    a.scores, a.scores_row_stride = 0x100000, 4096
+    a.current, a.topk_lengths = 0x200000, 0x300000
+    a.regions, a.regions_row_stride = 0x400000, 512
+    for k, v in over.items():
+        setattr(a, k, v)
+    return a
+
+
+SELECT_INVALID = [dict(rows=-1), dict(num_regions=-1), dict(topk=-1), dict(regions_row_stride=511),
+                  dict(current=None), dict(regions=None), dict(scores=None),
+                  dict(scores=0x100002), dict(current=0x200001), dict(regions=0x400003),
+                  dict(topk_lengths=0x300002)]
+SELECT_UNSUPPORTED = [dict(num_regions=32769), dict(rows=16777216)]
+
+
+@pytest.mark.parametrize("over", SELECT_INVALID, ids=[str(o) for o in SELECT_INVALID])
+def test_select_invalid_arguments_are_rejected(over):
+    assert B.sda_select_regions_raw(_valid_select(**over)) == B.SDA_ERR_INVALID
+
+
+@pytest.mark.parametrize("over", SELECT_UNSUPPORTED, ids=[str(o) for o in SELECT_UNSUPPORTED])
+def test_select_unsupported_arguments_are_rejected(over):
+    assert B.sda_select_regions_raw(_valid_select(**over)) == B.SDA_ERR_UNSUPPORTED
+
+
+def test_select_empty_calls_launch_nothing():
+    assert B.lib().sda_select_regions(None, None) == B.SDA_ERR_INVALID
+    assert B.sda_select_regions_raw(_valid_select(rows=0, scores=None, current=None,
+                                                  regions=None)) == B.SDA_OK
+    assert B.sda_select_regions_raw(_valid_select(topk=0, regions_row_stride=0)) == B.SDA_OK
+    # one row needs no row stride
+    assert B.sda_select_regions_raw(_valid_select(rows=1, regions_row_stride=0, topk=0)) == \
+        B.SDA_OK
