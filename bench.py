@@ -20,7 +20,9 @@ host cores.
 
 ``--swa NAME`` measures the gated sliding-window decode (``sda_swa_decode``)
 on one of its workloads instead; its algorithmic bytes are each row's window
-of K|V rows, plus Q and the output.
+of K|V rows, plus Q and the output.  ``--select NAME`` measures region
+selection (``sda_select_regions``): its bytes are the candidate scores, the
+row metadata and the selected ids.
 """
 from __future__ import annotations
 
@@ -38,11 +40,17 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBS = 8000.0
 METRIC = "effective KV GB/s (% of HBM peak) and rows/s for sparse decode attention"
 KERNEL_SRC = os.path.join(ROOT, "sparse_paged_decode_02_amd", "csrc", "sda_kernels.hip")
+SELECT_SRC = os.path.join(ROOT, "sparse_paged_decode_02_amd", "csrc", "sda_select.hip")
 
 
 def kernel_hash() -> str:
     """First 16 hex digits of the kernel source's SHA-256 (ties counters to code)."""
     with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def select_kernel_hash() -> str:
+    with open(SELECT_SRC, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
@@ -249,10 +257,79 @@ def run_swa(args, dev) -> int:
     return 0
 
 
-def load_traffic(workload_name: str, splits: int):
+def select_algorithmic_bytes(w, lengths) -> int:
+    """Candidate scores (fp32) + current and length (int32) per row + the
+    int32 [rows, topk] output."""
+    n = np.clip(np.asarray(lengths, dtype=np.int64), 0, w.num_regions)
+    return int(n.sum()) * 4 + w.rows * 8 + w.rows * w.topk * 4
+
+
+def select_cpu_baseline(inp, gpu_out, min_seconds: float):
+    """Time the oracle's selection (as it stands, one host thread) on the
+    first input set, repeated until min_seconds have been spent."""
+    from oracle import oracle
+    s = inp.scores.cpu().numpy()
+    cur = inp.current.cpu().numpy()
+    lens = inp.topk_lengths.cpu().numpy()
+    passes, dt, ref = timed_passes(lambda: oracle.select_regions(s, cur, inp.w.topk, lens),
+                                   min_seconds)
+    nbytes = select_algorithmic_bytes(inp.w, lens)
+    return {
+        "value": passes * nbytes / dt / 1e9,
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": "all %d rows of the first input set, %d passes (C oracle: sort per row, one "
+                  "thread), %.2f s wall; rows/s %.1f" % (inp.w.rows, passes, dt,
+                                                         passes * inp.w.rows / dt),
+        "parity_exact": bool(np.array_equal(gpu_out.cpu().numpy(), ref)),
+    }
+
+
+def run_select(args, dev) -> int:
+    import torch
+    from sparse_paged_decode_02_amd import binding as B
+    from sparse_paged_decode_02_amd import inputs as gen
+
+    w = gen.SELECT_CONFIGS[args.select]
+    desc = ("%s: %d rows, %d score columns (%d-token regions), topk %d, positions U[%d,%d]"
+            % (w.name, w.rows, w.num_regions, w.region_tokens, w.topk, w.pos_lo, w.pos_hi))
+    print("[bench] drawing %s" % desc, file=sys.stderr, flush=True)
+    sets = [gen.make_select_inputs(w, device=dev, seed=w.seed + 100003 * i)
+            for i in range(args.sets)]
+    nbytes = [select_algorithmic_bytes(w, s.topk_lengths.cpu().numpy()) for s in sets]
+    outs = [torch.empty((w.rows, w.topk), dtype=torch.int32, device=dev) for _ in sets]
+    stream = torch.cuda.current_stream(dev)
+    handle = ctypes.c_void_p(stream.cuda_stream)
+    prepared = [B.make_select_args(s.scores, s.current, w.topk, o, s.topk_lengths)
+                for s, o in zip(sets, outs)]
+
+    def call(i):
+        rc = B.sda_select_regions_raw(prepared[i % len(prepared)], handle)
+        if rc != B.SDA_OK:
+            raise B.SdaError(rc, B.status_string(rc))
+
+    wall, launch_avg_ms, launch_ms = time_calls(call, args.steps, args.warmup, stream)
+    total_bytes = sum(nbytes[i % len(sets)] for i in range(args.steps))
+    bytes_per_launch = float(np.mean([nbytes[i % len(sets)] for i in range(args.steps)]))
+    rec = record(args, value=total_bytes / wall / 1e9, wall=wall, launch_avg_ms=launch_avg_ms,
+                 launch_ms=launch_ms, bytes_per_launch=bytes_per_launch, rows=w.rows,
+                 dtype="fp32 scores, int32 ids",
+                 config={"workload": desc, "rows": w.rows, "num_regions": w.num_regions,
+                         "topk": w.topk, "input_sets": len(sets), "seed": w.seed},
+                 kernel="select_kernel", traffic=load_traffic(w.name, 1, "select_kernel"),
+                 metric="effective GB/s (% of HBM peak) and rows/s for region selection")
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline: oracle selection", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = select_cpu_baseline(sets[0], outs[0], args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+def load_traffic(workload_name: str, splits: int, kernel: str = "split_kernel"):
     """Counter-derived HBM bytes per launch from the committed profile summary,
     or None unless it was measured on the current kernel source and split count."""
-    path = os.path.join(ROOT, "profiles", "split_kernel_%s.md" % workload_name)
+    path = os.path.join(ROOT, "profiles", "%s_%s.md" % (kernel, workload_name))
     if not os.path.exists(path):
         return None
     fields = {}
@@ -260,7 +337,8 @@ def load_traffic(workload_name: str, splits: int):
         parts = line.strip().split("=")
         if len(parts) == 2:
             fields[parts[0].strip()] = parts[1].strip()
-    if fields.get("kernel_sha256_16") != kernel_hash() or fields.get("splits") != str(splits):
+    want_hash = select_kernel_hash() if kernel == "select_kernel" else kernel_hash()
+    if fields.get("kernel_sha256_16") != want_hash or fields.get("splits") != str(splits):
         return None
     try:
         return int(fields["traffic_bytes_per_launch"])
@@ -324,6 +402,9 @@ def main() -> int:
     ap.add_argument("--swa", default="", metavar="NAME",
                     help="measure the gated sliding-window decode on workload NAME "
                          "(swa-gated, swa-mtp) instead")
+    ap.add_argument("--select", default="", metavar="NAME",
+                    help="measure region selection on workload NAME (select-decode, "
+                         "select-large) instead")
     ap.add_argument("--pack", type=int, default=0,
                     help="with --swa: query tokens per workgroup (0: the library's plan)")
     ap.add_argument("--sets", type=int, default=4, help="rotating input sets")
@@ -364,6 +445,8 @@ def main() -> int:
         return 0
     if args.swa:
         return run_swa(args, dev)
+    if args.select:
+        return run_select(args, dev)
     w = gen.CONFIGS[args.config]
     splits = args.splits or w.splits or B.sda_splits(w.rows)
 

@@ -6,21 +6,24 @@
 // region always selected.  Equal scores go to the lower region id (-0.0 ranks
 // below +0.0), and the ids are written in ascending order, then -1.
 //
-// One 256-thread workgroup per row.
-//  1. Each thread loads its scores (ids tid + 256 i) as order-preserving
-//     32-bit keys into registers.
+// One 1024-thread workgroup (16 waves) per row; wave w owns the contiguous
+// ids [w L, (w+1) L), L = 256 I, and lane l holds ids w L + 4 l + 256 i + c.
+//  1. Keys: 16-byte loads (4-byte ones when the row is not 16-byte aligned)
+//     of the scores as order-preserving 32-bit keys, held in registers.
+//     Non-candidates get key 0, which no score maps to (NaN aside).
 //  2. Radix select of the threshold key T: three MSB-first passes of 12, 12
 //     and 8 bits.  Each pass histograms the keys that match the prefix found
 //     so far (LDS atomics), and a block scan from the top bin finds the digit
 //     where the count of larger keys reaches the number still needed.  After
 //     the last pass T is exact, together with how many keys equal to T are
 //     taken.
-//  3. Ordered compaction over blocks of 256 ids: keys > T, the forced region,
-//     and the first needed keys == T in id order are selected.  Wave ballots
-//     and one barrier per block give each selected id its output slot, so the
-//     output is ascending and deterministic.
-// The bytes are the row's scores (read once) and the output; the work is
-// LDS-atomic and scan bound for long rows, latency bound for short ones.
+//  3. Compaction in id order: keys > T, the forced region and the first
+//     needed keys == T are selected.  Each wave counts its selections, one
+//     barrier gives every wave its output offset, and each wave then writes
+//     its range in order with in-wave scans (no further barriers).
+// The bytes are the row's candidate scores (read once) and the output; the
+// work is LDS-atomic and scan bound for long rows, latency bound for short
+// ones.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -30,81 +33,102 @@
 namespace sda {
 namespace {
 
-constexpr int kSelThreads = 256;
+constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
 constexpr int kHistBins = 4096;
+constexpr int kCandCap = 4096;  // keys of the first pass's threshold bin kept in LDS
 
 // Keys that order like the floats: flip all bits of negatives, set the sign
 // bit of non-negatives.  -0.0 -> 0x7FFFFFFF < +0.0 -> 0x80000000.
 __device__ __forceinline__ uint32_t order_key(float f) {
   const uint32_t u = __float_as_uint(f);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
 
-__device__ __forceinline__ int lanes_below(uint64_t mask, int lane) {
-  return __popcll(mask & ((1ull << lane) - 1ull));
-}
-
-// Inclusive scan of v over the workgroup in thread order; `total` gets the sum.
-__device__ __forceinline__ int block_inclusive_scan(int v, int* s_w, int tid, int& total) {
-  const int lane = tid & 63, wave = tid >> 6;
+// Exclusive scan of v over the 64 lanes of a wave; `total` gets the sum.
+__device__ __forceinline__ int wave_exclusive_scan(int v, int lane, int& total) {
+  int x = v;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
-    const int u = __shfl_up(v, d);
-    if (lane >= d) v += u;
+    const int u = __shfl_up(x, d);
+    if (lane >= d) x += u;
   }
-  if (lane == 63) s_w[wave] = v;
-  __syncthreads();
-  int before = 0;
-  total = 0;
-#pragma unroll
-  for (int w = 0; w < kSelWaves; ++w) {
-    const int t = s_w[w];
-    before += w < wave ? t : 0;
-    total += t;
-  }
-  __syncthreads();
-  return v + before;
+  total = __shfl(x, 63);
+  return x - v;
 }
 
-// Digit d of a histogram with nb bins such that the count of keys in bins
-// above d is < need <= the count in bins >= d.  Returns d; `above` gets the
-// count in bins above d.  Thread t scans bins [nb - bpt (t+1), nb - bpt t).
-__device__ __forceinline__ int find_digit(const int* hist, int nb, int need, int* s_w,
-                                          int* s_pick, int tid, int& above) {
-  const int bpt = nb / kSelThreads;
-  const int hi = nb - bpt * tid;  // exclusive top of this thread's bins
-  int local = 0;
-  for (int b = hi - 1; b >= hi - bpt; --b) local += hist[b];
-  int total;
-  const int incl = block_inclusive_scan(local, s_w, tid, total);
-  const int excl = incl - local;
-  if (excl < need && need <= incl) {
-    int run = excl;
-    for (int b = hi - 1; b >= hi - bpt; --b) {
-      if (run + hist[b] >= need) {
-        s_pick[0] = b;
-        s_pick[1] = run;
-        break;
-      }
-      run += hist[b];
+// Sum of v over the 64 lanes of a wave (every lane gets it).
+__device__ __forceinline__ int wave_sum(int v, int lane) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d);
+  return v;
+}
+
+// Sum of cnt[w][f] over waves w < upto (upto <= 16), every lane gets it:
+// lane w reads wave w's entry, one wave reduction.
+__device__ __forceinline__ int wave_prefix_of(const int (*cnt)[2], int f, int upto, int lane) {
+  return wave_sum(lane < upto ? cnt[lane][f] : 0, lane);
+}
+
+// Lanes below this one whose bit is set in mask.
+__device__ __forceinline__ int mbcnt(uint64_t mask) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                        __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// Digit d of a histogram with nb bins (nb a multiple of 64, at most 4096)
+// such that the count of keys in bins above d is < need <= the count in bins
+// >= d.  Wave 0 searches in two levels: lane l sums the per = nb / 64 bins
+// [nb - per (l+1), nb - per l); a wave scan from the top finds the lane L
+// where the count reaches `need`; then lane l takes bin nb - per L - 1 - l
+// of L's range and a second scan finds the bin.  One barrier publishes the
+// result through s_pick.
+template <int NB>
+__device__ __forceinline__ int find_digit(const int* hist, int need, int* s_pick, int wave,
+                                          int lane, int& above) {
+  static_assert(NB % 256 == 0 && NB <= 4096, "bins: a multiple of 256, at most 4096");
+  constexpr int nb = NB;
+  if (wave == 0) {
+    constexpr int per = nb / 64;
+    const int hi = nb - per * lane;  // exclusive top of this lane's bins
+    int4 v4[per / 4];
+#pragma unroll
+    for (int q = 0; q < per / 4; ++q) v4[q] = *reinterpret_cast<const int4*>(hist + hi - per + 4 * q);
+    int local = 0;
+#pragma unroll
+    for (int q = 0; q < per / 4; ++q) local += v4[q].x + v4[q].y + v4[q].z + v4[q].w;
+    int total;
+    const int excl = wave_exclusive_scan(local, lane, total);
+    const uint64_t m1 = __ballot(excl < need && need <= excl + local);
+    const int L = (int)__builtin_ctzll(m1);
+    const int base = __shfl(excl, L);
+    const int top = nb - per * L - 1;  // L's highest bin
+    const int v = lane < per ? hist[top - lane] : 0;
+    int tot2;
+    const int ex2 = base + wave_exclusive_scan(v, lane, tot2);
+    const uint64_t m2 = __ballot(lane < per && ex2 < need && need <= ex2 + v);
+    const int L2 = (int)__builtin_ctzll(m2);
+    if (lane == L2) {
+      s_pick[0] = top - L2;
+      s_pick[1] = ex2;
     }
   }
   __syncthreads();
   above = s_pick[1];
-  const int d = s_pick[0];
-  __syncthreads();
-  return d;
+  return s_pick[0];
 }
 
-template <int KPT>
+template <int I>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(const SelParams p) {
+  constexpr int K4 = 4 * I;  // keys per lane
   const int r = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  __shared__ int hist[kHistBins];
-  __shared__ int s_w[kSelWaves];
+  // 64 padding bins past the histogram take the invalid keys of pass 1
+  // (one per lane, so they never contend), which keeps that pass branch-free.
+  __shared__ __attribute__((aligned(16))) int hist[kHistBins + 64];
   __shared__ int s_pick[2];
-  __shared__ int s_cnt[2][kSelWaves][2];  // per block (double-buffered): gt-or-forced, eq
+  __shared__ int s_cnt[kSelWaves][2];  // per wave: taken outright, eq
+  __shared__ uint32_t s_ckey[kCandCap];
 
   int n = p.lengths ? p.lengths[r] : p.S;
   n = n < 0 ? 0 : (n > p.S ? p.S : n);
@@ -115,112 +139,228 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const SelParams p) 
   const int want = p.topk - (forced ? 1 : 0);
   const int need0 = want < pool ? want : pool;  // pool keys to take
   int32_t* o = p.out + (int64_t)r * p.ors;
+  const int id0 = wave * (256 * I) + 4 * lane;  // id of key[4 i + c] = id0 + 256 i + c
 
-  // 1. keys of the pool (0 elsewhere; no float maps to 0 but a NaN)
+  // 1. keys of the pool (0 elsewhere)
   const float* srow = p.scores + (int64_t)r * p.srs;
-  uint32_t key[KPT];
+  // 16-byte loads when every 4-id group below n lies in the row (the row is
+  // 16-byte aligned and n is a multiple of 4); 4-byte loads otherwise.  The
+  // choice is per row, so each path issues all its loads back to back.
+  const bool vec = ((uintptr_t)srow & 15u) == 0 && (n & 3) == 0;
+  float sc[K4];
+  if (vec) {
 #pragma unroll
-  for (int i = 0; i < KPT; ++i) {
-    const int j = tid + kSelThreads * i;
-    key[i] = (j < n && j != curx) ? order_key(srow[j]) : 0u;
+    for (int i = 0; i < I; ++i) {
+      const int j = id0 + 256 * i;
+      float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (j < n) f = *reinterpret_cast<const float4*>(srow + j);
+      sc[4 * i + 0] = f.x;
+      sc[4 * i + 1] = f.y;
+      sc[4 * i + 2] = f.z;
+      sc[4 * i + 3] = f.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < I; ++i)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int j = id0 + 256 * i + c;
+        sc[4 * i + c] = j < n ? srow[j] : 0.f;
+      }
   }
+  uint32_t key[K4];
+#pragma unroll
+  for (int i = 0; i < I; ++i)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int j = id0 + 256 * i + c;
+      key[4 * i + c] = (j < n && j != curx) ? order_key(sc[4 * i + c]) : 0u;
+    }
 
   // 2. threshold: every pool key > T is taken, plus need_eq keys == T
   const bool take_all = need0 == pool;
+  const bool radix = !take_all && need0 > 0;
   uint32_t T = 0;
-  int need_eq = 0;
-  if (!take_all && need0 > 0) {
-    uint32_t prefix = 0, pmask = 0;
-    int need = need0;
+  int need_eq = 0, eq_total = 0;
+  if (radix) {
+    // pass 1 (bits 31..20) over the registers
+    for (int b = tid; b < kHistBins; b += kSelThreads) hist[b] = 0;
+    __syncthreads();
 #pragma unroll
-    for (int pass = 0; pass < 3; ++pass) {
-      const int shift = pass == 0 ? 20 : (pass == 1 ? 8 : 0);
+    for (int k = 0; k < K4; ++k)
+      atomicAdd(&hist[key[k] != 0u ? (int)(key[k] >> 20) : kHistBins + lane], 1);
+    __syncthreads();
+    int above;
+    const int d1 = find_digit<kHistBins>(hist, need0, s_pick, wave, lane, above);
+    int need = need0 - above;
+    uint32_t prefix = (uint32_t)d1 << 20, pmask = 0xFFF00000u;
+    const int inbin = hist[d1];
+    const bool listed = inbin <= kCandCap;
+    if (listed) {
+      // The keys of bin d1 (typically a few percent) go to an LDS list; the
+      // other two passes run over it.  Per-wave counts, one barrier, then
+      // each wave writes at its offset.
+      uint32_t cbits = 0;
+#pragma unroll
+      for (int k = 0; k < K4; ++k)
+        cbits |= (key[k] != 0u && (key[k] >> 20) == (uint32_t)d1 ? 1u : 0u) << k;
+      int cw;
+      int off = wave_exclusive_scan(__popc(cbits), lane, cw);
+      if (lane == 0) s_cnt[wave][0] = cw;
+      __syncthreads();
+      off += wave_prefix_of(s_cnt, 0, wave, lane);
+      while (cbits) {  // a lane has ~0.1-1 candidates: order within the list is free
+        const int k = __builtin_ctz(cbits);
+        cbits &= cbits - 1u;
+        uint32_t kk = 0;
+#pragma unroll
+        for (int q = 0; q < K4; ++q) kk = q == k ? key[q] : kk;
+        s_ckey[off++] = kk;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int pass = 1; pass < 3; ++pass) {
+      const int shift = pass == 1 ? 8 : 0;
       const int nb = pass == 2 ? 256 : kHistBins;
       const uint32_t dmask = (uint32_t)nb - 1u;
       for (int b = tid; b < nb; b += kSelThreads) hist[b] = 0;
       __syncthreads();
+      if (listed) {
+        for (int e = tid; e < inbin; e += kSelThreads) {
+          const uint32_t k = s_ckey[e];
+          if ((k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & dmask], 1);
+        }
+      } else {
 #pragma unroll
-      for (int i = 0; i < KPT; ++i) {
-        const int j = tid + kSelThreads * i;
-        if (j < n && j != curx && (key[i] & pmask) == prefix)
-          atomicAdd(&hist[(key[i] >> shift) & dmask], 1);
+        for (int k = 0; k < K4; ++k)
+          if (key[k] != 0u && (key[k] & pmask) == prefix)
+            atomicAdd(&hist[(key[k] >> shift) & dmask], 1);
       }
       __syncthreads();
-      int above;
-      const int d = find_digit(hist, nb, need, s_w, s_pick, tid, above);
+      const int d = pass == 2 ? find_digit<256>(hist, need, s_pick, wave, lane, above)
+                              : find_digit<kHistBins>(hist, need, s_pick, wave, lane, above);
       need -= above;
       prefix |= (uint32_t)d << shift;
       pmask |= dmask << shift;
+      if (pass == 2) eq_total = hist[d];  // pool keys == T
     }
     T = prefix;
     need_eq = need;
   }
+  // Without ties at T (all keys == T taken) the selection is key >= T.
+  const bool ties = radix && eq_total > need_eq;
+  const uint64_t t_take = (uint64_t)T + (ties ? 1u : 0u);  // taken outright: key >= t_take
 
-  // 3. ordered compaction
-  int base = 0, eqbase = 0;
+  // 3. compaction in id order.  gtf: taken outright (key >= t_take, every
+  // pool key when all are taken, or the forced region); eq (ties only):
+  // key == T, the first need_eq of which in id order are taken.
+  auto gtf_of = [&](int k, int id) -> bool {
+    return (key[k] != 0u && (take_all || (radix && (uint64_t)key[k] >= t_take))) || id == curx;
+  };
+  auto eq_of = [&](int k) -> bool { return ties && key[k] == T; };
+  // Bit k of tbits: key k is taken outright; of ebits (ties only): key == T.
+  uint32_t tbits = 0, ebits = 0;
 #pragma unroll
-  for (int i = 0; i < KPT; ++i) {
-    const int j = tid + kSelThreads * i;
-    const bool v = j < n && j != curx;
-    const bool gtf = (v && (take_all || (need0 > 0 && key[i] > T))) || j == curx;
-    const bool eq = v && !take_all && need0 > 0 && key[i] == T;
-    const uint64_t gm = __ballot(gtf), em = __ballot(eq);
-    int(*cnt)[2] = s_cnt[i & 1];
-    if (lane == 0) {
-      cnt[wave][0] = __popcll(gm);
-      cnt[wave][1] = __popcll(em);
-    }
-    __syncthreads();
-    int gtf_prev = 0, eq_prev = 0, gtf_blk = 0, eq_blk = 0;
+  for (int i = 0; i < I; ++i)
 #pragma unroll
-    for (int w = 0; w < kSelWaves; ++w) {
-      const int g = cnt[w][0], e = cnt[w][1];
-      gtf_prev += w < wave ? g : 0;
-      eq_prev += w < wave ? e : 0;
-      gtf_blk += g;
-      eq_blk += e;
+    for (int c = 0; c < 4; ++c) {
+      tbits |= (gtf_of(4 * i + c, id0 + 256 * i + c) ? 1u : 0u) << (4 * i + c);
+      if (ties) ebits |= (eq_of(4 * i + c) ? 1u : 0u) << (4 * i + c);
     }
-    // The first need_eq keys == T in id order are taken.
-    const int eq_left = need_eq - eqbase;  // still to take at the start of the block
-    const int eq_before = eq_prev + lanes_below(em, lane);
-    const bool sel = gtf || (eq && eq_before < eq_left);
-    const int eq_sel_prev = min(max(eq_left, 0), eq_prev);
-    const int eq_sel_lane = min(max(eq_left - eq_prev, 0), lanes_below(em, lane));
-    const int slot = base + gtf_prev + eq_sel_prev + lanes_below(gm, lane) + eq_sel_lane;
-    if (sel && slot < p.topk) o[slot] = j;
-    base += gtf_blk + min(max(eq_left, 0), eq_blk);
-    eqbase += eq_blk;
+  const int g_wave = wave_sum(__popc(tbits), lane);
+  const int e_wave = ties ? wave_sum(__popc(ebits), lane) : 0;
+  if (lane == 0) {
+    s_cnt[wave][0] = g_wave;
+    s_cnt[wave][1] = e_wave;
   }
-  // base == (forced ? 1 : 0) + need0 here
-  for (int s = base + tid; s < p.topk; s += kSelThreads) o[s] = -1;
+  __syncthreads();
+  const int g_prev = wave_prefix_of(s_cnt, 0, wave, lane);
+  const int e_prev = ties ? wave_prefix_of(s_cnt, 1, wave, lane) : 0;
+  const int g_all = wave_prefix_of(s_cnt, 0, kSelWaves, lane);
+  int e_all = ties ? wave_prefix_of(s_cnt, 1, kSelWaves, lane) : 0;
+  if (!ties) need_eq = 0;
+  // output slot of the wave's first selection; eq keys still to take there
+  int run = g_prev + min(need_eq, e_prev);
+  int eq_left = need_eq - e_prev;
+  if (!ties) {
+    if (g_wave > 0) {
+#pragma unroll
+      for (int i = 0; i < I; ++i) {
+        // In id order a 256-id group is lane-major: lane l holds ids 4l .. 4l+3.
+        const uint32_t nib = (tbits >> (4 * i)) & 15u;
+        if (__ballot(nib != 0u) == 0) continue;
+        const int c4 = __popc(nib);
+        const uint64_t b0 = __ballot(c4 & 1), b1 = __ballot(c4 & 2), b2 = __ballot(c4 & 4);
+        int slot = run + mbcnt(b0) + 2 * mbcnt(b1) + 4 * mbcnt(b2);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          if ((nib >> c) & 1u) {
+            if (slot < p.topk) o[slot] = id0 + 256 * i + c;
+            ++slot;
+          }
+        }
+        run += __popcll(b0) + 2 * __popcll(b1) + 4 * __popcll(b2);
+      }
+    }
+  } else if (g_wave + (eq_left > 0 ? e_wave : 0) > 0) {
+#pragma unroll
+    for (int i = 0; i < I; ++i) {
+      bool gt[4], eq[4];
+      int e_lanes = 0, e_tot = 0;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        gt[c] = (tbits >> (4 * i + c)) & 1u;
+        eq[c] = eq_left > 0 && ((ebits >> (4 * i + c)) & 1u);
+        const uint64_t em = __ballot(eq[c]);
+        e_lanes += mbcnt(em);
+        e_tot += __popcll(em);
+      }
+      bool sel[4];
+      int eseen = e_lanes;
+      int s_lanes = 0, s_tot = 0;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        sel[c] = gt[c] || (eq[c] && eseen < eq_left);
+        eseen += eq[c] ? 1 : 0;
+        const uint64_t sm = __ballot(sel[c]);
+        s_lanes += mbcnt(sm);
+        s_tot += __popcll(sm);
+      }
+      int slot = run + s_lanes;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        if (sel[c]) {
+          if (slot < p.topk) o[slot] = id0 + 256 * i + c;
+          ++slot;
+        }
+      }
+      run += s_tot;
+      eq_left -= e_tot;
+    }
+  }
+  const int total = g_all + min(need_eq, e_all);  // == (forced ? 1 : 0) + need0
+  for (int s = total + tid; s < p.topk; s += kSelThreads) o[s] = -1;
 }
 
-template <int KPT>
+template <int I>
 void launch_select(const SelParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL(select_kernel<KPT>, dim3((unsigned)p.rows), dim3(kSelThreads), 0, stream,
-                     p);
+  hipLaunchKernelGGL(select_kernel<I>, dim3((unsigned)p.rows), dim3(kSelThreads), 0, stream, p);
 }
 
 }  // namespace
 
 hipError_t launch_select(const SelParams& p, hipStream_t stream) {
-  const int kpt = (p.S + kSelThreads - 1) / kSelThreads;
-  if (kpt <= 1)
+  // I groups of 4 keys per lane: 4096 I ids per row
+  const int groups = (p.S + 4 * kSelThreads - 1) / (4 * kSelThreads);
+  if (groups <= 1)
     launch_select<1>(p, stream);
-  else if (kpt <= 2)
+  else if (groups <= 2)
     launch_select<2>(p, stream);
-  else if (kpt <= 4)
+  else if (groups <= 4)
     launch_select<4>(p, stream);
-  else if (kpt <= 8)
-    launch_select<8>(p, stream);
-  else if (kpt <= 16)
-    launch_select<16>(p, stream);
-  else if (kpt <= 32)
-    launch_select<32>(p, stream);
-  else if (kpt <= 64)
-    launch_select<64>(p, stream);
   else
-    launch_select<128>(p, stream);
+    launch_select<8>(p, stream);
   return hipGetLastError();
 }
 
