@@ -149,3 +149,45 @@ def swa_host_problem(query, cache, block_table, seq_lens, *, scale, window, quer
                           seq_lens=np.ascontiguousarray(lens), scale=float(scale),
                           window=int(window), query_len=int(query_len),
                           gate=None if gate is None else _bits16(gate))
+
+
+def logits_host_problem(inp, rows=None):
+    """The oracle's indexer-logits problem for a LogitsInputs bundle.  With a
+    large summary cache only the pages the ``rows`` can reach are copied
+    (block table renumbered, other entries -1)."""
+    from .oracle import LogitsHostProblem
+    w = inp.w
+    table = np.array(inp.block_table.detach().cpu().numpy(), dtype=np.int32, copy=True)
+    pos = np.array(inp.positions.detach().cpu().numpy(), dtype=np.int32, copy=True)
+    row_list = range(w.rows) if rows is None else [int(r) for r in rows]
+    sm, sc = inp.summaries, inp.scales
+    if sm.numel() <= _WHOLE_CACHE_BYTES:
+        host_sm = np.array(sm.detach().cpu().numpy(), copy=True)
+        host_sc = np.array(sc.detach().cpu().numpy(), dtype=np.float32, copy=True)
+        host_table = np.ascontiguousarray(table)
+    else:
+        need = set()
+        per_req = w.groups * w.query_len
+        for r in row_list:
+            req = r // per_req
+            if pos[r] < 0:
+                continue
+            last = min(int(pos[r]) // w.region_tokens, w.num_regions - 1)
+            for col in range(last // w.rpb + 1):
+                need.add((req, col))
+        pages = sorted({int(table[q, c]) for q, c in need})
+        remap = {p: i for i, p in enumerate(pages)}
+        idx = torch.tensor(pages if pages else [0], dtype=torch.long, device=sm.device)
+        host_sm = np.array(sm.index_select(0, idx).cpu().numpy(), copy=True)
+        host_sc = np.array(sc.index_select(0, idx).cpu().numpy(), dtype=np.float32, copy=True)
+        if not pages:
+            host_sm, host_sc = host_sm[:0], host_sc[:0]
+        host_table = np.full(table.shape, -1, dtype=np.int32)
+        for q, c in need:
+            host_table[q, c] = remap[int(table[q, c])]
+    return LogitsHostProblem(
+        query=np.array(inp.query.detach().cpu().numpy(), copy=True),
+        weights=np.array(inp.weights.detach().cpu().numpy(), dtype=np.float32, copy=True),
+        summaries=host_sm, scales=host_sc, block_table=host_table, positions=pos,
+        groups=w.groups, num_regions=w.num_regions, query_len=w.query_len,
+        region_tokens=w.region_tokens)

@@ -77,6 +77,24 @@ class _SwaProblem(ctypes.Structure):
     ]
 
 
+class _LogitsProblem(ctypes.Structure):
+    _fields_ = [
+        ("rows", ctypes.c_int32), ("heads", ctypes.c_int32), ("groups", ctypes.c_int32),
+        ("query_len", ctypes.c_int32), ("rpb", ctypes.c_int32), ("num_regions", ctypes.c_int32),
+        ("region_tokens", ctypes.c_int32),
+        ("query", ctypes.c_void_p), ("q_row_stride", ctypes.c_int64),
+        ("q_head_stride", ctypes.c_int64),
+        ("weights", ctypes.c_void_p), ("w_row_stride", ctypes.c_int64),
+        ("summaries", ctypes.c_void_p), ("s_page_stride", ctypes.c_int64),
+        ("s_region_stride", ctypes.c_int64),
+        ("scales", ctypes.c_void_p), ("sc_page_stride", ctypes.c_int64),
+        ("num_pages", ctypes.c_int64),
+        ("block_table", ctypes.c_void_p), ("table_row_stride", ctypes.c_int64),
+        ("table_cols", ctypes.c_int64),
+        ("positions", ctypes.c_void_p),
+    ]
+
+
 _lib = None
 _lib_lock = threading.Lock()
 
@@ -106,6 +124,9 @@ def lib():
             l.sdo_select_regions.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                              ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
                                              ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64]
+            l.sdo_indexer_logits.restype = ctypes.c_int
+            l.sdo_indexer_logits.argtypes = [ctypes.POINTER(_LogitsProblem), ctypes.c_void_p,
+                                             ctypes.c_int, ctypes.c_int]
             l.sdo_swa_decode.restype = ctypes.c_int
             l.sdo_swa_decode.argtypes = [ctypes.POINTER(_SwaProblem), ctypes.c_void_p,
                                          ctypes.c_int, ctypes.c_int]
@@ -363,4 +384,83 @@ def select_regions(scores: np.ndarray, current: np.ndarray, topk: int,
     _check_rc(lib().sdo_select_regions(rows, S, topk, scores.ctypes.data, rs, cur.ctypes.data,
                                        None if lens is None else lens.ctypes.data,
                                        out.ctypes.data, topk))
+    return out
+
+
+@dataclass
+class LogitsHostProblem:
+    """Host copies of the decode indexer-logits inputs.
+
+    query: uint8 e4m3 [rows, heads, 256]; weights: float32 [rows, heads];
+    summaries: uint8 e4m3 [pages, rpb, 256]; scales: float32 [pages, rpb];
+    block_table: int32 [requests, cols]; positions: int32 [rows].
+    """
+    query: np.ndarray
+    weights: np.ndarray
+    summaries: np.ndarray
+    scales: np.ndarray
+    block_table: np.ndarray
+    positions: np.ndarray
+    groups: int
+    num_regions: int
+    query_len: int = 1
+    region_tokens: int = 8
+
+
+def indexer_logits(hp: LogitsHostProblem, rows=None, threads: int = 1) -> np.ndarray:
+    """fp64 scores [rows, num_regions] (rows not listed stay NaN)."""
+    q, w, sm, sc = hp.query, hp.weights, hp.summaries, hp.scales
+    assert q.dtype == np.uint8 and q.ndim == 3 and q.shape[2] == 256 and q.strides[2] == 1
+    assert w.dtype == np.float32 and w.shape == q.shape[:2] and w.strides[1] == 4
+    assert sm.dtype == np.uint8 and sm.ndim == 3 and sm.shape[2] == 256 and sm.strides[2] == 1
+    assert sc.dtype == np.float32 and sc.shape == sm.shape[:2] and sc.strides[1] == 4
+    bt = hp.block_table
+    assert bt.dtype == np.int32 and bt.strides[1] == 4
+    pos = np.ascontiguousarray(hp.positions, dtype=np.int32)
+    p = _LogitsProblem()
+    p.rows, p.heads, p.groups = q.shape[0], q.shape[1], hp.groups
+    p.query_len, p.rpb, p.num_regions = hp.query_len, sm.shape[1], hp.num_regions
+    p.region_tokens = hp.region_tokens
+    p.query = q.ctypes.data
+    p.q_row_stride, p.q_head_stride = q.strides[0], q.strides[1]
+    p.weights = w.ctypes.data
+    p.w_row_stride = w.strides[0] // 4
+    p.summaries = sm.ctypes.data
+    p.s_page_stride, p.s_region_stride = sm.strides[0], sm.strides[1]
+    p.scales = sc.ctypes.data
+    p.sc_page_stride = sc.strides[0] // 4
+    p.num_pages = sm.shape[0]
+    p.block_table = bt.ctypes.data
+    p.table_row_stride = bt.strides[0] // 4
+    p.table_cols = bt.shape[1]
+    p.positions = pos.ctypes.data
+    out = np.full((q.shape[0], hp.num_regions), np.nan)
+    l = lib()
+    row_list = list(range(q.shape[0])) if rows is None else [int(r) for r in rows]
+    row_bytes = hp.num_regions * 8
+
+    def run(rs):
+        for r in rs:
+            _check_rc(l.sdo_indexer_logits(ctypes.byref(p), out.ctypes.data + r * row_bytes,
+                                           r, r + 1))
+
+    if threads <= 1 or len(row_list) < 2:
+        run(row_list)
+    else:
+        errs = []
+
+        def worker(rs):
+            try:
+                run(rs)
+            except Exception as e:  # surfaced below
+                errs.append(e)
+
+        ts = [threading.Thread(target=worker, args=(row_list[i::threads],))
+              for i in range(threads) if row_list[i::threads]]
+        for t in ts:
+            t.start()
+        for t in ts:
+            t.join()
+        if errs:
+            raise errs[0]
     return out

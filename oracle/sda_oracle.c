@@ -479,3 +479,70 @@ int sdo_select_regions(int32_t rows, int32_t S, int32_t topk, const float *score
   free(sel);
   return SDO_OK;
 }
+
+/* ---- decode indexer logits -------------------------------------------------
+ * [P3] `decode_logits`: score every region of a row's request for the region
+ * selection.  Queries are e4m3 [rows, heads, 256] (row r is group r % G of
+ * token r / G, query_len tokens per request, as in the decode), weights fp32
+ * [rows, heads].  The direct kernel (`decode_summary_scores`) and the paged
+ * MQA-logits kernel under the fallback are not shown.  Reading: region j's
+ * summary is 256 e4m3 bytes kept beside the KV in the page that holds the
+ * region's tokens (page block_table[req, j / rpb], slot j % rpb, rpb =
+ * regions per page), with an fp32 dequant scale s_j (the fallback's packed
+ * 260-byte entry: 256 e4m3 bytes + a 4-byte scale), and
+ *     score[r, j] = sum_h w[r,h] * max(0, s_j * sum_d q[r,h,d] * k_j[d])
+ * for the regions 0 .. positions[r] / region_tokens of the row; the other
+ * score columns are -inf.  PARITY UNPINNED: this formula is a reading; the
+ * pins below fix the oracle to it, not to the pages. */
+typedef struct {
+  int32_t rows, heads, groups, query_len, rpb, num_regions, region_tokens;
+  const uint8_t *query;             /* e4m3 [rows, heads, 256] */
+  int64_t q_row_stride, q_head_stride;
+  const float *weights;             /* [rows, heads] */
+  int64_t w_row_stride;
+  const uint8_t *summaries;         /* e4m3 [pages, rpb, 256] */
+  int64_t s_page_stride, s_region_stride;
+  const float *scales;              /* [pages, rpb] */
+  int64_t sc_page_stride;
+  int64_t num_pages;
+  const int32_t *block_table;
+  int64_t table_row_stride, table_cols;
+  const int32_t *positions;         /* [rows] */
+} sdo_logits_problem;
+
+#define SDO_IDX_DIM 256
+
+int sdo_indexer_logits(const sdo_logits_problem *p, double *out, int row_begin, int row_end) {
+  if (!p || p->heads < 1 || p->groups < 1 || p->query_len < 1 || p->rpb < 1 ||
+      p->num_regions < 0 || p->region_tokens < 1 || row_begin < 0 || row_end > p->rows ||
+      row_begin > row_end || p->rows % (p->groups * p->query_len))
+    return SDO_ERR_ARGS;
+  for (int r = row_begin; r < row_end; ++r) {
+    int req = r / (p->groups * p->query_len);
+    double *o = out + (int64_t)(r - row_begin) * p->num_regions;
+    int64_t pos = p->positions[r];
+    int64_t len = pos < 0 ? 0 : pos / p->region_tokens + 1;
+    if (len > p->num_regions) len = p->num_regions;
+    for (int64_t j = 0; j < p->num_regions; ++j) {
+      if (j >= len) { o[j] = -INFINITY; continue; }
+      int64_t col = j / p->rpb;
+      if (col >= p->table_cols) return SDO_ERR_TABLE;
+      int64_t page = p->block_table[(int64_t)req * p->table_row_stride + col];
+      if (page < 0 || page >= p->num_pages) return SDO_ERR_PAGE;
+      int slot = (int)(j % p->rpb);
+      const uint8_t *k = p->summaries + page * p->s_page_stride + (int64_t)slot * p->s_region_stride;
+      double s = (double)p->scales[page * p->sc_page_stride + slot];
+      double acc = 0.0;
+      for (int h = 0; h < p->heads; ++h) {
+        const uint8_t *q = p->query + (int64_t)r * p->q_row_stride + (int64_t)h * p->q_head_stride;
+        double dot = 0.0;
+        for (int d = 0; d < SDO_IDX_DIM; ++d)
+          dot += sdo_e4m3_to_double(q[d]) * sdo_e4m3_to_double(k[d]);
+        double x = s * dot;
+        acc += (double)p->weights[(int64_t)r * p->w_row_stride + h] * (x > 0.0 ? x : 0.0);
+      }
+      o[j] = acc;
+    }
+  }
+  return SDO_OK;
+}

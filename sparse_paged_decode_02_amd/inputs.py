@@ -373,3 +373,93 @@ def make_select_inputs(w: SelectWorkload, device="cpu", seed: int | None = None,
                                device=device).to(torch.float32)
     return SelectInputs(w=w, scores=scores, current=torch.from_numpy(cur).to(device),
                         topk_lengths=torch.from_numpy(lens).to(device))
+
+
+# ---- decode indexer logits ---------------------------------------------------
+# Rows (token, KV group) with `heads` indexer heads of dim 256 in e4m3, fp32
+# head weights, and per-region e4m3 summaries of dim 256 kept per page
+# (block // region_tokens regions per page) with an fp32 scale per region.
+
+@dataclass(frozen=True)
+class LogitsWorkload:
+    name: str
+    requests: int
+    query_len: int
+    groups: int
+    heads: int
+    block: int
+    pages_per_req: int
+    pos_lo: int
+    pos_hi: int
+    region_tokens: int = 8
+    seed: int = 0
+
+    @property
+    def rows(self) -> int:
+        return self.requests * self.query_len * self.groups
+
+    @property
+    def rpb(self) -> int:
+        return self.block // self.region_tokens
+
+    @property
+    def num_regions(self) -> int:
+        return self.pages_per_req * self.rpb
+
+    @property
+    def total_pages(self) -> int:
+        return self.requests * self.pages_per_req
+
+
+LOGITS_CONFIGS = {
+    # the bf16-gated decode batch (64 requests x G 4) over 32K contexts
+    "logits-decode": LogitsWorkload("logits-decode", requests=64, query_len=1, groups=4, heads=8,
+                                    block=64, pages_per_req=512, pos_lo=4096, pos_hi=32767,
+                                    seed=config_seed(31)),
+    # MTP verify: 2 tokens per request, 128 requests, 16K contexts
+    "logits-mtp": LogitsWorkload("logits-mtp", requests=128, query_len=2, groups=4, heads=8,
+                                 block=64, pages_per_req=256, pos_lo=8192, pos_hi=16382,
+                                 seed=config_seed(32)),
+}
+
+
+@dataclass
+class LogitsInputs:
+    w: LogitsWorkload
+    query: torch.Tensor          # uint8 (e4m3 bytes) [rows, heads, 256]
+    weights: torch.Tensor        # fp32 [rows, heads]
+    summaries: torch.Tensor      # uint8 (e4m3 bytes) [pages, rpb, 256]
+    scales: torch.Tensor         # fp32 [pages, rpb]
+    block_table: torch.Tensor    # int32 [requests, pages_per_req]
+    positions: torch.Tensor      # int32 [rows]
+
+
+def make_logits_inputs(w: LogitsWorkload, device="cpu", seed: int | None = None,
+                       summaries: torch.Tensor | None = None,
+                       scales: torch.Tensor | None = None) -> LogitsInputs:
+    """Block table = random permutation; token j of a request at first + j,
+    first ~ U[pos_lo, pos_hi]; query and summaries = e4m3(N(0,1)); scales ~
+    U[0.02, 0.1]; weights ~ N(0,1) / sqrt(heads)."""
+    seed = w.seed if seed is None else seed
+    rng = np.random.default_rng(seed)
+    table = rng.permutation(w.total_pages).astype(np.int32).reshape(w.requests, w.pages_per_req)
+    first = rng.integers(w.pos_lo, w.pos_hi + 1, size=w.requests)
+    req = np.repeat(np.arange(w.requests), w.query_len * w.groups)
+    j = np.tile(np.repeat(np.arange(w.query_len), w.groups), w.requests)
+    positions = (first[req] + j).astype(np.int32)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed * 2 + 1)
+    if summaries is None:
+        summaries = torch.empty((w.total_pages, w.rpb, 256), dtype=torch.uint8, device=device)
+        for p0 in range(0, w.total_pages, 65536):
+            p1 = min(w.total_pages, p0 + 65536)
+            x = torch.randn((p1 - p0, w.rpb, 256), generator=gen, device=device)
+            summaries[p0:p1] = x.to(torch.float8_e4m3fn).view(torch.uint8)
+        scales = 0.02 + 0.08 * torch.rand((w.total_pages, w.rpb), generator=gen, device=device)
+    gen.manual_seed(seed * 2)
+    query = torch.randn((w.rows, w.heads, 256), generator=gen, device=device).to(
+        torch.float8_e4m3fn).view(torch.uint8)
+    weights = torch.randn((w.rows, w.heads), generator=gen, device=device) / math.sqrt(w.heads)
+    return LogitsInputs(w=w, query=query, weights=weights, summaries=summaries, scales=scales,
+                        block_table=torch.from_numpy(table).to(device),
+                        positions=torch.from_numpy(positions).to(device))
