@@ -30,7 +30,7 @@
 extern "C" {
 #endif
 
-#define SDA_ABI_VERSION 3
+#define SDA_ABI_VERSION 4
 #define SDA_HEAD_DIM 192     /* query / key / value head dim (fixed) */
 #define SDA_KV_ROW 384       /* one cache token row: K[0:192] then V[192:384] */
 #define SDA_MAX_HEADS 16     /* GQA-packed query heads per KV group */
@@ -293,16 +293,76 @@ typedef struct sda_select_args {
  */
 int sda_select_regions(const sda_select_args *args, hipStream_t stream);
 
+/*
+ * Decode indexer logits: the region scores `decode_logits` produces on page
+ * "vllm.models.step5.nvidia.flashinfer_sparse" for the selection that follows
+ * (its kernels are not shown; this formula is a reading):
+ *     scores[r, j] = sum_h weights[r, h] * max(0, s_j * (q[r, h, :] . k_j))
+ * for regions j = 0 .. positions[r] / region_tokens of row r, and -inf for
+ * the other score columns.  q and k_j are OCP e4m3 (exact products, fp32
+ * sums); k_j is region j's 256-byte summary, kept in the page that holds its
+ * tokens: page block_table[request, j / regions_per_page], slot
+ * j % regions_per_page, with fp32 scale s_j.  Row r is group r % groups of
+ * token r / groups; the groups * query_len rows of a request share its
+ * block-table row, and its rows x heads query columns (<= 64) are scored
+ * together, reading each summary once per request.  Strides: bytes for the
+ * e4m3 tensors, elements otherwise.
+ *
+ *  rows, heads   rows (a multiple of groups * query_len); indexer heads per
+ *                row, a power of two <= 16.
+ *  regions_per_page  summaries per page (block / region_tokens).
+ *  num_regions   score columns S.
+ *  query         e4m3 [rows, heads, 256]; 16-byte aligned rows and heads.
+ *  weights       fp32 [rows, heads], unit head stride.
+ *  summaries     e4m3 [pages, regions_per_page, 256]; 16-byte aligned.
+ *  summary_scales fp32 [pages, regions_per_page], unit region stride.
+ *  block_table   int32 [requests, cols], unit inner stride; only the columns
+ *                of each request's scored regions are read.
+ *  positions     int32 [rows].
+ *  scores        fp32 [rows, S] output; 16-byte aligned, row stride % 4 == 0.
+ *  current, topk_lengths  optional int32 [rows] outputs for the selection:
+ *                positions / region_tokens (-1 for a negative position) and
+ *                the scored region count min(current + 1, S).
+ */
+#define SDA_LOGITS_MAX_COLUMNS 64
+
+typedef struct sda_logits_args {
+  int32_t rows, heads, groups, query_len, regions_per_page, num_regions, region_tokens;
+  const void *query;
+  int64_t q_row_stride, q_head_stride;
+  const float *weights;
+  int64_t w_row_stride;
+  const void *summaries;
+  int64_t s_page_stride, s_region_stride;
+  const float *summary_scales;
+  int64_t ss_page_stride;
+  const int32_t *block_table;
+  int64_t table_row_stride;
+  const int32_t *positions;
+  float *scores;
+  int64_t scores_row_stride;
+  int32_t *current;
+  int32_t *topk_lengths;
+} sda_logits_args;
+
+/*
+ * Enqueue one logits call: a (requests, ceil(S / 256)) grid of 256-thread
+ * workgroups.  Asynchronous, no allocation.  Returns an sda_status; on error
+ * nothing is launched.
+ */
+int sda_indexer_logits(const sda_logits_args *args, hipStream_t stream);
+
 /* Static description of a status code (never NULL). */
 const char *sda_status_string(int status);
 
 /* SDA_ABI_VERSION of the built library, and the sizes of sda_decode_args,
- * sda_swa_args and sda_select_args, so a binding can check that its mirrors
- * of the structs match. */
+ * sda_swa_args, sda_select_args and sda_logits_args, so a binding can check
+ * that its mirrors of the structs match. */
 int sda_abi_version(void);
 size_t sda_args_size(void);
 size_t sda_swa_args_size(void);
 size_t sda_select_args_size(void);
+size_t sda_logits_args_size(void);
 
 #ifdef __cplusplus
 }

@@ -23,7 +23,7 @@ SDA_ERR_WORKSPACE = -3
 SDA_ERR_LAUNCH = -4
 SDA_KV_BF16 = 0
 SDA_KV_FP8_E4M3 = 1
-ABI_VERSION = 3
+ABI_VERSION = 4
 HEAD_DIM = 192
 
 
@@ -90,6 +90,25 @@ class SelectArgs(ctypes.Structure):
     ]
 
 
+class LogitsArgs(ctypes.Structure):
+    """Mirror of ``sda_logits_args``; checked against sda_logits_args_size()."""
+    _fields_ = [
+        ("rows", ctypes.c_int32), ("heads", ctypes.c_int32), ("groups", ctypes.c_int32),
+        ("query_len", ctypes.c_int32), ("regions_per_page", ctypes.c_int32),
+        ("num_regions", ctypes.c_int32), ("region_tokens", ctypes.c_int32),
+        ("query", ctypes.c_void_p), ("q_row_stride", ctypes.c_int64),
+        ("q_head_stride", ctypes.c_int64),
+        ("weights", ctypes.c_void_p), ("w_row_stride", ctypes.c_int64),
+        ("summaries", ctypes.c_void_p), ("s_page_stride", ctypes.c_int64),
+        ("s_region_stride", ctypes.c_int64),
+        ("summary_scales", ctypes.c_void_p), ("ss_page_stride", ctypes.c_int64),
+        ("block_table", ctypes.c_void_p), ("table_row_stride", ctypes.c_int64),
+        ("positions", ctypes.c_void_p),
+        ("scores", ctypes.c_void_p), ("scores_row_stride", ctypes.c_int64),
+        ("current", ctypes.c_void_p), ("topk_lengths", ctypes.c_void_p),
+    ]
+
+
 _lib = None
 _lock = threading.Lock()
 
@@ -126,12 +145,19 @@ def lib() -> ctypes.CDLL:
             l.sda_select_regions.argtypes = [ctypes.POINTER(SelectArgs), ctypes.c_void_p]
             l.sda_select_args_size.restype = ctypes.c_size_t
             l.sda_select_args_size.argtypes = []
+            l.sda_indexer_logits.restype = ctypes.c_int
+            l.sda_indexer_logits.argtypes = [ctypes.POINTER(LogitsArgs), ctypes.c_void_p]
+            l.sda_logits_args_size.restype = ctypes.c_size_t
+            l.sda_logits_args_size.argtypes = []
             if l.sda_abi_version() != ABI_VERSION:
                 raise RuntimeError("libsda.so ABI version %d, binding expects %d"
                                    % (l.sda_abi_version(), ABI_VERSION))
             if l.sda_args_size() != ctypes.sizeof(DecodeArgs):
                 raise RuntimeError("sda_decode_args size mismatch: library %d, binding %d"
                                    % (l.sda_args_size(), ctypes.sizeof(DecodeArgs)))
+            if l.sda_logits_args_size() != ctypes.sizeof(LogitsArgs):
+                raise RuntimeError("sda_logits_args size mismatch: library %d, binding %d"
+                                   % (l.sda_logits_args_size(), ctypes.sizeof(LogitsArgs)))
             if l.sda_select_args_size() != ctypes.sizeof(SelectArgs):
                 raise RuntimeError("sda_select_args size mismatch: library %d, binding %d"
                                    % (l.sda_select_args_size(), ctypes.sizeof(SelectArgs)))
@@ -402,3 +428,79 @@ def sda_select_regions(scores, current, topk, *, topk_lengths=None, out=None,
 def sda_select_regions_raw(args: SelectArgs, stream_handle=None) -> int:
     """Call sda_select_regions on a prepared struct; returns the status code."""
     return int(lib().sda_select_regions(ctypes.byref(args), stream_handle))
+
+
+def make_logits_args(query, weights, summaries, summary_scales, block_table, positions, scores,
+                     *, groups, query_len=1, region_tokens=8, current=None,
+                     topk_lengths=None) -> LogitsArgs:
+    """Fill ``sda_logits_args`` from tensors.  e4m3 tensors are uint8 (or
+    float8_e4m3fn) storage; their strides become bytes."""
+    a = LogitsArgs()
+    a.rows, a.heads, a.groups, a.query_len = query.shape[0], query.shape[1], int(groups), \
+        int(query_len)
+    a.regions_per_page, a.num_regions = summaries.shape[1], scores.shape[1]
+    a.region_tokens = int(region_tokens)
+    a.query = _ptr(query)
+    a.q_row_stride, a.q_head_stride = query.stride(0), query.stride(1)
+    a.weights = _ptr(weights)
+    a.w_row_stride = weights.stride(0)
+    a.summaries = _ptr(summaries)
+    a.s_page_stride, a.s_region_stride = summaries.stride(0), summaries.stride(1)
+    a.summary_scales = _ptr(summary_scales)
+    a.ss_page_stride = summary_scales.stride(0)
+    a.block_table = _ptr(block_table)
+    a.table_row_stride = block_table.stride(0)
+    a.positions = _ptr(positions)
+    a.scores = _ptr(scores)
+    a.scores_row_stride = scores.stride(0)
+    a.current = _ptr(current)
+    a.topk_lengths = _ptr(topk_lengths)
+    return a
+
+
+def sda_indexer_logits(query, weights, summaries, summary_scales, block_table, positions, *,
+                       groups, num_regions, query_len=1, region_tokens=8, scores=None,
+                       current=None, topk_lengths=None, stream=None):
+    """Enqueue ``sda_indexer_logits``; returns the fp32 [rows, num_regions] scores.
+
+    Names follow ``decode_logits`` on the page "vllm.models.step5.nvidia.
+    flashinfer_sparse" (query, weights, the per-page region summaries with
+    their scales, table, positions)."""
+    e4 = (torch.uint8, torch.float8_e4m3fn)
+    if query.dtype not in e4 or query.dim() != 3 or query.shape[2] != 256 or query.stride(2) != 1:
+        raise SdaError(SDA_ERR_INVALID, "query must be e4m3 [rows, heads, 256]")
+    if summaries.dtype not in e4 or summaries.dim() != 3 or summaries.shape[2] != 256 or \
+            summaries.stride(2) != 1:
+        raise SdaError(SDA_ERR_INVALID, "summaries must be e4m3 [pages, regions_per_page, 256]")
+    if weights.dtype != torch.float32 or weights.shape != query.shape[:2] or (
+            weights.shape[1] > 1 and weights.stride(1) != 1):
+        raise SdaError(SDA_ERR_INVALID, "weights must be float32 [rows, heads]")
+    if summary_scales.dtype != torch.float32 or summary_scales.shape != summaries.shape[:2] or (
+            summary_scales.shape[1] > 1 and summary_scales.stride(1) != 1):
+        raise SdaError(SDA_ERR_INVALID, "summary_scales must be float32 [pages, regions_per_page]")
+    for t, name in ((block_table, "block_table"),):
+        if t.dtype != torch.int32 or t.dim() != 2 or t.stride(1) != 1:
+            raise SdaError(SDA_ERR_INVALID, "%s must be int32 2-D, unit inner stride" % name)
+    rows = query.shape[0]
+    for t, name in ((positions, "positions"), (current, "current"),
+                    (topk_lengths, "topk_lengths")):
+        if t is not None and (t.dtype != torch.int32 or not t.is_contiguous() or
+                              t.numel() != rows):
+            raise SdaError(SDA_ERR_INVALID, "%s must be contiguous int32 [rows]" % name)
+    if scores is None:
+        scores = torch.empty((rows, int(num_regions)), dtype=torch.float32, device=query.device)
+    a = make_logits_args(query, weights, summaries, summary_scales, block_table, positions,
+                         scores, groups=groups, query_len=query_len, region_tokens=region_tokens,
+                         current=current, topk_lengths=topk_lengths)
+    if stream is None:
+        stream = torch.cuda.current_stream(query.device) if query.is_cuda else None
+    handle = None if stream is None else ctypes.c_void_p(stream.cuda_stream)
+    rc = lib().sda_indexer_logits(ctypes.byref(a), handle)
+    if rc != SDA_OK:
+        raise SdaError(rc, status_string(rc))
+    return scores
+
+
+def sda_indexer_logits_raw(args: LogitsArgs, stream_handle=None) -> int:
+    """Call sda_indexer_logits on a prepared struct; returns the status code."""
+    return int(lib().sda_indexer_logits(ctypes.byref(args), stream_handle))

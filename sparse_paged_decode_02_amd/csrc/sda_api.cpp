@@ -280,4 +280,57 @@ int sda_select_regions(const sda_select_args* a, hipStream_t stream) {
   return e == hipSuccess ? SDA_OK : SDA_ERR_LAUNCH;
 }
 
+size_t sda_logits_args_size(void) { return sizeof(sda_logits_args); }
+
+int sda_indexer_logits(const sda_logits_args* a, hipStream_t stream) {
+  if (!a) return SDA_ERR_INVALID;
+  if (a->rows < 0 || a->heads < 1 || a->heads > SDA_MAX_HEADS || (a->heads & (a->heads - 1)) ||
+      a->groups < 1 || a->query_len < 1 || a->regions_per_page < 1 || a->num_regions < 0 ||
+      a->region_tokens < 1)
+    return SDA_ERR_INVALID;
+  const int64_t rpr = (int64_t)a->groups * a->query_len;
+  if (a->rows % rpr) return SDA_ERR_INVALID;
+  if (rpr * a->heads > SDA_LOGITS_MAX_COLUMNS || a->rows > SDA_MAX_ROWS)
+    return SDA_ERR_UNSUPPORTED;
+  if (a->rows == 0 || a->num_regions == 0) return SDA_OK;
+  if (!a->query || !a->weights || !a->summaries || !a->summary_scales || !a->block_table ||
+      !a->positions || !a->scores)
+    return SDA_ERR_INVALID;
+  // 16-byte query / summary loads and score stores
+  if (!aligned(a->query, 16) || a->q_row_stride % 16 || a->q_head_stride % 16 ||
+      !aligned(a->summaries, 16) || a->s_page_stride % 16 || a->s_region_stride % 16 ||
+      !aligned(a->scores, 16) || a->scores_row_stride % 4)
+    return SDA_ERR_UNSUPPORTED;
+  if (!aligned(a->weights, 4) || !aligned(a->summary_scales, 4) || !aligned(a->current, 4) ||
+      !aligned(a->topk_lengths, 4))
+    return SDA_ERR_INVALID;
+  sda::LogitsParams p{};
+  p.q = static_cast<const uint8_t*>(a->query);
+  p.qrs = a->q_row_stride;
+  p.qhs = a->q_head_stride;
+  p.w = a->weights;
+  p.wrs = a->w_row_stride;
+  p.sm = static_cast<const uint8_t*>(a->summaries);
+  p.sps = a->s_page_stride;
+  p.sms = a->s_region_stride;
+  p.sc = a->summary_scales;
+  p.scps = a->ss_page_stride;
+  p.table = a->block_table;
+  p.trs = a->table_row_stride;
+  p.positions = a->positions;
+  p.out = a->scores;
+  p.ors = a->scores_row_stride;
+  p.current = a->current;
+  p.lengths = a->topk_lengths;
+  p.rows = a->rows;
+  p.heads = a->heads;
+  p.hshift = __builtin_ctz((unsigned)a->heads);
+  p.rows_per_req = (int32_t)rpr;
+  p.rpb = a->regions_per_page;
+  p.S = a->num_regions;
+  p.rt = a->region_tokens;
+  hipError_t e = sda::launch_logits(p, stream);
+  return e == hipSuccess ? SDA_OK : SDA_ERR_LAUNCH;
+}
+
 }  // extern "C"

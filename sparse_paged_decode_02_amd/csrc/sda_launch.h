@@ -62,4 +62,26 @@ struct SelParams {
 
 hipError_t launch_select(const SelParams& p, hipStream_t stream);
 
+// Decode indexer logits (sda_logits.hip).
+struct LogitsParams {
+  const uint8_t* q;           // e4m3 [rows, heads, 256]
+  int64_t qrs, qhs;           // bytes
+  const float* w;             // [rows, heads]
+  int64_t wrs;
+  const uint8_t* sm;          // e4m3 summaries [pages, rpb, 256]
+  int64_t sps, sms;           // page / region strides (bytes)
+  const float* sc;            // [pages, rpb]
+  int64_t scps;               // page stride (elements)
+  const int32_t* table;
+  int64_t trs;
+  const int32_t* positions;
+  float* out;                 // [rows, S]
+  int64_t ors;
+  int32_t* current;           // [rows] or null
+  int32_t* lengths;           // [rows] or null
+  int32_t rows, heads, hshift, rows_per_req, rpb, S, rt;
+};
+
+hipError_t launch_logits(const LogitsParams& p, hipStream_t stream);
+
 }  // namespace sda

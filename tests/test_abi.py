@@ -20,7 +20,8 @@ def test_library_exports_every_declared_function():
     names = _declared_functions()
     assert {"sda_decode", "sda_splits", "sda_workspace_bytes", "sda_status_string",
             "sda_abi_version", "sda_args_size", "sda_swa_decode", "sda_swa_plan",
-            "sda_select_regions", "sda_select_args_size",
+            "sda_select_regions", "sda_select_args_size", "sda_indexer_logits",
+            "sda_logits_args_size",
             "sda_swa_args_size"} <= set(names)
     lib = B.lib()
     for n in names:
@@ -33,6 +34,7 @@ def test_abi_version_and_struct_size():
     assert lib.sda_args_size() == ctypes.sizeof(B.DecodeArgs)
     assert lib.sda_swa_args_size() == ctypes.sizeof(B.SwaArgs)
     assert lib.sda_select_args_size() == ctypes.sizeof(B.SelectArgs)
+    assert lib.sda_logits_args_size() == ctypes.sizeof(B.LogitsArgs)
 
 
 def _table(name):
@@ -259,3 +261,50 @@ def test_select_empty_calls_launch_nothing():
     # one row needs no row stride
     assert B.sda_select_regions_raw(_valid_select(rows=1, regions_row_stride=0, topk=0)) == \
         B.SDA_OK
+
+
+# ---- indexer logits entry point -----------------------------------------------
+
+def _valid_logits(**over):
+    a = B.LogitsArgs()
+    a.rows, a.heads, a.groups, a.query_len = 8, 8, 4, 1
+    a.regions_per_page, a.num_regions, a.region_tokens = 8, 4096, 8
+    a.query, a.q_row_stride, a.q_head_stride = 0x100000, 8 * 256, 256
+    a.weights, a.w_row_stride = 0x200000, 8
+    a.summaries, a.s_page_stride, a.s_region_stride = 0x300000, 8 * 256, 256
+    a.summary_scales, a.ss_page_stride = 0x400000, 8
+    a.block_table, a.table_row_stride = 0x500000, 512
+    a.positions = 0x600000
+    a.scores, a.scores_row_stride = 0x700000, 4096
+    a.current = a.topk_lengths = None
+    for k, v in over.items():
+        setattr(a, k, v)
+    return a
+
+
+LOGITS_INVALID = [dict(heads=0), dict(heads=3), dict(heads=32), dict(groups=0), dict(query_len=0),
+                  dict(regions_per_page=0), dict(num_regions=-1), dict(region_tokens=0),
+                  dict(rows=6), dict(rows=-4), dict(query=None), dict(weights=None),
+                  dict(summaries=None), dict(summary_scales=None), dict(block_table=None),
+                  dict(positions=None), dict(scores=None), dict(weights=0x200002),
+                  dict(current=0x800001)]
+LOGITS_UNSUPPORTED = [dict(heads=16, query_len=2), dict(query=0x100008),
+                      dict(q_head_stride=264), dict(s_region_stride=260),
+                      dict(summaries=0x300004), dict(scores=0x700004),
+                      dict(scores_row_stride=4098), dict(rows=16777216 * 4, groups=4)]
+
+
+@pytest.mark.parametrize("over", LOGITS_INVALID, ids=[str(o) for o in LOGITS_INVALID])
+def test_logits_invalid_arguments_are_rejected(over):
+    assert B.sda_indexer_logits_raw(_valid_logits(**over)) == B.SDA_ERR_INVALID
+
+
+@pytest.mark.parametrize("over", LOGITS_UNSUPPORTED, ids=[str(o) for o in LOGITS_UNSUPPORTED])
+def test_logits_unsupported_arguments_are_rejected(over):
+    assert B.sda_indexer_logits_raw(_valid_logits(**over)) == B.SDA_ERR_UNSUPPORTED
+
+
+def test_logits_empty_calls_launch_nothing():
+    assert B.lib().sda_indexer_logits(None, None) == B.SDA_ERR_INVALID
+    assert B.sda_indexer_logits_raw(_valid_logits(rows=0, query=None)) == B.SDA_OK
+    assert B.sda_indexer_logits_raw(_valid_logits(num_regions=0, scores=None)) == B.SDA_OK
