@@ -22,7 +22,10 @@ host cores.
 on one of its workloads instead; its algorithmic bytes are each row's window
 of K|V rows, plus Q and the output.  ``--select NAME`` measures region
 selection (``sda_select_regions``): its bytes are the candidate scores, the
-row metadata and the selected ids.
+row metadata and the selected ids.  ``--logits NAME`` measures the decode
+indexer logits (``sda_indexer_logits``): its bytes are each request's scored
+region summaries and scales (read once per request), the queries and
+weights, and the fp32 score matrix written.
 """
 from __future__ import annotations
 
@@ -41,6 +44,7 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "effective KV GB/s (% of HBM peak) and rows/s for sparse decode attention"
 KERNEL_SRC = os.path.join(ROOT, "sparse_paged_decode_02_amd", "csrc", "sda_kernels.hip")
 SELECT_SRC = os.path.join(ROOT, "sparse_paged_decode_02_amd", "csrc", "sda_select.hip")
+LOGITS_SRC = os.path.join(ROOT, "sparse_paged_decode_02_amd", "csrc", "sda_logits.hip")
 
 
 def kernel_hash() -> str:
@@ -51,6 +55,11 @@ def kernel_hash() -> str:
 
 def select_kernel_hash() -> str:
     with open(SELECT_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def logits_kernel_hash() -> str:
+    with open(LOGITS_SRC, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
@@ -286,6 +295,93 @@ def select_cpu_baseline(inp, gpu_out, min_seconds: float):
     }
 
 
+def logits_algorithmic_bytes(w, positions) -> int:
+    pos = np.asarray(positions, dtype=np.int64).reshape(w.requests, w.query_len * w.groups)
+    last = np.where(pos < 0, -1, pos // w.region_tokens).max(axis=1)
+    nreg = np.clip(last + 1, 0, w.num_regions)
+    summaries = int(nreg.sum()) * (256 + 4)
+    per_row = w.heads * 256 + w.heads * 4 + 4 + 8
+    return summaries + w.rows * per_row + w.rows * w.num_regions * 4
+
+
+def logits_cpu_baseline(inp, gpu_out, rows_sample: int, threads: int, min_seconds: float):
+    from oracle import oracle
+    from oracle.hostprep import logits_host_problem
+    w = inp.w
+    rng = np.random.default_rng(0)
+    rows = sorted(rng.choice(w.rows, size=min(rows_sample, w.rows), replace=False).tolist())
+    hp = logits_host_problem(inp, rows=rows)
+    passes, dt, ref = timed_passes(lambda: oracle.indexer_logits(hp, rows=rows, threads=threads),
+                                   min_seconds)
+    pos = inp.positions.cpu().numpy().astype(np.int64)[rows]
+    nreg = np.clip(np.where(pos < 0, -1, pos // w.region_tokens) + 1, 0, w.num_regions)
+    nbytes = int(nreg.sum()) * 260 + len(rows) * (w.heads * 260 + 12 + w.num_regions * 4)
+    g = gpu_out.cpu().numpy().astype(np.float64)[rows]
+    r = ref[rows]
+    m = np.isfinite(r)
+    max_abs = float(np.max(np.abs(g[m] - r[m]))) if m.any() else 0.0
+    return {
+        "value": passes * nbytes / dt / 1e9,
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": "%d rows of the first input set, %d passes (fp64 C oracle, %d threads), "
+                  "%.2f s wall; rows/s %.1f" % (len(rows), passes, threads, dt,
+                                               passes * len(rows) / dt),
+        "parity_max_abs": max_abs,
+    }
+
+
+def run_logits(args, dev) -> int:
+    import torch
+    from sparse_paged_decode_02_amd import binding as B
+    from sparse_paged_decode_02_amd import inputs as gen
+
+    w = gen.LOGITS_CONFIGS[args.logits]
+    desc = ("%s: %d rows = %d req x qlen %d x G %d, %d e4m3 heads x 256, %d regions of %d "
+            "tokens (%d per page), positions U[%d,%d]"
+            % (w.name, w.rows, w.requests, w.query_len, w.groups, w.heads, w.num_regions,
+               w.region_tokens, w.rpb, w.pos_lo, w.pos_hi))
+    print("[bench] drawing %s" % desc, file=sys.stderr, flush=True)
+    base = gen.make_logits_inputs(w, device=dev)
+    sets = [base] + [gen.make_logits_inputs(w, device=dev, seed=w.seed + 100003 * i,
+                                            summaries=base.summaries, scales=base.scales)
+                     for i in range(1, args.sets)]
+    nbytes = [logits_algorithmic_bytes(w, s.positions.cpu().numpy()) for s in sets]
+    outs = [torch.empty((w.rows, w.num_regions), dtype=torch.float32, device=dev) for _ in sets]
+    curs = [torch.empty(w.rows, dtype=torch.int32, device=dev) for _ in sets]
+    lens = [torch.empty(w.rows, dtype=torch.int32, device=dev) for _ in sets]
+    stream = torch.cuda.current_stream(dev)
+    handle = ctypes.c_void_p(stream.cuda_stream)
+    prepared = [B.make_logits_args(s.query, s.weights, s.summaries, s.scales, s.block_table,
+                                   s.positions, o, groups=w.groups, query_len=w.query_len,
+                                   region_tokens=w.region_tokens, current=c, topk_lengths=l)
+                for s, o, c, l in zip(sets, outs, curs, lens)]
+
+    def call(i):
+        rc = B.sda_indexer_logits_raw(prepared[i % len(prepared)], handle)
+        if rc != B.SDA_OK:
+            raise B.SdaError(rc, B.status_string(rc))
+
+    wall, launch_avg_ms, launch_ms = time_calls(call, args.steps, args.warmup, stream)
+    total_bytes = sum(nbytes[i % len(sets)] for i in range(args.steps))
+    bytes_per_launch = float(np.mean([nbytes[i % len(sets)] for i in range(args.steps)]))
+    rec = record(args, value=total_bytes / wall / 1e9, wall=wall, launch_avg_ms=launch_avg_ms,
+                 launch_ms=launch_ms, bytes_per_launch=bytes_per_launch, rows=w.rows,
+                 dtype="e4m3 inputs, bf16 MFMA, fp32 scores",
+                 config={"workload": desc, "rows": w.rows, "num_regions": w.num_regions,
+                         "input_sets": len(sets), "seed": w.seed},
+                 kernel="logits_kernel", traffic=load_traffic(w.name, 1, "logits_kernel"),
+                 metric="effective GB/s (% of HBM peak) and rows/s for decode indexer logits")
+    if not args.no_cpu_baseline:
+        threads = max(1, min(16, os.cpu_count() or 1))
+        print("[bench] cpu baseline: oracle logits", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = logits_cpu_baseline(base, outs[0], args.cpu_rows, threads,
+                                                  args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def run_select(args, dev) -> int:
     import torch
     from sparse_paged_decode_02_amd import binding as B
@@ -337,7 +433,8 @@ def load_traffic(workload_name: str, splits: int, kernel: str = "split_kernel"):
         parts = line.strip().split("=")
         if len(parts) == 2:
             fields[parts[0].strip()] = parts[1].strip()
-    want_hash = select_kernel_hash() if kernel == "select_kernel" else kernel_hash()
+    want_hash = {"select_kernel": select_kernel_hash, "logits_kernel": logits_kernel_hash}.get(
+        kernel, kernel_hash)()
     if fields.get("kernel_sha256_16") != want_hash or fields.get("splits") != str(splits):
         return None
     try:
@@ -405,6 +502,9 @@ def main() -> int:
     ap.add_argument("--select", default="", metavar="NAME",
                     help="measure region selection on workload NAME (select-decode, "
                          "select-large) instead")
+    ap.add_argument("--logits", default="", metavar="NAME",
+                    help="measure the decode indexer logits on workload NAME (logits-decode, "
+                         "logits-mtp) instead")
     ap.add_argument("--pack", type=int, default=0,
                     help="with --swa: query tokens per workgroup (0: the library's plan)")
     ap.add_argument("--sets", type=int, default=4, help="rotating input sets")
@@ -447,6 +547,8 @@ def main() -> int:
         return run_swa(args, dev)
     if args.select:
         return run_select(args, dev)
+    if args.logits:
+        return run_logits(args, dev)
     w = gen.CONFIGS[args.config]
     splits = args.splits or w.splits or B.sda_splits(w.rows)
 

@@ -59,6 +59,24 @@ __device__ __forceinline__ void e4m3x16_to_bf16(const u32x4 w, bf16x8& lo, bf16x
   hi = __builtin_bit_cast(bf16x8, u32x4{o[4], o[5], o[6], o[7]});
 }
 
+// x plus the value of another lane, moved by DPP (no LDS traffic).
+template <int kCtrl>
+__device__ __forceinline__ float dpp_add(float x) {
+  const int y = __builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, 0xF, 0xF, false);
+  return x + __int_as_float(y);
+}
+
+// Sum of x over each aligned group of n lanes (n = 1, 2, 4, 8, 16) inside a
+// row of 16: quad permutes for the first two steps, then the half-row and
+// row mirrors (each pairs every lane with one of the other half).
+__device__ __forceinline__ float group_sum(float x, int n) {
+  if (n >= 2) x = dpp_add<0xB1>(x);   // quad_perm [1,0,3,2]
+  if (n >= 4) x = dpp_add<0x4E>(x);   // quad_perm [2,3,0,1]
+  if (n >= 8) x = dpp_add<0x141>(x);  // row_half_mirror
+  if (n >= 16) x = dpp_add<0x140>(x); // row_mirror
+  return x;
+}
+
 __global__ __launch_bounds__(kLgThreads) void logits_kernel(const LogitsParams p) {
   const int req = blockIdx.x;
   const int chunk = blockIdx.y;
@@ -73,110 +91,135 @@ __global__ __launch_bounds__(kLgThreads) void logits_kernel(const LogitsParams p
   const int ncols = rpr * p.heads;
   const int ntiles = (ncols + 15) / 16;
 
-  // Region count of each row of the request (and, once, current / lengths).
-  for (int t = tid; t < rpr; t += kLgThreads) {
-    const int pos = p.positions[r0 + t];
+  // Region count of each row (lane t < rpr: row t), the request's maximum
+  // (every wave reduces it itself), and once the current / length outputs.
+  int lenv = 0;
+  if (lane < rpr) {
+    const int pos = p.positions[r0 + lane];
     const int cur = pos < 0 ? -1 : pos / p.rt;
-    const int len = cur + 1 < p.S ? cur + 1 : p.S;
-    s_len[t] = len;
-    if (chunk == 0) {
-      if (p.current) p.current[r0 + t] = cur;
-      if (p.lengths) p.lengths[r0 + t] = len;
+    lenv = cur + 1 < p.S ? cur + 1 : p.S;
+    if (wave == 0) {
+      s_len[lane] = lenv;
+      if (chunk == 0) {
+        if (p.current) p.current[r0 + lane] = cur;
+        if (p.lengths) p.lengths[r0 + lane] = lenv;
+      }
     }
   }
-  // Query columns as bf16, in the lane order of the MFMA B operand: entry
-  // (tile, lane) holds column 16 tile + (lane & 15), dims [64 (lane >> 4), +64).
-  for (int e = tid; e < ntiles * 64; e += kLgThreads) {
-    const int t = e >> 6, l = e & 63;
-    const int col = 16 * t + (l & 15);
-    __bf16* dst = &s_q[t][l][0];
-    if (col < ncols) {
-      const int row = r0 + (col >> p.hshift);
-      const int h = col & (p.heads - 1);
-      const uint8_t* src = p.q + (int64_t)row * p.qrs + (int64_t)h * p.qhs + 64 * (l >> 4);
+  int max_len = lenv;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        bf16x8 lo, hi;
-        e4m3x16_to_bf16(*reinterpret_cast<const u32x4*>(src + 16 * c), lo, hi);
-        *reinterpret_cast<bf16x8*>(dst + 16 * c) = lo;
-        *reinterpret_cast<bf16x8*>(dst + 16 * c + 8) = hi;
-      }
-    } else {
+  for (int d = 32; d >= 1; d >>= 1) max_len = max(max_len, __shfl_xor(max_len, d));
+
+  const int j_begin = chunk * kLgChunk;
+  const int j_end = min(p.S, j_begin + kLgChunk);
+  const int j_live = min(j_end, max_len);
+  // This wave's tiles start at j_begin + 16 wave + 64 t (t = 0..3).  Lane l
+  // resolves region j_begin + 16 wave + 64 (l >> 4) + (l & 15): its summary
+  // row offset and scale, shared with the MFMA lanes by shuffles, so the
+  // tile loop issues summary loads only.
+  const int jl = j_begin + kLgTile * wave + kLgTile * kLgWaves * (lane >> 4) + (lane & 15);
+  int64_t pg = 0;
+  if (jl < j_live) pg = p.table[(int64_t)req * p.trs + jl / p.rpb];
+  // Query columns (entry = thread: column tile tid >> 6, lane tid & 63),
+  // loaded while the table lookups are in flight, converted to bf16 in the
+  // lane order of the MFMA B operand: entry (tile, lane) holds column
+  // 16 tile + (lane & 15), dims [64 (lane >> 4), +64).
+  static_assert(kLgThreads == (kLgMaxCols / 16) * 64, "one query entry per thread");
+  const int qt = tid >> 6, ql = tid & 63;
+  const int qcol = 16 * qt + (ql & 15);
+  u32x4 qraw[4] = {};
+  if (qt < ntiles && qcol < ncols) {
+    const int row = r0 + (qcol >> p.hshift);
+    const int h = qcol & (p.heads - 1);
+    const uint8_t* src = p.q + (int64_t)row * p.qrs + (int64_t)h * p.qhs + 64 * (ql >> 4);
 #pragma unroll
-      for (int c = 0; c < 8; ++c) *reinterpret_cast<u32x4*>(dst + 8 * c) = u32x4{0, 0, 0, 0};
+    for (int c = 0; c < 4; ++c) qraw[c] = *reinterpret_cast<const u32x4*>(src + 16 * c);
+  }
+  int64_t roff_l = 0;
+  float scale_l = 0.f;
+  if (jl < j_live) {
+    roff_l = pg * p.sps + (int64_t)(jl % p.rpb) * p.sms;
+    scale_l = p.sc[pg * p.scps + jl % p.rpb];
+  }
+  if (qt < ntiles) {
+    __bf16* dst = &s_q[qt][ql][0];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      bf16x8 lo, hi;
+      e4m3x16_to_bf16(qraw[c], lo, hi);  // zeros for absent columns
+      *reinterpret_cast<bf16x8*>(dst + 16 * c) = lo;
+      *reinterpret_cast<bf16x8*>(dst + 16 * c + 8) = hi;
     }
   }
   for (int c = tid; c < kLgMaxCols; c += kLgThreads)
     s_w[c] = c < ncols ? p.w[(int64_t)(r0 + (c >> p.hshift)) * p.wrs + (c & (p.heads - 1))] : 0.f;
   __syncthreads();
 
-  int max_len = 0;
-  for (int t = 0; t < rpr; ++t) max_len = max(max_len, s_len[t]);
-
-  const int j_begin = chunk * kLgChunk;
-  for (int tile = wave; tile < kLgChunk / kLgTile; tile += kLgWaves) {
-    const int j0 = j_begin + kLgTile * tile;
-    if (j0 >= p.S) break;
-    if (j0 >= max_len) {
-      // Past every row's last region: -inf, and no summary read.
-      for (int e = lane; e < rpr * kLgTile; e += 64) {
-        const int row = e / kLgTile, j = j0 + (e - row * kLgTile);
-        if (j < p.S) p.out[(int64_t)(r0 + row) * p.ors + j] = -INFINITY;
-      }
-      continue;
+  // Tiles at or past the request's last region: -inf, and no summary read.
+  for (int j0 = j_begin + kLgTile * wave; j0 < j_end; j0 += kLgTile * kLgWaves) {
+    if (j0 < j_live) continue;
+    for (int e = lane; e < rpr * kLgTile; e += 64) {
+      const int row = e / kLgTile, j = j0 + (e - row * kLgTile);
+      if (j < p.S) p.out[(int64_t)(r0 + row) * p.ors + j] = -INFINITY;
     }
-    // A operand: region j0 + i16 (clamped into the request's regions for the
-    // load; masked below), bytes [64 g4, +64) as 8 bf16x8 k-slices.
-    const int ja = min(j0 + i16, max_len - 1);
-    const int64_t pa = p.table[(int64_t)req * p.trs + ja / p.rpb];
-    const uint8_t* asrc = p.sm + pa * p.sps + (int64_t)(ja % p.rpb) * p.sms + 64 * g4;
+  }
+  // A operand of tile t: region j0 + i16 (a region past j_live is masked;
+  // its lane borrows the tile's first region, always live), bytes [64 g4, +64).
+  auto load_tile = [&](int t, u32x4 (&raw)[4]) {
+    const int src = kLgTile * t + i16;
+    const int j = j_begin + kLgTile * wave + kLgTile * kLgWaves * t + i16;
+    const int64_t off = __shfl(roff_l, j < j_live ? src : kLgTile * t);
+    const uint8_t* a = p.sm + off + 64 * g4;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) raw[c] = *reinterpret_cast<const u32x4*>(a + 16 * c);
+  };
+  const int nt = (j_live - (j_begin + kLgTile * wave) + kLgTile * kLgWaves - 1) /
+                 (kLgTile * kLgWaves);  // live tiles of this wave (<= 4)
+  if (nt > 0) {
     u32x4 raw[4];
+    load_tile(0, raw);
+    for (int t = 0; t < nt; ++t) {
+      const int j0 = j_begin + kLgTile * wave + kLgTile * kLgWaves * t;
+      bf16x8 a[8];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) raw[c] = *reinterpret_cast<const u32x4*>(asrc + 16 * c);
-    // scales of this lane's C rows: regions j0 + 4 g4 + v
-    float sc[4];
+      for (int c = 0; c < 4; ++c) e4m3x16_to_bf16(raw[c], a[2 * c], a[2 * c + 1]);
+      if (t + 1 < nt) load_tile(t + 1, raw);  // next tile in flight
+      float scc[4];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int jc = min(j0 + 4 * g4 + v, max_len - 1);
-      const int64_t pc = p.table[(int64_t)req * p.trs + jc / p.rpb];
-      sc[v] = p.sc[pc * p.scps + jc % p.rpb];
-    }
-    bf16x8 a[8];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) e4m3x16_to_bf16(raw[c], a[2 * c], a[2 * c + 1]);
+      for (int v = 0; v < 4; ++v) scc[v] = __shfl(scale_l, kLgTile * t + 4 * g4 + v);
 
-    for (int ct = 0; ct < ntiles; ++ct) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      const __bf16* bq = &s_q[ct][lane][0];
+      for (int ct = 0; ct < ntiles; ++ct) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        const __bf16* bq = &s_q[ct][lane][0];
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const bf16x8 b = *reinterpret_cast<const bf16x8*>(bq + 8 * s);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], b, acc, 0, 0, 0);
-      }
-      // lane holds S[region j0 + 4 g4 + v][column 16 ct + i16]
-      const int col = 16 * ct + i16;
-      const float wc = s_w[col < kLgMaxCols ? col : 0];
-      float x[4];
+        for (int s = 0; s < 8; ++s) {
+          const bf16x8 b = *reinterpret_cast<const bf16x8*>(bq + 8 * s);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], b, acc, 0, 0, 0);
+        }
+        // lane holds S[region j0 + 4 g4 + v][column 16 ct + i16]
+        const int col = 16 * ct + i16;
+        const float wc = col < ncols ? s_w[col] : 0.f;
+        float x[4];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) x[v] = fmaxf(0.f, sc[v] * acc[v]) * (col < ncols ? wc : 0.f);
-      // sum over the row's heads: `heads` consecutive lanes of the 16-lane group
-      for (int d = 1; d < p.heads; d <<= 1)
+        for (int v = 0; v < 4; ++v) x[v] = fmaxf(0.f, scc[v] * acc[v]) * wc;
+        // sum over the row's heads: `heads` consecutive lanes of the 16-lane group
 #pragma unroll
-        for (int v = 0; v < 4; ++v) x[v] += __shfl_xor(x[v], d);
-      if (col < ncols && (col & (p.heads - 1)) == 0) {
-        const int rowi = col >> p.hshift;
-        const int len = s_len[rowi];
-        const int jb = j0 + 4 * g4;
-        float* dst = p.out + (int64_t)(r0 + rowi) * p.ors + jb;
-        float y[4];
+        for (int v = 0; v < 4; ++v) x[v] = group_sum(x[v], p.heads);
+        if (col < ncols && (col & (p.heads - 1)) == 0) {
+          const int rowi = col >> p.hshift;
+          const int len = s_len[rowi];
+          const int jb = j0 + 4 * g4;
+          float* dst = p.out + (int64_t)(r0 + rowi) * p.ors + jb;
+          float y[4];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) y[v] = jb + v < len ? x[v] : -INFINITY;
-        if (jb + 3 < p.S) {
-          *reinterpret_cast<float4*>(dst) = make_float4(y[0], y[1], y[2], y[3]);
-        } else {
+          for (int v = 0; v < 4; ++v) y[v] = jb + v < len ? x[v] : -INFINITY;
+          if (jb + 3 < p.S) {
+            *reinterpret_cast<float4*>(dst) = make_float4(y[0], y[1], y[2], y[3]);
+          } else {
 #pragma unroll
-          for (int v = 0; v < 4; ++v)
-            if (jb + v < p.S) dst[v] = y[v];
+            for (int v = 0; v < 4; ++v)
+              if (jb + v < p.S) dst[v] = y[v];
+          }
         }
       }
     }

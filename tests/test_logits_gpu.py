@@ -73,7 +73,7 @@ def check(inp, got, cur, lens, rows=None, what=""):
     assert np.array_equal(inf_ref, inf_got), what
     m = ~inf_ref
     bound = abs_bound(inp, rows)
-    err = np.abs(g - ref)
+    err = np.where(m, np.abs(np.where(m, g, 0.0) - np.where(m, ref, 0.0)), 0.0)
     _say("%s max_err=%.3e max_err/B=%.3e" % (what, err[m].max() if m.any() else 0.0,
                                                 (err[m] / np.maximum(bound[m], 1e-30)).max()
                                                 if m.any() else 0.0))
