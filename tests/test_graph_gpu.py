@@ -1,0 +1,89 @@
+"""Every entry point enqueues kernels only (no allocation, no host
+synchronisation, no memset), so it can be captured in a HIP graph.  Each
+call is captured once and replayed several times, with eager work between
+the replays; every replay must equal the eager result bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+from sparse_paged_decode_02_amd import binding as B
+from sparse_paged_decode_02_amd import inputs as gen
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+REPLAYS = 3
+
+
+def replay_and_compare(fn, outs, label):
+    """fn() enqueues the call writing `outs`; compare eager vs graph replays."""
+    fn()
+    torch.cuda.synchronize()
+    eager = [o.clone() for o in outs]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()                      # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    for k in range(REPLAYS):
+        for o in outs:
+            o.fill_(123)          # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for o, e in zip(outs, eager):
+            assert torch.equal(o, e), (label, k)
+
+
+@pytest.mark.parametrize("splits", [1, 3])
+def test_decode_in_graph(splits):
+    w = gen.scaled(gen.CONFIGS[2], name="graph", requests=4, pages_per_req=16, pos_lo=300,
+                   pos_hi=1023)
+    inp = gen.make_inputs(w, device=DEV)
+    out = torch.empty_like(inp.query)
+    ws = torch.empty(max(B.sda_workspace_bytes(w.rows, w.heads, splits), 1), dtype=torch.uint8,
+                     device=DEV)
+
+    def fn():
+        B.sda_decode(inp.query, inp.cache, inp.regions, inp.block_table, inp.positions,
+                     inp.active, out, scale=inp.scale, splits=splits, gate=inp.gate,
+                     workspace=ws if splits > 1 else None)
+
+    replay_and_compare(fn, [out], "decode splits=%d" % splits)
+
+
+def test_swa_in_graph():
+    w = gen.SwaWorkload("graph-swa", requests=4, query_len=2, groups=2, heads=4, block=64,
+                        pages_per_req=8, window=100, seq_lo=2, seq_hi=512, seed=3)
+    inp = gen.make_swa_inputs(w, device=DEV)
+    out = torch.empty_like(inp.query)
+    ws = torch.empty(B.sda_workspace_bytes(w.rows, w.heads, 2), dtype=torch.uint8, device=DEV)
+
+    def fn():
+        B.sda_swa_decode(inp.query, inp.cache, inp.block_table, inp.seq_lens, out,
+                         scale=inp.scale, window=w.window, query_len=w.query_len, splits=2,
+                         gate=inp.gate, workspace=ws)
+
+    replay_and_compare(fn, [out], "swa")
+
+
+def test_logits_and_selection_in_graph():
+    lw = gen.LogitsWorkload("graph-logits", requests=3, query_len=1, groups=2, heads=8, block=64,
+                            pages_per_req=6, pos_lo=100, pos_hi=383, seed=4)
+    li = gen.make_logits_inputs(lw, device=DEV)
+    scores = torch.empty((lw.rows, lw.num_regions), dtype=torch.float32, device=DEV)
+    cur = torch.empty(lw.rows, dtype=torch.int32, device=DEV)
+    lens = torch.empty_like(cur)
+    regions = torch.empty((lw.rows, 16), dtype=torch.int32, device=DEV)
+
+    def fn():
+        B.sda_indexer_logits(li.query, li.weights, li.summaries, li.scales, li.block_table,
+                             li.positions, groups=lw.groups, num_regions=lw.num_regions,
+                             scores=scores, current=cur, topk_lengths=lens)
+        B.sda_select_regions(scores, cur, 16, topk_lengths=lens, out=regions)
+
+    replay_and_compare(fn, [scores, cur, lens, regions], "logits+select")
