@@ -311,7 +311,7 @@ int sda_select_regions(const sda_select_args *args, hipStream_t stream);
  *  rows, heads   rows (a multiple of groups * query_len); indexer heads per
  *                row, a power of two <= 16.
  *  regions_per_page  summaries per page (block / region_tokens).
- *  num_regions   score columns S.
+ *  num_regions   score columns S, at most SDA_LOGITS_MAX_REGIONS.
  *  query         e4m3 [rows, heads, 256]; 16-byte aligned rows and heads.
  *  weights       fp32 [rows, heads], unit head stride.
  *  summaries     e4m3 [pages, regions_per_page, 256]; 16-byte aligned.
@@ -325,6 +325,7 @@ int sda_select_regions(const sda_select_args *args, hipStream_t stream);
  *                the scored region count min(current + 1, S).
  */
 #define SDA_LOGITS_MAX_COLUMNS 64
+#define SDA_LOGITS_MAX_REGIONS (65535 * 256) /* grid limit: 256 regions per workgroup */
 
 typedef struct sda_logits_args {
   int32_t rows, heads, groups, query_len, regions_per_page, num_regions, region_tokens;

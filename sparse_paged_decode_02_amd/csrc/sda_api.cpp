@@ -290,7 +290,8 @@ int sda_indexer_logits(const sda_logits_args* a, hipStream_t stream) {
     return SDA_ERR_INVALID;
   const int64_t rpr = (int64_t)a->groups * a->query_len;
   if (a->rows % rpr) return SDA_ERR_INVALID;
-  if (rpr * a->heads > SDA_LOGITS_MAX_COLUMNS || a->rows > SDA_MAX_ROWS)
+  if (rpr * a->heads > SDA_LOGITS_MAX_COLUMNS || a->rows > SDA_MAX_ROWS ||
+      a->num_regions > SDA_LOGITS_MAX_REGIONS)
     return SDA_ERR_UNSUPPORTED;
   if (a->rows == 0 || a->num_regions == 0) return SDA_OK;
   if (!a->query || !a->weights || !a->summaries || !a->summary_scales || !a->block_table ||
