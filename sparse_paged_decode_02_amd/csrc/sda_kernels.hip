@@ -78,6 +78,7 @@ enum Addr : int {
   kGeneral = 0,  // region list; a chunk may span regions (per-lane 64-bit addresses)
   kUniform = 1,  // region list; every chunk lies inside one region
   kWindow = 2,   // a contiguous sliding window of tokens, 16-token chunks
+  kPair = 3,     // region list of 8-token regions, bf16: a chunk is two regions
 };
 
 // Per cache dtype: tokens per chunk, V bytes per token, 16-byte V pieces per token.
@@ -164,6 +165,32 @@ __device__ __forceinline__ int swz_k(int row) {
       SDA_LDDMA("v2", addr, vsuf) SDA_NEXT SDA_LDDMA("v3", addr, vsuf) SDA_NEXT              \
       SDA_LDDMA("v4", addr, vsuf) SDA_NEXT SDA_LDDMA("v5", addr, vsuf)                       \
   "s_mov_b32 m0, %[sv]"
+
+// Two-region chunk (bf16, 8-token regions): the first three K and V DMAs
+// cover token rows 0..7 (pieces 0..191 of a 384-piece half) and the last
+// three rows 8..15, so each half takes its own uniform base.
+#define SDA_CHUNK_ASM2(addra, addrb, suf)                                                      \
+  "s_mov_b32 %[sv], m0\n\t"                                                                    \
+  "s_mov_b32 m0, %[st]\n\t" SDA_LDDMA("k0", addra, suf) SDA_NEXT SDA_LDDMA("k1", addra, suf)   \
+      SDA_NEXT SDA_LDDMA("k2", addra, suf) SDA_NEXT SDA_LDDMA("k3", addrb, suf) SDA_NEXT       \
+      SDA_LDDMA("k4", addrb, suf) SDA_NEXT SDA_LDDMA("k5", addrb, suf) SDA_NEXT                \
+      SDA_LDDMA("v0", addra, suf) SDA_NEXT SDA_LDDMA("v1", addra, suf) SDA_NEXT                \
+      SDA_LDDMA("v2", addra, suf) SDA_NEXT SDA_LDDMA("v3", addrb, suf) SDA_NEXT                \
+      SDA_LDDMA("v4", addrb, suf) SDA_NEXT SDA_LDDMA("v5", addrb, suf)                         \
+  "s_mov_b32 m0, %[sv]"
+
+__device__ __forceinline__ void dma_chunk_sbase2(const uint8_t* base_a, const uint8_t* base_b,
+                                                 uint32_t stage, const uint32_t (&ko)[6],
+                                                 const uint32_t (&vo)[6]) {
+  uint32_t saved;
+  __asm__ __volatile__(SDA_CHUNK_ASM2("%[b]", "%[b2]", " nt")
+                       : [sv] "=&s"(saved)
+                       : [st] "s"(stage), [b] "s"(base_a), [b2] "s"(base_b), [k0] "v"(ko[0]),
+                         [k1] "v"(ko[1]), [k2] "v"(ko[2]), [k3] "v"(ko[3]), [k4] "v"(ko[4]),
+                         [k5] "v"(ko[5]), [v0] "v"(vo[0]), [v1] "v"(vo[1]), [v2] "v"(vo[2]),
+                         [v3] "v"(vo[3]), [v4] "v"(vo[4]), [v5] "v"(vo[5])
+                       : "memory");
+}
 
 // dma_chunk_sbase: one uniform 64-bit base (SGPRs) plus 32-bit per-lane
 // byte offsets (chunks inside one region or one page).
@@ -298,6 +325,32 @@ __device__ __forceinline__ uint32_t issue_chunk(const Params& p, int c, int nreg
       vo[j] = roff + ld.voff[j];
     }
     dma_chunk_sbase<kFp8>(base, st, ko, vo);
+  } else if (kAddr == kPair) {
+    // 8-token regions (bf16): chunk c is regions 2c and 2c+1 of the list,
+    // each with a uniform base.  Rows past a region's visible count, and the
+    // second half when the list has no region 2c+1, load token 0 of region
+    // 2c (visible, finite, weight 0).
+    static_assert(!kFp8 || kAddr != kPair, "pair chunks are bf16");
+    const int i16 = lane & 15;
+    const int k0 = 2 * c;
+    const bool has1 = k0 + 1 < nreg;
+    const int n0 = __builtin_amdgcn_readfirstlane(s_n[k0]);
+    const int n1 = has1 ? __builtin_amdgcn_readfirstlane(s_n[k0 + 1]) : 0;
+    const int64_t rb0 = s_base[k0];
+    const int64_t rb1 = has1 ? s_base[k0 + 1] : rb0;
+    const uint8_t* base0 = uniform_ptr(p.cache + rb0 * C::kEsz);
+    const uint8_t* base1 = uniform_ptr(p.cache + rb1 * C::kEsz);
+    vbits = (i16 < 8 ? i16 < n0 : i16 - 8 < n1) ? 1u : 0u;
+    uint32_t ko[6], vo[6];
+#pragma unroll
+    for (int j = 0; j < 6; ++j) {
+      const int r8 = ld.row[j] & 7;  // rows 0..7 for j < 3, 8..15 for j >= 3
+      const int nn = j < 3 ? n0 : n1;
+      const uint32_t roff = r8 < nn ? (uint32_t)r8 * cts_bytes : 0u;
+      ko[j] = roff + ld.koff[j];
+      vo[j] = roff + ld.voff[j];
+    }
+    dma_chunk_sbase2(base0, base1, st, ko, vo);
   } else if (kAddr == kUniform) {
     const int i16 = lane & 15;
     // The chunk lies inside one region: uniform base, 32-bit lane offsets.
@@ -852,17 +905,23 @@ void launch_split(const Params& p, unsigned wgs, hipStream_t stream) {
                        dim3(64 * kWavesSmallGrid), 0, stream, p);
 }
 
+template <bool kFp8, bool kFused>
+void launch_region_list(const Params& p, hipStream_t stream) {
+  const unsigned wgs = (unsigned)p.rows;
+  if (p.rt % Cfg<kFp8>::kTok == 0)
+    launch_split<kFp8, kFused, kUniform>(p, wgs, stream);
+  else if (!kFp8 && p.rt == 8)
+    launch_split<kFp8, kFused, kFp8 ? kGeneral : kPair>(p, wgs, stream);
+  else
+    launch_split<kFp8, kFused, kGeneral>(p, wgs, stream);
+}
+
 template <bool kFp8>
 void launch_dtype(const Params& p, hipStream_t stream) {
-  const bool fused = p.splits == 1;
-  const bool uni = p.rt % Cfg<kFp8>::kTok == 0;
-  const unsigned wgs = (unsigned)p.rows;
-  if (fused)
-    uni ? launch_split<kFp8, true, kUniform>(p, wgs, stream)
-        : launch_split<kFp8, true, kGeneral>(p, wgs, stream);
+  if (p.splits == 1)
+    launch_region_list<kFp8, true>(p, stream);
   else
-    uni ? launch_split<kFp8, false, kUniform>(p, wgs, stream)
-        : launch_split<kFp8, false, kGeneral>(p, wgs, stream);
+    launch_region_list<kFp8, false>(p, stream);
 }
 
 hipError_t launch_combine(const Params& p, hipStream_t stream) {
