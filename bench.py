@@ -509,6 +509,9 @@ def main() -> int:
                     help="with --swa: query tokens per workgroup (0: the library's plan)")
     ap.add_argument("--sets", type=int, default=4, help="rotating input sets")
     ap.add_argument("--splits", type=int, default=0, help="0: the workload's rule")
+    ap.add_argument("--no-row-order", action="store_true",
+                    help="sparse decode with splits == 1: pass no workspace, so rows start "
+                         "in index order instead of heaviest first")
     ap.add_argument("--cpu-rows", type=int, default=48)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="repeat the CPU-baseline sample until this much host time is spent")
@@ -566,6 +569,13 @@ def main() -> int:
         nbytes.append(b)
     outs = [torch.empty_like(s.query) for s in sets]
     ws_bytes = B.sda_workspace_bytes(w.rows, w.heads, splits)
+    if args.no_row_order and splits == 1:
+        ws_bytes = 0
+    # The library ranks rows when given a workspace and the grid takes 2 to 4
+    # rounds of the resident workgroups (512 for grids of >= 512, else 256).
+    grid = w.rows * splits
+    resident = 512 if grid >= 512 else 256
+    ordered = ws_bytes > 0 and resident < grid <= 4 * resident
     workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     handle = ctypes.c_void_p(stream.cuda_stream)
@@ -594,8 +604,10 @@ def main() -> int:
                  launch_ms=launch_ms, bytes_per_launch=bytes_per_launch, rows=w.rows,
                  dtype="bf16" if w.kv == "bf16" else "fp8-e4m3 cache, bf16 MFMA",
                  config={"workload": workload_desc(w), "rows": w.rows, "heads": w.heads,
-                         "splits": splits, "input_sets": len(sets), "seed": w.seed},
-                 kernel="sda split kernel" + (" + combine" if splits > 1 else " (combine fused)"),
+                         "splits": splits, "row_order": "heaviest first" if ordered else "index",
+                         "input_sets": len(sets), "seed": w.seed},
+                 kernel=("sda order kernel + " if ordered else "") + "sda split kernel"
+                 + (" + combine" if splits > 1 else " (combine fused)"),
                  traffic=load_traffic(w.name, splits))
     if not args.no_cpu_baseline:
         threads = max(1, min(16, os.cpu_count() or 1))

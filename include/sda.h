@@ -30,7 +30,7 @@
 extern "C" {
 #endif
 
-#define SDA_ABI_VERSION 4
+#define SDA_ABI_VERSION 5
 #define SDA_HEAD_DIM 192     /* query / key / value head dim (fixed) */
 #define SDA_KV_ROW 384       /* one cache token row: K[0:192] then V[192:384] */
 #define SDA_MAX_HEADS 16     /* GQA-packed query heads per KV group */
@@ -105,7 +105,12 @@ typedef enum {
  *               sigmoid(gate[r / groups, (r % groups)*heads + h]).  This is
  *               the `_gate` helper on the same page.
  *  workspace    device scratch of at least sda_workspace_bytes(rows, heads,
- *               splits) bytes, 16-byte aligned.  May be NULL when splits == 1.
+ *               splits) bytes, 16-byte aligned.  May be NULL when splits == 1;
+ *               rows then start in index order.  Given a workspace, a call
+ *               whose grid of rows*splits workgroups takes 2 to 4 rounds of
+ *               the workgroups the chip holds at once (up to 2048) first
+ *               ranks rows by visible tokens and starts the heavy ones first
+ *               (the result is the same either way).
  */
 typedef struct sda_decode_args {
   int32_t rows, heads, groups, query_len, block, R, region_tokens;
@@ -153,9 +158,10 @@ int sda_decode(const sda_decode_args *args, hipStream_t stream);
 int sda_splits(int rows);
 
 /*
- * Bytes of workspace sda_decode needs: 0 when splits == 1, else
- * rows*splits*heads*(192+1)*4 rounded up to 256.  The workspace holds the
- * fp32 partial outputs and log-sum-exps.  Returns 0 for invalid sizes.
+ * Bytes of workspace for sda_decode: the row order and row bins, rows*8
+ * bytes rounded up to 256, plus, when splits > 1, the fp32 partial outputs
+ * and log-sum-exps, rows*splits*heads*(192+1)*4 bytes rounded up to 256.
+ * Returns 0 for invalid sizes.
  */
 size_t sda_workspace_bytes(int rows, int heads, int splits);
 

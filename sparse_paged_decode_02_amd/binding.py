@@ -23,7 +23,7 @@ SDA_ERR_WORKSPACE = -3
 SDA_ERR_LAUNCH = -4
 SDA_KV_BF16 = 0
 SDA_KV_FP8_E4M3 = 1
-ABI_VERSION = 4
+ABI_VERSION = 5
 HEAD_DIM = 192
 
 
@@ -257,18 +257,20 @@ def check_tensors(query, cache, regions, block_table, positions, active, output,
 
 def sda_decode(query, cache, regions, block_table, positions, active, output, *, scale,
                query_len=1, splits, clear_inactive=True, k_scale=None, v_scale=None,
-               gate=None, region_tokens=0, workspace=None, stream=None) -> None:
+               gate=None, region_tokens=0, workspace=None, row_order=True,
+               stream=None) -> None:
     """Enqueue ``sda_decode`` on ``stream`` (default: torch's current stream).
 
     Argument names follow ``sparse_decode_attention`` on the page
     "vllm.models.step5.nvidia.ops.sparse_decode_attention".  ``workspace``: a
     device tensor of at least sda_workspace_bytes(rows, heads, splits) bytes;
-    allocated here through torch when omitted and splits > 1.
+    allocated here through torch when omitted, unless splits == 1 and
+    ``row_order`` is false (no workspace: rows start in index order).
     """
     check_tensors(query, cache, regions, block_table, positions, active, output,
                   k_scale, v_scale, gate)
     rows, heads = query.shape[0], query.shape[1]
-    if workspace is None and splits > 1 and rows > 0:
+    if workspace is None and (splits > 1 or row_order) and rows > 0:
         nbytes = sda_workspace_bytes(rows, heads, splits)
         if nbytes:
             workspace = torch.empty(nbytes, dtype=torch.uint8, device=query.device)

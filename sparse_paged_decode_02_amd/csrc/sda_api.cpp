@@ -13,15 +13,27 @@ namespace {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+// Workspace layout: [row order and row bins: 2*rows int32][partials:
+// rows*splits*heads*192 fp32][log-sum-exps: rows*splits*heads fp32], each
+// area rounded up to 256 bytes.  Sets the partial and lse pointers when
+// splits > 1.
+void split_areas(sda::Params& p, void* workspace) {
+  char* base = static_cast<char*>(workspace) + round256((size_t)p.rows * 2 * sizeof(int32_t));
+  p.partial = reinterpret_cast<float*>(base);
+  p.lse = p.partial + (size_t)p.rows * p.splits * p.heads * SDA_HEAD_DIM;
+}
+
 // Split count for `rows` rows on MI355X.  The page "vllm.models.step5.nvidia.
 // ops.sparse_decode_attention" (`sparse_decode_splits`) doubles the split
 // count while rows*splits*2 <= 256, up to 32 splits.  On B300 that sizes the
-// grid for about 1.7 waves of programs.  Here one split workgroup (256
-// threads, ~157 KiB of LDS) occupies a whole compute unit, so the target is
-// one workgroup per CU: double while the doubled grid rows*splits*2 still
-// fits the 256 CUs.  That is the page's rule and bound, for a different
-// reason.  Measured on the bf16 gated workload (256 rows): 1 split 75 us,
-// 2 splits 86 us.
+// grid for about 1.7 waves of programs.  Here a grid of at most 256 split
+// workgroups runs them with 4 waves each (~121 KiB of LDS), one per compute
+// unit, so the target is one workgroup per CU: double while the doubled grid
+// rows*splits*2 still fits the 256 CUs.  That is the page's rule and bound,
+// for a different reason.  On the bf16 gated workload (256 rows) 2 splits
+// are slower than 1: the merge costs more than the idle CUs of inactive rows.
 constexpr int kComputeUnits = 256;
 constexpr int kMaxHeuristicSplits = 32;
 constexpr int kSwaMinChunksPerSplit = 8;
@@ -51,10 +63,10 @@ int sda_splits(int rows) {
 size_t sda_workspace_bytes(int rows, int heads, int splits) {
   if (rows < 0 || heads < 1 || heads > SDA_MAX_HEADS || splits < 1 || splits > SDA_MAX_SPLITS)
     return 0;
-  if (splits == 1) return 0;
+  const size_t order = round256((size_t)rows * 2 * sizeof(int32_t));
+  if (splits == 1) return order;
   size_t n = (size_t)rows * (size_t)splits * (size_t)heads;
-  size_t bytes = n * (SDA_HEAD_DIM + 1) * sizeof(float);
-  return (bytes + 255) & ~(size_t)255;
+  return order + round256(n * (SDA_HEAD_DIM + 1) * sizeof(float));
 }
 
 const char* sda_status_string(int status) {
@@ -142,12 +154,14 @@ int sda_decode(const sda_decode_args* a, hipStream_t stream) {
   p.clear = a->clear_inactive ? 1 : 0;
   p.gated = a->gate ? 1 : 0;
 
-  if (a->splits > 1) {
+  // splits == 1 needs no workspace; given one, the launch may use its order
+  // area to start heavy rows first.
+  if (a->splits > 1 || a->workspace) {
     size_t need = sda_workspace_bytes(a->rows, a->heads, a->splits);
     if (!a->workspace || a->workspace_bytes < need || !aligned(a->workspace, 16))
       return SDA_ERR_WORKSPACE;
-    p.partial = static_cast<float*>(a->workspace);
-    p.lse = p.partial + (size_t)a->rows * a->splits * a->heads * SDA_HEAD_DIM;
+    p.order_ws = static_cast<int32_t*>(a->workspace);
+    if (a->splits > 1) split_areas(p, a->workspace);
   }
 
   hipError_t e = sda::launch(p, fp8, stream);
@@ -246,8 +260,7 @@ int sda_swa_decode(const sda_swa_args* a, hipStream_t stream) {
     size_t need = sda_workspace_bytes(p.rows, a->heads, a->splits);
     if (!a->workspace || a->workspace_bytes < need || !aligned(a->workspace, 16))
       return SDA_ERR_WORKSPACE;
-    p.partial = static_cast<float*>(a->workspace);
-    p.lse = p.partial + (size_t)p.rows * a->splits * a->heads * SDA_HEAD_DIM;
+    split_areas(p, a->workspace);
   }
 
   hipError_t e = sda::launch_window(p, stream);

@@ -10,18 +10,24 @@
 // by log-sum-exp.  After the merge come the headwise sigmoid gate and the
 // inactive-row clear.
 //
-// Split kernel: one 256-thread workgroup (4 waves of 64) per (row, split).
+// Split kernel: one workgroup per (row, split), 4 waves of 64 (one workgroup
+// per CU) or, for grids of 512 or more workgroups, 2 waves (two per CU).
 //  * Prologue, per wave and without workgroup barriers: rank the row's
 //    visible region slots with ballots, take the split's balanced share, and
 //    resolve each region to a cache offset through the block table (only the
-//    share's entries are read).  The list goes into LDS.
+//    share's entries are read).  The list goes into LDS.  A sliding-window
+//    row instead resolves the pages of its contiguous token window.
+//  * Addressing: a chunk's 12 DMAs take their rows from per-lane 64-bit
+//    addresses when a chunk may straddle regions, from one scalar base when
+//    every chunk lies inside one region (or one window page), and from two
+//    scalar bases when bf16 regions of 8 tokens pair up into a chunk.
 //  * Main loop: every wave runs its own 2-stage pipeline over chunks of token
 //    slots (16 tokens for a bf16 cache, 32 for FP8: 6 KiB of K and 6 KiB of
 //    V either way).  A chunk is 12 LDS-DMAs (global_load_lds_dwordx4) into a
 //    wave-private stage.  They are issued from inline assembly and marked
 //    non-temporal (the bytes are read once), and their completion is awaited
-//    with an explicit vmcnt.  Chunk c+4 is in flight while chunk c is
-//    computed:
+//    with an explicit vmcnt.  The next chunk of the wave is in flight while
+//    the current one is computed:
 //      S^T[tok, head] = K[tok, :] . Q^T[:, head]   v_mfma_f32_16x16x32_bf16
 //      online softmax per head, in the exp2 domain, with lazy rescaling
 //      O^T[dim, head] += V^T[dim, tok] . P^T[tok, head]
@@ -32,9 +38,11 @@
 //    form.  FP8 K and V are converted exactly to bf16 (e4m3 is a subset of
 //    bf16).  k_scale is folded into the logit scale and v_scale into the
 //    final normalisation.
-//  * Epilogue: the 4 waves' (max, sum, acc) states are merged through LDS.
-//    With one split, the gate is applied and the result is written as bf16
-//    (combine fused).  Otherwise the fp32 partial output and its base-2
+//  * Epilogue: the waves' (max, sum, acc) states are merged through LDS:
+//    16 lanes turn the per-wave maxima and sums into one weight per (wave,
+//    head) that already holds v_scale, 1/sum and, with one split, the gate,
+//    and the output is the weighted sum of the wave accumulators, written
+//    as bf16 (combine fused).  Otherwise the fp32 partial output and its base-2
 //    log-sum-exp go to the workspace.
 // Combine kernel (splits > 1): one 64-thread workgroup per (row, head) merges
 // the partials, applies the gate and writes bf16, or clears an inactive row.
@@ -625,7 +633,7 @@ split_kernel(const Params p) {
       cw.lo = (int)max((int64_t)0, (int64_t)cw.hi - p.window + 1);
     }
   } else {
-    r = blockIdx.x;
+    r = p.order ? p.order[blockIdx.x] : (int)blockIdx.x;
     // The active flag, the position and the first 64 region ids do not
     // depend on each other: one round trip for all three.
     const int act = p.active[r];
@@ -894,10 +902,148 @@ __global__ __launch_bounds__(64) void combine_kernel(const Params p) {
   for (int u = 0; u < 3; ++u) orow[tid + 64 * u] = (uint16_t)float_to_bf16_bits(o[u] * gv);
 }
 
+// Row order for grids a few times larger than the chip holds at once.
+// Workgroups start in index order as earlier ones retire, so a heavy row that
+// starts late stretches the tail of the launch.  Two small kernels rank the
+// rows by visible tokens (0 for an inactive row) and write them heaviest
+// first within each block of 1024 rows:
+//  * bin_kernel: one wave per 16 rows, spread over the chip; writes each
+//    row's bin, 0 (heaviest) .. kOrderBins - 1, of width
+//    (R * region tokens + 1) / kOrderBins;
+//  * order_kernel: one 1024-thread workgroup per block of 1024 rows; a stable
+//    counting sort on the bins.
+// Rows of nearly equal work share a bin and keep index order: neighbouring
+// rows are the KV groups of one token, which read neighbouring slices of the
+// same pages.  Blocks of 1024 rows are at least as large as the resident grid
+// (512 workgroups), which is what keeps light rows at the end.  A row's
+// result does not depend on which workgroup computes it.
+constexpr int kOrderBlock = 1024;
+constexpr int kOrderWaves = kOrderBlock / 64;
+constexpr int kOrderBins = 32;
+constexpr int kOrderBatch = 16;  // rows per wave of the bin kernel
+constexpr int kOrderMaxRounds = 4;  // order grids of up to 4x the resident workgroups
+static_assert(kOrderBins * kOrderWaves <= kOrderBlock, "one scan entry per thread");
+
+__global__ __launch_bounds__(256) void bin_kernel(Params p, int64_t max_tokens, int32_t* bins) {
+  const int lane = threadIdx.x & 63;
+  // Wave w ranks kOrderBatch rows from rbase; lane i < kOrderBatch ends up
+  // with the tokens of row rbase + i.
+  const int rbase = (blockIdx.x * 4 + (threadIdx.x >> 6)) * kOrderBatch;
+  const int r = rbase + lane;
+  const int nrow = p.rows - rbase;  // rows of this wave, if below kOrderBatch
+  const bool valid = lane < kOrderBatch && r < p.rows;
+  const int act = valid ? p.active[r] : 0;
+  const int pos = valid ? p.positions[r] : -1;
+  // Region id i of this lane's row is visible in part or whole iff
+  // 0 <= i <= pq, wholly iff 0 <= i < pf; the one partial region shows
+  // pos % rt + 1 tokens.
+  const int pq = pos >= 0 ? pos / p.rt : -1;
+  const int pf = pos >= 0 ? (pos + 1) / p.rt : 0;
+  const int part = pos >= 0 ? pos - pq * p.rt + 1 : 0;
+  int64_t tokens = 0;
+  for (int c = 0; c < p.R; c += 64) {
+    // One coalesced load per row (lane l reads slot c + l), all issued
+    // before the first is used.
+    const bool in_r = c + lane < p.R;
+    const int32_t* ptr = p.regions + (int64_t)rbase * p.rrs + c + lane;
+    int ids[kOrderBatch];
+#pragma unroll
+    for (int i = 0; i < kOrderBatch; ++i) {
+      ids[i] = (i < nrow && in_r) ? *ptr : -1;
+      ptr += p.rrs;
+    }
+    // Row rbase + i: rt tokens per region that ends at or before its
+    // position, pos % rt + 1 per copy of the region that holds it.
+#pragma unroll
+    for (int i = 0; i < kOrderBatch; ++i) {
+      const int qi = __builtin_amdgcn_readlane(pq, i);
+      const int fi = __builtin_amdgcn_readlane(pf, i);
+      const uint64_t ba = __ballot(ids[i] >= 0 && ids[i] <= qi);
+      const uint64_t bf = __ballot(ids[i] >= 0 && ids[i] < fi);
+      if (lane == i) tokens += __popcll(bf) * p.rt + __popcll(ba & ~bf) * part;
+    }
+  }
+  if (valid) {
+    if (!act) tokens = 0;
+    bins[r] = kOrderBins - 1 - (int)(tokens * kOrderBins / (max_tokens + 1));
+  }
+}
+
+__global__ __launch_bounds__(kOrderBlock) void order_kernel(Params p, const int32_t* bins) {
+  // s_cnt[bin][wave]: rows of the wave in the bin, then their first slot.
+  __shared__ int s_cnt[kOrderBins * kOrderWaves];
+  __shared__ int s_wave[kOrderWaves];
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
+  const int r = blockIdx.x * kOrderBlock + t;
+  const int bin = r < p.rows ? bins[r] : -1;
+  // Lanes of the wave in the same bin, and this lane's rank among them.
+  uint64_t same = __ballot(bin >= 0);
+#pragma unroll
+  for (int b = 1; b < kOrderBins; b <<= 1) {
+    const uint64_t m = __ballot((bin & b) != 0);
+    same &= (bin & b) ? m : ~m;
+  }
+  const uint64_t below = lane ? ~0ull >> (64 - lane) : 0ull;
+  const int rank = __popcll(same & below);
+  if (t < kOrderBins * kOrderWaves) s_cnt[t] = 0;
+  __syncthreads();
+  if (bin >= 0 && rank == 0) s_cnt[bin * kOrderWaves + wave] = __popcll(same);
+  __syncthreads();
+  // Exclusive scan of s_cnt in (bin, wave) order: the first slot of each
+  // wave's rows of each bin.
+  const int own = t < kOrderBins * kOrderWaves ? s_cnt[t] : 0;
+  int v = own;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int n = __shfl_up(v, d, 64);
+    if (lane >= d) v += n;
+  }
+  if (lane == 63) s_wave[wave] = v;
+  __syncthreads();
+  if (wave == 0) {
+    int w = lane < kOrderWaves ? s_wave[lane] : 0;
+#pragma unroll
+    for (int d = 1; d < kOrderWaves; d <<= 1) {
+      const int n = __shfl_up(w, d, 64);
+      if (lane >= d) w += n;
+    }
+    if (lane < kOrderWaves) s_wave[lane] = w;
+  }
+  __syncthreads();
+  if (t < kOrderBins * kOrderWaves) s_cnt[t] = v - own + (wave ? s_wave[wave - 1] : 0);
+  __syncthreads();
+  if (bin >= 0) p.order_ws[blockIdx.x * kOrderBlock + s_cnt[bin * kOrderWaves + wave] + rank] = r;
+}
+
+// Workgroups resident at once for a grid of `wgs` workgroups (the wave
+// count, and with it the workgroups per CU, follows from the grid size).
+int64_t resident_workgroups(int64_t wgs) {
+  return wgs >= 2 * kComputeUnits ? 2 * kComputeUnits : kComputeUnits;
+}
+
+// Enqueue the bin and order kernels when they pay; returns the order to
+// follow, or null for index order.  They pay when the grid takes a few
+// rounds of resident workgroups: with one round every row starts at once,
+// and with many the tail is a small part of the launch.
+const int32_t* launch_order(const Params& p, hipStream_t stream) {
+  const int64_t wgs = (int64_t)p.rows * p.splits;
+  const int64_t resident = resident_workgroups(wgs);
+  if (!p.order_ws || wgs <= resident || wgs > kOrderMaxRounds * resident) return nullptr;
+  // The workspace's order area holds the bins ([rows] after the order).
+  int32_t* bins = p.order_ws + p.rows;
+  const int64_t max_tokens = (int64_t)p.R * p.rt;
+  const unsigned bin_wgs = (unsigned)((p.rows + 4 * kOrderBatch - 1) / (4 * kOrderBatch));
+  hipLaunchKernelGGL(bin_kernel, dim3(bin_wgs), dim3(256), 0, stream, p, max_tokens, bins);
+  hipLaunchKernelGGL(order_kernel, dim3((unsigned)((p.rows + kOrderBlock - 1) / kOrderBlock)),
+                     dim3(kOrderBlock), 0, stream, p, (const int32_t*)bins);
+  return p.order_ws;
+}
+
 template <bool kFp8, bool kFused, int kAddr>
 void launch_split(const Params& p, unsigned wgs, hipStream_t stream) {
   const dim3 grid(wgs, (unsigned)p.splits);
-  if ((int64_t)wgs * p.splits >= 2 * kComputeUnits)
+  if (resident_workgroups((int64_t)wgs * p.splits) == 2 * kComputeUnits)
     hipLaunchKernelGGL((split_kernel<kFp8, kFused, kAddr, kWavesLargeGrid>), grid,
                        dim3(64 * kWavesLargeGrid), 0, stream, p);
   else
@@ -933,7 +1079,9 @@ hipError_t launch_combine(const Params& p, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch(const Params& p, bool fp8, hipStream_t stream) {
+hipError_t launch(const Params& p0, bool fp8, hipStream_t stream) {
+  Params p = p0;
+  p.order = launch_order(p, stream);
   if (fp8)
     launch_dtype<true>(p, stream);
   else

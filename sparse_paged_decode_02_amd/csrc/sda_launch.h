@@ -29,6 +29,9 @@ struct Params {
   const float* v_scale;
   const uint16_t* gate;       // bf16 bits or null
   int64_t grs, ghs;
+  const int32_t* order;       // sparse: workgroup x serves row order[x]; null: row x
+  int32_t* order_ws;          // sparse: [2 * rows] scratch for the order and the row
+                              // bins, or null (index order)
   float* partial;             // [rows, splits, heads, 192] fp32 (splits > 1)
   float* lse;                 // [rows, splits, heads] fp32, base-2 (splits > 1)
   float scale;
@@ -39,7 +42,10 @@ struct Params {
 };
 
 // Enqueue the split kernel (and the combine kernel when splits > 1) over
-// region lists (sparse decode).
+// region lists (sparse decode).  When order_ws is set and the grid takes 2 to
+// 4 rounds of the workgroups the chip holds at once, two small kernels first
+// write a heaviest-first row order there (rows ranked by visible tokens
+// within each block of 1024 rows), and the split kernel follows it.
 hipError_t launch(const Params& p, bool fp8, hipStream_t stream);
 
 // The same kernels over each row's sliding window (bf16 cache): token j of a

@@ -52,10 +52,14 @@ def test_split_heuristic_table(rows, splits):
 
 
 def test_workspace_bytes():
-    assert B.sda_workspace_bytes(256, 16, 1) == 0
+    # [row order + row bins: 2*rows int32][partials + log-sum-exps when
+    # splits > 1], each area rounded up to 256 bytes
+    assert B.sda_workspace_bytes(256, 16, 1) == 2048
+    assert B.sda_workspace_bytes(1000, 16, 1) == 8192
+    assert B.sda_workspace_bytes(0, 16, 1) == 0
     n = 256 * 2 * 16 * 193 * 4
-    assert B.sda_workspace_bytes(256, 16, 2) == (n + 255) // 256 * 256
-    assert B.sda_workspace_bytes(3, 5, 7) == (3 * 7 * 5 * 193 * 4 + 255) // 256 * 256
+    assert B.sda_workspace_bytes(256, 16, 2) == 2048 + (n + 255) // 256 * 256
+    assert B.sda_workspace_bytes(3, 5, 7) == 256 + (3 * 7 * 5 * 193 * 4 + 255) // 256 * 256
     assert B.sda_workspace_bytes(-1, 16, 2) == 0
     assert B.sda_workspace_bytes(4, 17, 2) == 0
     assert B.sda_workspace_bytes(4, 16, 0) == 0
@@ -123,6 +127,14 @@ def test_workspace_checks():
                                         workspace_bytes=need - 1)) == B.SDA_ERR_WORKSPACE
     assert B.sda_decode_raw(_valid_args(splits=4, workspace=0x900004,
                                         workspace_bytes=need)) == B.SDA_ERR_WORKSPACE
+    # splits == 1: the workspace is optional, but one that is given must hold
+    # the row order and be aligned
+    need1 = B.sda_workspace_bytes(8, 16, 1)
+    assert need1 == 256
+    assert B.sda_decode_raw(_valid_args(splits=1, workspace=0x900000,
+                                        workspace_bytes=need1 - 1)) == B.SDA_ERR_WORKSPACE
+    assert B.sda_decode_raw(_valid_args(splits=1, workspace=0x900008,
+                                        workspace_bytes=need1)) == B.SDA_ERR_WORKSPACE
 
 
 def test_null_args_and_zero_rows():

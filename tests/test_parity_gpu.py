@@ -367,6 +367,43 @@ def test_large_grid_variant(kv, rt, splits):
     check_inactive_zero(out, inp)
 
 
+# --- heaviest-first row order (grids beyond the resident 512 workgroups) ------
+@pytest.mark.parametrize("kv,splits,strided,requests", [("bf16", 1, False, 192),
+                                                        ("fp8", 1, True, 192),
+                                                        ("bf16", 2, True, 97)])
+def test_row_order_matches_index_order(kv, splits, strided, requests):
+    # 1536 rows (a full and a half block of 1024; 776 rows with 2 splits) with
+    # 8..64 live regions per row, as in the multi-token workload: the grid
+    # takes 2 to 4 rounds of the 512 resident workgroups, so the order pass
+    # runs, and the result must be bit-identical to index order, with every
+    # row written.
+    w = gen.Workload("row-order", requests=requests, query_len=2, groups=4, heads=8, block=32,
+                     pages_per_req=64, R=64, kv=kv, pos_lo=1024, pos_hi=2046, live=(8, 64),
+                     inactive_frac=0.10, gated=True, splits=splits, seed=600 + splits)
+    assert 512 < w.rows * splits <= 2048
+    inp = gen.make_inputs(w, device=DEV)
+    regions = inp.regions
+    if strided:  # odd row stride: the order pass reads region ids one by one
+        wide = torch.full((w.rows, w.R + 1), -1, dtype=torch.int32, device=DEV)
+        wide[:, :w.R] = inp.regions
+        regions = wide[:, :w.R]
+    outs = []
+    for row_order in (True, False):
+        out = torch.full_like(inp.query, float("nan"))
+        _say("sda_decode row order=%s kv=%s splits=%d strided=%s" % (row_order, kv, splits,
+                                                                  strided))
+        B.sda_decode(inp.query, inp.cache, regions, inp.block_table, inp.positions, inp.active,
+                     out, scale=inp.scale, query_len=w.query_len, splits=splits,
+                     k_scale=inp.k_scale, v_scale=inp.v_scale, gate=inp.gate,
+                     row_order=row_order)
+        torch.cuda.synchronize()
+        assert torch.isfinite(out.float()).all(), "a row was not written"
+        outs.append(out)
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+    check_close(outs[0], oracle_out(inp), what="row order %s splits%d" % (kv, splits))
+    check_inactive_zero(outs[0], inp)
+
+
 # --- full-size workloads: sampled rows + properties ---------------------------
 @pytest.mark.parametrize("k", [2, 3, 4, 5, 6])
 def test_full_size_sampled(k):
