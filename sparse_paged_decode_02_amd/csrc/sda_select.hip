@@ -23,7 +23,8 @@
 //     its range in order with in-wave scans (no further barriers).
 // The bytes are the row's candidate scores (read once) and the output; the
 // work is LDS-atomic and scan bound for long rows, latency bound for short
-// ones.
+// ones.  The 1024-thread workgroup waits at each of its barriers, so beyond
+// one row per CU a second resident workgroup is what hides the waits.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -37,6 +38,7 @@ constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
 constexpr int kHistBins = 4096;
 constexpr int kCandCap = 4096;  // keys of the first pass's threshold bin kept in LDS
+constexpr int kComputeUnits = 256;
 
 // Keys that order like the floats: flip all bits of negatives, set the sign
 // bit of non-negatives.  -0.0 -> 0x7FFFFFFF < +0.0 -> 0x80000000.
@@ -82,8 +84,9 @@ __device__ __forceinline__ int mbcnt(uint64_t mask) {
 // [nb - per (l+1), nb - per l); a wave scan from the top finds the lane L
 // where the count reaches `need`; then lane l takes bin nb - per L - 1 - l
 // of L's range and a second scan finds the bin.  One barrier publishes the
-// result through s_pick.
-template <int NB>
+// result through s_pick.  kAllLoads: all of a lane's bins are read at once
+// (one LDS round trip, up to 64 VGPRs); otherwise 16 at a time.
+template <int NB, bool kAllLoads>
 __device__ __forceinline__ int find_digit(const int* hist, int need, int* s_pick, int wave,
                                           int lane, int& above) {
   static_assert(NB % 256 == 0 && NB <= 4096, "bins: a multiple of 256, at most 4096");
@@ -91,12 +94,21 @@ __device__ __forceinline__ int find_digit(const int* hist, int need, int* s_pick
   if (wave == 0) {
     constexpr int per = nb / 64;
     const int hi = nb - per * lane;  // exclusive top of this lane's bins
-    int4 v4[per / 4];
-#pragma unroll
-    for (int q = 0; q < per / 4; ++q) v4[q] = *reinterpret_cast<const int4*>(hist + hi - per + 4 * q);
     int local = 0;
+    if (kAllLoads) {
+      int4 v4[per / 4];
 #pragma unroll
-    for (int q = 0; q < per / 4; ++q) local += v4[q].x + v4[q].y + v4[q].z + v4[q].w;
+      for (int q = 0; q < per / 4; ++q)
+        v4[q] = *reinterpret_cast<const int4*>(hist + hi - per + 4 * q);
+#pragma unroll
+      for (int q = 0; q < per / 4; ++q) local += v4[q].x + v4[q].y + v4[q].z + v4[q].w;
+    } else {
+#pragma unroll 4
+      for (int q = 0; q < per / 4; ++q) {
+        const int4 v = *reinterpret_cast<const int4*>(hist + hi - per + 4 * q);
+        local += v.x + v.y + v.z + v.w;
+      }
+    }
     int total;
     const int excl = wave_exclusive_scan(local, lane, total);
     const uint64_t m1 = __ballot(excl < need && need <= excl + local);
@@ -118,8 +130,14 @@ __device__ __forceinline__ int find_digit(const int* hist, int need, int* s_pick
   return s_pick[0];
 }
 
-template <int I>
-__global__ __launch_bounds__(kSelThreads) void select_kernel(const SelParams p) {
+// kShared: up to 16 keys per lane the kernel fits 64 VGPRs, so two
+// workgroups share a CU (8 waves per SIMD).  Otherwise (one workgroup per
+// CU: few rows, or 32 keys per lane) registers buy latency instead.
+template <int I, bool kShared>
+__global__ __launch_bounds__(kSelThreads) __attribute__((amdgpu_waves_per_eu(kShared ? 8 : 4)))
+void select_kernel(const SelParams p) {
+  static_assert(!kShared || I <= 4, "32 keys per lane do not fit 64 VGPRs");
+  constexpr bool kAllLoads = !kShared && I <= 4;  // find_digit's bins in one round trip
   constexpr int K4 = 4 * I;  // keys per lane
   const int r = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -191,7 +209,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const SelParams p) 
       atomicAdd(&hist[key[k] != 0u ? (int)(key[k] >> 20) : kHistBins + lane], 1);
     __syncthreads();
     int above;
-    const int d1 = find_digit<kHistBins>(hist, need0, s_pick, wave, lane, above);
+    const int d1 = find_digit<kHistBins, kAllLoads>(hist, need0, s_pick, wave, lane, above);
     int need = need0 - above;
     uint32_t prefix = (uint32_t)d1 << 20, pmask = 0xFFF00000u;
     const int inbin = hist[d1];
@@ -238,8 +256,9 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const SelParams p) 
             atomicAdd(&hist[(key[k] >> shift) & dmask], 1);
       }
       __syncthreads();
-      const int d = pass == 2 ? find_digit<256>(hist, need, s_pick, wave, lane, above)
-                              : find_digit<kHistBins>(hist, need, s_pick, wave, lane, above);
+      const int d = pass == 2 ? find_digit<256, kAllLoads>(hist, need, s_pick, wave, lane, above)
+                              : find_digit<kHistBins, kAllLoads>(hist, need, s_pick, wave, lane,
+                                                                above);
       need -= above;
       prefix |= (uint32_t)d << shift;
       pmask |= dmask << shift;
@@ -343,9 +362,15 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const SelParams p) 
   for (int s = total + tid; s < p.topk; s += kSelThreads) o[s] = -1;
 }
 
+// Rows beyond one per CU run two workgroups per CU where the keys fit.
 template <int I>
 void launch_select(const SelParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL(select_kernel<I>, dim3((unsigned)p.rows), dim3(kSelThreads), 0, stream, p);
+  if (I <= 4 && p.rows > kComputeUnits)
+    hipLaunchKernelGGL((select_kernel<I, I <= 4>), dim3((unsigned)p.rows), dim3(kSelThreads), 0,
+                       stream, p);
+  else
+    hipLaunchKernelGGL((select_kernel<I, false>), dim3((unsigned)p.rows), dim3(kSelThreads), 0,
+                       stream, p);
 }
 
 }  // namespace

@@ -67,6 +67,21 @@ def test_sizes_and_distributions(S, dist):
         run_and_check(s, cur, topk, lens, label="S%d %s k%d" % (S, dist, topk))
 
 
+@pytest.mark.parametrize("S", [1000, 5000, 12000])
+@pytest.mark.parametrize("dist", ["normal", "ties", "range"])
+def test_two_workgroups_per_cu(S, dist):
+    # More rows than CUs: the variant that keeps 16 keys per lane within 64
+    # VGPRs (two workgroups per CU) for 4, 8 and 16 keys per lane.
+    rows = 300
+    rng = np.random.default_rng(S + 7)
+    s = _case(S + 3 * len(dist), rows, S, dist)
+    lens = torch.from_numpy(rng.integers(0, S + 2, size=rows).astype(np.int32))
+    cur = torch.from_numpy(np.array([rng.integers(-1, max(int(n), 1) + 1) for n in lens],
+                                    np.int32))
+    for topk in (64, 512):
+        run_and_check(s, cur, topk, lens, label="rows300 S%d %s k%d" % (S, dist, topk))
+
+
 def test_no_lengths_all_columns():
     s = _case(3, 32, 3000, "normal")
     cur = torch.arange(32, dtype=torch.int32) * 90
