@@ -56,6 +56,26 @@ def test_decode_in_graph(splits):
     replay_and_compare(fn, [out], "decode splits=%d" % splits)
 
 
+def test_decode_with_row_order_in_graph():
+    # 1024 rows with 8..64 live regions: the grid takes 2 resident rounds, so
+    # the bin and order kernels run before the split kernel, through the
+    # workspace, inside the graph too.
+    w = gen.Workload("graph-order", requests=128, query_len=2, groups=4, heads=8, block=32,
+                     pages_per_req=16, R=16, kv="bf16", pos_lo=200, pos_hi=510, live=(2, 16),
+                     inactive_frac=0.10, gated=True, splits=1, seed=9)
+    assert 512 < w.rows <= 2048
+    inp = gen.make_inputs(w, device=DEV)
+    out = torch.empty_like(inp.query)
+    ws = torch.empty(B.sda_workspace_bytes(w.rows, w.heads, 1), dtype=torch.uint8, device=DEV)
+
+    def fn():
+        B.sda_decode(inp.query, inp.cache, inp.regions, inp.block_table, inp.positions,
+                     inp.active, out, scale=inp.scale, query_len=w.query_len, splits=1,
+                     gate=inp.gate, workspace=ws)
+
+    replay_and_compare(fn, [out], "decode with row order")
+
+
 def test_swa_in_graph():
     w = gen.SwaWorkload("graph-swa", requests=4, query_len=2, groups=2, heads=4, block=64,
                         pages_per_req=8, window=100, seq_lo=2, seq_hi=512, seed=3)
