@@ -14,7 +14,9 @@
  *
  * All pointers in sda_decode_args are DEVICE pointers unless noted.  The
  * caller owns every buffer, including the workspace.  The library allocates
- * nothing and keeps no state, so every entry point is re-entrant.  sda_decode
+ * nothing and keeps no state, so every entry point is re-entrant; calls that
+ * may overlap (other streams, other threads) need workspaces of their own,
+ * since each call rewrites its workspace.  sda_decode
  * validates on the host and never reads device memory there; index contents
  * (region ids, block-table entries, positions) are trusted, as on the page.
  * On any error it returns before launching anything.
@@ -42,7 +44,7 @@ typedef enum {
   SDA_OK = 0,
   SDA_ERR_INVALID = -1,      /* an argument breaks the operation's contract */
   SDA_ERR_UNSUPPORTED = -2,  /* legal, but outside what this build handles */
-  SDA_ERR_WORKSPACE = -3,    /* workspace missing or too small for splits > 1 */
+  SDA_ERR_WORKSPACE = -3,    /* workspace missing (splits > 1), too small or misaligned */
   SDA_ERR_LAUNCH = -4        /* the HIP launch reported an error */
 } sda_status;
 

@@ -74,7 +74,7 @@ const char* sda_status_string(int status) {
     case SDA_OK: return "ok";
     case SDA_ERR_INVALID: return "invalid argument";
     case SDA_ERR_UNSUPPORTED: return "unsupported argument (alignment, stride or size limit)";
-    case SDA_ERR_WORKSPACE: return "workspace missing or too small";
+    case SDA_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
     case SDA_ERR_LAUNCH: return "kernel launch failed";
     default: return "unknown status";
   }

@@ -15,7 +15,8 @@
 //  * Setup: the columns' queries are converted exactly to bf16 (e4m3 is a
 //    subset of bf16) into LDS, with their weights; each row's region count.
 //  * Each wave takes 16-region tiles round-robin: lane (i, g) loads bytes
-//    [64g, 64g+64) of region i's summary (16-byte loads), converts them to
+//    [64c + 16g, +16), c = 0..3, of region i's summary (16-byte loads: each
+//    instruction reads 64 contiguous bytes of 16 regions), converts them to
 //    bf16, and for every 16-column tile runs 8 v_mfma_f32_16x16x32_bf16 with
 //    the query columns (the same 64 dims per lane on both sides, so the dim
 //    order inside the MFMA is immaterial).  Products are exact, sums fp32.
@@ -91,6 +92,24 @@ __global__ __launch_bounds__(kLgThreads) void logits_kernel(const LogitsParams p
   const int ncols = rpr * p.heads;
   const int ntiles = (ncols + 15) / 16;
 
+  // Loads that depend on nothing else go first: the positions, the query
+  // columns (entry = thread: column tile tid >> 6, lane tid & 63) and the
+  // head weights.
+  static_assert(kLgThreads == (kLgMaxCols / 16) * 64, "one query entry per thread");
+  const int qt = tid >> 6, ql = tid & 63;
+  const int qcol = 16 * qt + (ql & 15);
+  u32x4 qraw[4] = {};
+  if (qt < ntiles && qcol < ncols) {
+    const int row = r0 + (qcol >> p.hshift);
+    const int h = qcol & (p.heads - 1);
+    const uint8_t* src = p.q + (int64_t)row * p.qrs + (int64_t)h * p.qhs + 16 * (ql >> 4);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) qraw[c] = *reinterpret_cast<const u32x4*>(src + 64 * c);
+  }
+  static_assert(kLgMaxCols <= kLgThreads, "one weight per thread");
+  float wv = 0.f;
+  if (tid < ncols) wv = p.w[(int64_t)(r0 + (tid >> p.hshift)) * p.wrs + (tid & (p.heads - 1))];
+
   // Region count of each row (lane t < rpr: row t), the request's maximum
   // (every wave reduces it itself), and once the current / length outputs.
   int lenv = 0;
@@ -120,27 +139,34 @@ __global__ __launch_bounds__(kLgThreads) void logits_kernel(const LogitsParams p
   const int jl = j_begin + kLgTile * wave + kLgTile * kLgWaves * (lane >> 4) + (lane & 15);
   int64_t pg = 0;
   if (jl < j_live) pg = p.table[(int64_t)req * p.trs + jl / p.rpb];
-  // Query columns (entry = thread: column tile tid >> 6, lane tid & 63),
-  // loaded while the table lookups are in flight, converted to bf16 in the
-  // lane order of the MFMA B operand: entry (tile, lane) holds column
-  // 16 tile + (lane & 15), dims [64 (lane >> 4), +64).
-  static_assert(kLgThreads == (kLgMaxCols / 16) * 64, "one query entry per thread");
-  const int qt = tid >> 6, ql = tid & 63;
-  const int qcol = 16 * qt + (ql & 15);
-  u32x4 qraw[4] = {};
-  if (qt < ntiles && qcol < ncols) {
-    const int row = r0 + (qcol >> p.hshift);
-    const int h = qcol & (p.heads - 1);
-    const uint8_t* src = p.q + (int64_t)row * p.qrs + (int64_t)h * p.qhs + 64 * (ql >> 4);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) qraw[c] = *reinterpret_cast<const u32x4*>(src + 16 * c);
-  }
   int64_t roff_l = 0;
   float scale_l = 0.f;
   if (jl < j_live) {
     roff_l = pg * p.sps + (int64_t)(jl % p.rpb) * p.sms;
     scale_l = p.sc[pg * p.scps + jl % p.rpb];
   }
+  // A operand of tile t: region j0 + i16 (a region past j_live is masked;
+  // its lane borrows the tile's first region, always live), bytes
+  // [64 c + 16 g4, +16) for c = 0..3, so that each load instruction reads
+  // 64 contiguous bytes of each of the 16 regions.
+  auto load_tile = [&](int t, u32x4 (&raw)[4]) {
+    const int src = kLgTile * t + i16;
+    const int j = j_begin + kLgTile * wave + kLgTile * kLgWaves * t + i16;
+    const int64_t off = __shfl(roff_l, j < j_live ? src : kLgTile * t);
+    const uint8_t* a = p.sm + off + 16 * g4;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) raw[c] = *reinterpret_cast<const u32x4*>(a + 64 * c);
+  };
+  const int nt = (j_live - (j_begin + kLgTile * wave) + kLgTile * kLgWaves - 1) /
+                 (kLgTile * kLgWaves);  // live tiles of this wave (<= 4)
+  // The first tile's summaries are requested before the query conversion
+  // and the barrier, as soon as their offsets are known.
+  u32x4 raw[4];
+  if (nt > 0) load_tile(0, raw);
+
+  // Query columns converted to bf16 in the lane order of the MFMA B
+  // operand: entry (tile, lane) holds column 16 tile + (lane & 15), dims
+  // [64 c + 16 (lane >> 4), +16) for c = 0..3, the dims its A lanes hold.
   if (qt < ntiles) {
     __bf16* dst = &s_q[qt][ql][0];
 #pragma unroll
@@ -151,8 +177,7 @@ __global__ __launch_bounds__(kLgThreads) void logits_kernel(const LogitsParams p
       *reinterpret_cast<bf16x8*>(dst + 16 * c + 8) = hi;
     }
   }
-  for (int c = tid; c < kLgMaxCols; c += kLgThreads)
-    s_w[c] = c < ncols ? p.w[(int64_t)(r0 + (c >> p.hshift)) * p.wrs + (c & (p.heads - 1))] : 0.f;
+  if (tid < kLgMaxCols) s_w[tid] = wv;
   __syncthreads();
 
   // Tiles at or past the request's last region: -inf, and no summary read.
@@ -163,21 +188,7 @@ __global__ __launch_bounds__(kLgThreads) void logits_kernel(const LogitsParams p
       if (j < p.S) p.out[(int64_t)(r0 + row) * p.ors + j] = -INFINITY;
     }
   }
-  // A operand of tile t: region j0 + i16 (a region past j_live is masked;
-  // its lane borrows the tile's first region, always live), bytes [64 g4, +64).
-  auto load_tile = [&](int t, u32x4 (&raw)[4]) {
-    const int src = kLgTile * t + i16;
-    const int j = j_begin + kLgTile * wave + kLgTile * kLgWaves * t + i16;
-    const int64_t off = __shfl(roff_l, j < j_live ? src : kLgTile * t);
-    const uint8_t* a = p.sm + off + 64 * g4;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) raw[c] = *reinterpret_cast<const u32x4*>(a + 16 * c);
-  };
-  const int nt = (j_live - (j_begin + kLgTile * wave) + kLgTile * kLgWaves - 1) /
-                 (kLgTile * kLgWaves);  // live tiles of this wave (<= 4)
   if (nt > 0) {
-    u32x4 raw[4];
-    load_tile(0, raw);
     for (int t = 0; t < nt; ++t) {
       const int j0 = j_begin + kLgTile * wave + kLgTile * kLgWaves * t;
       bf16x8 a[8];
