@@ -47,29 +47,47 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
 
-// Exclusive scan of v over the 64 lanes of a wave; `total` gets the sum.
-__device__ __forceinline__ int wave_exclusive_scan(int v, int lane, int& total) {
-  int x = v;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int u = __shfl_up(x, d);
-    if (lane >= d) x += u;
-  }
-  total = __shfl(x, 63);
-  return x - v;
+// x plus lane (i - shift) of the same 16-lane row (0 where that lane is
+// outside the row), or with the row-broadcast controls, plus lane 15 (31) of
+// the previous row(s) in the rows that kRowMask selects.  DPP: a register
+// move between lanes, with no LDS traffic.
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ int dpp_add(int x) {
+  return x + __builtin_amdgcn_update_dpp(0, x, kCtrl, kRowMask, 0xF, false);
 }
 
-// Sum of v over the 64 lanes of a wave (every lane gets it).
-__device__ __forceinline__ int wave_sum(int v, int lane) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d);
+// Inclusive scan of v over the 64 lanes of a wave: shifts by 1, 2, 4 and 8
+// within each row of 16, then row 0's total into row 1 and row 2's into row
+// 3 (row broadcast of lane 15), then lane 31's sum into rows 2 and 3.
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  v = dpp_add<0x111, 0xF>(v);  // row_shr:1
+  v = dpp_add<0x112, 0xF>(v);  // row_shr:2
+  v = dpp_add<0x114, 0xF>(v);  // row_shr:4
+  v = dpp_add<0x118, 0xF>(v);  // row_shr:8
+  v = dpp_add<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  v = dpp_add<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
   return v;
 }
 
-// Sum of cnt[w][f] over waves w < upto (upto <= 16), every lane gets it:
-// lane w reads wave w's entry, one wave reduction.
-__device__ __forceinline__ int wave_prefix_of(const int (*cnt)[2], int f, int upto, int lane) {
-  return wave_sum(lane < upto ? cnt[lane][f] : 0, lane);
+// Exclusive scan of v over the 64 lanes of a wave; `total` gets the sum.
+__device__ __forceinline__ int wave_exclusive_scan(int v, int& total) {
+  const int x = wave_inclusive_scan(v);
+  total = __builtin_amdgcn_readlane(x, 63);
+  return x - v;
+}
+
+// Sum of v over the 64 lanes of a wave (uniform).
+__device__ __forceinline__ int wave_sum(int v) {
+  return __builtin_amdgcn_readlane(wave_inclusive_scan(v), 63);
+}
+
+// Sums of the 16 per-wave counts cnt[0..15] over waves < upto (uniform) and
+// over all: lane w reads wave w's count, one scan, two lane reads.
+__device__ __forceinline__ void wave_counts(const int* cnt, int upto, int lane, int& before,
+                                            int& all) {
+  const int x = wave_inclusive_scan(lane < kSelWaves ? cnt[lane] : 0);
+  all = __builtin_amdgcn_readlane(x, kSelWaves - 1);
+  before = upto > 0 ? __builtin_amdgcn_readlane(x, upto - 1) : 0;
 }
 
 // Lanes below this one whose bit is set in mask.
@@ -110,14 +128,14 @@ __device__ __forceinline__ int find_digit(const int* hist, int need, int* s_pick
       }
     }
     int total;
-    const int excl = wave_exclusive_scan(local, lane, total);
+    const int excl = wave_exclusive_scan(local, total);
     const uint64_t m1 = __ballot(excl < need && need <= excl + local);
     const int L = (int)__builtin_ctzll(m1);
     const int base = __shfl(excl, L);
     const int top = nb - per * L - 1;  // L's highest bin
     const int v = lane < per ? hist[top - lane] : 0;
     int tot2;
-    const int ex2 = base + wave_exclusive_scan(v, lane, tot2);
+    const int ex2 = base + wave_exclusive_scan(v, tot2);
     const uint64_t m2 = __ballot(lane < per && ex2 < need && need <= ex2 + v);
     const int L2 = (int)__builtin_ctzll(m2);
     if (lane == L2) {
@@ -145,7 +163,7 @@ void select_kernel(const SelParams p) {
   // (one per lane, so they never contend), which keeps that pass branch-free.
   __shared__ __attribute__((aligned(16))) int hist[kHistBins + 64];
   __shared__ int s_pick[2];
-  __shared__ int s_cnt[kSelWaves][2];  // per wave: taken outright, eq
+  __shared__ int s_cnt[2][kSelWaves];  // [taken outright | eq][wave]
   __shared__ uint32_t s_ckey[kCandCap];
 
   int n = p.lengths ? p.lengths[r] : p.S;
@@ -223,10 +241,12 @@ void select_kernel(const SelParams p) {
       for (int k = 0; k < K4; ++k)
         cbits |= (key[k] != 0u && (key[k] >> 20) == (uint32_t)d1 ? 1u : 0u) << k;
       int cw;
-      int off = wave_exclusive_scan(__popc(cbits), lane, cw);
-      if (lane == 0) s_cnt[wave][0] = cw;
+      int off = wave_exclusive_scan(__popc(cbits), cw);
+      if (lane == 0) s_cnt[0][wave] = cw;
       __syncthreads();
-      off += wave_prefix_of(s_cnt, 0, wave, lane);
+      int before, all;
+      wave_counts(s_cnt[0], wave, lane, before, all);
+      off += before;
       while (cbits) {  // a lane has ~0.1-1 candidates: order within the list is free
         const int k = __builtin_ctz(cbits);
         cbits &= cbits - 1u;
@@ -287,17 +307,16 @@ void select_kernel(const SelParams p) {
       tbits |= (gtf_of(4 * i + c, id0 + 256 * i + c) ? 1u : 0u) << (4 * i + c);
       if (ties) ebits |= (eq_of(4 * i + c) ? 1u : 0u) << (4 * i + c);
     }
-  const int g_wave = wave_sum(__popc(tbits), lane);
-  const int e_wave = ties ? wave_sum(__popc(ebits), lane) : 0;
+  const int g_wave = wave_sum(__popc(tbits));
+  const int e_wave = ties ? wave_sum(__popc(ebits)) : 0;
   if (lane == 0) {
-    s_cnt[wave][0] = g_wave;
-    s_cnt[wave][1] = e_wave;
+    s_cnt[0][wave] = g_wave;
+    s_cnt[1][wave] = e_wave;
   }
   __syncthreads();
-  const int g_prev = wave_prefix_of(s_cnt, 0, wave, lane);
-  const int e_prev = ties ? wave_prefix_of(s_cnt, 1, wave, lane) : 0;
-  const int g_all = wave_prefix_of(s_cnt, 0, kSelWaves, lane);
-  int e_all = ties ? wave_prefix_of(s_cnt, 1, kSelWaves, lane) : 0;
+  int g_prev, g_all, e_prev = 0, e_all = 0;
+  wave_counts(s_cnt[0], wave, lane, g_prev, g_all);
+  if (ties) wave_counts(s_cnt[1], wave, lane, e_prev, e_all);
   if (!ties) need_eq = 0;
   // output slot of the wave's first selection; eq keys still to take there
   int run = g_prev + min(need_eq, e_prev);

@@ -368,18 +368,20 @@ def test_large_grid_variant(kv, rt, splits):
 
 
 # --- heaviest-first row order (grids beyond the resident 512 workgroups) ------
-@pytest.mark.parametrize("kv,splits,strided,requests", [("bf16", 1, False, 192),
-                                                        ("fp8", 1, True, 192),
-                                                        ("bf16", 2, True, 97)])
-def test_row_order_matches_index_order(kv, splits, strided, requests):
-    # 1536 rows (a full and a half block of 1024; 776 rows with 2 splits) with
-    # 8..64 live regions per row, as in the multi-token workload: the grid
+@pytest.mark.parametrize("kv,splits,strided,requests,R", [("bf16", 1, False, 192, 64),
+                                                          ("fp8", 1, True, 192, 64),
+                                                          ("bf16", 2, True, 97, 64),
+                                                          ("bf16", 1, True, 96, 130)])
+def test_row_order_matches_index_order(kv, splits, strided, requests, R):
+    # 1536 rows (a full and a half block of 1024; 776 rows with 2 splits; 768
+    # rows with 130 region slots, three 64-slot passes of the bin kernel) with
+    # 8..R live regions per row, as in the multi-token workload: the grid
     # takes 2 to 4 rounds of the 512 resident workgroups, so the order pass
     # runs, and the result must be bit-identical to index order, with every
     # row written.
-    w = gen.Workload("row-order", requests=requests, query_len=2, groups=4, heads=8, block=32,
-                     pages_per_req=64, R=64, kv=kv, pos_lo=1024, pos_hi=2046, live=(8, 64),
-                     inactive_frac=0.10, gated=True, splits=splits, seed=600 + splits)
+    w = gen.Workload("row-order", requests=requests, query_len=2, groups=4, heads=8, block=16,
+                     pages_per_req=128, R=R, kv=kv, pos_lo=1024, pos_hi=2046, live=(8, R),
+                     inactive_frac=0.10, gated=True, splits=splits, seed=600 + splits + R)
     assert 512 < w.rows * splits <= 2048
     inp = gen.make_inputs(w, device=DEV)
     regions = inp.regions
