@@ -54,6 +54,7 @@
 #include <utility>
 
 #include "sda_launch.h"
+#include "sda_wave.h"
 
 #define SDA_LDS __attribute__((address_space(3)))
 
@@ -993,21 +994,11 @@ __global__ __launch_bounds__(kOrderBlock) void order_kernel(Params p, const int3
   // Exclusive scan of s_cnt in (bin, wave) order: the first slot of each
   // wave's rows of each bin.
   const int own = t < kOrderBins * kOrderWaves ? s_cnt[t] : 0;
-  int v = own;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int n = __shfl_up(v, d, 64);
-    if (lane >= d) v += n;
-  }
+  const int v = wave_inclusive_scan(own);
   if (lane == 63) s_wave[wave] = v;
   __syncthreads();
   if (wave == 0) {
-    int w = lane < kOrderWaves ? s_wave[lane] : 0;
-#pragma unroll
-    for (int d = 1; d < kOrderWaves; d <<= 1) {
-      const int n = __shfl_up(w, d, 64);
-      if (lane >= d) w += n;
-    }
+    const int w = wave_inclusive_scan(lane < kOrderWaves ? s_wave[lane] : 0);
     if (lane < kOrderWaves) s_wave[lane] = w;
   }
   __syncthreads();

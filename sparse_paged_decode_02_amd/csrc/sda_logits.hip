@@ -30,6 +30,7 @@
 #include <stdint.h>
 
 #include "sda_launch.h"
+#include "sda_wave.h"
 
 namespace sda {
 namespace {
@@ -62,7 +63,7 @@ __device__ __forceinline__ void e4m3x16_to_bf16(const u32x4 w, bf16x8& lo, bf16x
 
 // x plus the value of another lane, moved by DPP (no LDS traffic).
 template <int kCtrl>
-__device__ __forceinline__ float dpp_add(float x) {
+__device__ __forceinline__ float dpp_fadd(float x) {
   const int y = __builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, 0xF, 0xF, false);
   return x + __int_as_float(y);
 }
@@ -71,10 +72,10 @@ __device__ __forceinline__ float dpp_add(float x) {
 // row of 16: quad permutes for the first two steps, then the half-row and
 // row mirrors (each pairs every lane with one of the other half).
 __device__ __forceinline__ float group_sum(float x, int n) {
-  if (n >= 2) x = dpp_add<0xB1>(x);   // quad_perm [1,0,3,2]
-  if (n >= 4) x = dpp_add<0x4E>(x);   // quad_perm [2,3,0,1]
-  if (n >= 8) x = dpp_add<0x141>(x);  // row_half_mirror
-  if (n >= 16) x = dpp_add<0x140>(x); // row_mirror
+  if (n >= 2) x = dpp_fadd<0xB1>(x);   // quad_perm [1,0,3,2]
+  if (n >= 4) x = dpp_fadd<0x4E>(x);   // quad_perm [2,3,0,1]
+  if (n >= 8) x = dpp_fadd<0x141>(x);  // row_half_mirror
+  if (n >= 16) x = dpp_fadd<0x140>(x); // row_mirror
   return x;
 }
 
@@ -125,9 +126,7 @@ __global__ __launch_bounds__(kLgThreads) void logits_kernel(const LogitsParams p
       }
     }
   }
-  int max_len = lenv;
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) max_len = max(max_len, __shfl_xor(max_len, d));
+  const int max_len = wave_max(lenv);
 
   const int j_begin = chunk * kLgChunk;
   const int j_end = min(p.S, j_begin + kLgChunk);

@@ -30,6 +30,7 @@
 #include <stdint.h>
 
 #include "sda_launch.h"
+#include "sda_wave.h"
 
 namespace sda {
 namespace {
@@ -45,40 +46,6 @@ constexpr int kComputeUnits = 256;
 __device__ __forceinline__ uint32_t order_key(float f) {
   const uint32_t u = __float_as_uint(f);
   return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
-}
-
-// x plus lane (i - shift) of the same 16-lane row (0 where that lane is
-// outside the row), or with the row-broadcast controls, plus lane 15 (31) of
-// the previous row(s) in the rows that kRowMask selects.  DPP: a register
-// move between lanes, with no LDS traffic.
-template <int kCtrl, int kRowMask>
-__device__ __forceinline__ int dpp_add(int x) {
-  return x + __builtin_amdgcn_update_dpp(0, x, kCtrl, kRowMask, 0xF, false);
-}
-
-// Inclusive scan of v over the 64 lanes of a wave: shifts by 1, 2, 4 and 8
-// within each row of 16, then row 0's total into row 1 and row 2's into row
-// 3 (row broadcast of lane 15), then lane 31's sum into rows 2 and 3.
-__device__ __forceinline__ int wave_inclusive_scan(int v) {
-  v = dpp_add<0x111, 0xF>(v);  // row_shr:1
-  v = dpp_add<0x112, 0xF>(v);  // row_shr:2
-  v = dpp_add<0x114, 0xF>(v);  // row_shr:4
-  v = dpp_add<0x118, 0xF>(v);  // row_shr:8
-  v = dpp_add<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
-  v = dpp_add<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
-  return v;
-}
-
-// Exclusive scan of v over the 64 lanes of a wave; `total` gets the sum.
-__device__ __forceinline__ int wave_exclusive_scan(int v, int& total) {
-  const int x = wave_inclusive_scan(v);
-  total = __builtin_amdgcn_readlane(x, 63);
-  return x - v;
-}
-
-// Sum of v over the 64 lanes of a wave (uniform).
-__device__ __forceinline__ int wave_sum(int v) {
-  return __builtin_amdgcn_readlane(wave_inclusive_scan(v), 63);
 }
 
 // Sums of the 16 per-wave counts cnt[0..15] over waves < upto (uniform) and
