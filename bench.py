@@ -521,9 +521,9 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(rows shard across GPUs with no exchange; see DESIGN.md). Run with --gpus 1.",
-              file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path (rows "
+              "are independent and would shard across GPUs with no exchange). Run with "
+              "--gpus 1.", file=sys.stderr)
         return 2
 
     import torch

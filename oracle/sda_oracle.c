@@ -14,7 +14,7 @@
  *   [P3] "vllm.models.step5.nvidia.flashinfer_sparse":
  *        `select_and_run_decode_attention`, `_direct_sparse_decode`.
  *
- * Readings taken where the pages are silent (each is listed in the design doc):
+ * Readings taken where the pages are silent:
  *   - region r covers tokens [r*rt, r*rt + rt) with rt = region_tokens
  *     (0 means one region per page, rt = block);
  *   - the causal mask is inclusive: token t is visible iff t <= position;
