@@ -213,7 +213,7 @@ def run_swa(args, dev) -> int:
     from sparse_paged_decode_02_amd import binding as B
     from sparse_paged_decode_02_amd import inputs as gen
 
-    w = gen.SWA_CONFIGS[args.swa]
+    w = gen.SWA_WORKLOADS[args.swa]
     pack, plan_splits = B.sda_swa_plan(w.tokens, w.groups, w.heads, w.query_len, w.window)
     pack = args.pack or pack
     splits = args.splits or w.splits or plan_splits
@@ -337,7 +337,7 @@ def run_logits(args, dev) -> int:
     from sparse_paged_decode_02_amd import binding as B
     from sparse_paged_decode_02_amd import inputs as gen
 
-    w = gen.LOGITS_CONFIGS[args.logits]
+    w = gen.LOGITS_WORKLOADS[args.logits]
     desc = ("%s: %d rows = %d req x qlen %d x G %d, %d e4m3 heads x 256, %d regions of %d "
             "tokens (%d per page), positions U[%d,%d]"
             % (w.name, w.rows, w.requests, w.query_len, w.groups, w.heads, w.num_regions,
@@ -387,7 +387,7 @@ def run_select(args, dev) -> int:
     from sparse_paged_decode_02_amd import binding as B
     from sparse_paged_decode_02_amd import inputs as gen
 
-    w = gen.SELECT_CONFIGS[args.select]
+    w = gen.SELECT_WORKLOADS[args.select]
     desc = ("%s: %d rows, %d score columns (%d-token regions), topk %d, positions U[%d,%d]"
             % (w.name, w.rows, w.num_regions, w.region_tokens, w.topk, w.pos_lo, w.pos_hi))
     print("[bench] drawing %s" % desc, file=sys.stderr, flush=True)
@@ -552,7 +552,7 @@ def main() -> int:
         return run_select(args, dev)
     if args.logits:
         return run_logits(args, dev)
-    w = gen.CONFIGS[args.config]
+    w = gen.WORKLOADS[args.config]
     splits = args.splits or w.splits or B.sda_splits(w.rows)
 
     print("[bench] drawing %s" % workload_desc(w), file=sys.stderr, flush=True)

@@ -43,7 +43,7 @@ extern "C" {
 typedef enum {
   SDA_OK = 0,
   SDA_ERR_INVALID = -1,      /* an argument breaks the operation's contract */
-  SDA_ERR_UNSUPPORTED = -2,  /* legal, but outside what this build handles */
+  SDA_ERR_UNSUPPORTED = -2,  /* legal, but outside what the library handles */
   SDA_ERR_WORKSPACE = -3,    /* workspace missing (splits > 1), too small or misaligned */
   SDA_ERR_LAUNCH = -4        /* the HIP launch reported an error */
 } sda_status;

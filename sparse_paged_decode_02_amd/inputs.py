@@ -69,34 +69,34 @@ class Workload:
         return 1.0 / math.sqrt(HEAD_DIM)
 
 
-def config_seed(k: int) -> int:
+def workload_seed(k: int) -> int:
     return 1000 * k + 7
 
 
 # The five decode workloads (1-based numbering), and one at 8-token regions.
-CONFIGS = {
+WORKLOADS = {
     1: Workload("tiny-bf16", requests=4, query_len=1, groups=1, heads=8, block=16,
                 pages_per_req=16, R=8, kv="bf16", pos_lo=1, pos_hi=127,
-                live=None, inactive_rows=(3,), gated=False, splits=1, seed=config_seed(1)),
+                live=None, inactive_rows=(3,), gated=False, splits=1, seed=workload_seed(1)),
     2: Workload("bf16-gated", requests=64, query_len=1, groups=4, heads=16, block=64,
                 pages_per_req=512, R=32, kv="bf16", pos_lo=4096, pos_hi=32767,
-                inactive_frac=0.05, gated=True, splits=None, seed=config_seed(2)),
+                inactive_frac=0.05, gated=True, splits=None, seed=workload_seed(2)),
     3: Workload("fp8-cache", requests=256, query_len=1, groups=2, heads=16, block=64,
                 pages_per_req=2048, R=64, kv="fp8", pos_lo=65536, pos_hi=131071,
-                gated=False, splits=None, seed=config_seed(3)),
+                gated=False, splits=None, seed=workload_seed(3)),
     4: Workload("multi-token", requests=128, query_len=2, groups=4, heads=8, block=32,
                 pages_per_req=512, R=64, kv="bf16", pos_lo=8192, pos_hi=16382,
                 live=(8, 64), inactive_frac=0.10, gated=True, splits=None,
-                seed=config_seed(4)),
+                seed=workload_seed(4)),
     5: Workload("large-batch-fp8", requests=1024, query_len=1, groups=4, heads=16, block=64,
                 pages_per_req=256, R=32, kv="fp8", pos_lo=8192, pos_hi=16383,
-                gated=True, splits=1, seed=config_seed(5)),
+                gated=True, splits=1, seed=workload_seed(5)),
     # The pages' own region granularity (8 tokens, many regions per page) at the
     # bf16-gated shape: 256 slots of 8 tokens = the same 2048 tokens per row.
     6: Workload("bf16-gated-8tok", requests=64, query_len=1, groups=4, heads=16, block=64,
                 pages_per_req=512, R=256, kv="bf16", pos_lo=4096, pos_hi=32767,
                 inactive_frac=0.05, gated=True, splits=None, region_tokens=8,
-                seed=config_seed(6)),
+                seed=workload_seed(6)),
 }
 
 
@@ -264,15 +264,15 @@ class SwaWorkload:
         return 1.0 / math.sqrt(HEAD_DIM)
 
 
-SWA_CONFIGS = {
+SWA_WORKLOADS = {
     # decode, 16 heads per KV group, full 1024-token windows in 8K contexts
     "swa-gated": SwaWorkload("swa-gated", requests=256, query_len=1, groups=4, heads=16,
                              block=64, pages_per_req=128, window=1024, seq_lo=1024,
-                             seq_hi=8192, seed=config_seed(11)),
+                             seq_hi=8192, seed=workload_seed(11)),
     # MTP verify: 4 query tokens per request, 4 heads per KV group
     "swa-mtp": SwaWorkload("swa-mtp", requests=128, query_len=4, groups=4, heads=4,
                            block=64, pages_per_req=128, window=1024, seq_lo=4,
-                           seq_hi=8192, seed=config_seed(12)),
+                           seq_hi=8192, seed=workload_seed(12)),
 }
 
 
@@ -336,13 +336,13 @@ class SelectWorkload:
     seed: int = 0
 
 
-SELECT_CONFIGS = {
+SELECT_WORKLOADS = {
     # the bf16-gated decode batch (64 requests x G 4) over 32K contexts
     "select-decode": SelectWorkload("select-decode", rows=256, num_regions=4096, topk=512,
-                                    pos_lo=4096, pos_hi=32767, seed=config_seed(21)),
+                                    pos_lo=4096, pos_hi=32767, seed=workload_seed(21)),
     # the large batch (1024 requests x G 4) over 128K contexts
     "select-large": SelectWorkload("select-large", rows=4096, num_regions=16384, topk=512,
-                                   pos_lo=65536, pos_hi=131071, seed=config_seed(22)),
+                                   pos_lo=65536, pos_hi=131071, seed=workload_seed(22)),
 }
 
 
@@ -411,15 +411,15 @@ class LogitsWorkload:
         return self.requests * self.pages_per_req
 
 
-LOGITS_CONFIGS = {
+LOGITS_WORKLOADS = {
     # the bf16-gated decode batch (64 requests x G 4) over 32K contexts
     "logits-decode": LogitsWorkload("logits-decode", requests=64, query_len=1, groups=4, heads=8,
                                     block=64, pages_per_req=512, pos_lo=4096, pos_hi=32767,
-                                    seed=config_seed(31)),
+                                    seed=workload_seed(31)),
     # MTP verify: 2 tokens per request, 128 requests, 16K contexts
     "logits-mtp": LogitsWorkload("logits-mtp", requests=128, query_len=2, groups=4, heads=8,
                                  block=64, pages_per_req=256, pos_lo=8192, pos_hi=16382,
-                                 seed=config_seed(32)),
+                                 seed=workload_seed(32)),
 }
 
 

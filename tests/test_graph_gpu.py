@@ -41,7 +41,7 @@ def replay_and_compare(fn, outs, label):
 
 @pytest.mark.parametrize("splits", [1, 3])
 def test_decode_in_graph(splits):
-    w = gen.scaled(gen.CONFIGS[2], name="graph", requests=4, pages_per_req=16, pos_lo=300,
+    w = gen.scaled(gen.WORKLOADS[2], name="graph", requests=4, pages_per_req=16, pos_lo=300,
                    pos_hi=1023)
     inp = gen.make_inputs(w, device=DEV)
     out = torch.empty_like(inp.query)

@@ -119,7 +119,7 @@ def test_ragged_columns_and_strided_views():
 
 @pytest.mark.parametrize("name", ["logits-decode", "logits-mtp"])
 def test_full_size_sampled(name):
-    w = gen.LOGITS_CONFIGS[name]
+    w = gen.LOGITS_WORKLOADS[name]
     inp = gen.make_logits_inputs(w, device=DEV)
     got, cur, lens = run(inp, label=name)
     rng = np.random.default_rng(len(name))

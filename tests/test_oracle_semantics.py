@@ -57,7 +57,7 @@ def test_oracle_matches_dense_sdpa(seed):
 
 
 def test_config1_matches_dense_sdpa():
-    inp = gen.make_inputs(gen.CONFIGS[1], device="cpu")
+    inp = gen.make_inputs(gen.WORKLOADS[1], device="cpu")
     hp = host_problem_from_inputs(inp)
     got = oracle.decode(hp)
     ref = dense_reference(hp)

@@ -75,7 +75,7 @@ def check_inactive_zero(gpu, inp):
 def small(k, **kw):
     """Reduced versions of the five workloads: same heads/G/block/dtype/gate,
     fewer requests and shorter contexts, several tiles and ragged tails."""
-    base = gen.CONFIGS[k]
+    base = gen.WORKLOADS[k]
     table = {
         2: dict(requests=6, pages_per_req=40, pos_lo=1024, pos_hi=2559),
         3: dict(requests=8, pages_per_req=64, pos_lo=2048, pos_hi=4095),
@@ -88,7 +88,7 @@ def small(k, **kw):
 
 # ---------------------------------------------------------------------------
 def test_config1_full():
-    inp = gen.make_inputs(gen.CONFIGS[1], device=DEV)
+    inp = gen.make_inputs(gen.WORKLOADS[1], device=DEV)
     out = run(inp)
     ref = oracle_out(inp)
     check_close(out, ref, what="config1")
@@ -136,7 +136,7 @@ def test_sub_page_regions(rt):
 @pytest.mark.parametrize("splits", [1, 3])
 def test_maximum_region_slots(splits):
     """R at the library maximum (2048 slots of 8-token regions, 16K tokens)."""
-    w = gen.scaled(gen.CONFIGS[2], name="max-R", requests=2, groups=1, heads=4,
+    w = gen.scaled(gen.WORKLOADS[2], name="max-R", requests=2, groups=1, heads=4,
                    pages_per_req=256, pos_lo=12000, pos_hi=16383, R=2048,
                    region_tokens=8, inactive_frac=0.0, gated=False)
     inp = gen.make_inputs(w, device=DEV)
@@ -409,7 +409,7 @@ def test_row_order_matches_index_order(kv, splits, strided, requests, R):
 # --- full-size workloads: sampled rows + properties ---------------------------
 @pytest.mark.parametrize("k", [2, 3, 4, 5, 6])
 def test_full_size_sampled(k):
-    w = gen.CONFIGS[k]
+    w = gen.WORKLOADS[k]
     _say("drawing full workload %d (%s)" % (k, w.name))
     inp = gen.make_inputs(w, device=DEV)
     out = run(inp, label="full%d" % k)

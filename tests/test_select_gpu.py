@@ -115,7 +115,7 @@ def test_output_row_stride_and_untouched_padding_columns():
 @pytest.mark.parametrize("name", ["select-decode", "select-large"])
 @pytest.mark.parametrize("dist", ["normal", "ties"])
 def test_full_size_workloads(name, dist):
-    w = gen.SELECT_CONFIGS[name]
+    w = gen.SELECT_WORKLOADS[name]
     inp = gen.make_select_inputs(w, device=DEV, dist=dist)
     got = B.sda_select_regions(inp.scores, inp.current, w.topk, topk_lengths=inp.topk_lengths)
     torch.cuda.synchronize()

@@ -250,7 +250,7 @@ def test_large_grid_variant(qlen, heads, splits):
 # --- full-size workloads: sampled rows + properties ---------------------------
 @pytest.mark.parametrize("name", ["swa-gated", "swa-mtp"])
 def test_full_size_sampled(name):
-    w = gen.SWA_CONFIGS[name]
+    w = gen.SWA_WORKLOADS[name]
     _say("drawing full workload %s" % name)
     inp = gen.make_swa_inputs(w, device=DEV)
     out = run(inp, label="full " + name)
