@@ -406,6 +406,31 @@ def test_row_order_matches_index_order(kv, splits, strided, requests, R):
     check_inactive_zero(outs[0], inp)
 
 
+@pytest.mark.parametrize("rows", [513, 2048, 2049])
+def test_row_order_grid_bounds(rows):
+    # Grids just past the 512 resident workgroups and at / past 4 rounds: with
+    # or without the order pass, the output equals index order bit for bit and
+    # every row is written.
+    w = gen.Workload("order-bounds", requests=rows, query_len=1, groups=1, heads=4, block=16,
+                     pages_per_req=16, R=8, kv="bf16", pos_lo=16, pos_hi=255, live=(1, 8),
+                     inactive_frac=0.05, gated=True, splits=1, seed=700 + rows)
+    inp = gen.make_inputs(w, device=DEV)
+    outs = []
+    for row_order in (True, False):
+        out = torch.full_like(inp.query, float("nan"))
+        _say("sda_decode order bounds rows=%d row_order=%s" % (rows, row_order))
+        B.sda_decode(inp.query, inp.cache, inp.regions, inp.block_table, inp.positions,
+                     inp.active, out, scale=inp.scale, splits=1, gate=inp.gate,
+                     row_order=row_order)
+        torch.cuda.synchronize()
+        assert torch.isfinite(out.float()).all(), "a row was not written"
+        outs.append(out)
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+    sample = sorted({0, rows // 2, rows - 1})
+    check_close(outs[0], oracle_out(inp, rows=sample), rows=sample,
+                what="order bounds rows=%d" % rows)
+
+
 # --- full-size workloads: sampled rows + properties ---------------------------
 @pytest.mark.parametrize("k", [2, 3, 4, 5, 6])
 def test_full_size_sampled(k):
