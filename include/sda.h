@@ -271,7 +271,8 @@ int sda_swa_plan(int tokens, int groups, int heads, int query_len, int window, i
  * are outside the contract.  All pointers are device pointers; strides in
  * elements.
  *
- *  rows          rows (token, KV group), at most SDA_MAX_ROWS; 0 returns OK.
+ *  rows          rows (token, KV group), at most SDA_SELECT_MAX_ROWS; 0 returns
+ *                OK.
  *  num_regions   score columns S, 0..SDA_MAX_SCORE_COLUMNS.
  *  topk          output slots per row; 0 returns OK.
  *  scores        fp32 [rows, S], unit inner stride, 4-byte aligned.
@@ -282,6 +283,7 @@ int sda_swa_plan(int tokens, int groups, int heads, int query_len, int window, i
  *  regions       int32 [rows, topk] output; row stride >= topk.
  */
 #define SDA_MAX_SCORE_COLUMNS 32768
+#define SDA_SELECT_MAX_ROWS 4194303 /* grid limit: rows * 1024 threads < 2^32 */
 
 typedef struct sda_select_args {
   int32_t rows, num_regions, topk;
@@ -294,7 +296,7 @@ typedef struct sda_select_args {
 } sda_select_args;
 
 /*
- * Enqueue one selection call: one 256-thread workgroup per row (radix select
+ * Enqueue one selection call: one 1024-thread workgroup per row (radix select
  * of the threshold score in registers and LDS, then an ordered compaction).
  * Asynchronous, no allocation.  Returns an sda_status; on error nothing is
  * launched.

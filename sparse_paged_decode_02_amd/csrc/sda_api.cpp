@@ -273,7 +273,8 @@ int sda_select_regions(const sda_select_args* a, hipStream_t stream) {
   if (!a) return SDA_ERR_INVALID;
   if (a->rows < 0 || a->num_regions < 0 || a->topk < 0) return SDA_ERR_INVALID;
   if (a->rows > 1 && a->regions_row_stride < a->topk) return SDA_ERR_INVALID;
-  if (a->num_regions > SDA_MAX_SCORE_COLUMNS || a->rows > SDA_MAX_ROWS) return SDA_ERR_UNSUPPORTED;
+  if (a->num_regions > SDA_MAX_SCORE_COLUMNS || a->rows > SDA_SELECT_MAX_ROWS)
+    return SDA_ERR_UNSUPPORTED;
   if (a->rows == 0 || a->topk == 0) return SDA_OK;
   if (!a->current || !a->regions || (a->num_regions > 0 && !a->scores)) return SDA_ERR_INVALID;
   if (!aligned(a->scores, 4) || !aligned(a->current, 4) || !aligned(a->topk_lengths, 4) ||

@@ -601,7 +601,8 @@ split_kernel(const Params p) {
   __shared__ float s_fac[kWaves][16];
 
   // The workgroup's query columns (the 16 columns of the MFMA tiles).
-  //  * region modes: row r = blockIdx.x (token r / groups, group r % groups);
+  //  * region modes: row r = blockIdx.x, or order[blockIdx.x] when the rows
+  //    run heaviest first (token r / groups, group r % groups);
   //    column = head.
   //  * window mode: blockIdx.x = (request, token group, KV group), group
   //    fastest.  A token group is `pack` consecutive query tokens of the
@@ -867,10 +868,11 @@ split_kernel(const Params p) {
   }
 }
 
-// One 64-thread workgroup per (row, head): 3 dims per thread.
+// One 64-thread workgroup per (row, head), a (rows, heads) grid: 3 dims per
+// thread.
 __global__ __launch_bounds__(64) void combine_kernel(const Params p) {
-  const int r = blockIdx.x / p.heads;
-  const int h = blockIdx.x - r * p.heads;
+  const int r = blockIdx.x;
+  const int h = blockIdx.y;
   const int tid = threadIdx.x;
   uint16_t* orow = out_row(p, r) + (int64_t)h * p.ohs;
   if (p.active && !p.active[r]) {
@@ -1064,7 +1066,8 @@ void launch_dtype(const Params& p, hipStream_t stream) {
 hipError_t launch_combine(const Params& p, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)(p.rows * p.heads)), dim3(64), 0, stream, p);
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)p.rows, (unsigned)p.heads), dim3(64), 0, stream,
+                     p);
   return hipGetLastError();
 }
 

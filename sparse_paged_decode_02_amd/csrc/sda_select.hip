@@ -29,6 +29,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "sda.h"
 #include "sda_launch.h"
 #include "sda_wave.h"
 
@@ -36,6 +37,8 @@ namespace sda {
 namespace {
 
 constexpr int kSelThreads = 1024;
+static_assert((int64_t)SDA_SELECT_MAX_ROWS * kSelThreads < (int64_t(1) << 32),
+              "a grid of SDA_SELECT_MAX_ROWS workgroups fits 2^32 work-items");
 constexpr int kSelWaves = kSelThreads / 64;
 constexpr int kHistBins = 4096;
 constexpr int kCandCap = 4096;  // keys of the first pass's threshold bin kept in LDS

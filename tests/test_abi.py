@@ -252,7 +252,7 @@ SELECT_INVALID = [dict(rows=-1), dict(num_regions=-1), dict(topk=-1), dict(regio
                   dict(current=None), dict(regions=None), dict(scores=None),
                   dict(scores=0x100002), dict(current=0x200001), dict(regions=0x400003),
                   dict(topk_lengths=0x300002)]
-SELECT_UNSUPPORTED = [dict(num_regions=32769), dict(rows=16777216)]
+SELECT_UNSUPPORTED = [dict(num_regions=32769), dict(rows=4194304), dict(rows=16777216)]
 
 
 @pytest.mark.parametrize("over", SELECT_INVALID, ids=[str(o) for o in SELECT_INVALID])
