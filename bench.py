@@ -137,6 +137,27 @@ def time_calls(call, steps: int, warmup: int, stream):
     return wall, launch_avg_ms, launch_ms
 
 
+def time_flushed(call, steps: int, stream, flush_mib: int) -> dict:
+    """Per-call durations with `flush_mib` MiB written between calls (outside
+    the events), so that no call finds the previous calls' bytes in the
+    last-level cache: a cross-check of the rotating input sets."""
+    import torch
+    buf = torch.empty(flush_mib << 20, dtype=torch.uint8, device=stream.device)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for i in range(steps):
+        buf.fill_(i & 0xFF)
+        starts[i].record(stream)
+        call(i)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    us = np.array([starts[i].elapsed_time(ends[i]) * 1e3 for i in range(steps)])
+    del buf
+    return {"flush_mib": flush_mib, "calls": steps, "median_us": round(float(np.median(us)), 2),
+            "p10_us": round(float(np.percentile(us, 10)), 2),
+            "p90_us": round(float(np.percentile(us, 90)), 2)}
+
+
 def record(args, *, value, wall, launch_avg_ms, launch_ms, bytes_per_launch, rows, dtype,
            config, kernel, traffic, metric=METRIC):
     achieved = bytes_per_launch / (launch_avg_ms * 1e-3) / 1e9
@@ -509,6 +530,9 @@ def main() -> int:
                     help="with --swa: query tokens per workgroup (0: the library's plan)")
     ap.add_argument("--sets", type=int, default=4, help="rotating input sets")
     ap.add_argument("--splits", type=int, default=0, help="0: the workload's rule")
+    ap.add_argument("--flush-mib", type=int, default=0, metavar="MIB",
+                    help="sparse decode: also time each call after writing MIB MiB (a "
+                         "last-level-cache flush), reported as `flushed`")
     ap.add_argument("--no-row-order", action="store_true",
                     help="sparse decode with splits == 1: pass no workspace, so rows start "
                          "in index order instead of heaviest first")
@@ -609,6 +633,8 @@ def main() -> int:
                  kernel=("sda order kernel + " if ordered else "") + "sda split kernel"
                  + (" + combine" if splits > 1 else " (combine fused)"),
                  traffic=load_traffic(w.name, splits))
+    if args.flush_mib > 0:
+        rec["flushed"] = time_flushed(call, args.steps, stream, args.flush_mib)
     if not args.no_cpu_baseline:
         threads = max(1, min(16, os.cpu_count() or 1))
         print("[bench] cpu baseline: oracle on %d rows, %d threads" % (args.cpu_rows, threads),
