@@ -255,6 +255,19 @@ def check_tensors(query, cache, regions, block_table, positions, active, output,
         raise SdaError(SDA_ERR_INVALID, "gate must be bfloat16 [tokens, G*heads]")
 
 
+def check_table_rows(block_table, rows: int, rows_per_request: int) -> None:
+    """The library derives the request count from the row count (rows per
+    request = KV groups x query tokens) and sees only the table's row stride,
+    so a table with too few rows would be read past its end: refuse it here."""
+    if rows_per_request < 1 or rows % rows_per_request or block_table.dim() != 2:
+        return  # the C side rejects these shapes itself
+    need = rows // rows_per_request
+    if block_table.shape[0] < need:
+        raise SdaError(SDA_ERR_INVALID,
+                       "block_table has %d rows; %d rows at %d per request need %d" % (
+                           block_table.shape[0], rows, rows_per_request, need))
+
+
 def sda_decode(query, cache, regions, block_table, positions, active, output, *, scale,
                query_len=1, splits, clear_inactive=True, k_scale=None, v_scale=None,
                gate=None, region_tokens=0, workspace=None, row_order=True,
@@ -270,6 +283,7 @@ def sda_decode(query, cache, regions, block_table, positions, active, output, *,
     check_tensors(query, cache, regions, block_table, positions, active, output,
                   k_scale, v_scale, gate)
     rows, heads = query.shape[0], query.shape[1]
+    check_table_rows(block_table, rows, cache.shape[1] * int(query_len))
     if workspace is None and (splits > 1 or row_order) and rows > 0:
         nbytes = sda_workspace_bytes(rows, heads, splits)
         if nbytes:
@@ -363,6 +377,7 @@ def sda_swa_decode(query, cache, block_table, seq_lens, output, *, scale, window
     here through torch when omitted and splits > 1.
     """
     check_swa_tensors(query, cache, block_table, seq_lens, output, gate)
+    check_table_rows(block_table, query.shape[0], int(query_len))
     groups = cache.shape[1]
     rows, heads = query.shape[0] * groups, query.shape[1] // groups
     if workspace is None and splits > 1 and rows > 0:
@@ -484,6 +499,7 @@ def sda_indexer_logits(query, weights, summaries, summary_scales, block_table, p
         if t.dtype != torch.int32 or t.dim() != 2 or t.stride(1) != 1:
             raise SdaError(SDA_ERR_INVALID, "%s must be int32 2-D, unit inner stride" % name)
     rows = query.shape[0]
+    check_table_rows(block_table, rows, int(groups) * int(query_len))
     for t, name in ((positions, "positions"), (current, "current"),
                     (topk_lengths, "topk_lengths")):
         if t is not None and (t.dtype != torch.int32 or not t.is_contiguous() or

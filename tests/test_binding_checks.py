@@ -1,0 +1,57 @@
+"""Binding-side checks the C ABI cannot make because it sees only pointers
+and strides: a block table with fewer rows than the request count that the
+row count implies is refused before anything reaches the device."""
+import pytest
+import torch
+
+from sparse_paged_decode_02_amd import binding as B
+
+
+def _decode_tensors(requests, table_rows):
+    G, heads, block = 2, 4, 16
+    rows = requests * G
+    return dict(
+        query=torch.zeros((rows, heads, 192), dtype=torch.bfloat16),
+        cache=torch.zeros((4, G, block, 384), dtype=torch.bfloat16),
+        regions=torch.zeros((rows, 2), dtype=torch.int32),
+        block_table=torch.zeros((table_rows, 2), dtype=torch.int32),
+        positions=torch.zeros(rows, dtype=torch.int32),
+        active=torch.ones(rows, dtype=torch.uint8),
+        output=torch.zeros((rows, heads, 192), dtype=torch.bfloat16))
+
+
+def test_decode_refuses_short_block_table():
+    t = _decode_tensors(requests=4, table_rows=3)
+    with pytest.raises(B.SdaError) as e:
+        B.sda_decode(t["query"], t["cache"], t["regions"], t["block_table"], t["positions"],
+                     t["active"], t["output"], scale=1.0, splits=1, row_order=False)
+    assert e.value.status == B.SDA_ERR_INVALID and "block_table" in str(e.value)
+
+
+def test_swa_refuses_short_block_table():
+    G, heads, tokens = 2, 4, 4
+    with pytest.raises(B.SdaError) as e:
+        B.sda_swa_decode(torch.zeros((tokens, G * heads, 192), dtype=torch.bfloat16),
+                         torch.zeros((4, G, 64, 384), dtype=torch.bfloat16),
+                         torch.zeros((tokens - 1, 4), dtype=torch.int32),
+                         torch.full((tokens - 1,), 10, dtype=torch.int32),
+                         torch.zeros((tokens, G * heads, 192), dtype=torch.bfloat16),
+                         scale=1.0, window=8, query_len=1, splits=1)
+    assert e.value.status == B.SDA_ERR_INVALID and "block_table" in str(e.value)
+
+
+@pytest.mark.parametrize("query_len,table_rows", [(1, 3), (2, 1)])
+def test_logits_refuses_short_block_table(query_len, table_rows):
+    # 8 rows at 2 groups: 4 requests with one query token each, 2 with two.
+    # A caller that passes query_len=1 for two-token requests asks for twice
+    # the table rows it has; that is refused here.
+    rows, heads = 8, 8
+    with pytest.raises(B.SdaError) as e:
+        B.sda_indexer_logits(torch.zeros((rows, heads, 256), dtype=torch.uint8),
+                             torch.zeros((rows, heads), dtype=torch.float32),
+                             torch.zeros((4, 8, 256), dtype=torch.uint8),
+                             torch.zeros((4, 8), dtype=torch.float32),
+                             torch.zeros((table_rows, 4), dtype=torch.int32),
+                             torch.zeros(rows, dtype=torch.int32),
+                             groups=2, num_regions=32, query_len=query_len)
+    assert e.value.status == B.SDA_ERR_INVALID and "block_table" in str(e.value)
