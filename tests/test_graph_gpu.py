@@ -103,7 +103,8 @@ def test_logits_and_selection_in_graph():
     def fn():
         B.sda_indexer_logits(li.query, li.weights, li.summaries, li.scales, li.block_table,
                              li.positions, groups=lw.groups, num_regions=lw.num_regions,
-                             scores=scores, current=cur, topk_lengths=lens)
+                             query_len=lw.query_len, scores=scores, current=cur,
+                             topk_lengths=lens)
         B.sda_select_regions(scores, cur, 16, topk_lengths=lens, out=regions)
 
     replay_and_compare(fn, [scores, cur, lens, regions], "logits+select")
