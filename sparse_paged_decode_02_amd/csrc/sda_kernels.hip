@@ -756,20 +756,18 @@ split_kernel(const Params p) {
   const uint32_t my_stage_lds = lds_addr(my_stage);
 
   // kStages-deep per-wave pipeline over LDS stages: iteration i (chunk
-  // c = wave + 4i) computes stage i % kStages while the next kStages-1 chunks
-  // are in flight.  Every iteration issues exactly one chunk (12 DMA
-  // instructions), so chunk i has landed once at most 12*(kStages-1) are
-  // outstanding.  Past the last chunk the issue repeats the last one
-  // (clamped, in bounds, never computed).
+  // c = wave + kWaves*i) computes stage i % kStages while the next chunk is
+  // in flight.  An iteration with a next chunk issues it (12 DMA
+  // instructions) and waits until at most those 12 are outstanding, i.e.
+  // chunk c has landed; the last iteration issues nothing and waits for
+  // everything, so no load is left in flight past the loop.
+  static_assert(kStages == 2, "the tail wait assumes one chunk in flight");
   if (wave < nchunks) {
-    const int last = nchunks - 1;
     const LaneDma ld = lane_dma<kFp8>(lane);
     const uint32_t cts_bytes = (uint32_t)(p.cts * C::kEsz);
     uint32_t vb[kStages];
-#pragma unroll
-    for (int s = 0; s < kStages - 1; ++s)
-      vb[s] = issue_chunk<kFp8, kAddr>(p, min(wave + kWaves * s, last), nreg, s_base, s_n, lane,
-                                       my_stage_lds + s * kChunkBytes, ld, cts_bytes, win);
+    vb[0] = issue_chunk<kFp8, kAddr>(p, wave, nreg, s_base, s_n, lane, my_stage_lds, ld, cts_bytes,
+                                     win);
     auto step = [&](int i0, auto stage_c) -> bool {
       constexpr int S = decltype(stage_c)::value;
       constexpr int SN = (S + kStages - 1) % kStages;
@@ -777,10 +775,14 @@ split_kernel(const Params p) {
       if (c >= nchunks) return false;
       // Stage SN was last read by the previous iteration, whose reads all
       // completed before its MFMAs; the asm below keeps them above the DMA.
-      vb[SN] = issue_chunk<kFp8, kAddr>(p, min(c + kWaves * (kStages - 1), last), nreg, s_base,
-                                        s_n, lane, my_stage_lds + SN * kChunkBytes, ld, cts_bytes,
-                                        win);
-      wait_vmcnt<kOpsPerChunk * (kStages - 1)>();
+      const int cn = c + kWaves * (kStages - 1);
+      if (cn < nchunks) {
+        vb[SN] = issue_chunk<kFp8, kAddr>(p, cn, nreg, s_base, s_n, lane,
+                                          my_stage_lds + SN * kChunkBytes, ld, cts_bytes, win);
+        wait_vmcnt<kOpsPerChunk * (kStages - 1)>();
+      } else {
+        wait_vmcnt<0>();
+      }
       if (kAddr == kWindow) cw.t0 = win.t_base + 16 * c;
       compute_chunk<kFp8, kAddr == kWindow>(my_stage + S * kChunkBytes, vb[S], cw, qreg,
                                             qk_scale_log2, lane, st);
@@ -788,9 +790,6 @@ split_kernel(const Params p) {
     };
     for (int i0 = 0;; i0 += kStages)
       if (!run_steps(step, i0, std::make_integer_sequence<int, kStages>{})) break;
-    // Repeated issues past the end may still be in flight: drain them before
-    // the stage memory is reused below.
-    wait_vmcnt<0>();
   }
 
   // Merge the 4 waves.  The per-lane sums of a head live in its 4 lane groups.
