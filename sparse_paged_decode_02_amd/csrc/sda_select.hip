@@ -11,12 +11,15 @@
 //  1. Keys: 16-byte loads (4-byte ones when the row is not 16-byte aligned)
 //     of the scores as order-preserving 32-bit keys, held in registers.
 //     Non-candidates get key 0, which no score maps to (NaN aside).
-//  2. Radix select of the threshold key T: three MSB-first passes of 12, 12
-//     and 8 bits.  Each pass histograms the keys that match the prefix found
-//     so far (LDS atomics), and a block scan from the top bin finds the digit
-//     where the count of larger keys reaches the number still needed.  After
-//     the last pass T is exact, together with how many keys equal to T are
-//     taken.
+//  2. Threshold key T.  A 12-bit MSB-first radix pass histograms the keys
+//     (LDS atomics), and a block scan from the top bin finds the bin where
+//     the count of larger keys reaches the number still needed.  That bin's
+//     keys (typically 1-3% of the row) go to an LDS list.  With at most
+//     kRankCap of them, each listed key is ranked against the whole list
+//     (how many are greater, how many equal) by a group of lanes, and the key
+//     of the needed rank is T.  Larger bins take two more radix passes (12 and 8 bits) over
+//     the list, or over the registers when the bin exceeds the list.  Either
+//     way T is exact, together with how many keys equal to T are taken.
 //  3. Compaction in id order: keys > T, the forced region and the first
 //     needed keys == T are selected.  Each wave counts its selections, one
 //     barrier gives every wave its output offset, and each wave then writes
@@ -42,6 +45,8 @@ static_assert((int64_t)SDA_SELECT_MAX_ROWS * kSelThreads < (int64_t(1) << 32),
 constexpr int kSelWaves = kSelThreads / 64;
 constexpr int kHistBins = 4096;
 constexpr int kCandCap = 4096;  // keys of the first pass's threshold bin kept in LDS
+constexpr int kRankCap = 1024;  // listed keys ranked directly (at least one lane each)
+static_assert(kRankCap <= kSelThreads && kRankCap + 3 <= kCandCap, "rank list fits");
 constexpr int kComputeUnits = 256;
 
 // Keys that order like the floats: flip all bits of negatives, set the sign
@@ -132,9 +137,9 @@ void select_kernel(const SelParams p) {
   // 64 padding bins past the histogram take the invalid keys of pass 1
   // (one per lane, so they never contend), which keeps that pass branch-free.
   __shared__ __attribute__((aligned(16))) int hist[kHistBins + 64];
-  __shared__ int s_pick[2];
+  __shared__ int s_pick[3];
   __shared__ int s_cnt[2][kSelWaves];  // [taken outright | eq][wave]
-  __shared__ uint32_t s_ckey[kCandCap];
+  __shared__ __attribute__((aligned(16))) uint32_t s_ckey[kCandCap + 4];
 
   int n = p.lengths ? p.lengths[r] : p.S;
   n = n < 0 ? 0 : (n > p.S ? p.S : n);
@@ -202,6 +207,7 @@ void select_kernel(const SelParams p) {
     uint32_t prefix = (uint32_t)d1 << 20, pmask = 0xFFF00000u;
     const int inbin = hist[d1];
     const bool listed = inbin <= kCandCap;
+    const bool ranked = inbin <= kRankCap;
     if (listed) {
       // The keys of bin d1 (typically a few percent) go to an LDS list; the
       // other two passes run over it.  Per-wave counts, one barrier, then
@@ -225,37 +231,77 @@ void select_kernel(const SelParams p) {
         for (int q = 0; q < K4; ++q) kk = q == k ? key[q] : kk;
         s_ckey[off++] = kk;
       }
+      // Key 0 (never a candidate: neither greater nor equal) pads the list
+      // to whole 16-byte reads.
+      if (ranked && tid < 3) s_ckey[inbin + tid] = 0u;
     }
     __syncthreads();
-#pragma unroll
-    for (int pass = 1; pass < 3; ++pass) {
-      const int shift = pass == 1 ? 8 : 0;
-      const int nb = pass == 2 ? 256 : kHistBins;
-      const uint32_t dmask = (uint32_t)nb - 1u;
-      for (int b = tid; b < nb; b += kSelThreads) hist[b] = 0;
-      __syncthreads();
-      if (listed) {
-        for (int e = tid; e < inbin; e += kSelThreads) {
-          const uint32_t k = s_ckey[e];
-          if ((k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & dmask], 1);
+    if (ranked) {
+      // T is the need-th largest listed key: the one with fewer than `need`
+      // keys above it and at least `need` at or above it.  A group of P
+      // consecutive lanes (P a power of two, inbin * P <= kSelThreads, at
+      // most a wave) ranks one listed key, each lane over every P-th 16-byte
+      // piece of the list, and the group sums its counts.  Every group
+      // holding a key equal to T writes the same three values.
+      int P = 1;
+      while (P < 64 && inbin * P * 2 <= kSelThreads) P *= 2;
+      const int ci = tid / P, part = tid & (P - 1);
+      int gt = 0, eq = 0;
+      uint32_t kt = 0;
+      if (ci < inbin) {
+        kt = s_ckey[ci];
+        const uint4* l4 = reinterpret_cast<const uint4*>(s_ckey);
+#pragma unroll 1
+        for (int e = part; e < (inbin + 3) >> 2; e += P) {
+          const uint4 v = l4[e];
+          gt += (v.x > kt) + (v.y > kt) + (v.z > kt) + (v.w > kt);
+          eq += (v.x == kt) + (v.y == kt) + (v.z == kt) + (v.w == kt);
         }
-      } else {
-#pragma unroll
-        for (int k = 0; k < K4; ++k)
-          if (key[k] != 0u && (key[k] & pmask) == prefix)
-            atomicAdd(&hist[(key[k] >> shift) & dmask], 1);
+      }
+      for (int o = 1; o < P; o <<= 1) {
+        gt += __shfl_xor(gt, o);
+        eq += __shfl_xor(eq, o);
+      }
+      if (ci < inbin && part == 0 && gt < need && need <= gt + eq) {
+        s_pick[0] = (int)kt;
+        s_pick[1] = gt;
+        s_pick[2] = eq;
       }
       __syncthreads();
-      const int d = pass == 2 ? find_digit<256, kAllLoads>(hist, need, s_pick, wave, lane, above)
-                              : find_digit<kHistBins, kAllLoads>(hist, need, s_pick, wave, lane,
-                                                                above);
-      need -= above;
-      prefix |= (uint32_t)d << shift;
-      pmask |= dmask << shift;
-      if (pass == 2) eq_total = hist[d];  // pool keys == T
+      T = (uint32_t)s_pick[0];
+      need_eq = need - s_pick[1];
+      eq_total = s_pick[2];
+    } else {
+#pragma unroll
+      for (int pass = 1; pass < 3; ++pass) {
+        const int shift = pass == 1 ? 8 : 0;
+        const int nb = pass == 2 ? 256 : kHistBins;
+        const uint32_t dmask = (uint32_t)nb - 1u;
+        for (int b = tid; b < nb; b += kSelThreads) hist[b] = 0;
+        __syncthreads();
+        if (listed) {
+          for (int e = tid; e < inbin; e += kSelThreads) {
+            const uint32_t k = s_ckey[e];
+            if ((k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & dmask], 1);
+          }
+        } else {
+#pragma unroll
+          for (int k = 0; k < K4; ++k)
+            if (key[k] != 0u && (key[k] & pmask) == prefix)
+              atomicAdd(&hist[(key[k] >> shift) & dmask], 1);
+        }
+        __syncthreads();
+        const int d = pass == 2 ? find_digit<256, kAllLoads>(hist, need, s_pick, wave, lane, above)
+                                : find_digit<kHistBins, kAllLoads>(hist, need, s_pick, wave, lane,
+                                                                  above);
+        need -= above;
+        prefix |= (uint32_t)d << shift;
+        pmask |= dmask << shift;
+        if (pass == 2) eq_total = hist[d];  // pool keys == T
+      }
+      T = prefix;
+      need_eq = need;
     }
-    T = prefix;
-    need_eq = need;
   }
   // Without ties at T (all keys == T taken) the selection is key >= T.
   const bool ties = radix && eq_total > need_eq;

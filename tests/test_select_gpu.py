@@ -82,6 +82,44 @@ def test_two_workgroups_per_cu(S, dist):
         run_and_check(s, cur, topk, lens, label="rows300 S%d %s k%d" % (S, dist, topk))
 
 
+def _bin_case(seed, rows, S, m, tied):
+    """Rows whose threshold falls in one bin of the 12-bit first pass holding
+    exactly m keys: 100 keys in [4, 4.5), m keys in [1, 1.125) (distinct, or
+    drawn from m // 8 + 1 values when tied), the rest negative; positions
+    shuffled per row."""
+    g = torch.Generator().manual_seed(seed)
+    out = torch.empty((rows, S))
+    for r in range(rows):
+        hi = 4.0 + 0.5 * torch.rand(100, generator=g)
+        if tied:
+            nv = m // 8 + 1
+            mid = 1.0 + (0.12 / nv) * torch.randint(0, nv, (m,), generator=g).float()
+        else:
+            mid = 1.0 + 0.12 * torch.rand(m, generator=g)
+        lo = -1.0 - torch.rand(S - 100 - m, generator=g)
+        row = torch.cat([hi, mid, lo])
+        out[r] = row[torch.randperm(S, generator=g)]
+    return out.float()
+
+
+@pytest.mark.parametrize("m", [1, 3, 100, 1023, 1024, 1025, 4096, 4097])
+@pytest.mark.parametrize("tied", [False, True])
+def test_threshold_bin_sizes(m, tied):
+    # The threshold bin is ranked directly up to 1024 keys, takes two more
+    # radix passes over its LDS list up to 4096, and over the registers
+    # beyond: every path, with the threshold at the bin's first, middle and
+    # last key.
+    for rows, S in ((8, 8192), (260, 4400 if m <= 4096 else 8192)):
+        if rows == 260 and m not in (1, 1024, 1025, 4096, 4097):
+            continue
+        s = _bin_case(m + 31 * tied + rows, rows, S, m, tied)
+        cur = torch.full((rows,), -1, dtype=torch.int32)
+        for need in sorted({1, (m + 1) // 2, m}):
+            run_and_check(s, cur, 100 + need, None,
+                          label="bin m%d %s rows%d need%d" % (m, "tied" if tied else "distinct",
+                                                             rows, need))
+
+
 def test_no_lengths_all_columns():
     s = _case(3, 32, 3000, "normal")
     cur = torch.arange(32, dtype=torch.int32) * 90
