@@ -111,22 +111,20 @@ __global__ __launch_bounds__(kLgThreads) void logits_kernel(const LogitsParams p
   float wv = 0.f;
   if (tid < ncols) wv = p.w[(int64_t)(r0 + (tid >> p.hshift)) * p.wrs + (tid & (p.heads - 1))];
 
-  // Region count of each row (lane t < rpr: row t), the request's maximum
-  // (every wave reduces it itself), and once the current / length outputs.
-  int lenv = 0;
+  // Region count of each row (lane t < rpr: row t) and the request's maximum
+  // (every wave reduces it itself).
+  int lenv = 0, cur = -1;
   if (lane < rpr) {
     const int pos = p.positions[r0 + lane];
-    const int cur = pos < 0 ? -1 : pos / p.rt;
+    cur = pos < 0 ? -1 : pos / p.rt;
     lenv = cur + 1 < p.S ? cur + 1 : p.S;
-    if (wave == 0) {
-      s_len[lane] = lenv;
-      if (chunk == 0) {
-        if (p.current) p.current[r0 + lane] = cur;
-        if (p.lengths) p.lengths[r0 + lane] = lenv;
-      }
-    }
+    if (wave == 0) s_len[lane] = lenv;
   }
   const int max_len = wave_max(lenv);
+  // The queries and weights were requested before the positions, so they
+  // have landed: consume them here, where the wait for the positions
+  // covers them, rather than behind the block-table loads below.
+  __asm__ __volatile__("" : "+v"(wv), "+v"(qraw[0]), "+v"(qraw[1]), "+v"(qraw[2]), "+v"(qraw[3]));
 
   const int j_begin = chunk * kLgChunk;
   const int j_end = min(p.S, j_begin + kLgChunk);
@@ -138,6 +136,21 @@ __global__ __launch_bounds__(kLgThreads) void logits_kernel(const LogitsParams p
   const int jl = j_begin + kLgTile * wave + kLgTile * kLgWaves * (lane >> 4) + (lane & 15);
   int64_t pg = 0;
   if (jl < j_live) pg = p.table[(int64_t)req * p.trs + jl / p.rpb];
+  // The query conversion below overlaps the block-table round trip.
+  // Query columns converted to bf16 in the lane order of the MFMA B
+  // operand: entry (tile, lane) holds column 16 tile + (lane & 15), dims
+  // [64 c + 16 (lane >> 4), +16) for c = 0..3, the dims its A lanes hold.
+  if (qt < ntiles) {
+    __bf16* dst = &s_q[qt][ql][0];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      bf16x8 lo, hi;
+      e4m3x16_to_bf16(qraw[c], lo, hi);  // zeros for absent columns
+      *reinterpret_cast<bf16x8*>(dst + 16 * c) = lo;
+      *reinterpret_cast<bf16x8*>(dst + 16 * c + 8) = hi;
+    }
+  }
+  if (tid < kLgMaxCols) s_w[tid] = wv;
   int64_t roff_l = 0;
   float scale_l = 0.f;
   if (jl < j_live) {
@@ -158,26 +171,21 @@ __global__ __launch_bounds__(kLgThreads) void logits_kernel(const LogitsParams p
   };
   const int nt = (j_live - (j_begin + kLgTile * wave) + kLgTile * kLgWaves - 1) /
                  (kLgTile * kLgWaves);  // live tiles of this wave (<= 4)
-  // The first tile's summaries are requested before the query conversion
-  // and the barrier, as soon as their offsets are known.
+  // The first tile's summaries are requested before the barrier, as soon as
+  // their offsets are known.
   u32x4 raw[4];
   if (nt > 0) load_tile(0, raw);
 
-  // Query columns converted to bf16 in the lane order of the MFMA B
-  // operand: entry (tile, lane) holds column 16 tile + (lane & 15), dims
-  // [64 c + 16 (lane >> 4), +16) for c = 0..3, the dims its A lanes hold.
-  if (qt < ntiles) {
-    __bf16* dst = &s_q[qt][ql][0];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      bf16x8 lo, hi;
-      e4m3x16_to_bf16(qraw[c], lo, hi);  // zeros for absent columns
-      *reinterpret_cast<bf16x8*>(dst + 16 * c) = lo;
-      *reinterpret_cast<bf16x8*>(dst + 16 * c + 8) = hi;
-    }
+  // The barrier publishes LDS only (queries, weights, region counts): each
+  // wave waits for its own LDS writes, not for its global loads in flight,
+  // which a full __syncthreads() fence would also drain.
+  __asm__ __volatile__("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  // The selection's inputs, once per row, stored after the loads above are
+  // on their way (a store in flight would hold up the first wait).
+  if (chunk == 0 && wave == 0 && lane < rpr) {
+    if (p.current) p.current[r0 + lane] = cur;
+    if (p.lengths) p.lengths[r0 + lane] = lenv;
   }
-  if (tid < kLgMaxCols) s_w[tid] = wv;
-  __syncthreads();
 
   // Tiles at or past the request's last region: -inf, and no summary read.
   for (int j0 = j_begin + kLgTile * wave; j0 < j_end; j0 += kLgTile * kLgWaves) {
