@@ -179,6 +179,15 @@ void select_kernel(const SelParams p) {
         sc[4 * i + c] = j < n ? srow[j] : 0.f;
       }
   }
+  // The histogram is cleared while the scores are in flight: the barrier
+  // publishes LDS only (a full __syncthreads() fence would wait for the
+  // loads), and the keys are formed after it.
+  const bool take_all = need0 == pool;
+  const bool radix = !take_all && need0 > 0;
+  if (radix) {
+    for (int b = tid; b < kHistBins; b += kSelThreads) hist[b] = 0;
+    __asm__ __volatile__("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  }
   uint32_t key[K4];
 #pragma unroll
   for (int i = 0; i < I; ++i)
@@ -189,14 +198,10 @@ void select_kernel(const SelParams p) {
     }
 
   // 2. threshold: every pool key > T is taken, plus need_eq keys == T
-  const bool take_all = need0 == pool;
-  const bool radix = !take_all && need0 > 0;
   uint32_t T = 0;
   int need_eq = 0, eq_total = 0;
   if (radix) {
-    // pass 1 (bits 31..20) over the registers
-    for (int b = tid; b < kHistBins; b += kSelThreads) hist[b] = 0;
-    __syncthreads();
+    // pass 1 (bits 31..20) over the registers (histogram cleared above)
 #pragma unroll
     for (int k = 0; k < K4; ++k)
       atomicAdd(&hist[key[k] != 0u ? (int)(key[k] >> 20) : kHistBins + lane], 1);
