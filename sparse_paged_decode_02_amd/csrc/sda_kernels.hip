@@ -932,27 +932,38 @@ __global__ __launch_bounds__(256) void bin_kernel(Params p, int64_t max_tokens, 
   // with the tokens of row rbase + i.
   const int rbase = (blockIdx.x * 4 + (threadIdx.x >> 6)) * kOrderBatch;
   const int r = rbase + lane;
-  const int nrow = p.rows - rbase;  // rows of this wave, if below kOrderBatch
   const bool valid = lane < kOrderBatch && r < p.rows;
-  const int act = valid ? p.active[r] : 0;
-  const int pos = valid ? p.positions[r] : -1;
-  // Region id i of this lane's row is visible in part or whole iff
-  // 0 <= i <= pq, wholly iff 0 <= i < pf; the one partial region shows
-  // pos % rt + 1 tokens.
-  const int pq = pos >= 0 ? pos / p.rt : -1;
-  const int pf = pos >= 0 ? (pos + 1) / p.rt : 0;
-  const int part = pos >= 0 ? pos - pq * p.rt + 1 : 0;
+  // Every load below is unconditional, at an index clamped into the arrays
+  // (the launch has rows >= 1), and masked afterwards: the flag, the
+  // position and all region ids then share one round trip, where loads
+  // under branches had been waited for one by one.
+  const int rc = min(r, p.rows - 1);
+  const int act_raw = p.active[rc];
+  const int pos_raw = p.positions[rc];
   int64_t tokens = 0;
+  int pq = -1, pf = 0, part = 0;
   for (int c = 0; c < p.R; c += 64) {
     // One coalesced load per row (lane l reads slot c + l), all issued
     // before the first is used.
     const bool in_r = c + lane < p.R;
-    const int32_t* ptr = p.regions + (int64_t)rbase * p.rrs + c + lane;
+    const int32_t* col = p.regions + min(c + lane, p.R - 1);
     int ids[kOrderBatch];
 #pragma unroll
-    for (int i = 0; i < kOrderBatch; ++i) {
-      ids[i] = (i < nrow && in_r) ? *ptr : -1;
-      ptr += p.rrs;
+    for (int i = 0; i < kOrderBatch; ++i)
+      ids[i] = col[(int64_t)min(rbase + i, p.rows - 1) * p.rrs];
+#pragma unroll
+    for (int i = 0; i < kOrderBatch; ++i)
+      if (!(rbase + i < p.rows && in_r)) ids[i] = -1;
+    if (c == 0) {
+      // Region id i of this lane's row is visible in part or whole iff
+      // 0 <= i <= pq, wholly iff 0 <= i < pf; the one partial region shows
+      // pos % rt + 1 tokens.  (Formed once the first ids are requested.)
+      int pos = pos_raw;
+      __asm__ __volatile__("" : "+v"(pos));  // keeps the use below the loads
+      pos = valid ? pos : -1;
+      pq = pos >= 0 ? pos / p.rt : -1;
+      pf = pos >= 0 ? (pos + 1) / p.rt : 0;
+      part = pos >= 0 ? pos - pq * p.rt + 1 : 0;
     }
     // Row rbase + i: rt tokens per region that ends at or before its
     // position, pos % rt + 1 per copy of the region that holds it.
@@ -966,7 +977,7 @@ __global__ __launch_bounds__(256) void bin_kernel(Params p, int64_t max_tokens, 
     }
   }
   if (valid) {
-    if (!act) tokens = 0;
+    if (!act_raw) tokens = 0;
     bins[r] = kOrderBins - 1 - (int)(tokens * kOrderBins / (max_tokens + 1));
   }
 }
@@ -978,7 +989,12 @@ __global__ __launch_bounds__(kOrderBlock) void order_kernel(Params p, const int3
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
   const int r = blockIdx.x * kOrderBlock + t;
-  const int bin = r < p.rows ? bins[r] : -1;
+  const int bin_raw = bins[min(r, p.rows - 1)];
+  // The counts are cleared while the bins are in flight (an LDS-only
+  // barrier: a __syncthreads() fence would wait for the load).
+  if (t < kOrderBins * kOrderWaves) s_cnt[t] = 0;
+  __asm__ __volatile__("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  const int bin = r < p.rows ? bin_raw : -1;
   // Lanes of the wave in the same bin, and this lane's rank among them.
   uint64_t same = __ballot(bin >= 0);
 #pragma unroll
@@ -988,8 +1004,6 @@ __global__ __launch_bounds__(kOrderBlock) void order_kernel(Params p, const int3
   }
   const uint64_t below = lane ? ~0ull >> (64 - lane) : 0ull;
   const int rank = __popcll(same & below);
-  if (t < kOrderBins * kOrderWaves) s_cnt[t] = 0;
-  __syncthreads();
   if (bin >= 0 && rank == 0) s_cnt[bin * kOrderWaves + wave] = __popcll(same);
   __syncthreads();
   // Exclusive scan of s_cnt in (bin, wave) order: the first slot of each
