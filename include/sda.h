@@ -90,8 +90,11 @@ typedef enum {
  *               t % block.
  *  positions    int32 [rows]: 0-based position of the row's query token.
  *               Token t is visible iff t <= position (inclusive causal mask).
- *  active       uint8 [rows]; 0 marks an inactive (padding) row.  For such a
- *               row nothing else is read.
+ *  active       uint8 [rows]; 0 marks an inactive (padding) row.  Its query,
+ *               gate, block-table row and cache pages are never read, and its
+ *               output depends on nothing but the flag; its position and
+ *               region ids may be loaded (so they must be addressable), but
+ *               their values are never used.
  *  scale        softmax scale applied to q.k.
  *  splits       >= 1: the row's visible regions are dealt to `splits`
  *               workgroups, and their partials are merged by log-sum-exp.

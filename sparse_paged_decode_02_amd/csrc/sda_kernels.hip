@@ -643,7 +643,8 @@ split_kernel(const Params p) {
     id_first = lane < p.R ? p.regions[(int64_t)r * p.rrs + lane] : -1;
     __asm__ __volatile__("" : "+v"(pos), "+v"(id_first));
     if (!act) {
-      // Inactive rows read nothing else.  With splits > 1 the combine clears.
+      // An inactive row reads nothing further (the position and ids loaded
+      // with its flag go unused).  With splits > 1 the combine clears.
       if (kFused && p.clear) clear_row(p, r, tid, kThreads);
       return;
     }

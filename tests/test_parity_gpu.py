@@ -207,6 +207,43 @@ def test_inactive_rows_cleared_or_untouched(splits):
     assert torch.equal(kept[torch.from_numpy(act).to(DEV)], out[torch.from_numpy(act).to(DEV)])
 
 
+@pytest.mark.parametrize("splits,row_order", [(1, True), (1, False), (2, True)])
+def test_inactive_rows_poisoned_inputs(splits, row_order):
+    # An inactive row's values must not matter: its position (INT32_MAX),
+    # region ids (huge, never resolved), query and gate (NaN) are poisoned,
+    # and the output must be bit-identical to the clean call, with the
+    # inactive rows +0.0.  768 rows: the row-order pass runs when asked.
+    w = gen.Workload("poison", requests=96, query_len=2, groups=4, heads=8, block=16,
+                     pages_per_req=64, R=64, kv="bf16", pos_lo=512, pos_hi=1022, live=(8, 64),
+                     inactive_frac=0.10, gated=True, splits=splits, seed=640 + splits)
+    inp = gen.make_inputs(w, device=DEV)
+    ina = ~inp.active
+    assert ina.any()
+    pos = inp.positions.clone()
+    pos[ina] = 2 ** 31 - 1
+    reg = inp.regions.clone()
+    reg[ina] = 0x3FFFFFFF
+    q = inp.query.clone()
+    q[ina] = float("nan")
+    gate = inp.gate.clone()
+    for r in torch.nonzero(ina).flatten().tolist():
+        g = r % w.groups
+        gate[r // w.groups, g * w.heads:(g + 1) * w.heads] = float("nan")
+    outs = []
+    for args in ((inp.query, inp.regions, inp.positions, inp.gate), (q, reg, pos, gate)):
+        out = torch.full_like(inp.query, 7.0)
+        _say("sda_decode poisoned=%s splits=%d row_order=%s" % (len(outs) == 1, splits,
+                                                               row_order))
+        B.sda_decode(args[0], inp.cache, args[1], inp.block_table, args[2], inp.active, out,
+                     scale=inp.scale, query_len=w.query_len, splits=splits, gate=args[3],
+                     row_order=row_order)
+        torch.cuda.synchronize()
+        outs.append(out)
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+    check_inactive_zero(outs[1], inp)
+    check_close(outs[1], oracle_out(inp), what="poisoned inactive rows splits%d" % splits)
+
+
 @pytest.mark.parametrize("splits", [1, 2])
 def test_gate_closed_forms_bit_exact(splits):
     w = small(2, requests=2, pages_per_req=16, pos_lo=300, pos_hi=1023)
