@@ -157,12 +157,16 @@ __device__ __forceinline__ int swz_k(int row) {
 // the compiler does not tie later LDS reads to them; completion is awaited
 // with wait_vmcnt.  M0 is saved and restored around the block.
 //
-// Cache policy: K|V bytes are read exactly once, so the DMAs are
-// non-temporal (`nt`).  The exception is FP8 K.  A 384-byte FP8 token row
-// puts K[128:192] and V[0:64] in one 128-byte line, so K keeps the default
-// policy and the line stays cached for the V DMA that follows.  Measured on
-// MI355X: bf16 gated 72.4 -> 64.3 us with nt; FP8 large batch 629 us with
-// every DMA nt vs 601 us with V only.
+// Cache policy: K|V bytes are read exactly once, so every DMA is
+// non-temporal (`nt`); bf16 gated measured 72.4 -> 64.3 us with nt on
+// MI355X.  A 384-byte FP8 token row puts K[128:192] and V[0:64] in one
+// 128-byte line.  FP8 chunks therefore issue K DMA j and V DMA j, which cover
+// the same token rows, back to back (SDA_CHUNK_ASM_KV), so the second request
+// for the shared line meets the first in flight: all-nt FP8 then fetches
+// 1.000x the K|V bytes, where K-then-V order with nt fetched 1.024x.  (K had
+// kept the default policy to avoid that re-fetch, but its cacheable loads
+// evict dirty lines of earlier kernels, and the write-backs land inside the
+// call: 81 us on the FP8 cache workload after a 1 GiB write.)
 #define SDA_LDDMA(op, addr, suf) "global_load_lds_dwordx4 %[" op "], " addr suf "\n\t"
 #define SDA_NEXT "s_add_u32 m0, m0, 0x400\n\t"
 #define SDA_CHUNK_ASM(addr, ksuf, vsuf)                                                      \
@@ -174,6 +178,21 @@ __device__ __forceinline__ int swz_k(int row) {
       SDA_LDDMA("v2", addr, vsuf) SDA_NEXT SDA_LDDMA("v3", addr, vsuf) SDA_NEXT              \
       SDA_LDDMA("v4", addr, vsuf) SDA_NEXT SDA_LDDMA("v5", addr, vsuf)                       \
   "s_mov_b32 m0, %[sv]"
+
+// FP8 chunk: K DMA j then V DMA j for j = 0..5 (the same token rows), with
+// M0 set from the stage base for each: K slice j at stage + 1 KiB j, V slice
+// j at stage + 6 KiB + 1 KiB j, the layout SDA_CHUNK_ASM writes in order.
+#define SDA_M0(off) "s_add_u32 m0, %[st], " off "\n\t"
+#define SDA_CHUNK_ASM_KV(addr, suf)                                                          \
+  "s_mov_b32 %[sv], m0\n\t"                                                                  \
+  "s_mov_b32 m0, %[st]\n\t" SDA_LDDMA("k0", addr, suf) SDA_M0("0x1800")                      \
+      SDA_LDDMA("v0", addr, suf) SDA_M0("0x400") SDA_LDDMA("k1", addr, suf) SDA_M0("0x1c00")    \
+      SDA_LDDMA("v1", addr, suf) SDA_M0("0x800") SDA_LDDMA("k2", addr, suf) SDA_M0("0x2000")    \
+      SDA_LDDMA("v2", addr, suf) SDA_M0("0xc00") SDA_LDDMA("k3", addr, suf) SDA_M0("0x2400")    \
+      SDA_LDDMA("v3", addr, suf) SDA_M0("0x1000") SDA_LDDMA("k4", addr, suf) SDA_M0("0x2800")   \
+      SDA_LDDMA("v4", addr, suf) SDA_M0("0x1400") SDA_LDDMA("k5", addr, suf) SDA_M0("0x2c00")   \
+      SDA_LDDMA("v5", addr, suf) "s_mov_b32 m0, %[sv]"
+static_assert(kStageBytes == 0x1800, "SDA_CHUNK_ASM_KV: V slices start 6 KiB into the stage");
 
 // Two-region chunk (bf16, 8-token regions): the first three K and V DMAs
 // cover token rows 0..7 (pieces 0..191 of a 384-piece half) and the last
@@ -215,7 +234,7 @@ __device__ __forceinline__ void dma_chunk_sbase(const uint8_t* base, uint32_t st
     [v2] "v"(vo[2]), [v3] "v"(vo[3]), [v4] "v"(vo[4]), [v5] "v"(vo[5])                          \
   : "memory"
   if constexpr (kFp8)
-    __asm__ __volatile__(SDA_CHUNK_ASM("%[b]", "", " nt") SDA_SBASE_OPERANDS);
+    __asm__ __volatile__(SDA_CHUNK_ASM_KV("%[b]", " nt") SDA_SBASE_OPERANDS);
   else
     __asm__ __volatile__(SDA_CHUNK_ASM("%[b]", " nt", " nt") SDA_SBASE_OPERANDS);
 #undef SDA_SBASE_OPERANDS
@@ -233,7 +252,7 @@ __device__ __forceinline__ void dma_chunk_vaddr(uint32_t stage, const uint8_t* c
     [v3] "v"(va[3]), [v4] "v"(va[4]), [v5] "v"(va[5])                                          \
   : "memory"
   if constexpr (kFp8)
-    __asm__ __volatile__(SDA_CHUNK_ASM("off", "", " nt") SDA_VADDR_OPERANDS);
+    __asm__ __volatile__(SDA_CHUNK_ASM_KV("off", " nt") SDA_VADDR_OPERANDS);
   else
     __asm__ __volatile__(SDA_CHUNK_ASM("off", " nt", " nt") SDA_VADDR_OPERANDS);
 #undef SDA_VADDR_OPERANDS
