@@ -580,10 +580,15 @@ __device__ __forceinline__ uint16_t* out_row(const Params& p, int r) {
   return p.out + (int64_t)t * p.ots + (int64_t)(r - t * p.groups) * p.ogs;
 }
 
+// The output is written once and read by the next kernel, so it is stored
+// non-temporally: cacheable stores left dirty lines whose write-back landed
+// in later calls' streaming.  Measured on MI355X (back to back): large-batch
+// FP8 534 -> 503 us, sliding-window gated 134.4 -> 130.4 us, the 256- and
+// 512-row workloads unchanged, the 1024-row multi-token one 133.4 -> 135.9 us.
 __device__ __forceinline__ void store_row_pair(uint16_t* orow, const Params& p, int h, int d,
                                                float o0, float o1) {
   uint32_t v = float_to_bf16_bits(o0) | (float_to_bf16_bits(o1) << 16);
-  *reinterpret_cast<uint32_t*>(orow + (int64_t)h * p.ohs + d) = v;
+  __builtin_nontemporal_store(v, reinterpret_cast<uint32_t*>(orow + (int64_t)h * p.ohs + d));
 }
 
 __device__ __forceinline__ void clear_row(const Params& p, int r, int tid, int nthreads) {
