@@ -580,15 +580,20 @@ __device__ __forceinline__ uint16_t* out_row(const Params& p, int r) {
   return p.out + (int64_t)t * p.ots + (int64_t)(r - t * p.groups) * p.ogs;
 }
 
-// The output is written once and read by the next kernel, so it is stored
-// non-temporally: cacheable stores left dirty lines whose write-back landed
-// in later calls' streaming.  Measured on MI355X (back to back): large-batch
-// FP8 534 -> 503 us, sliding-window gated 134.4 -> 130.4 us, the 256- and
-// 512-row workloads unchanged, the 1024-row multi-token one 133.4 -> 135.9 us.
+// The output is written once and read by the next kernel.  A large output
+// (p.nt_out, see kNtOutputBytes) is stored non-temporally: cacheable stores
+// left dirty lines whose write-back landed in later calls' streaming.  The
+// policy is a template argument of the whole output loop: a branch around
+// the store alone is merged by the compiler into one plain store.
+template <bool kNt>
 __device__ __forceinline__ void store_row_pair(uint16_t* orow, const Params& p, int h, int d,
                                                float o0, float o1) {
   uint32_t v = float_to_bf16_bits(o0) | (float_to_bf16_bits(o1) << 16);
-  __builtin_nontemporal_store(v, reinterpret_cast<uint32_t*>(orow + (int64_t)h * p.ohs + d));
+  uint32_t* dst = reinterpret_cast<uint32_t*>(orow + (int64_t)h * p.ohs + d);
+  if constexpr (kNt)
+    __builtin_nontemporal_store(v, dst);
+  else
+    *dst = v;
 }
 
 __device__ __forceinline__ void clear_row(const Params& p, int r, int tid, int nthreads) {
@@ -864,6 +869,7 @@ split_kernel(const Params p) {
   }
   __syncthreads();
 
+  auto output_loop = [&](auto nt) {
   for (int e = tid; e < ncols * (kDim / 2); e += kThreads) {
     const int c = e / (kDim / 2), d = 2 * (e - c * (kDim / 2));
     // column c -> (token, head) and its output row
@@ -883,13 +889,18 @@ split_kernel(const Params p) {
     }
     if (kFused) {
       uint16_t* orow = p.out + (int64_t)token * p.ots + (int64_t)g * p.ogs;
-      store_row_pair(orow, p, h, d, o0, o1);
+      store_row_pair<decltype(nt)::value>(orow, p, h, d, o0, o1);
     } else {
       const int row = kAddr == kWindow ? token * p.groups + g : r;
       int64_t ph = ((int64_t)row * p.splits + split) * p.heads + h;
       *reinterpret_cast<float2*>(p.partial + ph * kDim + d) = make_float2(o0, o1);
     }
   }
+  };
+  if (kFused && p.nt_out)
+    output_loop(std::true_type{});
+  else
+    output_loop(std::false_type{});
 }
 
 // One 64-thread workgroup per (row, head), a (rows, heads) grid: 3 dims per
@@ -1111,8 +1122,20 @@ hipError_t launch_combine(const Params& p, hipStream_t stream) {
 
 }  // namespace
 
+// Output bytes per call from which the fused output is stored non-temporally
+// (0.5 MiB per XCD, against its 4 MiB L2).  Measured on MI355X, back to
+// back, non-temporal vs cacheable stores: 25 MB (large-batch FP8) 534 ->
+// 503 us and 6.3 MB (sliding-window gated) 134.4 -> 130.4 us; 1.5 and 3 MB
+// (bf16 gated, FP8 cache) unchanged; 3 MB (multi-token) 133.4 -> 135.9 us.
+static constexpr int64_t kNtOutputBytes = int64_t(4) << 20;
+
+static bool large_output(const Params& p) {
+  return (int64_t)p.rows * p.heads * kDim * 2 >= kNtOutputBytes;
+}
+
 hipError_t launch(const Params& p0, bool fp8, hipStream_t stream) {
   Params p = p0;
+  p.nt_out = large_output(p) ? 1 : 0;
   p.order = launch_order(p, stream);
   if (fp8)
     launch_dtype<true>(p, stream);
@@ -1121,7 +1144,9 @@ hipError_t launch(const Params& p0, bool fp8, hipStream_t stream) {
   return launch_combine(p, stream);
 }
 
-hipError_t launch_window(const Params& p, hipStream_t stream) {
+hipError_t launch_window(const Params& p0, hipStream_t stream) {
+  Params p = p0;
+  p.nt_out = large_output(p) ? 1 : 0;
   // grid.x = requests * token groups * KV groups; the combine runs per row.
   const unsigned wgs = (unsigned)(p.rows / p.rows_per_req * p.ntg * p.groups);
   if (p.splits == 1)

@@ -39,6 +39,7 @@ struct Params {
   int32_t rt_shift;           // log2(rt) when rt is a power of two, else -1
   int32_t query_len, window;  // window mode
   int32_t pack, ntg;          // window mode: tokens per workgroup, token groups per request
+  int32_t nt_out;             // set by the launch: store the output non-temporally
 };
 
 // Enqueue the split kernel (and the combine kernel when splits > 1) over
