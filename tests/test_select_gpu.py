@@ -120,6 +120,19 @@ def test_threshold_bin_sizes(m, tied):
                                                              rows, need))
 
 
+@pytest.mark.parametrize("rows,S", [(600, 32768), (1100, 5000)])
+def test_more_rows_than_resident_workgroups(rows, S):
+    # More rows than the chip holds workgroups at once (256 with 32 keys per
+    # lane, 512 with at most 16): later rows start as earlier ones retire.
+    rng = np.random.default_rng(rows)
+    s = _case(rows + S, rows, S, "normal")
+    lens = torch.from_numpy(rng.integers(0, S + 2, size=rows).astype(np.int32))
+    cur = torch.from_numpy(np.array([rng.integers(-1, max(int(n), 1) + 1) for n in lens],
+                                    np.int32))
+    run_and_check(s, cur, 512, lens, label="loop rows%d S%d" % (rows, S))
+    run_and_check(s, cur, 64, None, label="loop rows%d S%d no lengths" % (rows, S))
+
+
 def test_no_lengths_all_columns():
     s = _case(3, 32, 3000, "normal")
     cur = torch.arange(32, dtype=torch.int32) * 90
