@@ -516,7 +516,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=2,
-                    help="workload: 1..5, or 6 = bf16-gated shape at 8-token regions")
+                    help="workload: 1..5, or 6 / 7 = the bf16-gated / FP8-cache shape at "
+                         "8-token regions")
     ap.add_argument("--swa", default="", metavar="NAME",
                     help="measure the gated sliding-window decode on workload NAME "
                          "(swa-gated, swa-mtp) instead")

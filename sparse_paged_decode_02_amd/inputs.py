@@ -73,7 +73,7 @@ def workload_seed(k: int) -> int:
     return 1000 * k + 7
 
 
-# The five decode workloads (1-based numbering), and one at 8-token regions.
+# The five decode workloads (1-based numbering), and two at 8-token regions.
 WORKLOADS = {
     1: Workload("tiny-bf16", requests=4, query_len=1, groups=1, heads=8, block=16,
                 pages_per_req=16, R=8, kv="bf16", pos_lo=1, pos_hi=127,
@@ -97,6 +97,10 @@ WORKLOADS = {
                 pages_per_req=512, R=256, kv="bf16", pos_lo=4096, pos_hi=32767,
                 inactive_frac=0.05, gated=True, splits=None, region_tokens=8,
                 seed=workload_seed(6)),
+    # The same at the FP8-cache shape: 512 slots of 8 tokens = 4096 tokens per row.
+    7: Workload("fp8-cache-8tok", requests=256, query_len=1, groups=2, heads=16, block=64,
+                pages_per_req=2048, R=512, kv="fp8", pos_lo=65536, pos_hi=131071,
+                gated=False, splits=None, region_tokens=8, seed=workload_seed(7)),
 }
 
 

@@ -122,11 +122,12 @@ def test_head_counts(kv, heads):
     check_close(out, oracle_out(inp), what="heads=%d %s" % (heads, kv))
 
 
-@pytest.mark.parametrize("rt", [8, 16, 32])
-def test_sub_page_regions(rt):
+@pytest.mark.parametrize("kv,rt", [("bf16", 8), ("bf16", 16), ("bf16", 32), ("fp8", 8),
+                                   ("fp8", 16), ("fp8", 32)])
+def test_sub_page_regions(kv, rt):
     """Regions smaller than a page (region_tokens divides block)."""
-    w = small(2, requests=2, pages_per_req=16, pos_lo=300, pos_hi=1023, R=96,
-              region_tokens=rt)
+    w = small(2 if kv == "bf16" else 3, requests=2, pages_per_req=16, pos_lo=300, pos_hi=1023,
+              R=96, region_tokens=rt)
     inp = gen.make_inputs(w, device=DEV)
     for s in (1, 3):
         out = run(inp, splits=s)
@@ -469,7 +470,7 @@ def test_row_order_grid_bounds(rows):
 
 
 # --- full-size workloads: sampled rows + properties ---------------------------
-@pytest.mark.parametrize("k", [2, 3, 4, 5, 6])
+@pytest.mark.parametrize("k", [2, 3, 4, 5, 6, 7])
 def test_full_size_sampled(k):
     w = gen.WORKLOADS[k]
     _say("drawing full workload %d (%s)" % (k, w.name))
