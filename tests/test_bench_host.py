@@ -1,0 +1,86 @@
+"""Host logic of bench.py (CPU): the one-GPU refusal, the algorithmic byte
+counts the roofline divides by, and the counter-traffic lookup that ties a
+profile summary to the kernel source it was measured on."""
+import os
+import subprocess
+import sys
+
+import numpy as np
+
+import bench
+from sparse_paged_decode_02_amd import inputs as gen
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def _brute_force_tokens(w, positions, regions, active):
+    """Visible selected tokens, one token at a time: slot by slot, token t of
+    region id is counted iff id >= 0 and t <= the row's position."""
+    n = 0
+    for r in range(w.rows):
+        if not active[r]:
+            continue
+        for rid in regions[r]:
+            if rid < 0:
+                continue
+            for i in range(w.rt):
+                if rid * w.rt + i <= positions[r]:
+                    n += 1
+    return n
+
+
+def test_algorithmic_bytes_match_a_token_count():
+    for k, kw in ((2, dict(requests=3, pages_per_req=24, pos_lo=100, pos_hi=1500)),
+                  (3, dict(requests=4, pages_per_req=16, pos_lo=10, pos_hi=1023, R=12)),
+                  (4, dict(requests=3, pages_per_req=16, pos_lo=40, pos_hi=510)),
+                  (6, dict(requests=2, pages_per_req=16, pos_lo=7, pos_hi=1023, R=40))):
+        w = gen.scaled(gen.WORKLOADS[k], **kw)
+        idx = gen.draw_indices(w)
+        got, tokens = bench.algorithmic_bytes(w, idx.positions, idx.regions, idx.active)
+        want_tokens = _brute_force_tokens(w, idx.positions, idx.regions, idx.active)
+        assert tokens == want_tokens
+        e = 1 if w.kv == "fp8" else 2
+        nact = int((idx.active != 0).sum())
+        assert got == want_tokens * 384 * e + nact * w.heads * 384 + w.rows * w.heads * 384
+
+
+def test_swa_algorithmic_bytes_count_each_window_token_once():
+    w = gen.SWA_WORKLOADS["swa-mtp"]
+    lens = np.array([1, 3, 4, 5, 1025, 8192] + [2000] * (w.requests - 6))
+    got, tokens = bench.swa_algorithmic_bytes(w, lens)
+    want = 0
+    for L in lens:
+        union = set()
+        for j in range(w.query_len):
+            p = L - w.query_len + j
+            union.update(t for t in range(max(0, p - w.window + 1), p + 1) if t >= 0)
+        want += len(union) * w.groups
+    assert tokens == want
+    assert got == want * 384 * 2 + 2 * w.rows * w.heads * 384
+
+
+def test_traffic_is_read_only_for_the_profiled_kernel_and_split_count(tmp_path, monkeypatch):
+    # A summary names the kernel source hash and split count it was measured
+    # on; any other source or split count reads as no measurement (None).
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+
+    def summary(name, sha, splits, traffic):
+        (prof / ("split_kernel_%s.md" % name)).write_text(
+            "# x\n\n    kernel_sha256_16 = %s\n    splits = %d\n\n"
+            "    traffic_bytes_per_launch = %d\n" % (sha, splits, traffic))
+
+    summary("current", bench.kernel_hash(), 1, 12345)
+    summary("stale", "0123456789abcdef", 1, 777)
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.load_traffic("current", 1) == 12345
+    assert bench.load_traffic("current", 2) is None
+    assert bench.load_traffic("stale", 1) is None
+    assert bench.load_traffic("missing", 1) is None
