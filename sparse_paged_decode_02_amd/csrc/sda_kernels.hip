@@ -586,6 +586,20 @@ __device__ __forceinline__ uint16_t* out_row(const Params& p, int r) {
 // policy is a template argument of the whole output loop: a branch around
 // the store alone is merged by the compiler into one plain store.
 template <bool kNt>
+__device__ __forceinline__ void store_row_oct(uint16_t* orow, const Params& p, int h, int d,
+                                              const f32x4& lo, const f32x4& hi) {
+  const u32x4 v = {float_to_bf16_bits(lo[0]) | (float_to_bf16_bits(lo[1]) << 16),
+                   float_to_bf16_bits(lo[2]) | (float_to_bf16_bits(lo[3]) << 16),
+                   float_to_bf16_bits(hi[0]) | (float_to_bf16_bits(hi[1]) << 16),
+                   float_to_bf16_bits(hi[2]) | (float_to_bf16_bits(hi[3]) << 16)};
+  u32x4* dst = reinterpret_cast<u32x4*>(orow + (int64_t)h * p.ohs + d);
+  if constexpr (kNt)
+    __builtin_nontemporal_store(v, dst);
+  else
+    *dst = v;
+}
+
+template <bool kNt>
 __device__ __forceinline__ void store_row_pair(uint16_t* orow, const Params& p, int h, int d,
                                                float o0, float o1) {
   uint32_t v = float_to_bf16_bits(o0) | (float_to_bf16_bits(o1) << 16);
@@ -870,6 +884,31 @@ split_kernel(const Params p) {
   __syncthreads();
 
   auto output_loop = [&](auto nt) {
+  if (kFused && p.wide_out) {
+    // 16-byte aligned output: 8 dims per thread, one 16-byte store (the same
+    // sums in the same order as the pair loop below).
+    for (int e = tid; e < ncols * (kDim / 8); e += kThreads) {
+      const int c = e / (kDim / 8), d = 8 * (e - c * (kDim / 8));
+      int token = tok0, h = c;
+      if (kAddr == kWindow) {
+        const int jl = c / p.heads;
+        token += jl;
+        h = c - jl * p.heads;
+      }
+      f32x4 lo = {0.f, 0.f, 0.f, 0.f}, hi = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float fw = s_fac[w][c];
+        const f32x4* src =
+            reinterpret_cast<const f32x4*>(s_acc + (size_t)w * kWaveStride + c * kAccStride + d);
+        lo += src[0] * fw;
+        hi += src[1] * fw;
+      }
+      uint16_t* orow = p.out + (int64_t)token * p.ots + (int64_t)g * p.ogs;
+      store_row_oct<decltype(nt)::value>(orow, p, h, d, lo, hi);
+    }
+    return;
+  }
   for (int e = tid; e < ncols * (kDim / 2); e += kThreads) {
     const int c = e / (kDim / 2), d = 2 * (e - c * (kDim / 2));
     // column c -> (token, head) and its output row
@@ -1133,9 +1172,17 @@ static bool large_output(const Params& p) {
   return (int64_t)p.rows * p.heads * kDim * 2 >= kNtOutputBytes;
 }
 
+// Output rows and heads on 16-byte boundaries: the fused epilogue stores 8
+// dims per thread.
+static bool wide_output(const Params& p) {
+  return (reinterpret_cast<uintptr_t>(p.out) & 15) == 0 && p.ots % 8 == 0 && p.ogs % 8 == 0 &&
+         p.ohs % 8 == 0;
+}
+
 hipError_t launch(const Params& p0, bool fp8, hipStream_t stream) {
   Params p = p0;
   p.nt_out = large_output(p) ? 1 : 0;
+  p.wide_out = wide_output(p) ? 1 : 0;
   p.order = launch_order(p, stream);
   if (fp8)
     launch_dtype<true>(p, stream);
@@ -1147,6 +1194,7 @@ hipError_t launch(const Params& p0, bool fp8, hipStream_t stream) {
 hipError_t launch_window(const Params& p0, hipStream_t stream) {
   Params p = p0;
   p.nt_out = large_output(p) ? 1 : 0;
+  p.wide_out = wide_output(p) ? 1 : 0;
   // grid.x = requests * token groups * KV groups; the combine runs per row.
   const unsigned wgs = (unsigned)(p.rows / p.rows_per_req * p.ntg * p.groups);
   if (p.splits == 1)

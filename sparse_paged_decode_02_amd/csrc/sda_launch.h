@@ -40,6 +40,7 @@ struct Params {
   int32_t query_len, window;  // window mode
   int32_t pack, ntg;          // window mode: tokens per workgroup, token groups per request
   int32_t nt_out;             // set by the launch: store the output non-temporally
+  int32_t wide_out;           // set by the launch: 16-byte aligned output, 8 dims per store
 };
 
 // Enqueue the split kernel (and the combine kernel when splits > 1) over

@@ -272,13 +272,16 @@ def test_gated_matches_oracle_gate():
         check_close(run(inp, splits=s), oracle_out(inp), what="gated splits=%d" % s)
 
 
-def test_strided_views_match_contiguous():
+@pytest.mark.parametrize("splits", [1, 2])
+def test_strided_views_match_contiguous(splits):
     """Padded head/row strides on query and output, padded token/page strides
-    on the cache (e.g. summaries packed inside a block): same bits."""
+    on the cache (e.g. summaries packed inside a block): same bits.  With one
+    split the contiguous output takes the 16-byte store path and the padded
+    one (head stride 194) the 4-byte one."""
     for kv in ("bf16", "fp8"):
         w = small(2, requests=2, kv=kv, pages_per_req=16, pos_lo=300, pos_hi=1023)
         inp = gen.make_inputs(w, device=DEV)
-        ref = run(inp, splits=2)
+        ref = run(inp, splits=splits)
         qpad = torch.zeros((w.rows, w.heads, 200), dtype=torch.bfloat16, device=DEV)
         qpad[..., :192] = inp.query
         cshape = inp.cache.shape
@@ -286,7 +289,7 @@ def test_strided_views_match_contiguous():
                            dtype=inp.cache.dtype, device=DEV)
         cpad[..., :384] = inp.cache
         opad = torch.zeros((w.rows, w.heads + 1, 194), dtype=torch.bfloat16, device=DEV)
-        out = run(inp, splits=2, query=qpad[..., :192], cache=cpad[..., :384],
+        out = run(inp, splits=splits, query=qpad[..., :192], cache=cpad[..., :384],
                   out=opad[:, :w.heads, :192])
         assert torch.equal(out, ref)
         assert (opad[:, w.heads:].view(torch.int16) == 0).all()
