@@ -84,3 +84,26 @@ def test_traffic_is_read_only_for_the_profiled_kernel_and_split_count(tmp_path, 
     assert bench.load_traffic("current", 2) is None
     assert bench.load_traffic("stale", 1) is None
     assert bench.load_traffic("missing", 1) is None
+
+
+def test_record_keeps_the_one_line_contract():
+    # The fields and units of the JSON line, and the roofline arithmetic:
+    # achieved = algorithmic bytes per launch / average launch time.
+    class A:
+        steps, warmup = 10, 2
+    rec = bench.record(A, value=6000.0, wall=10 * 61e-6, launch_avg_ms=0.0605,
+                       launch_ms=np.full(10, 0.061), bytes_per_launch=379478208.0, rows=256,
+                       dtype="bf16", config={"workload": "x"}, kernel="k", traffic=380000000)
+    for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step",
+                "higher_is_better", "scaling", "vs_baseline", "dtype", "data", "config"):
+        assert key in rec
+    assert rec["metric"] == bench.METRIC and rec["unit"] == "GB/s" and rec["n_gpus"] == 1
+    assert rec["higher_is_better"] is True and rec["vs_baseline"] is None
+    assert rec["data"] == "synthetic" and rec["config"] == {"workload": "x"}
+    assert abs(rec["ms_per_step"] - 0.061) < 1e-9
+    roof = rec["roofline"]
+    assert roof["bound"] == "hbm" and roof["peak"] == 8000.0 and roof["unit"] == "GB/s"
+    assert abs(roof["achieved"] - 379478208.0 / 60.5e-6 / 1e9) < 0.01
+    assert abs(roof["frac"] - roof["achieved"] / 8000.0) < 1e-4
+    assert roof["traffic"] == 380000000
+    assert abs(rec["rows_per_s"] - 256 * 10 / (10 * 61e-6)) < 1.0
