@@ -123,6 +123,21 @@ def swa_dense_reference(hp: oracle.SwaHostProblem, gate_values=None) -> np.ndarr
     return out
 
 
+def gate_values(hp) -> np.ndarray:
+    """[rows, heads] gate factors of a sparse-decode problem from the
+    (separately pinned) oracle gate: row r = token r / G, group r % G, and
+    head h takes gate[token, g * heads + h]."""
+    G = hp.cache.shape[1]
+    rows, heads = hp.query.shape[0], hp.query.shape[1]
+    gv = np.ones((rows, heads))
+    if hp.gate is None:
+        return gv
+    for r in range(rows):
+        for h in range(heads):
+            gv[r, h] = oracle.gate_value(int(hp.gate[r // G, (r % G) * heads + h]))
+    return gv
+
+
 def swa_gate_values(hp: oracle.SwaHostProblem) -> np.ndarray:
     """[rows, heads] gate factors from the (separately pinned) oracle gate."""
     G = hp.cache.shape[1]

@@ -8,7 +8,7 @@ import torch
 from oracle import oracle
 from oracle.hostprep import host_problem_from_inputs
 from sparse_paged_decode_02_amd import inputs as gen
-from _util import DIM, dense_reference, tiny_workload
+from _util import DIM, dense_reference, gate_values, tiny_workload
 
 
 def _hp(w, **kw):
@@ -18,10 +18,10 @@ def _hp(w, **kw):
 
 def _random_case(seed):
     rng = np.random.default_rng(seed)
-    block = int(rng.choice([4, 8, 16, 32]))
+    block = int(rng.choice([4, 8, 16, 32, 64]))
     rts = [d for d in (block, block // 2, block // 4, 8, 4) if d >= 1 and block % d == 0]
     rt = int(rng.choice(rts))
-    groups = int(rng.choice([1, 2, 3]))
+    groups = int(rng.choice([1, 2, 3, 4]))
     qlen = int(rng.choice([1, 1, 2, 3]))
     requests = int(rng.integers(1, 4))
     R = int(rng.integers(1, 10))
@@ -31,13 +31,15 @@ def _random_case(seed):
     live = (1, R) if rng.random() < 0.5 else None
     rows = requests * qlen * groups
     inactive = tuple(rng.choice(rows, size=int(rng.integers(0, 2)), replace=False).tolist())
+    gated = bool(rng.random() < 0.5)
     w = tiny_workload(seed, requests=requests, query_len=qlen, groups=groups, heads=heads,
                       block=block, pages_per_req=pages, R=R, kv=kv, live=live,
-                      region_tokens=0 if rt == block else rt, inactive_rows=inactive)
+                      region_tokens=0 if rt == block else rt, inactive_rows=inactive,
+                      gated=gated)
     return w, rng
 
 
-@pytest.mark.parametrize("seed", range(60))
+@pytest.mark.parametrize("seed", range(200))
 def test_oracle_matches_dense_sdpa(seed):
     w, rng = _random_case(seed)
     inp = gen.make_inputs(w, device="cpu")
@@ -50,7 +52,7 @@ def test_oracle_matches_dense_sdpa(seed):
             reg[r, free[0]] = live[0]
     hp = host_problem_from_inputs(inp)
     got = oracle.decode(hp)
-    ref = dense_reference(hp)
+    ref = dense_reference(hp, gate_values=gate_values(hp) if w.gated else None)
     assert np.array_equal(np.isnan(got), np.isnan(ref))
     m = ~np.isnan(ref)
     np.testing.assert_allclose(got[m], ref[m], rtol=0, atol=1e-10)
