@@ -268,6 +268,19 @@ def check_table_rows(block_table, rows: int, rows_per_request: int) -> None:
                            block_table.shape[0], rows, rows_per_request, need))
 
 
+def check_gate_shape(gate, rows: int, groups: int, heads: int) -> None:
+    """gate [tokens, groups * heads]: the library reads gate[r / groups,
+    (r % groups) * heads + h] for every row r and head h, so a smaller gate
+    would be read past its end: refuse it here."""
+    if gate is None or groups < 1 or rows % groups or gate.dim() != 2:
+        return  # absent, or a shape the other checks reject
+    if gate.shape[0] < rows // groups or gate.shape[1] < groups * heads:
+        raise SdaError(SDA_ERR_INVALID,
+                       "gate is [%d, %d]; %d rows of %d heads in %d KV groups need "
+                       "[%d, %d]" % (gate.shape[0], gate.shape[1], rows, heads, groups,
+                                     rows // groups, groups * heads))
+
+
 def sda_decode(query, cache, regions, block_table, positions, active, output, *, scale,
                query_len=1, splits, clear_inactive=True, k_scale=None, v_scale=None,
                gate=None, region_tokens=0, workspace=None, row_order=True,
@@ -284,6 +297,7 @@ def sda_decode(query, cache, regions, block_table, positions, active, output, *,
                   k_scale, v_scale, gate)
     rows, heads = query.shape[0], query.shape[1]
     check_table_rows(block_table, rows, cache.shape[1] * int(query_len))
+    check_gate_shape(gate, rows, cache.shape[1], heads)
     if workspace is None and (splits > 1 or row_order) and rows > 0:
         nbytes = sda_workspace_bytes(rows, heads, splits)
         if nbytes:

@@ -1,6 +1,7 @@
 """Binding-side checks the C ABI cannot make because it sees only pointers
-and strides: a block table with fewer rows than the request count that the
-row count implies is refused before anything reaches the device."""
+and strides: dtypes and shapes, a block table with fewer rows than the
+request count that the row count implies, and a gate smaller than the rows
+and heads read from it, are refused before anything reaches the device."""
 import pytest
 import torch
 
@@ -55,3 +56,55 @@ def test_logits_refuses_short_block_table(query_len, table_rows):
                              torch.zeros(rows, dtype=torch.int32),
                              groups=2, num_regions=32, query_len=query_len)
     assert e.value.status == B.SDA_ERR_INVALID and "block_table" in str(e.value)
+
+
+def _call(t, **kw):
+    B.sda_decode(t["query"], t["cache"], t["regions"], t["block_table"], t["positions"],
+                 t["active"], t["output"], scale=1.0, splits=1, row_order=False, **kw)
+
+
+@pytest.mark.parametrize("gate_shape", [(3, 8), (4, 7)])
+def test_decode_refuses_small_gate(gate_shape):
+    t = _decode_tensors(requests=4, table_rows=4)  # 8 rows = 4 tokens x 2 groups, 4 heads
+    with pytest.raises(B.SdaError) as e:
+        _call(t, gate=torch.zeros(gate_shape, dtype=torch.bfloat16))
+    assert e.value.status == B.SDA_ERR_INVALID and "gate" in str(e.value)
+
+
+@pytest.mark.parametrize("bad", ["query_dtype", "head_dim", "output_shape", "query_stride",
+                                 "cache_width", "cache_dtype", "regions_rows",
+                                 "regions_dtype", "positions_len", "active_dtype",
+                                 "scale_dtype", "gate_dtype"])
+def test_decode_refuses_malformed_tensors(bad):
+    t = _decode_tensors(requests=2, table_rows=2)
+    kw = {}
+    rows = t["query"].shape[0]
+    if bad == "query_dtype":
+        t["query"] = t["query"].float()
+    elif bad == "head_dim":
+        t["query"] = torch.zeros((rows, 4, 128), dtype=torch.bfloat16)
+        t["output"] = torch.zeros((rows, 4, 128), dtype=torch.bfloat16)
+    elif bad == "output_shape":
+        t["output"] = torch.zeros((rows, 3, 192), dtype=torch.bfloat16)
+    elif bad == "query_stride":
+        t["query"] = torch.zeros((rows, 4, 384), dtype=torch.bfloat16)[..., ::2]
+    elif bad == "cache_width":
+        t["cache"] = torch.zeros((4, 2, 16, 256), dtype=torch.bfloat16)
+    elif bad == "cache_dtype":
+        t["cache"] = torch.zeros((4, 2, 16, 384), dtype=torch.float16)
+    elif bad == "regions_rows":
+        t["regions"] = torch.zeros((rows + 1, 2), dtype=torch.int32)
+    elif bad == "regions_dtype":
+        t["regions"] = torch.zeros((rows, 2), dtype=torch.int64)
+    elif bad == "positions_len":
+        t["positions"] = torch.zeros(rows - 1, dtype=torch.int32)
+    elif bad == "active_dtype":
+        t["active"] = torch.ones(rows, dtype=torch.int32)
+    elif bad == "scale_dtype":
+        t["cache"] = torch.zeros((4, 2, 16, 384), dtype=torch.uint8)
+        kw = dict(k_scale=torch.ones(1, dtype=torch.float64), v_scale=torch.ones(1))
+    elif bad == "gate_dtype":
+        kw = dict(gate=torch.zeros((rows // 2, 8), dtype=torch.float32))
+    with pytest.raises(B.SdaError) as e:
+        _call(t, **kw)
+    assert e.value.status == B.SDA_ERR_INVALID
