@@ -521,6 +521,11 @@ def sda_indexer_logits(query, weights, summaries, summary_scales, block_table, p
             raise SdaError(SDA_ERR_INVALID, "%s must be contiguous int32 [rows]" % name)
     if scores is None:
         scores = torch.empty((rows, int(num_regions)), dtype=torch.float32, device=query.device)
+    if scores.dtype != torch.float32 or scores.dim() != 2 or \
+            tuple(scores.shape) != (rows, int(num_regions)) or \
+            (scores.shape[1] > 1 and scores.stride(1) != 1):
+        raise SdaError(SDA_ERR_INVALID,
+                       "scores must be float32 [rows, num_regions], unit inner stride")
     a = make_logits_args(query, weights, summaries, summary_scales, block_table, positions,
                          scores, groups=groups, query_len=query_len, region_tokens=region_tokens,
                          current=current, topk_lengths=topk_lengths)

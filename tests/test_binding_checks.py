@@ -108,3 +108,16 @@ def test_decode_refuses_malformed_tensors(bad):
     with pytest.raises(B.SdaError) as e:
         _call(t, **kw)
     assert e.value.status == B.SDA_ERR_INVALID
+
+
+@pytest.mark.parametrize("shape,dtype", [((3, 64), torch.float32), ((4, 32), torch.float32),
+                                         ((4, 64), torch.float16)])
+def test_logits_refuses_mismatched_scores(shape, dtype):
+    # 4 rows (2 requests x 2 groups), 64 score columns requested
+    q = torch.zeros((4, 8, 256), dtype=torch.uint8)
+    with pytest.raises(B.SdaError) as e:
+        B.sda_indexer_logits(q, torch.zeros((4, 8)), torch.zeros((8, 8, 256), dtype=torch.uint8),
+                             torch.zeros((8, 8)), torch.zeros((2, 4), dtype=torch.int32),
+                             torch.zeros(4, dtype=torch.int32), groups=2, num_regions=64,
+                             scores=torch.zeros(shape, dtype=dtype))
+    assert e.value.status == B.SDA_ERR_INVALID and "scores" in str(e.value)
