@@ -473,6 +473,22 @@ def test_row_order_grid_bounds(rows):
 
 
 # --- full-size workloads: sampled rows + properties ---------------------------
+@pytest.mark.parametrize("splits", [2, 4])
+def test_full_size_with_splits(splits):
+    # The bf16-gated workload at full size through the split partials and the
+    # combine kernel (the library's heuristic gives it one split).
+    w = gen.WORKLOADS[2]
+    _say("drawing full workload 2 for splits=%d" % splits)
+    inp = gen.make_inputs(w, device=DEV)
+    out = run(inp, splits=splits, label="full2 splits%d" % splits)
+    rng = np.random.default_rng(100 + splits)
+    rows = sorted(set(rng.choice(w.rows, size=16, replace=False).tolist() + [0, w.rows - 1]))
+    check_close(out, oracle_out(inp, rows=rows), rows=rows, what="full2 splits%d" % splits)
+    check_inactive_zero(out, inp)
+    del inp, out
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("k", [2, 3, 4, 5, 6, 7])
 def test_full_size_sampled(k):
     w = gen.WORKLOADS[k]
