@@ -278,9 +278,9 @@ def run_swa(args, dev) -> int:
                  metric="effective KV GB/s (% of HBM peak) and rows/s for gated "
                         "sliding-window decode")
     if not args.no_cpu_baseline:
-        threads = max(1, min(16, os.cpu_count() or 1))
-        print("[bench] cpu baseline: oracle on %d rows, %d threads" % (args.cpu_rows, threads),
-              file=sys.stderr, flush=True)
+        threads, why = host_threads()
+        print("[bench] cpu baseline: oracle on %d rows, %d threads (%s)"
+              % (args.cpu_rows, threads, why), file=sys.stderr, flush=True)
         rec["cpu_baseline"] = swa_cpu_baseline(base, outs[0], args.cpu_rows, threads,
                                                args.cpu_seconds)
     print(json.dumps(rec), flush=True)
@@ -395,7 +395,7 @@ def run_logits(args, dev) -> int:
                  kernel="logits_kernel", traffic=load_traffic(w.name, 1, "logits_kernel"),
                  metric="effective GB/s (% of HBM peak) and rows/s for decode indexer logits")
     if not args.no_cpu_baseline:
-        threads = max(1, min(16, os.cpu_count() or 1))
+        threads, _ = host_threads()
         print("[bench] cpu baseline: oracle logits", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = logits_cpu_baseline(base, outs[0], args.cpu_rows, threads,
                                                   args.cpu_seconds)
@@ -510,14 +510,129 @@ def cpu_baseline(inp, gpu_out, rows_sample: int, threads: int, min_seconds: floa
     }
 
 
+def host_threads() -> tuple:
+    """(threads for the CPU baseline, how that count was chosen).  Every core
+    this process may run on, capped by OMP_NUM_THREADS when it is set: a
+    GPU host that shares its cores among GPUs states each GPU's share there."""
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    if cap.isdigit() and 0 < int(cap) < avail:
+        return int(cap), "%d usable cores, OMP_NUM_THREADS=%s" % (avail, cap)
+    return max(1, avail), "%d usable cores" % avail
+
+
+def parse_also(args) -> list:
+    """Workloads timed after the headline in the same run: by default the
+    other decode workloads (2, 3, 4) when the headline is workload 5."""
+    if args.also is None:
+        return [2, 3, 4] if args.config == 5 else []
+    return [int(x) for x in args.also.split(",") if x.strip()]
+
+
+def summary_of(rec: dict) -> dict:
+    """The per-workload fields of a record, for the `other_configs` key."""
+    keep = ("value", "unit", "ms_per_step", "pct_hbm_peak", "rows_per_s", "us_per_call",
+            "dtype", "config", "roofline")
+    return {k: rec[k] for k in keep if k in rec}
+
+
+def measure_sparse(args, dev, k: int, with_cpu: bool) -> dict:
+    """Time sda_decode on workload k: draw its cache and `args.sets` input
+    sets, marshal each set's arguments once, time the calls, and free
+    everything before returning the record."""
+    import torch
+    from sparse_paged_decode_02_amd import binding as B
+    from sparse_paged_decode_02_amd import inputs as gen
+
+    w = gen.WORKLOADS[k]
+    splits = args.splits or w.splits or B.sda_splits(w.rows)
+
+    print("[bench] drawing %s" % workload_desc(w), file=sys.stderr, flush=True)
+    base = gen.make_inputs(w, device=dev, splits=splits)
+    sets = [base]
+    bt = base.block_table.cpu().numpy()
+    for i in range(1, args.sets):
+        sets.append(gen.make_inputs(w, device=dev, seed=w.seed + 100003 * i, cache=base.cache,
+                                    block_table=bt, splits=splits))
+    nbytes = []
+    for s in sets:
+        b, _ = algorithmic_bytes(w, s.positions.cpu().numpy(), s.regions.cpu().numpy(),
+                                 s.active.cpu().numpy())
+        nbytes.append(b)
+    outs = [torch.empty_like(s.query) for s in sets]
+    ws_bytes = B.sda_workspace_bytes(w.rows, w.heads, splits)
+    if args.no_row_order and splits == 1:
+        ws_bytes = 0
+    # The library ranks rows when given a workspace and the grid takes 2 to 4
+    # rounds of the resident workgroups (two per CU for grids of at least two
+    # per CU, else one).
+    cus = B.sda_device_compute_units()
+    grid = w.rows * splits
+    resident = 2 * cus if grid >= 2 * cus else cus
+    ordered = ws_bytes > 0 and resident < grid <= 4 * resident
+    workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    handle = ctypes.c_void_p(stream.cuda_stream)
+
+    # The argument block of every input set is marshalled once (the tensors
+    # stay alive in `sets`/`outs`); each step is then one C call.
+    prepared = []
+    for s, o in zip(sets, outs):
+        B.check_tensors(s.query, s.cache, s.regions, s.block_table, s.positions, s.active, o,
+                        s.k_scale, s.v_scale, s.gate)
+        prepared.append(B.make_args(
+            s.query, s.cache, s.regions, s.block_table, s.positions, s.active, o,
+            scale=s.scale, query_len=w.query_len, splits=splits, k_scale=s.k_scale,
+            v_scale=s.v_scale, gate=s.gate, region_tokens=w.region_tokens,
+            workspace=workspace if ws_bytes else None))
+
+    def call(i):
+        rc = B.sda_decode_raw(prepared[i % len(prepared)], handle)
+        if rc != B.SDA_OK:
+            raise B.SdaError(rc, B.status_string(rc))
+
+    wall, launch_avg_ms, launch_ms = time_calls(call, args.steps, args.warmup, stream)
+    total_bytes = sum(nbytes[i % len(sets)] for i in range(args.steps))
+    bytes_per_launch = float(np.mean([nbytes[i % len(sets)] for i in range(args.steps)]))
+    rec = record(args, value=total_bytes / wall / 1e9, wall=wall, launch_avg_ms=launch_avg_ms,
+                 launch_ms=launch_ms, bytes_per_launch=bytes_per_launch, rows=w.rows,
+                 dtype="bf16" if w.kv == "bf16" else "fp8-e4m3 cache, bf16 MFMA",
+                 config={"workload": workload_desc(w), "rows": w.rows, "heads": w.heads,
+                         "splits": splits, "row_order": "heaviest first" if ordered else "index",
+                         "input_sets": len(sets), "seed": w.seed},
+                 kernel=("sda order kernel + " if ordered else "") + "sda split kernel"
+                 + (" + combine" if splits > 1 else " (combine fused)"),
+                 traffic=load_traffic(w.name, splits))
+    if args.flush_mib > 0:
+        rec["flushed"] = time_flushed(call, args.steps, stream, args.flush_mib)
+    if with_cpu:
+        threads, why = host_threads()
+        print("[bench] cpu baseline: oracle on %d rows, %d threads (%s)"
+              % (args.cpu_rows, threads, why), file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline(base, outs[0], args.cpu_rows, threads,
+                                           args.cpu_seconds)
+        rec["cpu_baseline"]["threads_from"] = why
+    del prepared, outs, workspace, sets, base
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return rec
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=2,
-                    help="workload: 1..5, or 6 / 7 = the bf16-gated / FP8-cache shape at "
-                         "8-token regions")
+    ap.add_argument("--config", type=int, default=5,
+                    help="headline workload: 1..5, or 6 / 7 = the bf16-gated / FP8-cache "
+                         "shape at 8-token regions (default 5, the largest)")
+    ap.add_argument("--also", default=None, metavar="LIST",
+                    help="comma-separated workloads timed after the headline in the same "
+                         "run, reported under `other_configs` (default: 2,3,4 when the "
+                         "headline is 5; '' for none)")
     ap.add_argument("--swa", default="", metavar="NAME",
                     help="measure the gated sliding-window decode on workload NAME "
                          "(swa-gated, swa-mtp) instead")
@@ -577,72 +692,16 @@ def main() -> int:
         return run_select(args, dev)
     if args.logits:
         return run_logits(args, dev)
-    w = gen.WORKLOADS[args.config]
-    splits = args.splits or w.splits or B.sda_splits(w.rows)
-
-    print("[bench] drawing %s" % workload_desc(w), file=sys.stderr, flush=True)
-    base = gen.make_inputs(w, device=dev, splits=splits)
-    sets = [base]
-    bt = base.block_table.cpu().numpy()
-    for i in range(1, args.sets):
-        sets.append(gen.make_inputs(w, device=dev, seed=w.seed + 100003 * i, cache=base.cache,
-                                    block_table=bt, splits=splits))
-    nbytes = []
-    for s in sets:
-        b, _ = algorithmic_bytes(w, s.positions.cpu().numpy(), s.regions.cpu().numpy(),
-                                 s.active.cpu().numpy())
-        nbytes.append(b)
-    outs = [torch.empty_like(s.query) for s in sets]
-    ws_bytes = B.sda_workspace_bytes(w.rows, w.heads, splits)
-    if args.no_row_order and splits == 1:
-        ws_bytes = 0
-    # The library ranks rows when given a workspace and the grid takes 2 to 4
-    # rounds of the resident workgroups (512 for grids of >= 512, else 256).
-    grid = w.rows * splits
-    resident = 512 if grid >= 512 else 256
-    ordered = ws_bytes > 0 and resident < grid <= 4 * resident
-    workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream(dev)
-    handle = ctypes.c_void_p(stream.cuda_stream)
-
-    # The argument block of every input set is marshalled once (the tensors
-    # stay alive in `sets`/`outs`); each step is then one C call.
-    prepared = []
-    for s, o in zip(sets, outs):
-        B.check_tensors(s.query, s.cache, s.regions, s.block_table, s.positions, s.active, o,
-                        s.k_scale, s.v_scale, s.gate)
-        prepared.append(B.make_args(
-            s.query, s.cache, s.regions, s.block_table, s.positions, s.active, o,
-            scale=s.scale, query_len=w.query_len, splits=splits, k_scale=s.k_scale,
-            v_scale=s.v_scale, gate=s.gate, region_tokens=w.region_tokens,
-            workspace=workspace if ws_bytes else None))
-
-    def call(i):
-        rc = B.sda_decode_raw(prepared[i % len(prepared)], handle)
-        if rc != B.SDA_OK:
-            raise B.SdaError(rc, B.status_string(rc))
-
-    wall, launch_avg_ms, launch_ms = time_calls(call, args.steps, args.warmup, stream)
-    total_bytes = sum(nbytes[i % len(sets)] for i in range(args.steps))
-    bytes_per_launch = float(np.mean([nbytes[i % len(sets)] for i in range(args.steps)]))
-    rec = record(args, value=total_bytes / wall / 1e9, wall=wall, launch_avg_ms=launch_avg_ms,
-                 launch_ms=launch_ms, bytes_per_launch=bytes_per_launch, rows=w.rows,
-                 dtype="bf16" if w.kv == "bf16" else "fp8-e4m3 cache, bf16 MFMA",
-                 config={"workload": workload_desc(w), "rows": w.rows, "heads": w.heads,
-                         "splits": splits, "row_order": "heaviest first" if ordered else "index",
-                         "input_sets": len(sets), "seed": w.seed},
-                 kernel=("sda order kernel + " if ordered else "") + "sda split kernel"
-                 + (" + combine" if splits > 1 else " (combine fused)"),
-                 traffic=load_traffic(w.name, splits))
-    if args.flush_mib > 0:
-        rec["flushed"] = time_flushed(call, args.steps, stream, args.flush_mib)
-    if not args.no_cpu_baseline:
-        threads = max(1, min(16, os.cpu_count() or 1))
-        print("[bench] cpu baseline: oracle on %d rows, %d threads" % (args.cpu_rows, threads),
-              file=sys.stderr, flush=True)
-        rec["cpu_baseline"] = cpu_baseline(base, outs[0], args.cpu_rows, threads,
-                                           args.cpu_seconds)
-    print(json.dumps(rec), flush=True)
+    headline = measure_sparse(args, dev, args.config, with_cpu=not args.no_cpu_baseline)
+    others = parse_also(args)
+    if others:
+        # The other decode workloads of the same run, one after another (each
+        # draws its own cache; the previous one is freed first).
+        headline["other_configs"] = {}
+        for k in others:
+            rec = measure_sparse(args, dev, k, with_cpu=False)
+            headline["other_configs"][gen.WORKLOADS[k].name] = summary_of(rec)
+    print(json.dumps(headline), flush=True)
     return 0
 
 

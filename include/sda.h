@@ -32,7 +32,7 @@
 extern "C" {
 #endif
 
-#define SDA_ABI_VERSION 5
+#define SDA_ABI_VERSION 6
 #define SDA_HEAD_DIM 192     /* query / key / value head dim (fixed) */
 #define SDA_KV_ROW 384       /* one cache token row: K[0:192] then V[192:384] */
 #define SDA_MAX_HEADS 16     /* GQA-packed query heads per KV group */
@@ -68,7 +68,10 @@ typedef enum {
  *  groups       KV groups G (cache dim 1).
  *  query_len    query tokens per request (1 for decode, >1 for MTP verify).
  *  block        tokens per cache page (cache dim 2).
- *  R            region slots per row (regions dim 1), 0..SDA_MAX_R.
+ *  R            region slots per row (regions dim 1), 0..SDA_MAX_R.  R = 0
+ *               is accepted (every active row then outputs zeros), where
+ *               the page's kernel needs a regions tensor with at least one
+ *               column.
  *  region_tokens tokens per region; 0 means one region per page (= block).
  *               It must divide block.  Region id i covers tokens
  *               [i*region_tokens, (i+1)*region_tokens).
@@ -166,6 +169,9 @@ int sda_splits(int rows);
  * Bytes of workspace for sda_decode: the row order and row bins, rows*8
  * bytes rounded up to 256, plus, when splits > 1, the fp32 partial outputs
  * and log-sum-exps, rows*splits*heads*(192+1)*4 bytes rounded up to 256.
+ * The partials are the split outputs and log-sum-exps that
+ * `sparse_decode_attention` (page "...ops.sparse_decode_attention") allocates
+ * with torch.empty for its combine; here the caller owns that memory.
  * Returns 0 for invalid sizes.
  */
 size_t sda_workspace_bytes(int rows, int heads, int splits);
@@ -213,7 +219,7 @@ size_t sda_workspace_bytes(int rows, int heads, int splits);
  *  seq_lens     int32 [requests]: tokens of the request, the new ones
  *               included.
  *  scale        softmax scale applied to q.k.
- *  splits       >= 1 (sda_swa_splits): each row's window is cut into
+ *  splits       >= 1 (sda_swa_plan): each row's window is cut into
  *               `splits` contiguous runs whose partials are merged by
  *               log-sum-exp.  The result does not depend on it beyond
  *               rounding.
@@ -250,15 +256,31 @@ int sda_swa_decode(const sda_swa_args *args, hipStream_t stream);
 
 /*
  * Plan of a sliding-window call, the MI355X counterpart of `swa_decode_plan`
- * (named on page "vllm.models.step5.nvidia.sparse_attention"): writes the
- * pack (the largest, min(query_len, 16 / heads)) to *pack if pack is not NULL
- * and returns the split count: the rule of sda_splits applied to the
- * workgroup count requests * ceil(query_len / pack) * groups, further capped
- * so that every split keeps at least 8 chunks of 16 tokens of the packed
- * tokens' union window.  Host-only and pure; returns 1 (and pack 1) for
- * invalid sizes.
+ * (page "vllm.models.step5.nvidia.sparse_attention",
+ * `forward_with_headwise_gate`, which passes it the device's SM count before
+ * the window): writes the pack (the largest, min(query_len, 16 / heads)) to
+ * *pack if pack is not NULL and returns the split count: double while the
+ * doubled grid of requests * ceil(query_len / pack) * groups * splits * 2
+ * workgroups fits `compute_units` (up to 32 splits), further capped so that
+ * every split keeps at least 8 chunks of 16 tokens of the packed tokens'
+ * union window.  compute_units <= 0 reads the current device's count
+ * (sda_device_compute_units); given a count, the call is host-only and pure.
+ * Returns 1 (and pack 1) for invalid sizes.
  */
-int sda_swa_plan(int tokens, int groups, int heads, int query_len, int window, int *pack);
+int sda_swa_plan(int tokens, int groups, int heads, int query_len, int compute_units, int window,
+                 int *pack);
+
+/*
+ * Compute units of HIP device `device` (the current device when negative),
+ * from hipDeviceAttributeMultiprocessorCount, read once per device; 0 if the
+ * runtime cannot report it.  sda_decode, sda_swa_decode and
+ * sda_select_regions size their residency decisions (waves per workgroup,
+ * the row-order pass, two selection workgroups per CU) from the count of the
+ * device their stream runs on; they return SDA_ERR_LAUNCH when it cannot be
+ * read.  sda_splits does not use it: like the page's
+ * `sparse_decode_splits`, it depends on rows only.
+ */
+int sda_device_compute_units(int device);
 
 /*
  * Region selection: `select_regions` on page "vllm.models.step5.nvidia.

@@ -23,7 +23,7 @@ SDA_ERR_WORKSPACE = -3
 SDA_ERR_LAUNCH = -4
 SDA_KV_BF16 = 0
 SDA_KV_FP8_E4M3 = 1
-ABI_VERSION = 5
+ABI_VERSION = 6
 HEAD_DIM = 192
 
 
@@ -138,7 +138,9 @@ def lib() -> ctypes.CDLL:
             l.sda_swa_decode.restype = ctypes.c_int
             l.sda_swa_decode.argtypes = [ctypes.POINTER(SwaArgs), ctypes.c_void_p]
             l.sda_swa_plan.restype = ctypes.c_int
-            l.sda_swa_plan.argtypes = [ctypes.c_int] * 5 + [ctypes.POINTER(ctypes.c_int)]
+            l.sda_swa_plan.argtypes = [ctypes.c_int] * 6 + [ctypes.POINTER(ctypes.c_int)]
+            l.sda_device_compute_units.restype = ctypes.c_int
+            l.sda_device_compute_units.argtypes = [ctypes.c_int]
             l.sda_swa_args_size.restype = ctypes.c_size_t
             l.sda_swa_args_size.argtypes = []
             l.sda_select_regions.restype = ctypes.c_int
@@ -222,9 +224,21 @@ def make_args(query, cache, regions, block_table, positions, active, output, *, 
     return a
 
 
+def check_device(ref, **tensors) -> None:
+    """Every tensor the library dereferences must live on ``ref``'s GPU: the
+    C ABI sees only pointers, and a host pointer reaching a kernel would fault
+    the device.  ``None`` entries (optional arguments) are skipped."""
+    if not ref.is_cuda:
+        raise SdaError(SDA_ERR_INVALID, "tensors must be on a GPU (got %s)" % ref.device)
+    for name, t in tensors.items():
+        if t is not None and (not t.is_cuda or t.device != ref.device):
+            raise SdaError(SDA_ERR_INVALID, "%s is on %s; every tensor must be on %s"
+                           % (name, t.device, ref.device))
+
+
 def check_tensors(query, cache, regions, block_table, positions, active, output,
                   k_scale, v_scale, gate):
-    """dtype checks the C ABI cannot make (it sees only pointers)."""
+    """dtype and shape checks the C ABI cannot make (it sees only pointers)."""
     if query.dtype != torch.bfloat16 or output.dtype != torch.bfloat16:
         raise SdaError(SDA_ERR_INVALID, "query and output must be bfloat16")
     if query.dim() != 3 or output.shape != query.shape or query.shape[2] != HEAD_DIM:
@@ -298,6 +312,9 @@ def sda_decode(query, cache, regions, block_table, positions, active, output, *,
     rows, heads = query.shape[0], query.shape[1]
     check_table_rows(block_table, rows, cache.shape[1] * int(query_len))
     check_gate_shape(gate, rows, cache.shape[1], heads)
+    check_device(query, cache=cache, regions=regions, block_table=block_table,
+                 positions=positions, active=active, output=output, k_scale=k_scale,
+                 v_scale=v_scale, gate=gate, workspace=workspace)
     if workspace is None and (splits > 1 or row_order) and rows > 0:
         nbytes = sda_workspace_bytes(rows, heads, splits)
         if nbytes:
@@ -307,8 +324,8 @@ def sda_decode(query, cache, regions, block_table, positions, active, output, *,
                   k_scale=k_scale, v_scale=v_scale, gate=gate, region_tokens=region_tokens,
                   workspace=workspace)
     if stream is None:
-        stream = torch.cuda.current_stream(query.device) if query.is_cuda else None
-    handle = None if stream is None else ctypes.c_void_p(stream.cuda_stream)
+        stream = torch.cuda.current_stream(query.device)
+    handle = ctypes.c_void_p(stream.cuda_stream)
     rc = lib().sda_decode(ctypes.byref(a), handle)
     if rc != SDA_OK:
         raise SdaError(rc, status_string(rc))
@@ -319,12 +336,20 @@ def sda_decode_raw(args: DecodeArgs, stream_handle=None) -> int:
     return int(lib().sda_decode(ctypes.byref(args), stream_handle))
 
 
-def sda_swa_plan(tokens: int, groups: int, heads: int, query_len: int, window: int) -> tuple:
-    """(pack, splits) the library picks for a sliding-window call."""
+def sda_swa_plan(tokens: int, groups: int, heads: int, query_len: int, window: int,
+                 compute_units: int = 0) -> tuple:
+    """(pack, splits) the library picks for a sliding-window call on a device
+    with ``compute_units`` CUs (0: the current device)."""
     pack = ctypes.c_int(0)
     splits = lib().sda_swa_plan(int(tokens), int(groups), int(heads), int(query_len),
-                                int(window), ctypes.byref(pack))
+                                int(compute_units), int(window), ctypes.byref(pack))
     return int(pack.value), int(splits)
+
+
+def sda_device_compute_units(device: int = -1) -> int:
+    """Compute units of HIP device ``device`` (-1: the current one); 0 if the
+    runtime cannot report it."""
+    return int(lib().sda_device_compute_units(int(device)))
 
 
 def make_swa_args(query, cache, block_table, seq_lens, output, *, scale, window, query_len=1,
@@ -392,6 +417,8 @@ def sda_swa_decode(query, cache, block_table, seq_lens, output, *, scale, window
     """
     check_swa_tensors(query, cache, block_table, seq_lens, output, gate)
     check_table_rows(block_table, query.shape[0], int(query_len))
+    check_device(query, cache=cache, block_table=block_table, seq_lens=seq_lens,
+                 output=output, gate=gate, workspace=workspace)
     groups = cache.shape[1]
     rows, heads = query.shape[0] * groups, query.shape[1] // groups
     if workspace is None and splits > 1 and rows > 0:
@@ -402,8 +429,8 @@ def sda_swa_decode(query, cache, block_table, seq_lens, output, *, scale, window
                       query_len=query_len, splits=splits, pack=pack, gate=gate,
                       workspace=workspace)
     if stream is None:
-        stream = torch.cuda.current_stream(query.device) if query.is_cuda else None
-    handle = None if stream is None else ctypes.c_void_p(stream.cuda_stream)
+        stream = torch.cuda.current_stream(query.device)
+    handle = ctypes.c_void_p(stream.cuda_stream)
     rc = lib().sda_swa_decode(ctypes.byref(a), handle)
     if rc != SDA_OK:
         raise SdaError(rc, status_string(rc))
@@ -446,10 +473,11 @@ def sda_select_regions(scores, current, topk, *, topk_lengths=None, out=None,
     if out.dtype != torch.int32 or out.dim() != 2 or out.shape != (rows, int(topk)) or (
             topk > 1 and out.stride(1) != 1):
         raise SdaError(SDA_ERR_INVALID, "out must be int32 [rows, topk], unit inner stride")
+    check_device(scores, current=current, topk_lengths=topk_lengths, out=out)
     a = make_select_args(scores, current, topk, out, topk_lengths)
     if stream is None:
-        stream = torch.cuda.current_stream(scores.device) if scores.is_cuda else None
-    handle = None if stream is None else ctypes.c_void_p(stream.cuda_stream)
+        stream = torch.cuda.current_stream(scores.device)
+    handle = ctypes.c_void_p(stream.cuda_stream)
     rc = lib().sda_select_regions(ctypes.byref(a), handle)
     if rc != SDA_OK:
         raise SdaError(rc, status_string(rc))
@@ -526,12 +554,15 @@ def sda_indexer_logits(query, weights, summaries, summary_scales, block_table, p
             (scores.shape[1] > 1 and scores.stride(1) != 1):
         raise SdaError(SDA_ERR_INVALID,
                        "scores must be float32 [rows, num_regions], unit inner stride")
+    check_device(query, weights=weights, summaries=summaries, summary_scales=summary_scales,
+                 block_table=block_table, positions=positions, scores=scores, current=current,
+                 topk_lengths=topk_lengths)
     a = make_logits_args(query, weights, summaries, summary_scales, block_table, positions,
                          scores, groups=groups, query_len=query_len, region_tokens=region_tokens,
                          current=current, topk_lengths=topk_lengths)
     if stream is None:
-        stream = torch.cuda.current_stream(query.device) if query.is_cuda else None
-    handle = None if stream is None else ctypes.c_void_p(stream.cuda_stream)
+        stream = torch.cuda.current_stream(query.device)
+    handle = ctypes.c_void_p(stream.cuda_stream)
     rc = lib().sda_indexer_logits(ctypes.byref(a), handle)
     if rc != SDA_OK:
         raise SdaError(rc, status_string(rc))

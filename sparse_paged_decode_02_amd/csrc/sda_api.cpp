@@ -5,6 +5,8 @@
 
 #include <hip/hip_runtime_api.h>
 
+#include <atomic>
+
 #include "sda_launch.h"
 
 static_assert(SDA_MAX_R == sda::kMaxRegions, "LDS region list must hold SDA_MAX_R slots");
@@ -34,7 +36,7 @@ void split_areas(sda::Params& p, void* workspace) {
 // rows*splits*2 still fits the 256 CUs.  That is the page's rule and bound,
 // for a different reason.  On the bf16 gated workload (256 rows) 2 splits
 // are slower than 1: the merge costs more than the idle CUs of inactive rows.
-constexpr int kComputeUnits = 256;
+constexpr int kComputeUnits = 256;  // MI355X; the target of sda_splits, which stays pure
 constexpr int kMaxHeuristicSplits = 32;
 constexpr int kSwaMinChunksPerSplit = 8;
 
@@ -45,9 +47,44 @@ int max_pack(int heads, int query_len) {
   return fit < query_len ? fit : query_len;
 }
 
+// Compute units of each device, read once (0 = not read yet).  The plans
+// and residency decisions size grids from the device the call runs on, as
+// the pages size theirs from `multi_processor_count`.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_device_cus[kMaxDevices];
+
+int device_cus(int device) {
+  if (device < 0) {
+    if (hipGetDevice(&device) != hipSuccess) return 0;
+  }
+  if (device >= kMaxDevices) {
+    int n = 0;
+    return hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, device) == hipSuccess
+               ? n
+               : 0;
+  }
+  int n = g_device_cus[device].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess ||
+      n <= 0)
+    return 0;
+  g_device_cus[device].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+// The device a launch on `stream` runs on: the stream's own, or the current
+// device for the null stream.
+int stream_cus(hipStream_t stream) {
+  int device = -1;
+  if (stream && hipStreamGetDevice(stream, &device) != hipSuccess) return 0;
+  return device_cus(device);
+}
+
 }  // namespace
 
 extern "C" {
+
+int sda_device_compute_units(int device) { return device_cus(device); }
 
 int sda_abi_version(void) { return SDA_ABI_VERSION; }
 
@@ -163,6 +200,8 @@ int sda_decode(const sda_decode_args* a, hipStream_t stream) {
     p.order_ws = static_cast<int32_t*>(a->workspace);
     if (a->splits > 1) split_areas(p, a->workspace);
   }
+  p.cus = stream_cus(stream);
+  if (p.cus <= 0) return SDA_ERR_LAUNCH;
 
   hipError_t e = sda::launch(p, fp8, stream);
   return e == hipSuccess ? SDA_OK : SDA_ERR_LAUNCH;
@@ -170,20 +209,23 @@ int sda_decode(const sda_decode_args* a, hipStream_t stream) {
 
 size_t sda_swa_args_size(void) { return sizeof(sda_swa_args); }
 
-int sda_swa_plan(int tokens, int groups, int heads, int query_len, int window, int* pack) {
+int sda_swa_plan(int tokens, int groups, int heads, int query_len, int compute_units, int window,
+                 int* pack) {
   if (pack) *pack = 1;
   if (tokens <= 0 || groups <= 0 || window <= 0 || heads < 1 || heads > SDA_MAX_HEADS ||
       query_len < 1 || tokens % query_len)
     return 1;
+  const int cus = compute_units > 0 ? compute_units : device_cus(-1);
+  if (cus <= 0) return 1;
   const int pk = max_pack(heads, query_len);
   if (pack) *pack = pk;
-  // The row-count rule of sda_splits on workgroups, and at least
-  // kSwaMinChunksPerSplit 16-token chunks per split so that each of the 4
-  // waves keeps its pipeline.
+  // The row-count rule of sda_splits on workgroups, for the device's compute
+  // units, and at least kSwaMinChunksPerSplit 16-token chunks per split so
+  // that each of the 4 waves keeps its pipeline.
   const int64_t wgs = (int64_t)(tokens / query_len) * ((query_len + pk - 1) / pk) * groups;
   const int64_t chunks = ((int64_t)window + pk - 1 + 15) / 16;
   int splits = 1;
-  while (splits < kMaxHeuristicSplits && wgs * splits * 2 <= kComputeUnits &&
+  while (splits < kMaxHeuristicSplits && wgs * splits * 2 <= cus &&
          chunks >= (int64_t)kSwaMinChunksPerSplit * splits * 2)
     splits *= 2;
   return splits;
@@ -262,6 +304,8 @@ int sda_swa_decode(const sda_swa_args* a, hipStream_t stream) {
       return SDA_ERR_WORKSPACE;
     split_areas(p, a->workspace);
   }
+  p.cus = stream_cus(stream);
+  if (p.cus <= 0) return SDA_ERR_LAUNCH;
 
   hipError_t e = sda::launch_window(p, stream);
   return e == hipSuccess ? SDA_OK : SDA_ERR_LAUNCH;
@@ -290,6 +334,8 @@ int sda_select_regions(const sda_select_args* a, hipStream_t stream) {
   p.rows = a->rows;
   p.S = a->num_regions;
   p.topk = a->topk;
+  p.cus = stream_cus(stream);
+  if (p.cus <= 0) return SDA_ERR_LAUNCH;
   hipError_t e = sda::launch_select(p, stream);
   return e == hipSuccess ? SDA_OK : SDA_ERR_LAUNCH;
 }

@@ -67,7 +67,6 @@ constexpr int kDim = 192;
 // that one workgroup's prologue and epilogue overlap the other's streaming).
 constexpr int kWavesSmallGrid = 4;
 constexpr int kWavesLargeGrid = 2;
-constexpr int kComputeUnits = 256;
 constexpr int kStages = 2;          // LDS stages per wave: 1 computed, 1 in flight
 constexpr int kOpsPerChunk = 12;    // vector-memory instructions per chunk issue
 constexpr int kStageBytes = 6144;   // K (or V) bytes of one chunk (16 bf16 / 32 FP8 tokens)
@@ -1097,11 +1096,14 @@ __global__ __launch_bounds__(kOrderBlock) void order_kernel(Params p, const int3
   if (bin >= 0) p.order_ws[blockIdx.x * kOrderBlock + s_cnt[bin * kOrderWaves + wave] + rank] = r;
 }
 
-// Workgroups resident at once for a grid of `wgs` workgroups (the wave
-// count, and with it the workgroups per CU, follows from the grid size).
-int64_t resident_workgroups(int64_t wgs) {
-  return wgs >= 2 * kComputeUnits ? 2 * kComputeUnits : kComputeUnits;
+// Workgroups resident at once for a grid of `wgs` workgroups on `cus`
+// compute units (the wave count, and with it the workgroups per CU, follows
+// from the grid size).
+int64_t resident_workgroups(int64_t wgs, int cus) {
+  return wgs >= 2 * (int64_t)cus ? 2 * (int64_t)cus : (int64_t)cus;
 }
+
+bool two_per_cu(int64_t wgs, int cus) { return wgs >= 2 * (int64_t)cus; }
 
 // Enqueue the bin and order kernels when they pay; returns the order to
 // follow, or null for index order.  They pay when the grid takes a few
@@ -1109,7 +1111,7 @@ int64_t resident_workgroups(int64_t wgs) {
 // and with many the tail is a small part of the launch.
 const int32_t* launch_order(const Params& p, hipStream_t stream) {
   const int64_t wgs = (int64_t)p.rows * p.splits;
-  const int64_t resident = resident_workgroups(wgs);
+  const int64_t resident = resident_workgroups(wgs, p.cus);
   if (!p.order_ws || wgs <= resident || wgs > kOrderMaxRounds * resident) return nullptr;
   // The workspace's order area holds the bins ([rows] after the order).
   int32_t* bins = p.order_ws + p.rows;
@@ -1124,7 +1126,7 @@ const int32_t* launch_order(const Params& p, hipStream_t stream) {
 template <bool kFp8, bool kFused, int kAddr>
 void launch_split(const Params& p, unsigned wgs, hipStream_t stream) {
   const dim3 grid(wgs, (unsigned)p.splits);
-  if (resident_workgroups((int64_t)wgs * p.splits) == 2 * kComputeUnits)
+  if (two_per_cu((int64_t)wgs * p.splits, p.cus))
     hipLaunchKernelGGL((split_kernel<kFp8, kFused, kAddr, kWavesLargeGrid>), grid,
                        dim3(64 * kWavesLargeGrid), 0, stream, p);
   else

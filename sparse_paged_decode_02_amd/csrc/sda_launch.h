@@ -41,6 +41,7 @@ struct Params {
   int32_t pack, ntg;          // window mode: tokens per workgroup, token groups per request
   int32_t nt_out;             // set by the launch: store the output non-temporally
   int32_t wide_out;           // set by the launch: 16-byte aligned output, 8 dims per store
+  int32_t cus;                // compute units of the device the call runs on
 };
 
 // Enqueue the split kernel (and the combine kernel when splits > 1) over
@@ -66,6 +67,7 @@ struct SelParams {
   int32_t* out;               // [rows, topk]
   int64_t ors;
   int32_t rows, S, topk;
+  int32_t cus;                // compute units of the device the call runs on
 };
 
 hipError_t launch_select(const SelParams& p, hipStream_t stream);

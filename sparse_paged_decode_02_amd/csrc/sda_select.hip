@@ -47,7 +47,6 @@ constexpr int kHistBins = 4096;
 constexpr int kCandCap = 4096;  // keys of the first pass's threshold bin kept in LDS
 constexpr int kRankCap = 1024;  // listed keys ranked directly (at least one lane each)
 static_assert(kRankCap <= kSelThreads && kRankCap + 3 <= kCandCap, "rank list fits");
-constexpr int kComputeUnits = 256;
 
 // Keys that order like the floats: flip all bits of negatives, set the sign
 // bit of non-negatives.  -0.0 -> 0x7FFFFFFF < +0.0 -> 0x80000000.
@@ -405,7 +404,7 @@ void select_kernel(const SelParams p) {
 // Rows beyond one per CU run two workgroups per CU where the keys fit.
 template <int I>
 void launch_select(const SelParams& p, hipStream_t stream) {
-  if (I <= 4 && p.rows > kComputeUnits)
+  if (I <= 4 && p.rows > p.cus)
     hipLaunchKernelGGL((select_kernel<I, I <= 4>), dim3((unsigned)p.rows), dim3(kSelThreads), 0,
                        stream, p);
   else

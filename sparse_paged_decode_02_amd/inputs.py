@@ -248,7 +248,7 @@ class SwaWorkload:
     seq_lo: int                  # sequence length ~ U[seq_lo, seq_hi]
     seq_hi: int
     gated: bool = True
-    splits: int | None = None    # None: sda_swa_splits(...)
+    splits: int | None = None    # None: sda_swa_plan(...)
     seed: int = 0
 
     @property

@@ -21,7 +21,7 @@ def test_library_exports_every_declared_function():
     assert {"sda_decode", "sda_splits", "sda_workspace_bytes", "sda_status_string",
             "sda_abi_version", "sda_args_size", "sda_swa_decode", "sda_swa_plan",
             "sda_select_regions", "sda_select_args_size", "sda_indexer_logits",
-            "sda_logits_args_size",
+            "sda_logits_args_size", "sda_device_compute_units",
             "sda_swa_args_size"} <= set(names)
     lib = B.lib()
     for n in names:
@@ -161,8 +161,24 @@ def test_rows_limit():
 @pytest.mark.parametrize("tokens,groups,heads,qlen,window,pack,splits",
                          _table("swa_plan_mi355x.txt"))
 def test_swa_plan_table(tokens, groups, heads, qlen, window, pack, splits):
-    assert B.sda_swa_plan(tokens, groups, heads, qlen, window) == (pack, splits)
-    assert B.lib().sda_swa_plan(tokens, groups, heads, qlen, window, None) == splits
+    # the table is worked for MI355X's 256 compute units, passed explicitly
+    # (the page's swa_decode_plan takes the device's SM count the same way)
+    assert B.sda_swa_plan(tokens, groups, heads, qlen, window, compute_units=256) == (pack,
+                                                                                     splits)
+    assert B.lib().sda_swa_plan(tokens, groups, heads, qlen, 256, window, None) == splits
+
+
+@pytest.mark.parametrize("cus,splits", [(256, 4), (128, 2), (64, 1), (512, 8), (1024, 8)])
+def test_swa_plan_follows_compute_units(cus, splits):
+    # 16 requests x 4 groups = 64 workgroups, window 1024 (64 chunks): double
+    # while 64 * splits * 2 <= cus and 64 >= 16 * splits (the chunk rule
+    # holds 1024 CUs at 8).
+    assert B.sda_swa_plan(16, 4, 16, 1, 1024, compute_units=cus) == (1, splits)
+
+
+def test_device_compute_units_without_a_device():
+    # No GPU in this process (or an out-of-range id): 0, never a guess.
+    assert B.sda_device_compute_units(1 << 20) == 0
 
 
 def _valid_swa(**over):

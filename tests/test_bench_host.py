@@ -107,3 +107,49 @@ def test_record_keeps_the_one_line_contract():
     assert abs(roof["frac"] - roof["achieved"] / 8000.0) < 1e-4
     assert roof["traffic"] == 380000000
     assert abs(rec["rows_per_s"] - 256 * 10 / (10 * 61e-6)) < 1.0
+
+
+def _parsed(*argv):
+    class A:
+        pass
+    a = A()
+    a.config, a.also = 5, None
+    for k, v in zip(argv[::2], argv[1::2]):
+        setattr(a, k, v)
+    return a
+
+
+def test_default_headline_is_the_largest_workload_with_the_others_after_it():
+    # The driver runs bench.py with no --config: the headline is workload 5
+    # (large-batch FP8, the largest), and workloads 2-4 follow in the same run.
+    r = subprocess.run([sys.executable, "-c",
+                        "import sys, bench; sys.argv = ['bench.py', '--help']; bench.main()"],
+                       capture_output=True, text=True, timeout=120, cwd=ROOT)
+    assert "default 5" in r.stdout
+    assert bench.parse_also(_parsed()) == [2, 3, 4]
+    assert bench.parse_also(_parsed("config", 2)) == []
+    assert bench.parse_also(_parsed("also", "")) == []
+    assert bench.parse_also(_parsed("config", 3, "also", "2,4")) == [2, 4]
+    assert gen.WORKLOADS[5].rows == max(w.rows for k, w in gen.WORKLOADS.items() if k <= 5)
+
+
+def test_summary_keeps_each_workloads_roofline():
+    class A:
+        steps, warmup = 10, 2
+    rec = bench.record(A, value=6000.0, wall=1e-3, launch_avg_ms=0.1, launch_ms=np.full(10, 0.1),
+                       bytes_per_launch=6e8, rows=512, dtype="bf16", config={"workload": "y"},
+                       kernel="k", traffic=None)
+    s = bench.summary_of(rec)
+    assert s["roofline"] == rec["roofline"] and s["config"] == {"workload": "y"}
+    assert "metric" not in s and "n_gpus" not in s
+
+
+def test_host_threads_use_every_usable_core_up_to_the_stated_share(monkeypatch):
+    avail = len(os.sched_getaffinity(0))
+    monkeypatch.delenv("OMP_NUM_THREADS", raising=False)
+    assert bench.host_threads()[0] == avail
+    monkeypatch.setenv("OMP_NUM_THREADS", "1")
+    n, why = bench.host_threads()
+    assert n == 1 and "OMP_NUM_THREADS=1" in why
+    monkeypatch.setenv("OMP_NUM_THREADS", str(avail + 5))
+    assert bench.host_threads()[0] == avail

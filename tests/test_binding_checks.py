@@ -121,3 +121,70 @@ def test_logits_refuses_mismatched_scores(shape, dtype):
                              torch.zeros(4, dtype=torch.int32), groups=2, num_regions=64,
                              scores=torch.zeros(shape, dtype=dtype))
     assert e.value.status == B.SDA_ERR_INVALID and "scores" in str(e.value)
+
+
+# --- every tensor the library dereferences must be on the query's GPU --------
+def test_decode_refuses_host_tensors():
+    # Well-formed shapes on the host: refused before the C call (a host
+    # pointer reaching a kernel would fault the device).
+    t = _decode_tensors(requests=2, table_rows=2)
+    with pytest.raises(B.SdaError) as e:
+        _call(t)
+    assert e.value.status == B.SDA_ERR_INVALID and "GPU" in str(e.value)
+
+
+def test_swa_select_logits_refuse_host_tensors():
+    G, heads, tokens = 2, 4, 4
+    with pytest.raises(B.SdaError) as e:
+        B.sda_swa_decode(torch.zeros((tokens, G * heads, 192), dtype=torch.bfloat16),
+                         torch.zeros((4, G, 64, 384), dtype=torch.bfloat16),
+                         torch.zeros((tokens, 4), dtype=torch.int32),
+                         torch.full((tokens,), 10, dtype=torch.int32),
+                         torch.zeros((tokens, G * heads, 192), dtype=torch.bfloat16),
+                         scale=1.0, window=8, query_len=1, splits=1)
+    assert e.value.status == B.SDA_ERR_INVALID and "GPU" in str(e.value)
+    with pytest.raises(B.SdaError) as e:
+        B.sda_select_regions(torch.zeros((4, 16)), torch.zeros(4, dtype=torch.int32), 4)
+    assert e.value.status == B.SDA_ERR_INVALID and "GPU" in str(e.value)
+    with pytest.raises(B.SdaError) as e:
+        B.sda_indexer_logits(torch.zeros((4, 8, 256), dtype=torch.uint8), torch.zeros((4, 8)),
+                             torch.zeros((8, 8, 256), dtype=torch.uint8), torch.zeros((8, 8)),
+                             torch.zeros((2, 4), dtype=torch.int32),
+                             torch.zeros(4, dtype=torch.int32), groups=2, num_regions=64)
+    assert e.value.status == B.SDA_ERR_INVALID and "GPU" in str(e.value)
+
+
+class _OnDevice:
+    """Stand-in for a tensor on a given device (no GPU needed to test the
+    rule itself)."""
+
+    def __init__(self, device: str):
+        self.device = torch.device(device)
+        self.is_cuda = self.device.type == "cuda"
+
+
+@pytest.mark.parametrize("name,where", [("k_scale", "cpu"), ("gate", "cpu"),
+                                        ("workspace", "cuda:1"), ("out", "cpu")])
+def test_check_device_names_the_stray_tensor(name, where):
+    ref = _OnDevice("cuda:0")
+    others = {"cache": _OnDevice("cuda:0"), "v_scale": None, name: _OnDevice(where)}
+    with pytest.raises(B.SdaError) as e:
+        B.check_device(ref, **others)
+    assert e.value.status == B.SDA_ERR_INVALID and name in str(e.value)
+    B.check_device(ref, cache=_OnDevice("cuda:0"), v_scale=None)  # all on the GPU: fine
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("stray", ["k_scale", "gate"])
+def test_decode_refuses_host_scale_or_gate_gpu(stray):
+    dev = "cuda:0"
+    t = {k: v.to(dev) for k, v in _decode_tensors(requests=2, table_rows=2).items()}
+    kw = {}
+    if stray == "k_scale":
+        t["cache"] = torch.zeros((4, 2, 16, 384), dtype=torch.uint8, device=dev)
+        kw = dict(k_scale=torch.tensor([0.05]), v_scale=torch.tensor([0.04], device=dev))
+    else:
+        kw = dict(gate=torch.zeros((2, 8), dtype=torch.bfloat16))
+    with pytest.raises(B.SdaError) as e:
+        _call(t, **kw)
+    assert e.value.status == B.SDA_ERR_INVALID and stray in str(e.value)

@@ -351,16 +351,12 @@ def test_one_hot_probes(kv, splits):
             if mode == 1 and (int(pos[r]) + 1) // w.block < w.pages_per_req:
                 _hot(inp, kv, req, g, int(pos[r]) + 1, hot_val * 1.5)   # masked: must lose
         targets[r] = (req, g, t)
-    # rows of one request share (req, g) slabs only within a group; give each
-    # row its own group slot so targets cannot collide
+    # with query_len 1 each (request, group) slab belongs to one row, so the
+    # hot tokens of different rows cannot collide
     seen = {}
     for r, (req, g, t) in targets.items():
-        key = (req, g)
-        assert key not in seen or True
-        seen.setdefault(key, []).append(r)
-    for key, rs in seen.items():
-        if len(rs) > 1:       # query_len 1: one row per (req, g)
-            raise AssertionError("probe layout")
+        seen.setdefault((req, g), []).append(r)
+    assert all(len(rs) == 1 for rs in seen.values()), "probe layout"
     for r, (req, g, t) in targets.items():
         targets[r] = (req, g, t) + _hot(inp, kv, req, g, t, hot_val)
     out = run(inp, splits=splits, label="one-hot %s" % kv)
