@@ -27,15 +27,34 @@ KV_FP8_E4M3 = 1
 DIM = 192
 
 
-def build(force: bool = False) -> str:
-    """Compile the oracle with gcc (plain -O2, no fast-math)."""
-    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        tmp = _LIB + ".tmp%d" % os.getpid()
+_LIB_SAN = os.path.join(_HERE, "libsda_oracle_san.so")
+# Sanitizer flags for the checked build: every report aborts the process.
+SANITIZE_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+                  "-fno-omit-frame-pointer", "-g"]
+
+
+def sanitized() -> bool:
+    """True when the checked build is selected (SDA_ORACLE_SANITIZE=1).  The
+    process must then have the ASan and UBSan runtimes preloaded."""
+    return os.environ.get("SDA_ORACLE_SANITIZE", "") == "1"
+
+
+def build(force: bool = False, sanitize: bool | None = None) -> str:
+    """Compile the oracle with gcc (plain -O2, no fast-math).  ``sanitize``
+    (default: ``sanitized()``) builds the AddressSanitizer +
+    UndefinedBehaviorSanitizer variant instead, libsda_oracle_san.so."""
+    if sanitize is None:
+        sanitize = sanitized()
+    lib_path = _LIB_SAN if sanitize else _LIB
+    if force or not os.path.exists(lib_path) or \
+            os.path.getmtime(lib_path) < os.path.getmtime(_SRC):
+        tmp = lib_path + ".tmp%d" % os.getpid()
         subprocess.check_call(
             ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fno-fast-math",
-             "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"])
-        os.replace(tmp, _LIB)
-    return _LIB
+             "-Wall", "-Wextra"] + (SANITIZE_FLAGS if sanitize else []) +
+            ["-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, lib_path)
+    return lib_path
 
 
 class _Problem(ctypes.Structure):

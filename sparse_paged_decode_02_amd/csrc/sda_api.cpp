@@ -222,7 +222,7 @@ int sda_swa_plan(int tokens, int groups, int heads, int query_len, int compute_u
   // The row-count rule of sda_splits on workgroups, for the device's compute
   // units, and at least kSwaMinChunksPerSplit 16-token chunks per split so
   // that each of the 4 waves keeps its pipeline.
-  const int64_t wgs = (int64_t)(tokens / query_len) * ((query_len + pk - 1) / pk) * groups;
+  const int64_t wgs = (int64_t)(tokens / query_len) * (((int64_t)query_len + pk - 1) / pk) * groups;
   const int64_t chunks = ((int64_t)window + pk - 1 + 15) / 16;
   int splits = 1;
   while (splits < kMaxHeuristicSplits && wgs * splits * 2 <= cus &&
