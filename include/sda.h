@@ -45,7 +45,9 @@ typedef enum {
   SDA_ERR_INVALID = -1,      /* an argument breaks the operation's contract */
   SDA_ERR_UNSUPPORTED = -2,  /* legal, but outside what the library handles */
   SDA_ERR_WORKSPACE = -3,    /* workspace missing (splits > 1), too small or misaligned */
-  SDA_ERR_LAUNCH = -4        /* the HIP launch reported an error */
+  SDA_ERR_LAUNCH = -4,       /* the HIP launch reported an error */
+  SDA_ERR_SCRATCH = -5       /* sda_decode_static: the call needs more than the
+                                library's static scratch (SDA_STATIC_SCRATCH_BYTES) */
 } sda_status;
 
 typedef enum {
@@ -156,6 +158,26 @@ typedef struct sda_decode_args {
  * Returns an sda_status.
  */
 int sda_decode(const sda_decode_args *args, hipStream_t stream);
+
+/*
+ * sda_decode without a caller workspace, for callers that cannot allocate:
+ * code under HIP graph capture, serving loops and harnesses that forbid
+ * hipMalloc.  It is sda_decode (same arguments, validation, kernels and
+ * result) with the library's own static device array of
+ * SDA_STATIC_SCRATCH_BYTES as the workspace; the caller still passes every
+ * input and output.  args->workspace must be NULL and args->workspace_bytes
+ * 0 (else SDA_ERR_INVALID).  A call whose sda_workspace_bytes(rows, heads,
+ * splits) exceeds SDA_STATIC_SCRATCH_BYTES returns SDA_ERR_SCRATCH before
+ * touching the device; with splits from sda_splits every call up to 2M rows
+ * fits.  The call allocates nothing: each GPU holds its own copy of the
+ * array from the first call on it until the process ends, and the array
+ * keeps the last call's contents (nothing in it has to start at zero).  All
+ * calls on one GPU share that GPU's array, so calls that may overlap on one
+ * GPU (other streams, other threads) race: serialise them, or use
+ * sda_decode with a workspace each.
+ */
+#define SDA_STATIC_SCRATCH_BYTES (16u << 20)
+int sda_decode_static(const sda_decode_args *args, hipStream_t stream);
 
 /*
  * Split count for `rows` rows.  This is the MI355X counterpart of

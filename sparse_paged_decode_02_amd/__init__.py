@@ -11,6 +11,7 @@ the same cache.  Seeded synthetic workloads live in
 from .binding import (  # noqa: F401
     SdaError,
     sda_decode,
+    sda_decode_static,
     sda_device_compute_units,
     sda_indexer_logits,
     sda_select_regions,

@@ -21,6 +21,8 @@ SDA_ERR_INVALID = -1
 SDA_ERR_UNSUPPORTED = -2
 SDA_ERR_WORKSPACE = -3
 SDA_ERR_LAUNCH = -4
+SDA_ERR_SCRATCH = -5
+STATIC_SCRATCH_BYTES = 16 << 20
 SDA_KV_BF16 = 0
 SDA_KV_FP8_E4M3 = 1
 ABI_VERSION = 6
@@ -125,6 +127,8 @@ def lib() -> ctypes.CDLL:
             l = ctypes.CDLL(LIB_PATH)
             l.sda_decode.restype = ctypes.c_int
             l.sda_decode.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.c_void_p]
+            l.sda_decode_static.restype = ctypes.c_int
+            l.sda_decode_static.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.c_void_p]
             l.sda_splits.restype = ctypes.c_int
             l.sda_splits.argtypes = [ctypes.c_int]
             l.sda_workspace_bytes.restype = ctypes.c_size_t
@@ -329,6 +333,35 @@ def sda_decode(query, cache, regions, block_table, positions, active, output, *,
     rc = lib().sda_decode(ctypes.byref(a), handle)
     if rc != SDA_OK:
         raise SdaError(rc, status_string(rc))
+
+
+def sda_decode_static(query, cache, regions, block_table, positions, active, output, *,
+                      scale, query_len=1, splits, clear_inactive=True, k_scale=None,
+                      v_scale=None, gate=None, region_tokens=0, stream=None) -> None:
+    """Enqueue ``sda_decode_static``: ``sda_decode`` with the library's static
+    device scratch as its workspace, so that nothing is allocated, here or in
+    the library.  Calls that overlap on one GPU share that scratch."""
+    check_tensors(query, cache, regions, block_table, positions, active, output,
+                  k_scale, v_scale, gate)
+    rows, heads = query.shape[0], query.shape[1]
+    check_table_rows(block_table, rows, cache.shape[1] * int(query_len))
+    check_gate_shape(gate, rows, cache.shape[1], heads)
+    check_device(query, cache=cache, regions=regions, block_table=block_table,
+                 positions=positions, active=active, output=output, k_scale=k_scale,
+                 v_scale=v_scale, gate=gate)
+    a = make_args(query, cache, regions, block_table, positions, active, output, scale=scale,
+                  query_len=query_len, splits=splits, clear_inactive=clear_inactive,
+                  k_scale=k_scale, v_scale=v_scale, gate=gate, region_tokens=region_tokens)
+    if stream is None:
+        stream = torch.cuda.current_stream(query.device)
+    rc = lib().sda_decode_static(ctypes.byref(a), ctypes.c_void_p(stream.cuda_stream))
+    if rc != SDA_OK:
+        raise SdaError(rc, status_string(rc))
+
+
+def sda_decode_static_raw(args: DecodeArgs, stream_handle=None) -> int:
+    """Call sda_decode_static on a prepared struct; returns the status code."""
+    return int(lib().sda_decode_static(ctypes.byref(args), stream_handle))
 
 
 def sda_decode_raw(args: DecodeArgs, stream_handle=None) -> int:

@@ -14,7 +14,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libsda.so")
 SOURCES = [os.path.join(CSRC, "sda_api.cpp"), os.path.join(CSRC, "sda_kernels.hip"),
-           os.path.join(CSRC, "sda_select.hip"), os.path.join(CSRC, "sda_logits.hip")]
+           os.path.join(CSRC, "sda_select.hip"), os.path.join(CSRC, "sda_logits.hip"),
+           os.path.join(CSRC, "sda_static.hip")]
 ARCH = os.environ.get("SDA_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [

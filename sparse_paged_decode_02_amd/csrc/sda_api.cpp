@@ -113,6 +113,8 @@ const char* sda_status_string(int status) {
     case SDA_ERR_UNSUPPORTED: return "unsupported argument (alignment, stride or size limit)";
     case SDA_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
     case SDA_ERR_LAUNCH: return "kernel launch failed";
+    case SDA_ERR_SCRATCH:
+      return "the call needs more workspace than the static scratch (SDA_STATIC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
