@@ -105,11 +105,35 @@ def swa_workload_desc(w) -> str:
                                             w.heads, w.block, w.window, w.seq_lo, w.seq_hi))
 
 
-def time_calls(call, steps: int, warmup: int, stream):
-    """Warm up, then time `steps` back-to-back calls: wall seconds (between
-    synchronisations), average launch ms (two HIP events on the launch stream
-    around the timed region) and a second pass of per-launch durations."""
+# Untimed calls before the warmup steps, until this much back-to-back work has
+# run.  After the GPU has idled (the host draws the next workload's inputs),
+# the first ~15 ms of calls run up to 15% slower (large-batch FP8 on MI355X:
+# 540 us on average over calls 5..25 after a 3 s idle, 498 us once settled);
+# decode steps in serving run back to back.
+SETTLE_MS = 50.0
+
+
+def settle(call, stream, settle_ms: float = SETTLE_MS) -> int:
+    """Run calls until settle_ms of wall time has passed; returns the count."""
     import torch
+    n = 0
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < settle_ms:
+        for _ in range(8):
+            call(n)
+            n += 1
+        torch.cuda.synchronize()
+    return n
+
+
+def time_calls(call, steps: int, warmup: int, stream, settle_ms: float = SETTLE_MS):
+    """Settle, warm up, then time `steps` back-to-back calls: wall seconds
+    (between synchronisations), average launch ms (two HIP events on the
+    launch stream around the timed region) and a second pass of per-launch
+    durations.  The settle count is kept in time_calls.settled."""
+    import torch
+    time_calls.settled = settle(call, stream, settle_ms) if settle_ms > 0 else 0
     for i in range(warmup):
         call(i)
     torch.cuda.synchronize()
@@ -161,6 +185,7 @@ def time_flushed(call, steps: int, stream, flush_mib: int) -> dict:
 def record(args, *, value, wall, launch_avg_ms, launch_ms, bytes_per_launch, rows, dtype,
            config, kernel, traffic, metric=METRIC):
     achieved = bytes_per_launch / (launch_avg_ms * 1e-3) / 1e9
+    settled = getattr(time_calls, "settled", 0)
     return {
         "metric": metric,
         "value": round(value, 2),
@@ -175,6 +200,7 @@ def record(args, *, value, wall, launch_avg_ms, launch_ms, bytes_per_launch, row
         "dtype": dtype,
         "data": "synthetic",
         "config": config,
+        "settle_calls": settled,
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "rows_per_s": round(rows * args.steps / wall, 1),
         "us_per_call": {"median": round(float(np.median(launch_ms)) * 1e3, 2),
@@ -262,7 +288,7 @@ def run_swa(args, dev) -> int:
         if rc != B.SDA_OK:
             raise B.SdaError(rc, B.status_string(rc))
 
-    wall, launch_avg_ms, launch_ms = time_calls(call, args.steps, args.warmup, stream)
+    wall, launch_avg_ms, launch_ms = time_calls(call, args.steps, args.warmup, stream, args.settle_ms)
     total_bytes = sum(nbytes[i % len(sets)] for i in range(args.steps))
     bytes_per_launch = float(np.mean([nbytes[i % len(sets)] for i in range(args.steps)]))
     rec = record(args, value=total_bytes / wall / 1e9, wall=wall, launch_avg_ms=launch_avg_ms,
@@ -384,7 +410,7 @@ def run_logits(args, dev) -> int:
         if rc != B.SDA_OK:
             raise B.SdaError(rc, B.status_string(rc))
 
-    wall, launch_avg_ms, launch_ms = time_calls(call, args.steps, args.warmup, stream)
+    wall, launch_avg_ms, launch_ms = time_calls(call, args.steps, args.warmup, stream, args.settle_ms)
     total_bytes = sum(nbytes[i % len(sets)] for i in range(args.steps))
     bytes_per_launch = float(np.mean([nbytes[i % len(sets)] for i in range(args.steps)]))
     rec = record(args, value=total_bytes / wall / 1e9, wall=wall, launch_avg_ms=launch_avg_ms,
@@ -426,7 +452,7 @@ def run_select(args, dev) -> int:
         if rc != B.SDA_OK:
             raise B.SdaError(rc, B.status_string(rc))
 
-    wall, launch_avg_ms, launch_ms = time_calls(call, args.steps, args.warmup, stream)
+    wall, launch_avg_ms, launch_ms = time_calls(call, args.steps, args.warmup, stream, args.settle_ms)
     total_bytes = sum(nbytes[i % len(sets)] for i in range(args.steps))
     bytes_per_launch = float(np.mean([nbytes[i % len(sets)] for i in range(args.steps)]))
     rec = record(args, value=total_bytes / wall / 1e9, wall=wall, launch_avg_ms=launch_avg_ms,
@@ -534,8 +560,8 @@ def parse_also(args) -> list:
 
 def summary_of(rec: dict) -> dict:
     """The per-workload fields of a record, for the `other_configs` key."""
-    keep = ("value", "unit", "ms_per_step", "pct_hbm_peak", "rows_per_s", "us_per_call",
-            "dtype", "config", "roofline")
+    keep = ("value", "unit", "ms_per_step", "settle_calls", "pct_hbm_peak", "rows_per_s",
+            "us_per_call", "dtype", "config", "roofline")
     return {k: rec[k] for k in keep if k in rec}
 
 
@@ -594,7 +620,7 @@ def measure_sparse(args, dev, k: int, with_cpu: bool) -> dict:
         if rc != B.SDA_OK:
             raise B.SdaError(rc, B.status_string(rc))
 
-    wall, launch_avg_ms, launch_ms = time_calls(call, args.steps, args.warmup, stream)
+    wall, launch_avg_ms, launch_ms = time_calls(call, args.steps, args.warmup, stream, args.settle_ms)
     total_bytes = sum(nbytes[i % len(sets)] for i in range(args.steps))
     bytes_per_launch = float(np.mean([nbytes[i % len(sets)] for i in range(args.steps)]))
     rec = record(args, value=total_bytes / wall / 1e9, wall=wall, launch_avg_ms=launch_avg_ms,
@@ -621,6 +647,143 @@ def measure_sparse(args, dev, k: int, with_cpu: bool) -> dict:
     return rec
 
 
+class ProbeArgs(ctypes.Structure):
+    """Mirror of ``sda_probe_args`` (include/sda_probe.h)."""
+    _fields_ = [("base", ctypes.c_void_p), ("kv_dtype", ctypes.c_int32),
+                ("token_stride", ctypes.c_int64), ("groups", ctypes.c_int32),
+                ("block_tokens", ctypes.c_int32), ("block_offsets", ctypes.c_void_p),
+                ("group_start", ctypes.c_void_p), ("sink", ctypes.c_void_p)]
+
+
+def probe_lib():
+    """libsda_probe.so, the gather-ceiling probe built beside libsda.so."""
+    from sparse_paged_decode_02_amd import build as sda_build
+    if not os.path.exists(sda_build.PROBE_LIB):
+        raise RuntimeError("libsda_probe.so is not built; run __graft_entry__.build()")
+    lib = ctypes.CDLL(sda_build.PROBE_LIB)
+    lib.sda_probe_gather.restype = ctypes.c_int
+    lib.sda_probe_gather.argtypes = [ctypes.POINTER(ProbeArgs), ctypes.c_void_p]
+    lib.sda_probe_args_size.restype = ctypes.c_size_t
+    if lib.sda_probe_args_size() != ctypes.sizeof(ProbeArgs):
+        raise RuntimeError("sda_probe_args size mismatch")
+    return lib
+
+
+def probe_blocks(w, cache_strides, positions, regions, active, block_table) -> tuple:
+    """Each active row's visible regions as byte offsets into the cache (the
+    blocks its split workgroup reads), in slot order: (offsets, group_start).
+    A region is visible iff its id >= 0 and its first token <= the row's
+    position; the probe reads all of its rt token rows."""
+    e = 1 if w.kv == "fp8" else 2
+    cps, cgs, cts = cache_strides
+    rt, G = w.rt, w.groups
+    reg = regions.astype(np.int64)
+    pos = positions.astype(np.int64)[:, None]
+    rows = np.arange(w.rows)
+    req = rows // (G * w.query_len)
+    vis = (reg >= 0) & (reg * rt <= pos) & (active != 0)[:, None]
+    t0 = np.where(vis, reg * rt, 0)
+    page = block_table.astype(np.int64)[req[:, None], t0 // w.block]
+    off = (page * cps + (rows % G)[:, None] * cgs + (t0 % w.block) * cts) * e
+    offsets = off[vis]  # row-major: each row's visible slots in slot order
+    start = np.zeros(w.rows + 1, dtype=np.int32)
+    start[1:] = np.cumsum(vis.sum(axis=1))
+    return offsets.astype(np.int64), start
+
+
+def run_gather(args, dev) -> int:
+    """The split kernel against the gather ceiling of its own access pattern:
+    the probe reads the same region blocks (every visible region of every
+    active row, all rt token rows) through the same chunk loop and launch
+    shape, with no attention math.  Both are timed on the same rotating input
+    sets in one run; ``kernel_frac_of_ceiling`` is the probe's time over the
+    kernel's."""
+    import torch
+    from sparse_paged_decode_02_amd import binding as B
+    from sparse_paged_decode_02_amd import inputs as gen
+
+    w = gen.WORKLOADS[args.gather_ceiling]
+    splits = w.splits or B.sda_splits(w.rows)
+    plib = probe_lib()
+    print("[bench] drawing %s" % workload_desc(w), file=sys.stderr, flush=True)
+    base = gen.make_inputs(w, device=dev, splits=splits)
+    bt = base.block_table.cpu().numpy()
+    sets = [base] + [gen.make_inputs(w, device=dev, seed=w.seed + 100003 * i, cache=base.cache,
+                                     block_table=bt, splits=splits) for i in range(1, args.sets)]
+    e = 1 if w.kv == "fp8" else 2
+    row_bytes = 384 * e
+    cstr = tuple(int(x) for x in base.cache.stride()[:3])
+    stream = torch.cuda.current_stream(dev)
+    handle = ctypes.c_void_p(stream.cuda_stream)
+    keep, probe_args, kernel_args, pbytes, kbytes = [], [], [], [], []
+    ws = torch.empty(B.sda_workspace_bytes(w.rows, w.heads, splits), dtype=torch.uint8,
+                     device=dev)
+    sink = torch.zeros(w.rows * 4, dtype=torch.int32, device=dev)
+    block_bytes = w.rt * cstr[2] * e
+    for s in sets:
+        pos, reg, act = (s.positions.cpu().numpy(), s.regions.cpu().numpy(),
+                         s.active.cpu().numpy())
+        offs, start = probe_blocks(w, cstr, pos, reg, act, bt)
+        if args.sequential:
+            offs = np.arange(len(offs), dtype=np.int64) * block_bytes
+            assert len(offs) * block_bytes <= base.cache.numel() * e
+        t_off = torch.from_numpy(offs).to(dev)
+        t_start = torch.from_numpy(start).to(dev)
+        a = ProbeArgs()
+        a.base = base.cache.data_ptr()
+        a.kv_dtype = B.SDA_KV_FP8_E4M3 if w.kv == "fp8" else B.SDA_KV_BF16
+        a.token_stride = cstr[2] * e
+        a.groups, a.block_tokens = w.rows, w.rt
+        a.block_offsets, a.group_start, a.sink = t_off.data_ptr(), t_start.data_ptr(), \
+            sink.data_ptr()
+        probe_args.append(a)
+        pbytes.append(len(offs) * w.rt * row_bytes)
+        o = torch.empty_like(s.query)
+        keep += [t_off, t_start, o]
+        kernel_args.append(B.make_args(
+            s.query, s.cache, s.regions, s.block_table, s.positions, s.active, o,
+            scale=s.scale, query_len=w.query_len, splits=splits, k_scale=s.k_scale,
+            v_scale=s.v_scale, gate=s.gate, region_tokens=w.region_tokens, workspace=ws))
+        kbytes.append(algorithmic_bytes(w, pos, reg, act)[0])
+
+    def probe_call(i):
+        rc = plib.sda_probe_gather(ctypes.byref(probe_args[i % len(probe_args)]), handle)
+        if rc != B.SDA_OK:
+            raise B.SdaError(rc, B.status_string(rc))
+
+    def kernel_call(i):
+        rc = B.sda_decode_raw(kernel_args[i % len(kernel_args)], handle)
+        if rc != B.SDA_OK:
+            raise B.SdaError(rc, B.status_string(rc))
+
+    res = {}
+    for name, fn, nb in (("probe", probe_call, pbytes), ("kernel", kernel_call, kbytes)):
+        _, avg_ms, launch_ms = time_calls(fn, args.steps, args.warmup, stream, args.settle_ms)
+        mean_bytes = float(np.mean([nb[i % len(nb)] for i in range(args.steps)]))
+        gbs = mean_bytes / (avg_ms * 1e-3) / 1e9
+        res[name] = {"avg_launch_us": round(avg_ms * 1e3, 3),
+                     "median_us": round(float(np.median(launch_ms)) * 1e3, 2),
+                     "bytes_per_call": int(mean_bytes), "GB/s": round(gbs, 1),
+                     "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
+    res["probe"]["bytes"] = ("every visible region's %d token rows of %d bytes%s"
+                             % (w.rt, row_bytes, ", consecutive blocks" if args.sequential
+                                else ""))
+    res["kernel"]["bytes"] = "algorithmic (visible K|V rows, Q of active rows, output)"
+    kernel_alg_at_probe_time = np.mean(kbytes) / (res["probe"]["avg_launch_us"] * 1e-6) / 1e9
+    rec = {"metric": "gather ceiling of the sparse decode access pattern",
+           "workload": workload_desc(w), "splits": splits,
+           "pattern": "sequential blocks" if args.sequential else "the workload's blocks",
+           "steps": args.steps, "warmup": args.warmup, "settle_ms": args.settle_ms,
+           "input_sets": len(sets), "seed": w.seed, "probe": res["probe"],
+           "kernel": res["kernel"],
+           "ceiling_for_kernel_metric_GBps": round(float(kernel_alg_at_probe_time), 1),
+           "kernel_frac_of_ceiling": round(res["probe"]["avg_launch_us"]
+                                           / res["kernel"]["avg_launch_us"], 4),
+           "kernel_sha256_16": kernel_hash()}
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -642,9 +805,18 @@ def main() -> int:
     ap.add_argument("--logits", default="", metavar="NAME",
                     help="measure the decode indexer logits on workload NAME (logits-decode, "
                          "logits-mtp) instead")
+    ap.add_argument("--gather-ceiling", type=int, default=0, metavar="K",
+                    help="time the gather probe on workload K's region blocks beside the "
+                         "split kernel on the same inputs (one JSON line)")
+    ap.add_argument("--sequential", action="store_true",
+                    help="with --gather-ceiling: consecutive blocks instead of the "
+                         "workload's")
     ap.add_argument("--pack", type=int, default=0,
                     help="with --swa: query tokens per workgroup (0: the library's plan)")
     ap.add_argument("--sets", type=int, default=4, help="rotating input sets")
+    ap.add_argument("--settle-ms", type=float, default=SETTLE_MS,
+                    help="untimed back-to-back calls before the warmup steps, until this many "
+                         "ms have passed (0: none)")
     ap.add_argument("--splits", type=int, default=0, help="0: the workload's rule")
     ap.add_argument("--flush-mib", type=int, default=0, metavar="MIB",
                     help="sparse decode: also time each call after writing MIB MiB (a "
@@ -686,6 +858,8 @@ def main() -> int:
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": n, "calls": args.steps}), flush=True)
         return 0
+    if args.gather_ceiling:
+        return run_gather(args, dev)
     if args.swa:
         return run_swa(args, dev)
     if args.select:

@@ -13,6 +13,10 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libsda.so")
+# The gather-ceiling probe (include/sda_probe.h): a measurement library that
+# bench.py --gather-ceiling loads; the decode path never does.
+PROBE_LIB = os.path.join(PKG, "libsda_probe.so")
+PROBE_SOURCES = [os.path.join(CSRC, "sda_probe.hip")]
 SOURCES = [os.path.join(CSRC, "sda_api.cpp"), os.path.join(CSRC, "sda_kernels.hip"),
            os.path.join(CSRC, "sda_select.hip"), os.path.join(CSRC, "sda_logits.hip"),
            os.path.join(CSRC, "sda_static.hip")]
@@ -38,14 +42,20 @@ HIPCC_FLAGS = [
 ]
 
 
-def build(verbose: bool = True) -> str:
+def _hipcc(sources, out, verbose):
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc] + HIPCC_FLAGS + ["-o", tmp] + SOURCES
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = [hipcc] + HIPCC_FLAGS + ["-o", tmp] + sources
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.check_call(cmd, cwd=PKG)
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = True) -> str:
+    """Build libsda.so and the probe library beside it; returns libsda.so."""
+    _hipcc(SOURCES, LIB, verbose)
+    _hipcc(PROBE_SOURCES, PROBE_LIB, verbose)
     return LIB
 
 

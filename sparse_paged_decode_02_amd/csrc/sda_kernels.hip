@@ -53,24 +53,20 @@
 #include <type_traits>
 #include <utility>
 
+#include "sda_dma.h"
 #include "sda_launch.h"
 #include "sda_wave.h"
 
-#define SDA_LDS __attribute__((address_space(3)))
 
 namespace sda {
 namespace {
 
-constexpr int kDim = 192;
 // Waves per split workgroup: 4 (one workgroup per CU, ~121 KiB of LDS) when
 // the grid is at most one workgroup per CU, else 2 (~72 KiB, two per CU, so
 // that one workgroup's prologue and epilogue overlap the other's streaming).
 constexpr int kWavesSmallGrid = 4;
 constexpr int kWavesLargeGrid = 2;
 constexpr int kStages = 2;          // LDS stages per wave: 1 computed, 1 in flight
-constexpr int kOpsPerChunk = 12;    // vector-memory instructions per chunk issue
-constexpr int kStageBytes = 6144;   // K (or V) bytes of one chunk (16 bf16 / 32 FP8 tokens)
-constexpr int kChunkBytes = 2 * kStageBytes;  // one stage: K then V
 constexpr int kAccStride = 196;     // floats per head row in the wave-merge area
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -89,15 +85,6 @@ enum Addr : int {
   kPair = 3,     // region list of 8-token regions, bf16: a chunk is two regions
 };
 
-// Per cache dtype: tokens per chunk, V bytes per token, 16-byte V pieces per token.
-template <bool kFp8>
-struct Cfg {
-  static constexpr int kTok = kFp8 ? 32 : 16;
-  static constexpr int kEsz = kFp8 ? 1 : 2;
-  static constexpr int kVBytes = kDim * kEsz;
-  static constexpr int kPieces = kVBytes / 16;
-  static_assert(kTok * kVBytes == kStageBytes, "one chunk of V fills one stage");
-};
 
 __device__ __forceinline__ float bf16_bits_to_float(uint32_t b) {
   return __uint_as_float(b << 16);
@@ -132,141 +119,6 @@ __device__ __forceinline__ u32x2 fp8x4_to_bf16(uint32_t w) {
   return u32x2{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b)};
 }
 
-// LDS swizzles.  A stage holds one chunk's V rows, one per token, as 16-byte
-// pieces.  Piece p of token row r is stored at piece position p ^ swz(r).
-// The XOR keeps a piece inside its aligned 8-piece (bf16) or 4-piece (FP8)
-// block.  The swizzle makes the transposing reads of one 16-lane group hit 32
-// distinct banks:
-//  bf16: lanes 4y+q of group g read row 4g+y, pieces 2nt+(q>>1);
-//  FP8:  lanes 2y+h of group g read row 16(y>>2)+4g+(y&3), piece nt.
-template <bool kFp8>
-__device__ __forceinline__ int swz(int row) {
-  return kFp8 ? 2 * ((row >> 4) & 1) + ((row >> 1) & 1) : 2 * (row & 3) + ((row >> 2) & 1);
-}
-// K pieces: the A-operand reads of 8 consecutive lanes (rows i..i+7 of one
-// tile, one piece) hit 32 distinct banks.
-template <bool kFp8>
-__device__ __forceinline__ int swz_k(int row) {
-  return kFp8 ? (row >> 1) & 3 : row & 7;
-}
-
-// One chunk's 12 LDS-DMAs (global_load_lds_dwordx4: each lane moves 16 bytes
-// to LDS address M0 + 16 * lane).  K pieces land at stage + 1024*j, V pieces
-// at stage + 6144 + 1024*j, j = 0..5.  Issued from inline assembly so that
-// the compiler does not tie later LDS reads to them; completion is awaited
-// with wait_vmcnt.  M0 is saved and restored around the block.
-//
-// Cache policy: K|V bytes are read exactly once, so every DMA is
-// non-temporal (`nt`); bf16 gated measured 72.4 -> 64.3 us with nt on
-// MI355X.  A 384-byte FP8 token row puts K[128:192] and V[0:64] in one
-// 128-byte line.  FP8 chunks therefore issue K DMA j and V DMA j, which cover
-// the same token rows, back to back (SDA_CHUNK_ASM_KV), so the second request
-// for the shared line meets the first in flight: all-nt FP8 then fetches
-// 1.000x the K|V bytes, where K-then-V order with nt fetched 1.024x.  (K had
-// kept the default policy to avoid that re-fetch, but its cacheable loads
-// evict dirty lines of earlier kernels, and the write-backs land inside the
-// call: 81 us on the FP8 cache workload after a 1 GiB write.)
-#define SDA_LDDMA(op, addr, suf) "global_load_lds_dwordx4 %[" op "], " addr suf "\n\t"
-#define SDA_NEXT "s_add_u32 m0, m0, 0x400\n\t"
-#define SDA_CHUNK_ASM(addr, ksuf, vsuf)                                                      \
-  "s_mov_b32 %[sv], m0\n\t"                                                                  \
-  "s_mov_b32 m0, %[st]\n\t" SDA_LDDMA("k0", addr, ksuf) SDA_NEXT SDA_LDDMA("k1", addr, ksuf) \
-      SDA_NEXT SDA_LDDMA("k2", addr, ksuf) SDA_NEXT SDA_LDDMA("k3", addr, ksuf) SDA_NEXT     \
-      SDA_LDDMA("k4", addr, ksuf) SDA_NEXT SDA_LDDMA("k5", addr, ksuf) SDA_NEXT              \
-      SDA_LDDMA("v0", addr, vsuf) SDA_NEXT SDA_LDDMA("v1", addr, vsuf) SDA_NEXT              \
-      SDA_LDDMA("v2", addr, vsuf) SDA_NEXT SDA_LDDMA("v3", addr, vsuf) SDA_NEXT              \
-      SDA_LDDMA("v4", addr, vsuf) SDA_NEXT SDA_LDDMA("v5", addr, vsuf)                       \
-  "s_mov_b32 m0, %[sv]"
-
-// FP8 chunk: K DMA j then V DMA j for j = 0..5 (the same token rows), with
-// M0 set from the stage base for each: K slice j at stage + 1 KiB j, V slice
-// j at stage + 6 KiB + 1 KiB j, the layout SDA_CHUNK_ASM writes in order.
-#define SDA_M0(off) "s_add_u32 m0, %[st], " off "\n\t"
-#define SDA_CHUNK_ASM_KV(addr, suf)                                                          \
-  "s_mov_b32 %[sv], m0\n\t"                                                                  \
-  "s_mov_b32 m0, %[st]\n\t" SDA_LDDMA("k0", addr, suf) SDA_M0("0x1800")                      \
-      SDA_LDDMA("v0", addr, suf) SDA_M0("0x400") SDA_LDDMA("k1", addr, suf) SDA_M0("0x1c00")    \
-      SDA_LDDMA("v1", addr, suf) SDA_M0("0x800") SDA_LDDMA("k2", addr, suf) SDA_M0("0x2000")    \
-      SDA_LDDMA("v2", addr, suf) SDA_M0("0xc00") SDA_LDDMA("k3", addr, suf) SDA_M0("0x2400")    \
-      SDA_LDDMA("v3", addr, suf) SDA_M0("0x1000") SDA_LDDMA("k4", addr, suf) SDA_M0("0x2800")   \
-      SDA_LDDMA("v4", addr, suf) SDA_M0("0x1400") SDA_LDDMA("k5", addr, suf) SDA_M0("0x2c00")   \
-      SDA_LDDMA("v5", addr, suf) "s_mov_b32 m0, %[sv]"
-static_assert(kStageBytes == 0x1800, "SDA_CHUNK_ASM_KV: V slices start 6 KiB into the stage");
-
-// Two-region chunk (bf16, 8-token regions): the first three K and V DMAs
-// cover token rows 0..7 (pieces 0..191 of a 384-piece half) and the last
-// three rows 8..15, so each half takes its own uniform base.
-#define SDA_CHUNK_ASM2(addra, addrb, suf)                                                      \
-  "s_mov_b32 %[sv], m0\n\t"                                                                    \
-  "s_mov_b32 m0, %[st]\n\t" SDA_LDDMA("k0", addra, suf) SDA_NEXT SDA_LDDMA("k1", addra, suf)   \
-      SDA_NEXT SDA_LDDMA("k2", addra, suf) SDA_NEXT SDA_LDDMA("k3", addrb, suf) SDA_NEXT       \
-      SDA_LDDMA("k4", addrb, suf) SDA_NEXT SDA_LDDMA("k5", addrb, suf) SDA_NEXT                \
-      SDA_LDDMA("v0", addra, suf) SDA_NEXT SDA_LDDMA("v1", addra, suf) SDA_NEXT                \
-      SDA_LDDMA("v2", addra, suf) SDA_NEXT SDA_LDDMA("v3", addrb, suf) SDA_NEXT                \
-      SDA_LDDMA("v4", addrb, suf) SDA_NEXT SDA_LDDMA("v5", addrb, suf)                         \
-  "s_mov_b32 m0, %[sv]"
-
-__device__ __forceinline__ void dma_chunk_sbase2(const uint8_t* base_a, const uint8_t* base_b,
-                                                 uint32_t stage, const uint32_t (&ko)[6],
-                                                 const uint32_t (&vo)[6]) {
-  uint32_t saved;
-  __asm__ __volatile__(SDA_CHUNK_ASM2("%[b]", "%[b2]", " nt")
-                       : [sv] "=&s"(saved)
-                       : [st] "s"(stage), [b] "s"(base_a), [b2] "s"(base_b), [k0] "v"(ko[0]),
-                         [k1] "v"(ko[1]), [k2] "v"(ko[2]), [k3] "v"(ko[3]), [k4] "v"(ko[4]),
-                         [k5] "v"(ko[5]), [v0] "v"(vo[0]), [v1] "v"(vo[1]), [v2] "v"(vo[2]),
-                         [v3] "v"(vo[3]), [v4] "v"(vo[4]), [v5] "v"(vo[5])
-                       : "memory");
-}
-
-// dma_chunk_sbase: one uniform 64-bit base (SGPRs) plus 32-bit per-lane
-// byte offsets (chunks inside one region or one page).
-template <bool kFp8>
-__device__ __forceinline__ void dma_chunk_sbase(const uint8_t* base, uint32_t stage,
-                                                const uint32_t (&ko)[6],
-                                                const uint32_t (&vo)[6]) {
-  uint32_t saved;
-#define SDA_SBASE_OPERANDS                                                                      \
-  : [sv] "=&s"(saved)                                                                           \
-  : [st] "s"(stage), [b] "s"(base), [k0] "v"(ko[0]), [k1] "v"(ko[1]), [k2] "v"(ko[2]),          \
-    [k3] "v"(ko[3]), [k4] "v"(ko[4]), [k5] "v"(ko[5]), [v0] "v"(vo[0]), [v1] "v"(vo[1]),        \
-    [v2] "v"(vo[2]), [v3] "v"(vo[3]), [v4] "v"(vo[4]), [v5] "v"(vo[5])                          \
-  : "memory"
-  if constexpr (kFp8)
-    __asm__ __volatile__(SDA_CHUNK_ASM_KV("%[b]", " nt") SDA_SBASE_OPERANDS);
-  else
-    __asm__ __volatile__(SDA_CHUNK_ASM("%[b]", " nt", " nt") SDA_SBASE_OPERANDS);
-#undef SDA_SBASE_OPERANDS
-}
-
-// dma_chunk_vaddr: per-lane 64-bit addresses (chunks spanning regions).
-template <bool kFp8>
-__device__ __forceinline__ void dma_chunk_vaddr(uint32_t stage, const uint8_t* const (&ka)[6],
-                                                const uint8_t* const (&va)[6]) {
-  uint32_t saved;
-#define SDA_VADDR_OPERANDS                                                                     \
-  : [sv] "=&s"(saved)                                                                          \
-  : [st] "s"(stage), [k0] "v"(ka[0]), [k1] "v"(ka[1]), [k2] "v"(ka[2]), [k3] "v"(ka[3]),       \
-    [k4] "v"(ka[4]), [k5] "v"(ka[5]), [v0] "v"(va[0]), [v1] "v"(va[1]), [v2] "v"(va[2]),       \
-    [v3] "v"(va[3]), [v4] "v"(va[4]), [v5] "v"(va[5])                                          \
-  : "memory"
-  if constexpr (kFp8)
-    __asm__ __volatile__(SDA_CHUNK_ASM_KV("off", " nt") SDA_VADDR_OPERANDS);
-  else
-    __asm__ __volatile__(SDA_CHUNK_ASM("off", " nt", " nt") SDA_VADDR_OPERANDS);
-#undef SDA_VADDR_OPERANDS
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __asm__ __volatile__("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const SDA_LDS void*)p;
-}
-
 // Where token slot `slot` of a split lives (general addressing: a chunk may
 // span regions).  A masked slot is redirected to the first token of a region
 // of the split (always visible), so every load stays in bounds and every V
@@ -281,47 +133,12 @@ __device__ __forceinline__ int64_t token_elem(const Params& p, int slot, const i
   return s_base[kk] + (int64_t)(valid ? off : 0) * p.cts;
 }
 
-// Loop-invariant DMA geometry of one lane.  Stage slot 64j + lane (j = 0..5)
-// is token row r = slot / kPieces, piece position slot % kPieces, which holds
-// global piece (position ^ swizzle(r)).  koff/voff are that piece's byte
-// offsets within the token's cache row (V after the 192 K elements).
-struct LaneDma {
-  int row[6];
-  uint32_t koff[6], voff[6];
-};
-
-template <bool kFp8>
-__device__ __forceinline__ LaneDma lane_dma(int lane) {
-  using C = Cfg<kFp8>;
-  LaneDma d;
-#pragma unroll
-  for (int j = 0; j < 6; ++j) {
-    const int slot = 64 * j + lane;
-    const int r = slot / C::kPieces;
-    const int pos = slot - r * C::kPieces;
-    d.row[j] = r;
-    d.koff[j] = 16u * (uint32_t)(pos ^ swz_k<kFp8>(r));
-    d.voff[j] = (uint32_t)C::kVBytes + 16u * (uint32_t)(pos ^ swz<kFp8>(r));
-  }
-  return d;
-}
-
 // A split's sliding window: w0..pos is the union of the windows of the
 // workgroup's query tokens; chunk c starts at token t_base + 16c; s_base[k]
 // is the cache offset of block-table column col_lo + k (page and KV group).
 struct Win {
   int w0, pos, t_base, col_lo;
 };
-
-// Wave-uniform 64-bit address from a per-lane value that is uniform in fact.
-// readfirstlane returns int: go through uint32_t so the low half is
-// zero-extended, never sign-extended into the high half.
-__device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* ptr) {
-  const uint64_t b64 = (uint64_t)(uintptr_t)ptr;
-  const uint32_t b_lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b64);
-  const uint32_t b_hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b64 >> 32));
-  return (const uint8_t*)(uintptr_t)(((uint64_t)b_hi << 32) | (uint64_t)b_lo);
-}
 
 // Issue chunk c into LDS stage `stage`.  Returns the visibility of this
 // lane's S^T rows (bit t: token slot 16t + i16).  Masked slots load a visible
@@ -941,6 +758,291 @@ split_kernel(const Params p) {
     output_loop(std::false_type{});
 }
 
+// Row-stream kernel, for batches of at least two rows per wave of the chip:
+// every wave owns whole rows (rows w, w + W, w + 2W, ... for wave w of W)
+// and streams them back to back through its own two-stage chunk pipeline, so
+// the pipeline never drains between rows.
+//  * Up front, each wave resolves the region lists of all its rows at once:
+//    their flags, positions, region ids and gate logits in one round trip,
+//    their block-table entries in a second.  The lists go to the wave's part
+//    of LDS; no workgroup barrier is ever taken.
+//  * A row's query (16 columns x 192 bf16) moves to one of two per-wave LDS
+//    buffers by LDS-DMA, issued together with the row's first chunk, and is
+//    read into the MFMA B-operand registers when that chunk is computed.
+//  * After a row's last chunk, the wave folds its running sums, v_scale and
+//    the gate into one factor per column, rounds the output to bf16 through
+//    the chunk's just-computed LDS stage and writes it with 16-byte stores,
+//    while the next row's first chunk is already in flight.
+// The arithmetic per chunk is the split kernel's (issue_chunk,
+// compute_chunk); one wave sums a row's chunks in order.
+constexpr int kStreamWaves = 4;
+constexpr int kStreamMaxRows = 8;   // rows per wave
+constexpr int kStreamList = 256;    // region-list entries per wave (all its rows)
+constexpr int kStreamMaxR = 64;     // region slots per row (one id per lane)
+constexpr int kQueryBytes = 16 * kDim * 2;
+static_assert(kQueryBytes == 6 * 1024, "a query is six 1 KiB LDS-DMAs");
+static_assert(kStreamMaxRows <= 64 && kStreamMaxR <= 64, "one lane per row / slot");
+
+// The six LDS-DMAs of one row's query: piece P = 64k + lane of 16 bytes
+// (column P / 24, dims 8 (P % 24) ..) lands at buffer byte 16 P, i.e. the
+// buffer is [16 columns][192] bf16.  Per-lane 64-bit addresses.
+__device__ __forceinline__ void dma_query(uint32_t buf, const uint8_t* const (&a)[6]) {
+  uint32_t saved;
+  __asm__ __volatile__(
+      "s_mov_b32 %[sv], m0\n\t"
+      "s_mov_b32 m0, %[st]\n\t" SDA_LDDMA("a0", "off", "") SDA_NEXT SDA_LDDMA("a1", "off", "")
+          SDA_NEXT SDA_LDDMA("a2", "off", "") SDA_NEXT SDA_LDDMA("a3", "off", "") SDA_NEXT
+              SDA_LDDMA("a4", "off", "") SDA_NEXT SDA_LDDMA("a5", "off", "")
+      "s_mov_b32 m0, %[sv]"
+      : [sv] "=&s"(saved)
+      : [st] "s"(buf), [a0] "v"(a[0]), [a1] "v"(a[1]), [a2] "v"(a[2]), [a3] "v"(a[3]),
+        [a4] "v"(a[4]), [a5] "v"(a[5])
+      : "memory");
+}
+
+template <bool kFp8, int kAddr, bool kNt>
+__global__ __launch_bounds__(64 * kStreamWaves) __attribute__((amdgpu_waves_per_eu(1, 1))) void
+row_stream_kernel(const Params p) {
+  using C = Cfg<kFp8>;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int i16 = lane & 15, g4 = lane >> 4;
+
+  __shared__ __attribute__((aligned(1024))) uint8_t s_stage[kStreamWaves][2][kChunkBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t s_query[kStreamWaves][2][kQueryBytes];
+  __shared__ int64_t s_base[kStreamWaves][kStreamList];
+  __shared__ int s_n[kStreamWaves][kStreamList];
+
+  // This wave's rows: r_j = gw + j * W, j < nrows (the launch guarantees
+  // 1 <= nrows <= kStreamMaxRows and nrows * R <= kStreamList).
+  const int W = gridDim.x * kStreamWaves;
+  const int gw = blockIdx.x * kStreamWaves + wave;
+  const int nrows = (p.rows - gw + W - 1) / W;
+
+  // Round trip 1: lane j holds row j's flag and position; ids[j] holds slot
+  // `lane` of row j; gl[j] the gate logit of column i16 of row j.  Loads are
+  // unconditional at clamped indices (one round trip), masked afterwards.
+  const int rl = gw + min(lane, nrows - 1) * W;
+  const int act_l = p.active[rl];
+  const int pos_l = p.positions[rl];
+  int ids[kStreamMaxRows];
+  uint32_t gl[kStreamMaxRows];
+  const int slot = min(lane, max(p.R - 1, 0));
+#pragma unroll
+  for (int j = 0; j < kStreamMaxRows; ++j) {
+    const int r = gw + min(j, nrows - 1) * W;
+    ids[j] = -1;
+    gl[j] = 0;
+    if (j >= nrows) continue;  // wave-uniform: no requests for absent rows
+    if (p.R > 0) ids[j] = p.regions[(int64_t)r * p.rrs + slot];
+    if (p.gated) {
+      const int t = r / p.groups;
+      const int col = min(i16, p.heads - 1);
+      gl[j] = p.gate[(int64_t)t * p.grs + (int64_t)((r - t * p.groups) * p.heads + col) * p.ghs];
+    }
+  }
+  const float kscale = kFp8 ? *p.k_scale : 1.0f;
+  const float vscale = kFp8 ? *p.v_scale : 1.0f;
+  const float qk_scale_log2 = p.scale * kscale * 1.4426950408889634f;
+
+  // Round trip 2: the block-table entries of every visible slot of every row.
+  const int rt = p.rt;
+  int64_t pages[kStreamMaxRows];
+  uint64_t vis[kStreamMaxRows];
+#pragma unroll
+  for (int j = 0; j < kStreamMaxRows; ++j) {
+    const int r = gw + min(j, nrows - 1) * W;
+    const int act = __builtin_amdgcn_readlane(act_l, min(j, nrows - 1));
+    const int pos = __builtin_amdgcn_readlane(pos_l, min(j, nrows - 1));
+    const int id = lane < p.R ? ids[j] : -1;
+    const bool v = j < nrows && act && id >= 0 && (int64_t)id * rt <= pos;
+    vis[j] = __ballot(v);
+    const int64_t t0 = v ? (int64_t)id * rt : 0;
+    const int req = r / p.rows_per_req;
+    pages[j] = v ? p.table[(int64_t)req * p.trs + t0 / p.block] : 0;
+  }
+  // Lists: row j's visible slots in slot order at entries off_j .. off_j +
+  // nreg_j.  Lane j keeps nreg_j and off_j (read back with readlane: row
+  // indices are wave-uniform, and register arrays are never indexed at run
+  // time).
+  int off = 0, nreg_l = 0, off_l = 0;
+  int64_t* lb = s_base[wave];
+  int* ln = s_n[wave];
+#pragma unroll
+  for (int j = 0; j < kStreamMaxRows; ++j) {
+    const int r = gw + min(j, nrows - 1) * W;
+    const int pos = __builtin_amdgcn_readlane(pos_l, min(j, nrows - 1));
+    const int g = r % p.groups;
+    const uint64_t m = vis[j];
+    if ((m >> lane) & 1) {
+      const int k = off + __popcll(m & ((1ull << lane) - 1ull));
+      const int64_t t0 = (int64_t)ids[j] * rt;
+      lb[k] = pages[j] * p.cps + (int64_t)g * p.cgs + (t0 % p.block) * p.cts;
+      ln[k] = (int)min((int64_t)rt, (int64_t)pos - t0 + 1);
+    }
+    if (lane == j) {
+      nreg_l = __popcll(m);
+      off_l = off;
+    }
+    off += __popcll(m);
+  }
+  // the list reads below follow this wave's own list writes
+  __asm__ __volatile__("" ::: "memory");
+  // rows with visible tokens, one bit per row
+  const uint64_t live = __ballot(lane < nrows && nreg_l > 0);
+
+  // Rows with nothing to stream (inactive, or no visible token): zeros,
+  // unless inactive and not cleared.
+  for (int j = 0; j < nrows; ++j) {
+    if ((live >> j) & 1) continue;
+    const int act = __builtin_amdgcn_readlane(act_l, j);
+    if (!act && !p.clear) continue;
+    uint16_t* orow = out_row(p, gw + j * W);
+    for (int e = lane; e < p.heads * (kDim / 8); e += 64) {
+      const int h = e / (kDim / 8), d = 8 * (e - h * (kDim / 8));
+      *reinterpret_cast<u32x4*>(orow + (int64_t)h * p.ohs + d) = u32x4{0, 0, 0, 0};
+    }
+  }
+
+  // The stream of (row j, chunk c) items over the rows with visible tokens.
+  auto row_nreg = [&](int j) { return __builtin_amdgcn_readlane(nreg_l, j); };
+  auto row_chunks = [&](int j) {
+    return (int)(((int64_t)row_nreg(j) * rt + C::kTok - 1) / C::kTok);
+  };
+  auto next_row = [&](int j) {  // first row after j with visible tokens, or nrows
+    const uint64_t after = live & ~((2ull << j) - 1ull);
+    return after ? (int)__builtin_ctzll(after) : nrows;
+  };
+
+  const uint8_t* my_stage = &s_stage[wave][0][0];
+  const uint32_t my_stage_lds = lds_addr(my_stage);
+  const uint32_t my_query_lds = lds_addr(&s_query[wave][0][0]);
+  const LaneDma ld = lane_dma<kFp8>(lane);
+  const uint32_t cts_bytes = (uint32_t)(p.cts * C::kEsz);
+  const Win win{0, 0, 0, 0};
+
+  // Query DMA of row r into buffer qb.
+  auto issue_query = [&](int r, int qb) {
+    const int t = r / p.groups;
+    const uint16_t* qrow = p.q + (int64_t)t * p.qts + (int64_t)(r - t * p.groups) * p.qgs;
+    const uint8_t* a[6];
+#pragma unroll
+    for (int k = 0; k < 6; ++k) {
+      const int P = 64 * k + lane;
+      const int col = P / 24;
+      const int c = col < p.heads ? col : 0;
+      a[k] = reinterpret_cast<const uint8_t*>(qrow + (int64_t)c * p.qhs + 8 * (P - 24 * col));
+    }
+    dma_query((uint32_t)__builtin_amdgcn_readfirstlane(my_query_lds + qb * kQueryBytes), a);
+  };
+  auto issue_item = [&](int j, int c, int stage) {
+    const int o = __builtin_amdgcn_readlane(off_l, j);
+    return issue_chunk<kFp8, kAddr>(p, c, row_nreg(j), lb + o, ln + o, lane,
+                                    my_stage_lds + stage * kChunkBytes, ld, cts_bytes, win);
+  };
+
+  int j = live ? (int)__builtin_ctzll(live) : nrows;
+  if (j >= nrows) return;
+  int qb = 0;
+  issue_query(gw + j * W, qb);
+  uint32_t vb[2];
+  vb[0] = issue_item(j, 0, 0);
+  int c = 0, nch = row_chunks(j);
+  int s = 0;
+
+  RowState st;
+#pragma unroll
+  for (int nt = 0; nt < 12; ++nt) st.acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  st.m = -INFINITY;
+  st.l = 0.f;
+  u32x4 qreg[6];
+  const ColWin cw{0, 1, 0};
+
+  for (;;) {
+    // the next item: chunk c + 1 of this row, or the first chunk of the next
+    // row with visible tokens (its query DMA goes first)
+    int jn = j, cn = c + 1;
+    if (cn >= nch) {
+      jn = next_row(j);
+      cn = 0;
+    }
+    if (jn < nrows) {
+      if (cn == 0) {
+        issue_query(gw + jn * W, qb ^ 1);
+        vb[s ^ 1] = issue_item(jn, 0, s ^ 1);
+        wait_vmcnt<kOpsPerChunk + 6>();
+      } else {
+        vb[s ^ 1] = issue_item(jn, cn, s ^ 1);
+        wait_vmcnt<kOpsPerChunk>();
+      }
+    } else {
+      wait_vmcnt<0>();
+    }
+    if (c == 0) {
+      // this row's query has landed with its first chunk: B operand, column i16
+      const SDA_LDS uint8_t* qcol =
+          (const SDA_LDS uint8_t*)&s_query[wave][qb][0] + i16 * (kDim * 2);
+#pragma unroll
+      for (int cc = 0; cc < 6; ++cc) {
+        const int d = kFp8 ? 64 * (cc >> 1) + 16 * g4 + 8 * (cc & 1) : 32 * cc + 8 * g4;
+        qreg[cc] = i16 < p.heads ? *(const SDA_LDS u32x4*)(qcol + 2 * d) : u32x4{0, 0, 0, 0};
+      }
+    }
+    compute_chunk<kFp8, false>(my_stage + s * kChunkBytes, vb[s], cw, qreg, qk_scale_log2, lane,
+                               st);
+    if (c + 1 == nch) {
+      // Row j is complete: fold the sums, v_scale and the gate into one
+      // factor per column and write the row through the computed stage.
+      float l = st.l;
+      l += __shfl_xor(l, 16);
+      l += __shfl_xor(l, 32);
+      float f = st.m == -INFINITY ? 0.f : vscale / l;
+      if (p.gated) {
+        uint32_t gj = gl[0];
+#pragma unroll
+        for (int i = 1; i < kStreamMaxRows; ++i) gj = i == j ? gl[i] : gj;  // no run-time index
+        f *= gate_sigmoid(gj);
+      }
+      uint8_t* stg = const_cast<uint8_t*>(my_stage) + s * kChunkBytes;
+#pragma unroll
+      for (int nt = 0; nt < 12; ++nt) {
+        const f32x4 v = st.acc[nt] * f;
+        const u32x2 w = {float_to_bf16_bits(v[0]) | (float_to_bf16_bits(v[1]) << 16),
+                         float_to_bf16_bits(v[2]) | (float_to_bf16_bits(v[3]) << 16)};
+        *(SDA_LDS u32x2*)((SDA_LDS uint8_t*)stg + (i16 * kDim + 16 * nt + 4 * g4) * 2) = w;
+      }
+      __asm__ __volatile__("" ::: "memory");  // a wave's LDS operations run in order
+      uint16_t* orow = out_row(p, gw + j * W);
+#pragma unroll
+      for (int k = 0; k < 6; ++k) {
+        const int P = 64 * k + lane;
+        const int col = P / 24;
+        if (col < p.heads) {
+          const u32x4 v = *(const SDA_LDS u32x4*)((SDA_LDS uint8_t*)stg + 16 * P);
+          u32x4* dst = reinterpret_cast<u32x4*>(orow + (int64_t)col * p.ohs + 8 * (P - 24 * col));
+          if constexpr (kNt)
+            __builtin_nontemporal_store(v, dst);
+          else
+            *dst = v;
+        }
+      }
+      // the next DMA into this stage (next iteration) follows these reads
+      __asm__ __volatile__("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int nt = 0; nt < 12; ++nt) st.acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      st.m = -INFINITY;
+      st.l = 0.f;
+    }
+    if (jn >= nrows) break;
+    if (jn != j) {
+      j = jn;
+      nch = row_chunks(j);
+      qb ^= 1;
+    }
+    c = cn;
+    s ^= 1;
+  }
+}
+
 // One 64-thread workgroup per (row, head), a (rows, heads) grid: 3 dims per
 // thread.
 __global__ __launch_bounds__(64) void combine_kernel(const Params p) {
@@ -1145,9 +1247,41 @@ void launch_region_list(const Params& p, hipStream_t stream) {
     launch_split<kFp8, kFused, kGeneral>(p, wgs, stream);
 }
 
+// The row-stream kernel serves fused calls with at least two rows per wave
+// of the chip (one 4-wave workgroup per CU), at most kStreamMaxRows rows per
+// wave whose lists fit the wave's kStreamList entries, and an output on
+// 16-byte boundaries.
+bool use_row_stream(const Params& p) {
+  if (p.splits != 1 || !p.wide_out || p.R > kStreamMaxR || p.cus <= 0) return false;
+  const int64_t waves = (int64_t)kStreamWaves * p.cus;
+  const int64_t per_wave = (p.rows + waves - 1) / waves;
+  return p.rows >= 2 * waves && per_wave <= kStreamMaxRows && per_wave * p.R <= kStreamList;
+}
+
+template <bool kFp8, int kAddr>
+void launch_row_stream_addr(const Params& p, hipStream_t stream) {
+  const dim3 grid((unsigned)p.cus), block(64 * kStreamWaves);
+  if (p.nt_out)
+    hipLaunchKernelGGL((row_stream_kernel<kFp8, kAddr, true>), grid, block, 0, stream, p);
+  else
+    hipLaunchKernelGGL((row_stream_kernel<kFp8, kAddr, false>), grid, block, 0, stream, p);
+}
+
+template <bool kFp8>
+void launch_row_stream(const Params& p, hipStream_t stream) {
+  if (p.rt % Cfg<kFp8>::kTok == 0)
+    launch_row_stream_addr<kFp8, kUniform>(p, stream);
+  else if (!kFp8 && p.rt == 8)
+    launch_row_stream_addr<kFp8, kFp8 ? kGeneral : kPair>(p, stream);
+  else
+    launch_row_stream_addr<kFp8, kGeneral>(p, stream);
+}
+
 template <bool kFp8>
 void launch_dtype(const Params& p, hipStream_t stream) {
-  if (p.splits == 1)
+  if (use_row_stream(p))
+    launch_row_stream<kFp8>(p, stream);
+  else if (p.splits == 1)
     launch_region_list<kFp8, true>(p, stream);
   else
     launch_region_list<kFp8, false>(p, stream);
@@ -1185,7 +1319,7 @@ hipError_t launch(const Params& p0, bool fp8, hipStream_t stream) {
   Params p = p0;
   p.nt_out = large_output(p) ? 1 : 0;
   p.wide_out = wide_output(p) ? 1 : 0;
-  p.order = launch_order(p, stream);
+  p.order = use_row_stream(p) ? nullptr : launch_order(p, stream);
   if (fp8)
     launch_dtype<true>(p, stream);
   else

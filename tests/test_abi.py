@@ -10,8 +10,8 @@ from sparse_paged_decode_02_amd import binding as B
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def _declared_functions():
-    text = open(os.path.join(ROOT, "include", "sda.h")).read()
+def _declared_functions(header="sda.h"):
+    text = open(os.path.join(ROOT, "include", header)).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(sda_\w+)\s*\(", text, flags=re.M)))
 
@@ -337,3 +337,13 @@ def test_logits_empty_calls_launch_nothing():
     assert B.lib().sda_indexer_logits(None, None) == B.SDA_ERR_INVALID
     assert B.sda_indexer_logits_raw(_valid_logits(rows=0, query=None)) == B.SDA_OK
     assert B.sda_indexer_logits_raw(_valid_logits(num_regions=0, scores=None)) == B.SDA_OK
+
+
+def test_probe_library_exports_its_header():
+    import ctypes
+    from sparse_paged_decode_02_amd import build as sda_build
+    names = _declared_functions("sda_probe.h")
+    assert names == ["sda_probe_args_size", "sda_probe_gather"]
+    lib = ctypes.CDLL(sda_build.PROBE_LIB)
+    for n in names:
+        assert hasattr(lib, n), n

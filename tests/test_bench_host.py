@@ -153,3 +153,30 @@ def test_host_threads_use_every_usable_core_up_to_the_stated_share(monkeypatch):
     assert n == 1 and "OMP_NUM_THREADS=1" in why
     monkeypatch.setenv("OMP_NUM_THREADS", str(avail + 5))
     assert bench.host_threads()[0] == avail
+
+
+def test_probe_blocks_are_each_rows_visible_regions():
+    # Byte offsets of the blocks the gather probe reads, against a slot-by-slot
+    # walk: every visible region (id >= 0, first token <= position) of every
+    # active row, in slot order, at page * ps + g * gs + (t0 % block) * ts.
+    for k, kw in ((2, dict(requests=3, pages_per_req=24, pos_lo=100, pos_hi=1500)),
+                  (4, dict(requests=3, pages_per_req=16, pos_lo=40, pos_hi=510)),
+                  (7, dict(requests=2, pages_per_req=16, pos_lo=7, pos_hi=1023, R=40))):
+        w = gen.scaled(gen.WORKLOADS[k], **kw)
+        idx = gen.draw_indices(w)
+        e = 1 if w.kv == "fp8" else 2
+        strides = (w.groups * w.block * 384 + 64, w.block * 384 + 32, 384 + 16)
+        offs, start = bench.probe_blocks(w, strides, idx.positions, idx.regions, idx.active,
+                                         idx.block_table)
+        want, wstart = [], [0]
+        for r in range(w.rows):
+            if idx.active[r]:
+                req, g = r // (w.groups * w.query_len), r % w.groups
+                for rid in idx.regions[r]:
+                    if rid >= 0 and rid * w.rt <= idx.positions[r]:
+                        t0 = int(rid) * w.rt
+                        page = int(idx.block_table[req, t0 // w.block])
+                        want.append((page * strides[0] + g * strides[1]
+                                     + (t0 % w.block) * strides[2]) * e)
+            wstart.append(len(want))
+        assert offs.tolist() == want and start.tolist() == wstart

@@ -529,3 +529,87 @@ def test_full_size(k):
     assert o.abs().max().item() <= vmax
     del inp, out
     torch.cuda.empty_cache()
+
+
+# --- large batches: the row-stream kernel (each wave streams whole rows) -----
+def _stream_rows(per_wave_min=2, extra=0, multiple=4):
+    """A row count with at least `per_wave_min` rows per wave of the chip (4
+    waves per CU), plus `extra`, rounded up to `multiple`."""
+    waves = 4 * B.sda_device_compute_units()
+    rows = per_wave_min * waves + extra
+    return -(-rows // multiple) * multiple
+
+
+@pytest.mark.parametrize("kv,block,rt,gated,extra", [
+    ("bf16", 16, 0, True, 4), ("fp8", 16, 0, True, 0), ("fp8", 64, 0, True, 1028),
+    ("bf16", 64, 0, False, 8), ("bf16", 16, 8, True, 36), ("fp8", 16, 16, False, 4)])
+def test_row_stream_all_rows(kv, block, rt, gated, extra):
+    # 2-3 rows per wave (ragged when `extra` is not a multiple of the waves),
+    # live regions 1..R per row, 10% inactive, the current region partly
+    # masked; every row against the oracle.  Blocks of 64 take the one-base
+    # chunk addressing for both dtypes, bf16 8-token regions the paired one,
+    # FP8 at 16 tokens the per-lane one.
+    G = 4
+    rows = _stream_rows(extra=extra, multiple=G)
+    R = 16 if rt == 0 else 48
+    w = gen.Workload("row-stream", requests=rows // G, query_len=1, groups=G, heads=16,
+                     block=block, pages_per_req=192 // block, R=R, kv=kv, pos_lo=20,
+                     pos_hi=191, live=(1, R), inactive_frac=0.10, gated=gated, splits=1,
+                     region_tokens=rt, seed=800 + extra + rt + block)
+    inp = gen.make_inputs(w, device=DEV)
+    out = run(inp, out=torch.full_like(inp.query, float("nan")), label="row stream")
+    assert torch.isfinite(out.float()).all(), "a row was not written"
+    check_close(out, oracle_out(inp), what="row stream %s rt%d rows%d" % (kv, rt, rows))
+    check_inactive_zero(out, inp)
+
+
+def test_row_stream_block_48_and_eight_rows_per_wave():
+    # 24-token regions in 48-token pages (per-lane addresses with a division),
+    # 8 heads, at the most rows per wave the kernel takes (8), R = 32.
+    G = 2
+    rows = _stream_rows(per_wave_min=8, multiple=G)
+    w = gen.Workload("row-stream-48", requests=rows // G, query_len=1, groups=G, heads=8,
+                     block=48, pages_per_req=6, R=32, kv="bf16", pos_lo=30, pos_hi=287,
+                     live=(1, 12), inactive_frac=0.05, gated=True, splits=1, region_tokens=24,
+                     seed=871)
+    inp = gen.make_inputs(w, device=DEV)
+    out = run(inp, out=torch.full_like(inp.query, float("nan")), label="row stream block48")
+    assert torch.isfinite(out.float()).all()
+    rng = np.random.default_rng(3)
+    rows_s = sorted(set(rng.choice(w.rows, size=1024, replace=False).tolist() + [0, w.rows - 1]))
+    check_close(out, oracle_out(inp, rows=rows_s), rows=rows_s, what="row stream block48")
+    check_inactive_zero(out, inp)
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_row_stream_inactive_untouched_and_poisoned(kv):
+    # clear_inactive off leaves inactive rows as they were; poisoned inputs of
+    # inactive rows (NaN query and gate, huge ids, INT32_MAX position) change
+    # no bit of the output.
+    G = 4
+    rows = _stream_rows(extra=4, multiple=G)
+    w = gen.Workload("row-stream-poison", requests=rows // G, query_len=1, groups=G, heads=16,
+                     block=16, pages_per_req=12, R=16, kv=kv, pos_lo=20, pos_hi=191,
+                     live=(1, 16), inactive_frac=0.10, gated=True, splits=1, seed=890)
+    inp = gen.make_inputs(w, device=DEV)
+    ina = ~inp.active
+    sentinel = torch.full_like(inp.query, 3.5)
+    kept = run(inp, clear_inactive=False, out=sentinel.clone(), label="row stream keep")
+    assert torch.equal(kept[ina], sentinel[ina])
+    clean = run(inp, out=torch.full_like(inp.query, 7.0), label="row stream clean")
+    assert torch.equal(kept[~ina], clean[~ina])
+    pos = inp.positions.clone()
+    pos[ina] = 2 ** 31 - 1
+    reg = inp.regions.clone()
+    reg[ina] = 0x3FFFFFFF
+    q = inp.query.clone()
+    q[ina] = float("nan")
+    gate = inp.gate.clone()
+    for r in torch.nonzero(ina).flatten().tolist():
+        g = r % G
+        gate[r // G, g * w.heads:(g + 1) * w.heads] = float("nan")
+    poisoned = gen.Inputs(**{**inp.__dict__, "positions": pos, "regions": reg, "query": q,
+                             "gate": gate})
+    out = run(poisoned, out=torch.full_like(inp.query, 7.0), label="row stream poisoned")
+    assert torch.equal(out.view(torch.int16), clean.view(torch.int16))
+    check_inactive_zero(out, inp)
