@@ -67,6 +67,7 @@ namespace {
 constexpr int kWavesSmallGrid = 4;
 constexpr int kWavesLargeGrid = 2;
 constexpr int kStages = 2;          // LDS stages per wave: 1 computed, 1 in flight
+constexpr int kSlotBatch = 8;       // 64-slot groups of a region list loaded together
 constexpr int kAccStride = 196;     // floats per head row in the wave-merge area
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -565,33 +566,77 @@ split_kernel(const Params p) {
     // Each wave ranks the visible slots (id >= 0, first token <= pos) in
     // slot order, 64 at a time.  It takes this split's balanced share, ranks
     // [ceil(s*V/S), ceil((s+1)*V/S)), and writes the share's cache offsets
-    // and visible counts to the LDS list.
-    // The first 64 slots (id_first) stay in registers for the second pass.
-    int nvis = 0;
-    for (int j0 = 0; j0 < p.R; j0 += 64) {
-      const int j = j0 + lane;
-      const int id = j0 == 0 ? id_first : (j < p.R ? reg[j] : -1);
-      nvis += __popcll(__ballot(id >= 0 && (int64_t)id * rt <= pos));
-    }
-    const int lo = (int)(((int64_t)split * nvis + p.splits - 1) / p.splits);
-    const int hi = (int)(((int64_t)(split + 1) * nvis + p.splits - 1) / p.splits);
-    nreg = hi - lo;
-    int base_rank = 0;
-    for (int j0 = 0; j0 < p.R; j0 += 64) {
-      const int j = j0 + lane;
-      const int id = j0 == 0 ? id_first : (j < p.R ? reg[j] : -1);
-      const bool vis = id >= 0 && (int64_t)id * rt <= pos;
+    // and visible counts to the LDS list.  With one split every visible slot
+    // is in the share, so the count pass is skipped.  Up to kSlotBatch
+    // groups of 64 slots are loaded together (their ids, then their
+    // block-table entries): two round trips per 512 slots.
+    // The first 64 slots (id_first) were loaded with the row's flag.
+    const int ngroups = (p.R + 63) / 64;
+    if (ngroups <= 1) {
+      // At most 64 slots: the ids loaded with the flag are the whole list.
+      const bool vis = id_first >= 0 && (int64_t)id_first * rt <= pos;
       const uint64_t m = __ballot(vis);
-      const int k = base_rank + __popcll(m & ((1ull << lane) - 1ull));
-      if (vis && k >= lo && k < hi) {
-        const int64_t t0 = (int64_t)id * rt;
+      const int nvis = __popcll(m);
+      const int lo1 = (int)(((int64_t)split * nvis + p.splits - 1) / p.splits);
+      const int hi1 = (int)(((int64_t)(split + 1) * nvis + p.splits - 1) / p.splits);
+      const int k = __popcll(m & ((1ull << lane) - 1ull));
+      if (vis && k >= lo1 && k < hi1) {
+        const int64_t t0 = (int64_t)id_first * rt;
         const int64_t col = t0 / p.block;
         const int off0 = (int)(t0 - col * p.block);
         const int64_t page = p.table[(int64_t)req * p.trs + col];
-        s_base[k - lo] = page * p.cps + (int64_t)g * p.cgs + (int64_t)off0 * p.cts;
-        s_n[k - lo] = (int)min((int64_t)rt, (int64_t)pos - t0 + 1);
+        s_base[k - lo1] = page * p.cps + (int64_t)g * p.cgs + (int64_t)off0 * p.cts;
+        s_n[k - lo1] = (int)min((int64_t)rt, (int64_t)pos - t0 + 1);
       }
-      base_rank += __popcll(m);
+      nreg = hi1 - lo1;
+    } else {
+      auto load_ids = [&](int k0, int (&idb)[kSlotBatch]) {
+#pragma unroll
+        for (int b = 0; b < kSlotBatch; ++b) {
+          const int j = 64 * (k0 + b) + lane;
+          idb[b] = k0 + b == 0 ? id_first : (k0 + b < ngroups && j < p.R ? reg[j] : -1);
+        }
+      };
+      int lo = 0, hi = 0x7FFFFFFF;
+      if (p.splits > 1) {
+        int nvis = 0;
+        for (int k0 = 0; k0 < ngroups; k0 += kSlotBatch) {
+          int idb[kSlotBatch];
+          load_ids(k0, idb);
+#pragma unroll
+          for (int b = 0; b < kSlotBatch; ++b)
+            nvis += __popcll(__ballot(idb[b] >= 0 && (int64_t)idb[b] * rt <= pos));
+        }
+        lo = (int)(((int64_t)split * nvis + p.splits - 1) / p.splits);
+        hi = (int)(((int64_t)(split + 1) * nvis + p.splits - 1) / p.splits);
+      }
+      int base_rank = 0;
+      for (int k0 = 0; k0 < ngroups; k0 += kSlotBatch) {
+        int idb[kSlotBatch];
+        load_ids(k0, idb);
+        int64_t pg[kSlotBatch];
+        int kk[kSlotBatch];
+#pragma unroll
+        for (int b = 0; b < kSlotBatch; ++b) {
+          const bool vis = idb[b] >= 0 && (int64_t)idb[b] * rt <= pos;
+          const uint64_t m = __ballot(vis);
+          const int k = base_rank + __popcll(m & ((1ull << lane) - 1ull));
+          const bool mine = vis && k >= lo && k < hi;
+          kk[b] = mine ? k - lo : -1;
+          pg[b] = mine ? p.table[(int64_t)req * p.trs + (int64_t)idb[b] * rt / p.block] : 0;
+          base_rank += __popcll(m);
+        }
+#pragma unroll
+        for (int b = 0; b < kSlotBatch; ++b) {
+          if (kk[b] >= 0) {
+            const int64_t t0 = (int64_t)idb[b] * rt;
+            const int off0 = (int)(t0 % p.block);
+            s_base[kk[b]] = pg[b] * p.cps + (int64_t)g * p.cgs + (int64_t)off0 * p.cts;
+            s_n[kk[b]] = (int)min((int64_t)rt, (int64_t)pos - t0 + 1);
+          }
+        }
+      }
+      nreg = p.splits > 1 ? hi - lo : base_rank;
     }
     nchunks = (int)(((int64_t)nreg * rt + C::kTok - 1) / C::kTok);
   }
