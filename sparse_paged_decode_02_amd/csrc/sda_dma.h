@@ -156,6 +156,21 @@ __device__ __forceinline__ void dma_chunk_vaddr(uint32_t stage, const uint8_t* c
 #undef SDA_VADDR_OPERANDS
 }
 
+// One global_load_lds_dword: each lane moves the 4 bytes at its address to
+// LDS address lds + 4 * lane.  No register receives the data, so nothing
+// depends on the load until an explicit wait.  M0 is saved and restored.
+__device__ __forceinline__ void dma_dword(uint32_t lds, const int32_t* addr) {
+  uint32_t saved;
+  __asm__ __volatile__(
+      "s_mov_b32 %[sv], m0\n\t"
+      "s_mov_b32 m0, %[st]\n\t"
+      "global_load_lds_dword %[a], off\n\t"
+      "s_mov_b32 m0, %[sv]"
+      : [sv] "=&s"(saved)
+      : [st] "s"(lds), [a] "v"(addr)
+      : "memory");
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");

@@ -459,6 +459,9 @@ split_kernel(const Params p) {
   __shared__ float s_m[kWaves][16];
   __shared__ float s_l[kWaves][16];
   __shared__ float s_fac[kWaves][16];
+  // block-table entries of slot groups 1 .. kSlotBatch - 1 in the deferred
+  // list mode (below), one per slot, landed by LDS-DMA
+  __shared__ int32_t s_pages[kSlotBatch - 1][64];
 
   // The workgroup's query columns (the 16 columns of the MFMA tiles).
   //  * region modes: row r = blockIdx.x, or order[blockIdx.x] when the rows
@@ -538,6 +541,14 @@ split_kernel(const Params p) {
   // operations in order), so the list is consistent without synchronisation.
   int nreg = 0, nchunks = 0;
   Win win{0, 0, 0, 0};
+  // Deferred list mode (one split, 65..512 region slots): group 0's entries
+  // are written before the pipeline starts; the block-table entries of
+  // groups 1..7 are requested by LDS-DMA behind the first chunk and turned
+  // into list entries after the first wait.  ids_d / kk_d: slot 64b + lane's
+  // region id and list entry (-1: not visible); n0: group 0's entries.
+  bool pending = false;
+  int n0 = 0;
+  int ids_d[kSlotBatch], kk_d[kSlotBatch];
   if (kAddr == kWindow) {
     // The union window's 16-token chunks, aligned down to a multiple of 16
     // so that a chunk never straddles a page, are dealt to the splits in
@@ -590,53 +601,93 @@ split_kernel(const Params p) {
       }
       nreg = hi1 - lo1;
     } else {
-      auto load_ids = [&](int k0, int (&idb)[kSlotBatch]) {
+      bool deferred = p.splits == 1 && ngroups <= kSlotBatch;
+      if (deferred) {
+        // Deferred list mode.  Group 0's block-table entries and the ids of
+        // groups 1..7 share one round trip; every slot's rank is known after
+        // it.
+        const bool vis0 = id_first >= 0 && (int64_t)id_first * rt <= pos;
+        int64_t page0 = 0;
+        if (vis0) page0 = p.table[(int64_t)req * p.trs + (int64_t)id_first * rt / p.block];
+        ids_d[0] = id_first;
+#pragma unroll
+        for (int b = 1; b < kSlotBatch; ++b) {
+          const int j = 64 * b + lane;
+          ids_d[b] = b < ngroups && j < p.R ? reg[j] : -1;
+        }
+        int base_rank = 0;
 #pragma unroll
         for (int b = 0; b < kSlotBatch; ++b) {
-          const int j = 64 * (k0 + b) + lane;
-          idb[b] = k0 + b == 0 ? id_first : (k0 + b < ngroups && j < p.R ? reg[j] : -1);
+          const bool vis = ids_d[b] >= 0 && (int64_t)ids_d[b] * rt <= pos;
+          const uint64_t m = __ballot(vis);
+          kk_d[b] = vis ? base_rank + __popcll(m & ((1ull << lane) - 1ull)) : -1;
+          base_rank += __popcll(m);
+          if (b == 0) n0 = base_rank;
         }
-      };
-      int lo = 0, hi = 0x7FFFFFFF;
-      if (p.splits > 1) {
-        int nvis = 0;
+        // The first two chunks of every wave are issued before the first
+        // wait: group 0 must cover them, or the row takes the path below.
+        const int cover = (int)(((int64_t)2 * kWaves * C::kTok - 1) / rt) + 1;
+        if (n0 < cover && base_rank > n0) {
+          deferred = false;
+        } else {
+          if (vis0) {
+            const int64_t t0 = (int64_t)id_first * rt;
+            s_base[kk_d[0]] = page0 * p.cps + (int64_t)g * p.cgs + (t0 % p.block) * p.cts;
+            s_n[kk_d[0]] = (int)min((int64_t)rt, (int64_t)pos - t0 + 1);
+          }
+          nreg = base_rank;
+          pending = nreg > n0;
+        }
+      }
+      if (!deferred) {
+        auto load_ids = [&](int k0, int (&idb)[kSlotBatch]) {
+#pragma unroll
+          for (int b = 0; b < kSlotBatch; ++b) {
+            const int j = 64 * (k0 + b) + lane;
+            idb[b] = k0 + b == 0 ? id_first : (k0 + b < ngroups && j < p.R ? reg[j] : -1);
+          }
+        };
+        int lo = 0, hi = 0x7FFFFFFF;
+        if (p.splits > 1) {
+          int nvis = 0;
+          for (int k0 = 0; k0 < ngroups; k0 += kSlotBatch) {
+            int idb[kSlotBatch];
+            load_ids(k0, idb);
+#pragma unroll
+            for (int b = 0; b < kSlotBatch; ++b)
+              nvis += __popcll(__ballot(idb[b] >= 0 && (int64_t)idb[b] * rt <= pos));
+          }
+          lo = (int)(((int64_t)split * nvis + p.splits - 1) / p.splits);
+          hi = (int)(((int64_t)(split + 1) * nvis + p.splits - 1) / p.splits);
+        }
+        int base_rank = 0;
         for (int k0 = 0; k0 < ngroups; k0 += kSlotBatch) {
           int idb[kSlotBatch];
           load_ids(k0, idb);
+          int64_t pg[kSlotBatch];
+          int kk[kSlotBatch];
 #pragma unroll
-          for (int b = 0; b < kSlotBatch; ++b)
-            nvis += __popcll(__ballot(idb[b] >= 0 && (int64_t)idb[b] * rt <= pos));
-        }
-        lo = (int)(((int64_t)split * nvis + p.splits - 1) / p.splits);
-        hi = (int)(((int64_t)(split + 1) * nvis + p.splits - 1) / p.splits);
-      }
-      int base_rank = 0;
-      for (int k0 = 0; k0 < ngroups; k0 += kSlotBatch) {
-        int idb[kSlotBatch];
-        load_ids(k0, idb);
-        int64_t pg[kSlotBatch];
-        int kk[kSlotBatch];
+          for (int b = 0; b < kSlotBatch; ++b) {
+            const bool vis = idb[b] >= 0 && (int64_t)idb[b] * rt <= pos;
+            const uint64_t m = __ballot(vis);
+            const int k = base_rank + __popcll(m & ((1ull << lane) - 1ull));
+            const bool mine = vis && k >= lo && k < hi;
+            kk[b] = mine ? k - lo : -1;
+            pg[b] = mine ? p.table[(int64_t)req * p.trs + (int64_t)idb[b] * rt / p.block] : 0;
+            base_rank += __popcll(m);
+          }
 #pragma unroll
-        for (int b = 0; b < kSlotBatch; ++b) {
-          const bool vis = idb[b] >= 0 && (int64_t)idb[b] * rt <= pos;
-          const uint64_t m = __ballot(vis);
-          const int k = base_rank + __popcll(m & ((1ull << lane) - 1ull));
-          const bool mine = vis && k >= lo && k < hi;
-          kk[b] = mine ? k - lo : -1;
-          pg[b] = mine ? p.table[(int64_t)req * p.trs + (int64_t)idb[b] * rt / p.block] : 0;
-          base_rank += __popcll(m);
-        }
-#pragma unroll
-        for (int b = 0; b < kSlotBatch; ++b) {
-          if (kk[b] >= 0) {
-            const int64_t t0 = (int64_t)idb[b] * rt;
-            const int off0 = (int)(t0 % p.block);
-            s_base[kk[b]] = pg[b] * p.cps + (int64_t)g * p.cgs + (int64_t)off0 * p.cts;
-            s_n[kk[b]] = (int)min((int64_t)rt, (int64_t)pos - t0 + 1);
+          for (int b = 0; b < kSlotBatch; ++b) {
+            if (kk[b] >= 0) {
+              const int64_t t0 = (int64_t)idb[b] * rt;
+              const int off0 = (int)(t0 % p.block);
+              s_base[kk[b]] = pg[b] * p.cps + (int64_t)g * p.cgs + (int64_t)off0 * p.cts;
+              s_n[kk[b]] = (int)min((int64_t)rt, (int64_t)pos - t0 + 1);
+            }
           }
         }
+        nreg = p.splits > 1 ? hi - lo : base_rank;
       }
-      nreg = p.splits > 1 ? hi - lo : base_rank;
     }
     nchunks = (int)(((int64_t)nreg * rt + C::kTok - 1) / C::kTok);
   }
@@ -673,6 +724,34 @@ split_kernel(const Params p) {
     uint32_t vb[kStages];
     vb[0] = issue_chunk<kFp8, kAddr>(p, wave, nreg, s_base, s_n, lane, my_stage_lds, ld, cts_bytes,
                                      win);
+    // Deferred list mode: the block-table entries of groups 1..7 go to
+    // s_pages by LDS-DMA (one dword per lane; slots that are not visible
+    // read the row's first entry); the first wait below covers them.
+    if (kAddr != kWindow && pending) {
+      const int32_t* trow = p.table + (int64_t)req * p.trs;
+#pragma unroll
+      for (int b = 1; b < kSlotBatch; ++b) {
+        if (64 * b >= p.R) break;
+        const int32_t* a = kk_d[b] >= 0 ? trow + (int64_t)ids_d[b] * p.rt / p.block : trow;
+        dma_dword((uint32_t)__builtin_amdgcn_readfirstlane(lds_addr(&s_pages[b - 1][0])), a);
+      }
+    }
+    // List entries of groups 1..7 from the landed block-table entries.
+    auto convert = [&]() {
+#pragma unroll
+      for (int b = 1; b < kSlotBatch; ++b) {
+        if (kk_d[b] >= 0) {
+          const int64_t page = s_pages[b - 1][lane];
+          const int64_t t0 = (int64_t)ids_d[b] * p.rt;
+          s_base[kk_d[b]] = page * p.cps + (int64_t)g * p.cgs + (t0 % p.block) * p.cts;
+          s_n[kk_d[b]] = (int)min((int64_t)p.rt, (int64_t)pos - t0 + 1);
+        }
+      }
+      // later list reads follow these writes (a wave's LDS operations run
+      // in order)
+      __asm__ __volatile__("" ::: "memory");
+      pending = false;
+    };
     auto step = [&](int i0, auto stage_c) -> bool {
       constexpr int S = decltype(stage_c)::value;
       constexpr int SN = (S + kStages - 1) % kStages;
@@ -681,6 +760,13 @@ split_kernel(const Params p) {
       // Stage SN was last read by the previous iteration, whose reads all
       // completed before its MFMAs; the asm below keeps them above the DMA.
       const int cn = c + kWaves * (kStages - 1);
+      if (kAddr != kWindow && pending && cn < nchunks &&
+          (int)(((int64_t)(cn + 1) * C::kTok - 1) / p.rt) >= n0) {
+        // the next chunk reaches past group 0 before the entries were
+        // converted: wait for everything in flight and convert now
+        wait_vmcnt<0>();
+        convert();
+      }
       if (cn < nchunks) {
         vb[SN] = issue_chunk<kFp8, kAddr>(p, cn, nreg, s_base, s_n, lane,
                                           my_stage_lds + SN * kChunkBytes, ld, cts_bytes, win);
@@ -688,6 +774,7 @@ split_kernel(const Params p) {
       } else {
         wait_vmcnt<0>();
       }
+      if (kAddr != kWindow && pending) convert();
       if (kAddr == kWindow) cw.t0 = win.t_base + 16 * c;
       compute_chunk<kFp8, kAddr == kWindow>(my_stage + S * kChunkBytes, vb[S], cw, qreg,
                                             qk_scale_log2, lane, st);

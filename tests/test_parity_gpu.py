@@ -613,3 +613,28 @@ def test_row_stream_inactive_untouched_and_poisoned(kv):
     out = run(poisoned, out=torch.full_like(inp.query, 7.0), label="row stream poisoned")
     assert torch.equal(out.view(torch.int16), clean.view(torch.int16))
     check_inactive_zero(out, inp)
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+@pytest.mark.parametrize("group0", ["full", "sparse", "empty"])
+def test_long_lists_group0_coverage(kv, group0):
+    # One split, 200 slots of 8-token regions.  With the first 64 slots full,
+    # the list entries past them are resolved behind the first chunks; with
+    # only a few (or no) visible regions among them the row is resolved
+    # before streaming.  Every case matches the oracle on all rows.
+    w = small(2 if kv == "bf16" else 3, requests=3, pages_per_req=16, pos_lo=700, pos_hi=1023,
+              R=200, region_tokens=8, splits=1)
+    inp = gen.make_inputs(w, device=DEV)
+    if group0 != "full":
+        reg = inp.regions.cpu().numpy()
+        for r in range(reg.shape[0]):
+            live = reg[r][reg[r] >= 0]
+            keep = 3 if group0 == "sparse" else 0
+            row = np.full(w.R, -1, dtype=np.int32)
+            row[:keep] = live[:keep]
+            row[64:64 + len(live) - keep] = live[keep:w.R - 64 + keep]
+            reg[r] = row
+        inp.regions = torch.from_numpy(reg).to(DEV)
+    out = run(inp, splits=1, label="long list %s %s" % (kv, group0))
+    check_close(out, oracle_out(inp), what="long list %s group0 %s" % (kv, group0))
+    check_inactive_zero(out, inp)
