@@ -592,13 +592,6 @@ def measure_sparse(args, dev, k: int, with_cpu: bool) -> dict:
     ws_bytes = B.sda_workspace_bytes(w.rows, w.heads, splits)
     if args.no_row_order and splits == 1:
         ws_bytes = 0
-    # The library ranks rows when given a workspace and the grid takes 2 to 4
-    # rounds of the resident workgroups (two per CU for grids of at least two
-    # per CU, else one).
-    cus = B.sda_device_compute_units()
-    grid = w.rows * splits
-    resident = 2 * cus if grid >= 2 * cus else cus
-    ordered = ws_bytes > 0 and resident < grid <= 4 * resident
     workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     handle = ctypes.c_void_p(stream.cuda_stream)
@@ -615,6 +608,14 @@ def measure_sparse(args, dev, k: int, with_cpu: bool) -> dict:
             v_scale=s.v_scale, gate=s.gate, region_tokens=w.region_tokens,
             workspace=workspace if ws_bytes else None))
 
+    # The library names the kernels it launches for these arguments on this
+    # device (the schedule depends on the compute-unit count).
+    rc, kernels = B.sda_decode_kernels_raw(prepared[0], handle)
+    if rc != B.SDA_OK:
+        raise B.SdaError(rc, B.status_string(rc))
+    ordered = bool(kernels & B.SDA_KERNEL_ORDER)
+    row_stream = bool(kernels & B.SDA_KERNEL_ROW_STREAM)
+
     def call(i):
         rc = B.sda_decode_raw(prepared[i % len(prepared)], handle)
         if rc != B.SDA_OK:
@@ -629,9 +630,11 @@ def measure_sparse(args, dev, k: int, with_cpu: bool) -> dict:
                  config={"workload": workload_desc(w), "rows": w.rows, "heads": w.heads,
                          "splits": splits, "row_order": "heaviest first" if ordered else "index",
                          "input_sets": len(sets), "seed": w.seed},
-                 kernel=("sda order kernel + " if ordered else "") + "sda split kernel"
-                 + (" + combine" if splits > 1 else " (combine fused)"),
-                 traffic=load_traffic(w.name, splits))
+                 kernel=("sda row-stream kernel (combine fused)" if row_stream else
+                         ("sda order kernel + " if ordered else "") + "sda split kernel"
+                         + (" + combine" if splits > 1 else " (combine fused)")),
+                 traffic=load_traffic(w.name, splits,
+                                      "row_stream_kernel" if row_stream else "split_kernel"))
     if args.flush_mib > 0:
         rec["flushed"] = time_flushed(call, args.steps, stream, args.flush_mib)
     if with_cpu:
@@ -645,6 +648,9 @@ def measure_sparse(args, dev, k: int, with_cpu: bool) -> dict:
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     return rec
+
+
+SDA_PROBE_MAX_BLOCKS = 2048  # include/sda_probe.h
 
 
 class ProbeArgs(ctypes.Structure):
@@ -718,12 +724,19 @@ def run_gather(args, dev) -> int:
     keep, probe_args, kernel_args, pbytes, kbytes = [], [], [], [], []
     ws = torch.empty(B.sda_workspace_bytes(w.rows, w.heads, splits), dtype=torch.uint8,
                      device=dev)
-    sink = torch.zeros(w.rows * 4, dtype=torch.int32, device=dev)
+    sink = torch.zeros(max(w.rows, args.balanced_groups) * 4, dtype=torch.int32, device=dev)
     block_bytes = w.rt * cstr[2] * e
     for s in sets:
         pos, reg, act = (s.positions.cpu().numpy(), s.regions.cpu().numpy(),
                          s.active.cpu().numpy())
         offs, start = probe_blocks(w, cstr, pos, reg, act, bt)
+        groups = w.rows
+        if args.balanced_groups:
+            # the same blocks dealt in equal contiguous shares to N groups:
+            # the balanced decomposition's ceiling (no idle CU, no tail)
+            groups = args.balanced_groups
+            start = np.round(np.linspace(0, len(offs), groups + 1)).astype(np.int32)
+            assert int(np.diff(start).max()) <= SDA_PROBE_MAX_BLOCKS
         if args.sequential:
             offs = np.arange(len(offs), dtype=np.int64) * block_bytes
             assert len(offs) * block_bytes <= base.cache.numel() * e
@@ -733,7 +746,7 @@ def run_gather(args, dev) -> int:
         a.base = base.cache.data_ptr()
         a.kv_dtype = B.SDA_KV_FP8_E4M3 if w.kv == "fp8" else B.SDA_KV_BF16
         a.token_stride = cstr[2] * e
-        a.groups, a.block_tokens = w.rows, w.rt
+        a.groups, a.block_tokens = groups, w.rt
         a.block_offsets, a.group_start, a.sink = t_off.data_ptr(), t_start.data_ptr(), \
             sink.data_ptr()
         probe_args.append(a)
@@ -772,7 +785,9 @@ def run_gather(args, dev) -> int:
     kernel_alg_at_probe_time = np.mean(kbytes) / (res["probe"]["avg_launch_us"] * 1e-6) / 1e9
     rec = {"metric": "gather ceiling of the sparse decode access pattern",
            "workload": workload_desc(w), "splits": splits,
-           "pattern": "sequential blocks" if args.sequential else "the workload's blocks",
+           "pattern": ("sequential blocks" if args.sequential else "the workload's blocks")
+           + (", dealt evenly to %d groups" % args.balanced_groups if args.balanced_groups
+              else ", one group per row"),
            "steps": args.steps, "warmup": args.warmup, "settle_ms": args.settle_ms,
            "input_sets": len(sets), "seed": w.seed, "probe": res["probe"],
            "kernel": res["kernel"],
@@ -811,6 +826,9 @@ def main() -> int:
     ap.add_argument("--sequential", action="store_true",
                     help="with --gather-ceiling: consecutive blocks instead of the "
                          "workload's")
+    ap.add_argument("--balanced-groups", type=int, default=0, metavar="N",
+                    help="--gather-ceiling: deal all blocks evenly to N workgroups instead "
+                         "of one per row")
     ap.add_argument("--pack", type=int, default=0,
                     help="with --swa: query tokens per workgroup (0: the library's plan)")
     ap.add_argument("--sets", type=int, default=4, help="rotating input sets")

@@ -32,7 +32,7 @@
 extern "C" {
 #endif
 
-#define SDA_ABI_VERSION 6
+#define SDA_ABI_VERSION 7
 #define SDA_HEAD_DIM 192     /* query / key / value head dim (fixed) */
 #define SDA_KV_ROW 384       /* one cache token row: K[0:192] then V[192:384] */
 #define SDA_MAX_HEADS 16     /* GQA-packed query heads per KV group */
@@ -154,10 +154,32 @@ typedef struct sda_decode_args {
  * be captured in a HIP graph.  It launches the split kernel, a (rows, splits)
  * grid.  When splits > 1 it also launches the combine kernel, which merges
  * the partials and then applies the gate and the inactive-row clear.  When
- * splits == 1 the combine is fused into the split kernel.
+ * splits == 1 the combine is fused into the split kernel.  Two variants of
+ * the schedule depend on the device's compute-unit count (the result is the
+ * same): a grid of 2 to 4 rounds of resident workgroups with a workspace is
+ * preceded by the bin and order kernels (heaviest rows first), and a large
+ * batch of short region lists runs the row-stream kernel instead of the
+ * split kernel: one 4-wave workgroup per CU whose waves take whole rows
+ * back to back (splits == 1, output on 16-byte boundaries, R <= 64, and
+ * with w = 4 * CUs waves, 2w <= rows <= 8w and ceil(rows / w) * R <= 256).
+ * sda_decode_kernels reports which.
  * Returns an sda_status.
  */
 int sda_decode(const sda_decode_args *args, hipStream_t stream);
+
+/*
+ * The kernels sda_decode(args, stream) would launch, as SDA_KERNEL_* bits in
+ * *kernels (0 when rows == 0).  It validates exactly as sda_decode does and
+ * returns the same status, but launches nothing and touches no device
+ * memory: only the device's compute-unit count is queried.  *kernels is 0
+ * on any error; kernels == NULL gives SDA_ERR_INVALID.  For profilers and
+ * benchmarks that name the kernel they measure.
+ */
+#define SDA_KERNEL_ORDER 1      /* bin + order kernels (row ranking) */
+#define SDA_KERNEL_SPLIT 2      /* split kernel, (rows, splits) grid */
+#define SDA_KERNEL_ROW_STREAM 4 /* row-stream kernel, one workgroup per CU */
+#define SDA_KERNEL_COMBINE 8    /* combine kernel (splits > 1) */
+int sda_decode_kernels(const sda_decode_args *args, hipStream_t stream, int *kernels);
 
 /*
  * sda_decode without a caller workspace, for callers that cannot allocate:

@@ -25,7 +25,11 @@ SDA_ERR_SCRATCH = -5
 STATIC_SCRATCH_BYTES = 16 << 20
 SDA_KV_BF16 = 0
 SDA_KV_FP8_E4M3 = 1
-ABI_VERSION = 6
+SDA_KERNEL_ORDER = 1
+SDA_KERNEL_SPLIT = 2
+SDA_KERNEL_ROW_STREAM = 4
+SDA_KERNEL_COMBINE = 8
+ABI_VERSION = 7
 HEAD_DIM = 192
 
 
@@ -127,6 +131,9 @@ def lib() -> ctypes.CDLL:
             l = ctypes.CDLL(LIB_PATH)
             l.sda_decode.restype = ctypes.c_int
             l.sda_decode.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.c_void_p]
+            l.sda_decode_kernels.restype = ctypes.c_int
+            l.sda_decode_kernels.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.c_void_p,
+                                             ctypes.POINTER(ctypes.c_int)]
             l.sda_decode_static.restype = ctypes.c_int
             l.sda_decode_static.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.c_void_p]
             l.sda_splits.restype = ctypes.c_int
@@ -299,18 +306,10 @@ def check_gate_shape(gate, rows: int, groups: int, heads: int) -> None:
                                      rows // groups, groups * heads))
 
 
-def sda_decode(query, cache, regions, block_table, positions, active, output, *, scale,
-               query_len=1, splits, clear_inactive=True, k_scale=None, v_scale=None,
-               gate=None, region_tokens=0, workspace=None, row_order=True,
-               stream=None) -> None:
-    """Enqueue ``sda_decode`` on ``stream`` (default: torch's current stream).
-
-    Argument names follow ``sparse_decode_attention`` on the page
-    "vllm.models.step5.nvidia.ops.sparse_decode_attention".  ``workspace``: a
-    device tensor of at least sda_workspace_bytes(rows, heads, splits) bytes;
-    allocated here through torch when omitted, unless splits == 1 and
-    ``row_order`` is false (no workspace: rows start in index order).
-    """
+def _decode_call(query, cache, regions, block_table, positions, active, output, scale,
+                 query_len, splits, clear_inactive, k_scale, v_scale, gate, region_tokens,
+                 workspace, row_order, stream):
+    """Checked sda_decode_args and stream handle for one decode call."""
     check_tensors(query, cache, regions, block_table, positions, active, output,
                   k_scale, v_scale, gate)
     rows, heads = query.shape[0], query.shape[1]
@@ -329,10 +328,43 @@ def sda_decode(query, cache, regions, block_table, positions, active, output, *,
                   workspace=workspace)
     if stream is None:
         stream = torch.cuda.current_stream(query.device)
-    handle = ctypes.c_void_p(stream.cuda_stream)
+    # the workspace tensor must outlive the enqueue: keep it with the args
+    return a, ctypes.c_void_p(stream.cuda_stream), workspace
+
+
+def sda_decode(query, cache, regions, block_table, positions, active, output, *, scale,
+               query_len=1, splits, clear_inactive=True, k_scale=None, v_scale=None,
+               gate=None, region_tokens=0, workspace=None, row_order=True,
+               stream=None) -> None:
+    """Enqueue ``sda_decode`` on ``stream`` (default: torch's current stream).
+
+    Argument names follow ``sparse_decode_attention`` on the page
+    "vllm.models.step5.nvidia.ops.sparse_decode_attention".  ``workspace``: a
+    device tensor of at least sda_workspace_bytes(rows, heads, splits) bytes;
+    allocated here through torch when omitted, unless splits == 1 and
+    ``row_order`` is false (no workspace: rows start in index order).
+    """
+    a, handle, _ws = _decode_call(query, cache, regions, block_table, positions, active, output,
+                                  scale, query_len, splits, clear_inactive, k_scale, v_scale,
+                                  gate, region_tokens, workspace, row_order, stream)
     rc = lib().sda_decode(ctypes.byref(a), handle)
     if rc != SDA_OK:
         raise SdaError(rc, status_string(rc))
+
+
+def sda_decode_kernels(query, cache, regions, block_table, positions, active, output, *, scale,
+                       query_len=1, splits, clear_inactive=True, k_scale=None, v_scale=None,
+                       gate=None, region_tokens=0, workspace=None, row_order=True,
+                       stream=None) -> int:
+    """SDA_KERNEL_* bits of the kernels ``sda_decode`` with the same arguments
+    would launch; nothing is launched."""
+    a, handle, _ws = _decode_call(query, cache, regions, block_table, positions, active, output,
+                                  scale, query_len, splits, clear_inactive, k_scale, v_scale,
+                                  gate, region_tokens, workspace, row_order, stream)
+    rc, bits = sda_decode_kernels_raw(a, handle)
+    if rc != SDA_OK:
+        raise SdaError(rc, status_string(rc))
+    return bits
 
 
 def sda_decode_static(query, cache, regions, block_table, positions, active, output, *,
@@ -367,6 +399,14 @@ def sda_decode_static_raw(args: DecodeArgs, stream_handle=None) -> int:
 def sda_decode_raw(args: DecodeArgs, stream_handle=None) -> int:
     """Call the C entry point on a prepared struct; returns the status code."""
     return int(lib().sda_decode(ctypes.byref(args), stream_handle))
+
+
+def sda_decode_kernels_raw(args: DecodeArgs, stream_handle=None) -> tuple:
+    """(status, SDA_KERNEL_* bits) of the kernels sda_decode would launch for
+    a prepared struct; nothing is launched."""
+    bits = ctypes.c_int(0)
+    rc = int(lib().sda_decode_kernels(ctypes.byref(args), stream_handle, ctypes.byref(bits)))
+    return rc, int(bits.value)
 
 
 def sda_swa_plan(tokens: int, groups: int, heads: int, query_len: int, window: int,

@@ -119,7 +119,15 @@ const char* sda_status_string(int status) {
   }
 }
 
-int sda_decode(const sda_decode_args* a, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Validate a decode call and fill the kernel parameters.  Returns SDA_OK with
+// *empty set when there is nothing to launch (rows == 0).
+int prepare_decode(const sda_decode_args* a, hipStream_t stream, sda::Params& p, bool& fp8,
+                   bool& empty) {
+  empty = false;
   if (!a) return SDA_ERR_INVALID;
   // Shape contract: the asserts of `sparse_decode_attention` and the
   // `_direct_sparse_decode` eligibility rule (dim 192, <= 16 heads, 384-wide
@@ -132,11 +140,14 @@ int sda_decode(const sda_decode_args* a, hipStream_t stream) {
   if (a->block % rt) return SDA_ERR_INVALID;
   const int64_t rows_per_req = (int64_t)a->groups * a->query_len;
   if (a->rows % rows_per_req) return SDA_ERR_INVALID;
-  const bool fp8 = a->kv_dtype == SDA_KV_FP8_E4M3;
+  fp8 = a->kv_dtype == SDA_KV_FP8_E4M3;
   if (fp8 && (!a->k_scale || !a->v_scale)) return SDA_ERR_INVALID;
   if (a->R > SDA_MAX_R || a->splits > SDA_MAX_SPLITS || a->rows > SDA_MAX_ROWS)
     return SDA_ERR_UNSUPPORTED;
-  if (a->rows == 0) return SDA_OK;  // nothing to do, nothing launched
+  if (a->rows == 0) {  // nothing to do, nothing launched
+    empty = true;
+    return SDA_OK;
+  }
 
   if (!a->query || !a->output || !a->cache || !a->block_table || !a->positions || !a->active ||
       (a->R > 0 && !a->regions))
@@ -155,7 +166,7 @@ int sda_decode(const sda_decode_args* a, hipStream_t stream) {
   if (a->c_token_stride < 0 || (int64_t)a->block * a->c_token_stride * esz + 2 * SDA_KV_ROW > 0xFFFFFFFFll)
     return SDA_ERR_UNSUPPORTED;
 
-  sda::Params p{};
+  p = sda::Params{};
   // row r = token r / groups, group r % groups: row stride per group
   p.q = static_cast<const uint16_t*>(a->query);
   p.qts = a->q_row_stride * a->groups;
@@ -204,9 +215,35 @@ int sda_decode(const sda_decode_args* a, hipStream_t stream) {
   }
   p.cus = stream_cus(stream);
   if (p.cus <= 0) return SDA_ERR_LAUNCH;
+  return SDA_OK;
+}
 
+}  // namespace
+
+extern "C" {
+
+int sda_decode(const sda_decode_args* a, hipStream_t stream) {
+  sda::Params p;
+  bool fp8 = false, empty = false;
+  const int rc = prepare_decode(a, stream, p, fp8, empty);
+  if (rc != SDA_OK || empty) return rc;
   hipError_t e = sda::launch(p, fp8, stream);
   return e == hipSuccess ? SDA_OK : SDA_ERR_LAUNCH;
+}
+
+int sda_decode_kernels(const sda_decode_args* a, hipStream_t stream, int* kernels) {
+  if (!kernels) return SDA_ERR_INVALID;
+  *kernels = 0;
+  sda::Params p;
+  bool fp8 = false, empty = false;
+  const int rc = prepare_decode(a, stream, p, fp8, empty);
+  if (rc != SDA_OK || empty) return rc;
+  const int bits = sda::plan(p);
+  *kernels = ((bits & sda::kPlanOrder) ? SDA_KERNEL_ORDER : 0) |
+             ((bits & sda::kPlanSplit) ? SDA_KERNEL_SPLIT : 0) |
+             ((bits & sda::kPlanRowStream) ? SDA_KERNEL_ROW_STREAM : 0) |
+             ((bits & sda::kPlanCombine) ? SDA_KERNEL_COMBINE : 0);
+  return SDA_OK;
 }
 
 size_t sda_swa_args_size(void) { return sizeof(sda_swa_args); }

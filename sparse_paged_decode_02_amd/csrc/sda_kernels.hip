@@ -1343,10 +1343,15 @@ bool two_per_cu(int64_t wgs, int cus) { return wgs >= 2 * (int64_t)cus; }
 // follow, or null for index order.  They pay when the grid takes a few
 // rounds of resident workgroups: with one round every row starts at once,
 // and with many the tail is a small part of the launch.
-const int32_t* launch_order(const Params& p, hipStream_t stream) {
+// Whether the split kernel's grid is worth ranking first: a workspace is
+// given and the grid takes 2 to kOrderMaxRounds rounds of resident workgroups.
+bool wants_order(const Params& p) {
   const int64_t wgs = (int64_t)p.rows * p.splits;
   const int64_t resident = resident_workgroups(wgs, p.cus);
-  if (!p.order_ws || wgs <= resident || wgs > kOrderMaxRounds * resident) return nullptr;
+  return p.order_ws && wgs > resident && wgs <= kOrderMaxRounds * resident;
+}
+
+const int32_t* launch_order(const Params& p, hipStream_t stream) {
   // The workspace's order area holds the bins ([rows] after the order).
   int32_t* bins = p.order_ws + p.rows;
   const int64_t max_tokens = (int64_t)p.R * p.rt;
@@ -1447,11 +1452,22 @@ static bool wide_output(const Params& p) {
          p.ohs % 8 == 0;
 }
 
-hipError_t launch(const Params& p0, bool fp8, hipStream_t stream) {
+static Params with_output_policy(const Params& p0) {
   Params p = p0;
   p.nt_out = large_output(p) ? 1 : 0;
   p.wide_out = wide_output(p) ? 1 : 0;
-  p.order = use_row_stream(p) ? nullptr : launch_order(p, stream);
+  return p;
+}
+
+int plan(const Params& p0) {
+  const Params p = with_output_policy(p0);
+  if (use_row_stream(p)) return kPlanRowStream;
+  return (wants_order(p) ? kPlanOrder : 0) | kPlanSplit | (p.splits > 1 ? kPlanCombine : 0);
+}
+
+hipError_t launch(const Params& p0, bool fp8, hipStream_t stream) {
+  Params p = with_output_policy(p0);
+  p.order = !use_row_stream(p) && wants_order(p) ? launch_order(p, stream) : nullptr;
   if (fp8)
     launch_dtype<true>(p, stream);
   else

@@ -51,6 +51,14 @@ struct Params {
 // within each block of 1024 rows), and the split kernel follows it.
 hipError_t launch(const Params& p, bool fp8, hipStream_t stream);
 
+// The kernels `launch` enqueues for these parameters (kPlan* bits), without
+// launching anything.  For grids of at least two rows per resident wave and
+// short region lists (splits == 1, 16-byte aligned output) the split kernel
+// gives way to the row-stream kernel: one workgroup per CU whose waves take
+// whole rows back to back.
+constexpr int kPlanOrder = 1, kPlanSplit = 2, kPlanRowStream = 4, kPlanCombine = 8;
+int plan(const Params& p);
+
 // The same kernels over each row's sliding window (bf16 cache): token j of a
 // request of length L sits at position L - query_len + j and attends over
 // positions max(0, pos - window + 1) .. pos.  One split workgroup serves

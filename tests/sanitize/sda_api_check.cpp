@@ -31,6 +31,10 @@ hipError_t launch(const Params& p, bool, hipStream_t) {
   g_last = p;
   return hipSuccess;
 }
+int plan(const Params& p) {
+  g_last = p;
+  return kPlanRowStream | kPlanOrder;
+}
 hipError_t launch_window(const Params& p, hipStream_t) {
   ++g_launches;
   g_last = p;
@@ -157,7 +161,17 @@ static void check_decode_launch(const sda_decode_args& a) {
 
 static int call_decode(sda_decode_args a) {
   const int before = g_launches;
+  int kernels = -1;
+  const int rc_plan = sda_decode_kernels(&a, nullptr, &kernels);
+  CHECK(g_launches == before, "sda_decode_kernels launched");
+  if (rc_plan == SDA_OK && a.rows > 0) {
+    CHECK(kernels == (SDA_KERNEL_ROW_STREAM | SDA_KERNEL_ORDER), "kernel bits %d", kernels);
+    check_decode_launch(a);
+  } else {
+    CHECK(kernels == 0, "kernel bits %d on status %d", kernels, rc_plan);
+  }
   const int rc = sda_decode(&a, nullptr);
+  CHECK(rc == rc_plan, "sda_decode_kernels status %d, sda_decode %d", rc_plan, rc);
   CHECK(valid_status(rc), "status %d", rc);
   if (rc == SDA_OK && a.rows > 0) {
     CHECK(g_launches == before + 1, "an OK call with rows must launch once");

@@ -4,6 +4,7 @@ import os
 import re
 
 import pytest
+import torch
 
 from sparse_paged_decode_02_amd import binding as B
 
@@ -21,7 +22,7 @@ def test_library_exports_every_declared_function():
     assert {"sda_decode", "sda_splits", "sda_workspace_bytes", "sda_status_string",
             "sda_abi_version", "sda_args_size", "sda_swa_decode", "sda_swa_plan",
             "sda_select_regions", "sda_select_args_size", "sda_indexer_logits",
-            "sda_logits_args_size", "sda_device_compute_units",
+            "sda_logits_args_size", "sda_device_compute_units", "sda_decode_kernels",
             "sda_swa_args_size"} <= set(names)
     lib = B.lib()
     for n in names:
@@ -144,6 +145,29 @@ def test_null_args_and_zero_rows():
     assert B.sda_decode_raw(a) == B.SDA_OK
     # ... but the shape contract is still checked first
     assert B.sda_decode_raw(_valid_args(rows=0, heads=17)) == B.SDA_ERR_INVALID
+
+
+@pytest.mark.parametrize("over", INVALID + UNSUPPORTED + [dict(splits=4)],
+                         ids=[str(o) for o in INVALID + UNSUPPORTED] + ["no workspace"])
+def test_kernel_report_validates_like_decode(over):
+    # sda_decode_kernels returns sda_decode's status and reports no kernels
+    a = _valid_args(**over)
+    rc, bits = B.sda_decode_kernels_raw(a)
+    assert rc == B.sda_decode_raw(a) and rc != B.SDA_OK
+    assert bits == 0
+
+
+def test_kernel_report_edges():
+    kernels = ctypes.c_int(7)
+    assert B.lib().sda_decode_kernels(None, None, ctypes.byref(kernels)) == B.SDA_ERR_INVALID
+    assert kernels.value == 0
+    assert B.lib().sda_decode_kernels(ctypes.byref(_valid_args()), None, None) == B.SDA_ERR_INVALID
+    a = _valid_args(rows=0, query=None, output=None, regions=None, positions=None, active=None)
+    assert B.sda_decode_kernels_raw(a) == (B.SDA_OK, 0)
+    # a valid call needs the device's CU count: without a device it fails as
+    # sda_decode does, before any launch
+    if not torch.cuda.is_available():
+        assert B.sda_decode_kernels_raw(_valid_args()) == (B.SDA_ERR_LAUNCH, 0)
 
 
 def test_fp8_scale_pointers_required_only_for_fp8():

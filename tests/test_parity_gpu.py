@@ -48,6 +48,19 @@ def run(inp, splits=None, clear_inactive=True, out=None, gate="inp", query=None,
     return out
 
 
+def kernels(inp, splits=None, out=None):
+    """SDA_KERNEL_* bits the library reports for run(inp, splits)."""
+    splits = inp.splits if splits is None else splits
+    if splits is None:
+        splits = B.sda_splits(inp.w.rows)
+    return B.sda_decode_kernels(inp.query, inp.cache, inp.regions, inp.block_table,
+                                inp.positions, inp.active,
+                                torch.empty_like(inp.query) if out is None else out,
+                                scale=inp.scale, query_len=inp.w.query_len, splits=splits,
+                                k_scale=inp.k_scale, v_scale=inp.v_scale, gate=inp.gate,
+                                region_tokens=inp.w.region_tokens)
+
+
 def oracle_out(inp, rows=None, gate="inp"):
     if gate != "inp":
         inp = gen.Inputs(**{**inp.__dict__, "gate": gate})
@@ -437,6 +450,7 @@ def test_row_order_matches_index_order(kv, splits, strided, requests, R):
                      inactive_frac=0.10, gated=True, splits=splits, seed=600 + splits + R)
     assert 512 < w.rows * splits <= 2048
     inp = gen.make_inputs(w, device=DEV)
+    assert kernels(inp, splits=splits) & B.SDA_KERNEL_ORDER
     regions = inp.regions
     if strided:  # odd row stride: the order pass reads region ids one by one
         wide = torch.full((w.rows, w.R + 1), -1, dtype=torch.int32, device=DEV)
@@ -459,15 +473,40 @@ def test_row_order_matches_index_order(kv, splits, strided, requests, R):
     check_inactive_zero(outs[0], inp)
 
 
-@pytest.mark.parametrize("rows", [513, 2048, 2049])
+def expected_kernels(rows, R, splits, row_order, cus):
+    """The schedule sda_decode documents for an aligned output: the
+    row-stream kernel for 2 to 8 rows per wave (4 waves per CU) with at most
+    256 region slots per wave and one split; else the split kernel, preceded
+    by the order pass when a workspace is given and the grid takes 2 to 4
+    rounds of the resident workgroups (2 per CU from a grid of 2 per CU)."""
+    waves = 4 * cus
+    per_wave = -(-rows // waves)
+    if splits == 1 and R <= 64 and rows >= 2 * waves and per_wave <= 8 and per_wave * R <= 256:
+        return B.SDA_KERNEL_ROW_STREAM
+    grid = rows * splits
+    resident = 2 * cus if grid >= 2 * cus else cus
+    bits = B.SDA_KERNEL_SPLIT | (B.SDA_KERNEL_COMBINE if splits > 1 else 0)
+    if row_order and resident < grid <= 4 * resident:
+        bits |= B.SDA_KERNEL_ORDER
+    return bits
+
+
+@pytest.mark.parametrize("rows", [513, 2047, 2048, 2049])
 def test_row_order_grid_bounds(rows):
-    # Grids just past the 512 resident workgroups and at / past 4 rounds: with
-    # or without the order pass, the output equals index order bit for bit and
-    # every row is written.
+    # Grids just past the 512 resident workgroups and up to 4 rounds take the
+    # order pass; from 2 rows per wave the row-stream kernel takes the grid
+    # instead.  With or without the order pass, the output equals index order
+    # bit for bit and every row is written.
     w = gen.Workload("order-bounds", requests=rows, query_len=1, groups=1, heads=4, block=16,
                      pages_per_req=16, R=8, kv="bf16", pos_lo=16, pos_hi=255, live=(1, 8),
                      inactive_frac=0.05, gated=True, splits=1, seed=700 + rows)
     inp = gen.make_inputs(w, device=DEV)
+    cus = B.sda_device_compute_units()
+    for row_order in (True, False):
+        got = B.sda_decode_kernels(inp.query, inp.cache, inp.regions, inp.block_table,
+                                   inp.positions, inp.active, torch.empty_like(inp.query),
+                                   scale=inp.scale, splits=1, gate=inp.gate, row_order=row_order)
+        assert got == expected_kernels(rows, w.R, 1, row_order, cus), (rows, row_order, got)
     outs = []
     for row_order in (True, False):
         out = torch.full_like(inp.query, float("nan"))
@@ -511,6 +550,15 @@ def test_full_size(k):
     _say("drawing full workload %d (%s)" % (k, w.name))
     inp = gen.make_inputs(w, device=DEV)
     out = run(inp, label="full%d" % k)
+    bits = kernels(inp, out=out)
+    # the large batch of short lists takes the row-stream kernel, the others
+    # the split kernel (with the combine when split)
+    if k == 5:
+        assert bits == B.SDA_KERNEL_ROW_STREAM, bits
+    else:
+        splits = inp.splits if inp.splits is not None else B.sda_splits(w.rows)
+        assert bits & B.SDA_KERNEL_SPLIT and not bits & B.SDA_KERNEL_ROW_STREAM, bits
+        assert bool(bits & B.SDA_KERNEL_COMBINE) == (splits > 1), bits
     n = FULL_SIZE_ORACLE_ROWS[k]
     if n is None:
         rows = None
@@ -557,6 +605,7 @@ def test_row_stream_all_rows(kv, block, rt, gated, extra):
                      pos_hi=191, live=(1, R), inactive_frac=0.10, gated=gated, splits=1,
                      region_tokens=rt, seed=800 + extra + rt + block)
     inp = gen.make_inputs(w, device=DEV)
+    assert kernels(inp) == B.SDA_KERNEL_ROW_STREAM
     out = run(inp, out=torch.full_like(inp.query, float("nan")), label="row stream")
     assert torch.isfinite(out.float()).all(), "a row was not written"
     check_close(out, oracle_out(inp), what="row stream %s rt%d rows%d" % (kv, rt, rows))
@@ -573,6 +622,7 @@ def test_row_stream_block_48_and_eight_rows_per_wave():
                      live=(1, 12), inactive_frac=0.05, gated=True, splits=1, region_tokens=24,
                      seed=871)
     inp = gen.make_inputs(w, device=DEV)
+    assert kernels(inp) == B.SDA_KERNEL_ROW_STREAM
     out = run(inp, out=torch.full_like(inp.query, float("nan")), label="row stream block48")
     assert torch.isfinite(out.float()).all()
     rng = np.random.default_rng(3)
