@@ -117,6 +117,36 @@ def test_ragged_columns_and_strided_views():
     assert (buf[:, S:] == 7.0).all()
 
 
+@pytest.mark.parametrize("requests,qlen", [(256, 1), (257, 1), (300, 2)])
+def test_many_requests(requests, qlen):
+    # Grids of 256 to 300 requests of 80 regions (a partial 256-region chunk
+    # each), lengths from 0 to the whole row, every row.
+    w = case(900 + requests, requests=requests, query_len=qlen, groups=2, heads=4, block=16,
+             pages_per_req=40, pos_lo=-3, pos_hi=40 * 16 - qlen)
+    inp = gen.make_logits_inputs(w, device=DEV)
+    got, cur, lens = run(inp, label="requests=%d" % requests)
+    check(inp, got, cur, lens, what="requests=%d qlen=%d" % (requests, qlen))
+
+
+def test_no_live_region():
+    # Every position negative: no live tile anywhere, every column -inf.
+    w = case(31, requests=6, groups=2, heads=8, pos_lo=-40, pos_hi=-1)
+    inp = gen.make_logits_inputs(w, device=DEV)
+    got, cur, lens = run(inp, label="no live region")
+    assert torch.isneginf(got).all()
+    check(inp, got, cur, lens, what="no live region")
+
+
+def test_long_row():
+    # One request of 327680 regions (1280 chunks of 256), every one live:
+    # the row against the oracle in full.
+    w = case(77, requests=1, groups=1, heads=2, block=64, pages_per_req=40960,
+             pos_lo=40960 * 64 - 1, pos_hi=40960 * 64 - 1)
+    inp = gen.make_logits_inputs(w, device=DEV)
+    got, cur, lens = run(inp, label="long row")
+    check(inp, got, cur, lens, what="long row")
+
+
 @pytest.mark.parametrize("name", ["logits-decode", "logits-mtp"])
 def test_full_size_sampled(name):
     w = gen.LOGITS_WORKLOADS[name]
