@@ -632,6 +632,46 @@ def test_row_stream_block_48_and_eight_rows_per_wave():
 
 
 @pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_row_stream_multi_token_and_strided_views(kv):
+    # query_len 2 x G 2 (rows of one request at positions p and p + 1), at
+    # 2-3 rows per wave; query and output views with padded row and head
+    # strides (still 16-byte aligned: the row-stream kernel) give the same
+    # bits as contiguous tensors, and all rows match the oracle.  An output
+    # whose rows are not 16-byte aligned takes the split kernel (which sums a
+    # row's chunks over four waves, so its rounding differs): all rows match
+    # the oracle there too.
+    G, qlen = 2, 2
+    rows = _stream_rows(extra=12, multiple=G * qlen)
+    w = gen.Workload("row-stream-mtp", requests=rows // (G * qlen), query_len=qlen, groups=G,
+                     heads=8, block=16, pages_per_req=12, R=12, kv=kv, pos_lo=20, pos_hi=180,
+                     live=(1, 12), inactive_frac=0.05, gated=True, splits=1, seed=930)
+    inp = gen.make_inputs(w, device=DEV)
+    assert kernels(inp) == B.SDA_KERNEL_ROW_STREAM
+    base = run(inp, out=torch.full_like(inp.query, float("nan")), label="row stream mtp")
+    assert torch.isfinite(base.float()).all()
+    ref = oracle_out(inp)
+    check_close(base, ref, what="row stream mtp %s" % kv)
+    check_inactive_zero(base, inp)
+    qbig = torch.zeros((w.rows, w.heads + 1, 192 + 8), dtype=torch.bfloat16, device=DEV)
+    qbig[:, :w.heads, 8:200] = inp.query
+    q_view = qbig[:, :w.heads, 8:200]
+    obig = torch.full((w.rows, w.heads, 192 + 16), 5.0, dtype=torch.bfloat16, device=DEV)
+    o_view = obig[:, :, 8:200]
+    assert kernels(inp, out=o_view) == B.SDA_KERNEL_ROW_STREAM
+    out = run(inp, out=o_view, query=q_view, label="row stream strided")
+    assert torch.equal(out.view(torch.int16), base.view(torch.int16))
+    assert (obig[:, :, :8] == 5.0).all() and (obig[:, :, 200:] == 5.0).all()
+    # an output row stride of 8 * 192 + 2 elements breaks the 16-byte rows
+    flat = torch.full((w.rows * (w.heads * 192 + 2),), 5.0, dtype=torch.bfloat16, device=DEV)
+    o_odd = flat.as_strided((w.rows, w.heads, 192), (w.heads * 192 + 2, 192, 1))
+    bits = kernels(inp, out=o_odd)
+    assert bits & B.SDA_KERNEL_SPLIT and not bits & B.SDA_KERNEL_ROW_STREAM, bits
+    out = run(inp, out=o_odd, label="row stream fallback")
+    check_close(out.contiguous(), ref, what="split fallback %s" % kv)
+    check_inactive_zero(out.contiguous(), inp)
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
 def test_row_stream_inactive_untouched_and_poisoned(kv):
     # clear_inactive off leaves inactive rows as they were; poisoned inputs of
     # inactive rows (NaN query and gate, huge ids, INT32_MAX position) change
