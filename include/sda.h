@@ -14,9 +14,11 @@
  *
  * All pointers in sda_decode_args are DEVICE pointers unless noted.  The
  * caller owns every buffer, including the workspace.  The library allocates
- * nothing and keeps no state, so every entry point is re-entrant; calls that
- * may overlap (other streams, other threads) need workspaces of their own,
- * since each call rewrites its workspace.  sda_decode
+ * nothing; its only state is a per-device cache of the compute-unit count
+ * (read once, thread-safe) and, for sda_decode_static alone, a static device
+ * scratch array.  Every other entry point is re-entrant; calls that may
+ * overlap (other streams, other threads) need workspaces of their own, since
+ * each call rewrites its workspace.  sda_decode
  * validates on the host and never reads device memory there; index contents
  * (region ids, block-table entries, positions) are trusted, as on the page.
  * On any error it returns before launching anything.

@@ -1339,18 +1339,18 @@ int64_t resident_workgroups(int64_t wgs, int cus) {
 
 bool two_per_cu(int64_t wgs, int cus) { return wgs >= 2 * (int64_t)cus; }
 
-// Enqueue the bin and order kernels when they pay; returns the order to
-// follow, or null for index order.  They pay when the grid takes a few
-// rounds of resident workgroups: with one round every row starts at once,
-// and with many the tail is a small part of the launch.
 // Whether the split kernel's grid is worth ranking first: a workspace is
-// given and the grid takes 2 to kOrderMaxRounds rounds of resident workgroups.
+// given and the grid takes 2 to kOrderMaxRounds rounds of resident
+// workgroups.  With one round every row starts at once, and with many the
+// tail is a small part of the launch.
 bool wants_order(const Params& p) {
   const int64_t wgs = (int64_t)p.rows * p.splits;
   const int64_t resident = resident_workgroups(wgs, p.cus);
   return p.order_ws && wgs > resident && wgs <= kOrderMaxRounds * resident;
 }
 
+// Enqueue the bin and order kernels (the caller has checked wants_order);
+// returns the order to follow.
 const int32_t* launch_order(const Params& p, hipStream_t stream) {
   // The workspace's order area holds the bins ([rows] after the order).
   int32_t* bins = p.order_ws + p.rows;
