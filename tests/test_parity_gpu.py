@@ -163,15 +163,18 @@ def test_block_48_regions(kv, rt):
         check_inactive_zero(out, inp)
 
 
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
 @pytest.mark.parametrize("splits", [1, 3])
-def test_maximum_region_slots(splits):
-    """R at the library maximum (2048 slots of 8-token regions, 16K tokens)."""
-    w = gen.scaled(gen.WORKLOADS[2], name="max-R", requests=2, groups=1, heads=4,
-                   pages_per_req=256, pos_lo=12000, pos_hi=16383, R=2048,
+def test_maximum_region_slots(kv, splits):
+    """R at the library maximum (2048 slots of 8-token regions, 16K tokens):
+    lists past 512 slots, resolved eight 64-slot groups per round trip."""
+    w = gen.scaled(gen.WORKLOADS[2 if kv == "bf16" else 3], name="max-R", requests=2, groups=1,
+                   heads=4, pages_per_req=256, pos_lo=12000, pos_hi=16383, R=2048,
                    region_tokens=8, inactive_frac=0.0, gated=False)
     inp = gen.make_inputs(w, device=DEV)
     assert (inp.regions >= 0).sum().item() > 2 * 1400
-    check_close(run(inp, splits=splits), oracle_out(inp), what="R=2048 splits=%d" % splits)
+    check_close(run(inp, splits=splits), oracle_out(inp),
+                what="R=2048 %s splits=%d" % (kv, splits))
 
 
 def test_query_len_three_and_duplicates():
@@ -628,6 +631,32 @@ def test_row_stream_block_48_and_eight_rows_per_wave():
     rng = np.random.default_rng(3)
     rows_s = sorted(set(rng.choice(w.rows, size=1024, replace=False).tolist() + [0, w.rows - 1]))
     check_close(out, oracle_out(inp, rows=rows_s), rows=rows_s, what="row stream block48")
+    check_inactive_zero(out, inp)
+
+
+def test_row_stream_rule_edges():
+    # The documented rule at its edges, checked against the library's report:
+    # 2w - 1 / 2w / 8w / 8w + 1 rows (w waves), R = 64 / 65, and 256 list
+    # entries per wave; then R = 64 at 2 rows per wave against the oracle.
+    waves = 4 * B.sda_device_compute_units()
+    cus = waves // 4
+    for rows, R in [(2 * waves - 1, 8), (2 * waves, 8), (8 * waves, 8), (8 * waves + 1, 8),
+                    (2 * waves, 64), (2 * waves, 65), (4 * waves, 64), (4 * waves + 1, 64)]:
+        w = gen.Workload("rule", requests=rows, query_len=1, groups=1, heads=2, block=16,
+                         pages_per_req=8, R=R, kv="bf16", pos_lo=0, pos_hi=127, live=(1, 4),
+                         inactive_frac=0.0, gated=False, splits=1, seed=5)
+        inp = gen.make_inputs(w, device=DEV)
+        assert kernels(inp) == expected_kernels(rows, R, 1, True, cus), (rows, R)
+        del inp
+    rows = 2 * waves
+    w = gen.Workload("row-stream-R64", requests=rows // 2, query_len=1, groups=2, heads=16,
+                     block=16, pages_per_req=80, R=64, kv="fp8", pos_lo=700, pos_hi=1279,
+                     live=(1, 64), inactive_frac=0.05, gated=True, splits=1, seed=940)
+    inp = gen.make_inputs(w, device=DEV)
+    assert kernels(inp) == B.SDA_KERNEL_ROW_STREAM
+    out = run(inp, out=torch.full_like(inp.query, float("nan")), label="row stream R64")
+    assert torch.isfinite(out.float()).all()
+    check_close(out, oracle_out(inp), what="row stream R=64")
     check_inactive_zero(out, inp)
 
 
