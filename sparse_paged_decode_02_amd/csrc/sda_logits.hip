@@ -196,17 +196,47 @@ __global__ __launch_bounds__(kLgThreads) void logits_kernel(const LogitsParams p
     }
   }
   if (nt > 0) {
-    for (int t = 0; t < nt; ++t) {
+    // Everything a tile's epilogue needs beyond its accumulators is fixed for
+    // the workgroup or known now: each column's weight and row length (LDS),
+    // and every tile's summary offsets and region scales (from the lanes that
+    // resolved them).  Fetched once here, they keep LDS round trips out of
+    // the tile loop.
+    float wcol[kLgMaxCols / 16];
+    int lcol[kLgMaxCols / 16];
+#pragma unroll
+    for (int ct = 0; ct < kLgMaxCols / 16; ++ct) {
+      const int col = 16 * ct + i16;
+      wcol[ct] = col < ncols ? s_w[col] : 0.f;
+      lcol[ct] = col < ncols ? s_len[col >> p.hshift] : 0;
+    }
+    int64_t toff[4];
+    float tsc[4][4];
+#pragma unroll
+    for (int t = 1; t < 4; ++t) {
+      const int j = j_begin + kLgTile * wave + kLgTile * kLgWaves * t + i16;
+      toff[t] = __shfl(roff_l, j < j_live ? kLgTile * t + i16 : kLgTile * t);
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) tsc[t][v] = __shfl(scale_l, kLgTile * t + 4 * g4 + v);
+    toff[0] = 0;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      if (t >= nt) break;
       const int j0 = j_begin + kLgTile * wave + kLgTile * kLgWaves * t;
       bf16x8 a[8];
 #pragma unroll
       for (int c = 0; c < 4; ++c) e4m3x16_to_bf16(raw[c], a[2 * c], a[2 * c + 1]);
-      if (t + 1 < nt) load_tile(t + 1, raw);  // next tile in flight
-      float scc[4];
+      if (t + 1 < nt) {  // next tile in flight
+        const uint8_t* an = p.sm + toff[t + 1 < 4 ? t + 1 : 3] + 16 * g4;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) scc[v] = __shfl(scale_l, kLgTile * t + 4 * g4 + v);
+        for (int c = 0; c < 4; ++c) raw[c] = *reinterpret_cast<const u32x4*>(an + 64 * c);
+      }
 
-      for (int ct = 0; ct < ntiles; ++ct) {
+#pragma unroll
+      for (int ct = 0; ct < kLgMaxCols / 16; ++ct) {
+        if (ct >= ntiles) break;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         const __bf16* bq = &s_q[ct][lane][0];
 #pragma unroll
@@ -216,16 +246,15 @@ __global__ __launch_bounds__(kLgThreads) void logits_kernel(const LogitsParams p
         }
         // lane holds S[region j0 + 4 g4 + v][column 16 ct + i16]
         const int col = 16 * ct + i16;
-        const float wc = col < ncols ? s_w[col] : 0.f;
         float x[4];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) x[v] = fmaxf(0.f, scc[v] * acc[v]) * wc;
+        for (int v = 0; v < 4; ++v) x[v] = fmaxf(0.f, tsc[t][v] * acc[v]) * wcol[ct];
         // sum over the row's heads: `heads` consecutive lanes of the 16-lane group
 #pragma unroll
         for (int v = 0; v < 4; ++v) x[v] = group_sum(x[v], p.heads);
         if (col < ncols && (col & (p.heads - 1)) == 0) {
           const int rowi = col >> p.hshift;
-          const int len = s_len[rowi];
+          const int len = lcol[ct];
           const int jb = j0 + 4 * g4;
           float* dst = p.out + (int64_t)(r0 + rowi) * p.ors + jb;
           float y[4];
