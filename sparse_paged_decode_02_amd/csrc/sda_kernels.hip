@@ -11,7 +11,8 @@
 // inactive-row clear.
 //
 // Split kernel: one workgroup per (row, split), 4 waves of 64 (one workgroup
-// per CU) or, for grids of 512 or more workgroups, 2 waves (two per CU).
+// per CU) or, for grids of at least two workgroups per CU, 2 waves (two per
+// CU).
 //  * Prologue, per wave and without workgroup barriers: rank the row's
 //    visible region slots with ballots, take the split's balanced share, and
 //    resolve each region to a cache offset through the block table (only the
@@ -46,6 +47,12 @@
 //    log-sum-exp go to the workspace.
 // Combine kernel (splits > 1): one 64-thread workgroup per (row, head) merges
 // the partials, applies the gate and writes bf16, or clears an inactive row.
+// Row-stream kernel (one split, large batches of short region lists): one
+// 4-wave workgroup per CU, each wave streaming whole rows back to back
+// through the same chunk pipeline and arithmetic, with no cross-wave merge.
+// Bin and order kernels (grids of 2 to 4 rounds of resident workgroups,
+// given a workspace): rank the rows by visible tokens so that the split
+// kernel starts the heaviest first.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
