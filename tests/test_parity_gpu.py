@@ -648,6 +648,24 @@ def test_row_stream_rule_edges():
         inp = gen.make_inputs(w, device=DEV)
         assert kernels(inp) == expected_kernels(rows, R, 1, True, cus), (rows, R)
         del inp
+    # R = 0 through the row-stream kernel: active rows output zeros; inactive
+    # rows are cleared, or left as they were without the clear.
+    rows = 2 * waves
+    w = gen.Workload("row-stream-R0", requests=rows, query_len=1, groups=1, heads=4, block=16,
+                     pages_per_req=4, R=8, kv="bf16", pos_lo=0, pos_hi=63, live=(1, 4),
+                     inactive_frac=0.1, gated=True, splits=1, seed=6)
+    inp = gen.make_inputs(w, device=DEV)
+    empty = gen.Inputs(**{**inp.__dict__, "regions": torch.empty((w.rows, 0), dtype=torch.int32,
+                                                                 device=DEV)})
+    assert kernels(empty) == B.SDA_KERNEL_ROW_STREAM
+    out = run(empty, out=torch.full_like(inp.query, 3.0), label="row stream R=0")
+    assert (out.view(torch.int16) == 0).all()
+    kept = run(empty, out=torch.full_like(inp.query, 3.0), clear_inactive=False,
+               label="row stream R=0 keep")
+    act = inp.active.bool()
+    assert (kept[~act] == 3.0).all() and (kept[act].view(torch.int16) == 0).all()
+    del inp, empty
+
     rows = 2 * waves
     w = gen.Workload("row-stream-R64", requests=rows // 2, query_len=1, groups=2, heads=16,
                      block=16, pages_per_req=80, R=64, kv="fp8", pos_lo=700, pos_hi=1279,
