@@ -76,6 +76,49 @@ def test_decode_with_row_order_in_graph():
     replay_and_compare(fn, [out], "decode with row order")
 
 
+def _stream_workload(name, seed, fp8=False):
+    # 2 rows per wave of the chip: the row-stream kernel
+    waves = 4 * B.sda_device_compute_units()
+    return gen.Workload(name, requests=waves // 2, query_len=1, groups=4, heads=16, block=64,
+                        pages_per_req=8, R=8, kv="fp8" if fp8 else "bf16", pos_lo=100,
+                        pos_hi=511, live=(1, 8), inactive_frac=0.05, gated=True, splits=1,
+                        seed=seed)
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_row_stream_in_graph(fp8):
+    w = _stream_workload("graph-stream", 11, fp8)
+    inp = gen.make_inputs(w, device=DEV)
+    out = torch.empty_like(inp.query)
+    assert B.sda_decode_kernels(inp.query, inp.cache, inp.regions, inp.block_table,
+                                inp.positions, inp.active, out, scale=inp.scale, splits=1,
+                                k_scale=inp.k_scale, v_scale=inp.v_scale,
+                                gate=inp.gate) == B.SDA_KERNEL_ROW_STREAM
+
+    def fn():
+        B.sda_decode(inp.query, inp.cache, inp.regions, inp.block_table, inp.positions,
+                     inp.active, out, scale=inp.scale, splits=1, k_scale=inp.k_scale,
+                     v_scale=inp.v_scale, gate=inp.gate, row_order=False)
+
+    replay_and_compare(fn, [out], "row stream fp8=%s" % fp8)
+
+
+@pytest.mark.parametrize("splits", [1, 2])
+def test_static_entry_point_in_graph(splits):
+    # The allocation-free entry point is meant for capture: nothing allocated
+    # on the way in, its scratch is the library's own device array.
+    w = gen.scaled(gen.WORKLOADS[2], name="graph-static", requests=4, pages_per_req=16,
+                   pos_lo=300, pos_hi=1023)
+    inp = gen.make_inputs(w, device=DEV)
+    out = torch.empty_like(inp.query)
+
+    def fn():
+        B.sda_decode_static(inp.query, inp.cache, inp.regions, inp.block_table, inp.positions,
+                            inp.active, out, scale=inp.scale, splits=splits, gate=inp.gate)
+
+    replay_and_compare(fn, [out], "static splits=%d" % splits)
+
+
 def test_swa_in_graph():
     w = gen.SwaWorkload("graph-swa", requests=4, query_len=2, groups=2, heads=4, block=64,
                         pages_per_req=8, window=100, seq_lo=2, seq_hi=512, seed=3)
