@@ -8,26 +8,35 @@
 //
 // One 1024-thread workgroup (16 waves) per row; wave w owns the contiguous
 // ids [w L, (w+1) L), L = 256 I, and lane l holds ids w L + 4 l + 256 i + c.
+// The 256-id groups below the row's length are the live ones; every other
+// group holds no candidate, and each phase skips it for the whole wave.
 //  1. Keys: 16-byte loads (4-byte ones when the row is not 16-byte aligned)
 //     of the scores as order-preserving 32-bit keys, held in registers.
-//     Non-candidates get key 0, which no score maps to (NaN aside).
-//  2. Threshold key T.  A 12-bit MSB-first radix pass histograms the keys
-//     (LDS atomics), and a block scan from the top bin finds the bin where
-//     the count of larger keys reaches the number still needed.  That bin's
-//     keys (typically 1-3% of the row) go to an LDS list.  With at most
-//     kRankCap of them, each listed key is ranked against the whole list
-//     (how many are greater, how many equal) by a group of lanes, and the key
-//     of the needed rank is T.  Larger bins take two more radix passes (12 and 8 bits) over
-//     the list, or over the registers when the bin exceeds the list.  Either
-//     way T is exact, together with how many keys equal to T are taken.
-//  3. Compaction in id order: keys > T, the forced region and the first
-//     needed keys == T are selected.  Each wave counts its selections, one
-//     barrier gives every wave its output offset, and each wave then writes
-//     its range in order with in-wave scans (no further barriers).
+//     Ids past the length read the bit pattern 0xFFFFFFFF, whose key is 0,
+//     and the one wave holding the current region clears its key, so key 0
+//     marks a non-candidate (no finite score maps to it).
+//  2. Threshold key T.  A 12- or 13-bit MSB-first radix pass histograms
+//     the keys (LDS atomics; non-candidates land in bin 0, below every
+//     finite score).  All threads then read 4 or 8 bins each from the top,
+//     one barrier publishes the per-wave totals, and the wave whose range
+//     reaches the count still needed finds the bin and publishes it.  That
+//     bin's keys (typically under 1% of the row) go to an LDS list, each
+//     wave taking its slots from a shared counter.  With at most kRankCap of
+//     them, each listed key is ranked against the whole list (how many are
+//     greater, how many equal) by a group of lanes, and the key of the
+//     needed rank is T.  Larger bins take two more radix passes (down to
+//     bit 8, then 8 bits) over the list, or over the registers when the bin
+//     exceeds the list.  Either way T is exact, together with how many keys
+//     equal to T are taken.
+//  3. Compaction in id order.  Without ties at T the selection is key >= T
+//     (the current region's key raised to the maximum): per-lane counts of
+//     each live group, packed two groups to a word, one wave scan per word,
+//     and one barrier for the per-wave offsets; each lane then writes its
+//     ids at its own slots.  With ties, keys > T, the current region and
+//     the first needed keys == T are selected with ballots per 4-id column.
 // The bytes are the row's candidate scores (read once) and the output; the
-// work is LDS-atomic and scan bound for long rows, latency bound for short
-// ones.  The 1024-thread workgroup waits at each of its barriers, so beyond
-// one row per CU a second resident workgroup is what hides the waits.
+// work is a chain of barrier-separated phases per row, so beyond one row per
+// CU a second resident workgroup is what hides the waits.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -43,10 +52,25 @@ constexpr int kSelThreads = 1024;
 static_assert((int64_t)SDA_SELECT_MAX_ROWS * kSelThreads < (int64_t(1) << 32),
               "a grid of SDA_SELECT_MAX_ROWS workgroups fits 2^32 work-items");
 constexpr int kSelWaves = kSelThreads / 64;
-constexpr int kHistBins = 4096;
+// Pass 1 takes the top 12 key bits, or 13 (8192 bins, 32 KiB: two
+// workgroups still share a CU) for rows of 16 keys per lane: there the
+// threshold bin, which the ranking compares pairwise, then holds about half
+// the keys.  Passes 2 and 3 (tied or crowded bins) take the bits below down
+// to bit 8, then bits 7..0.
+template <int I>
+struct Pass1 {
+  static constexpr int kShift = I >= 4 ? 19 : 20;
+  static constexpr int kBins = 1 << (32 - kShift);
+  static constexpr int kBinsPerThread = kBins / kSelThreads;
+  static constexpr int kP2Bins = 1 << (kShift - 8);
+};
 constexpr int kCandCap = 4096;  // keys of the first pass's threshold bin kept in LDS
 constexpr int kRankCap = 1024;  // listed keys ranked directly (at least one lane each)
-static_assert(kRankCap <= kSelThreads && kRankCap + 3 <= kCandCap, "rank list fits");
+constexpr int kRankPad = 4;     // list slots past kCandCap
+// The ranking reads 16-byte pieces up to 3 P past the list's last piece
+// (P <= 64 lanes per listed key), all zero-padded.
+static_assert(kRankCap <= kSelThreads && kRankCap + 3 + 12 * 64 <= kCandCap + kRankPad,
+              "rank list fits");
 
 // Keys that order like the floats: flip all bits of negatives, set the sign
 // bit of non-negatives.  -0.0 -> 0x7FFFFFFF < +0.0 -> 0x80000000.
@@ -72,7 +96,8 @@ __device__ __forceinline__ int mbcnt(uint64_t mask) {
 
 // Digit d of a histogram with nb bins (nb a multiple of 64, at most 4096)
 // such that the count of keys in bins above d is < need <= the count in bins
-// >= d.  Wave 0 searches in two levels: lane l sums the per = nb / 64 bins
+// >= d, for the later radix passes (crowded or tied threshold bins).  Wave 0
+// searches in two levels: lane l sums the per = nb / 64 bins
 // [nb - per (l+1), nb - per l); a wave scan from the top finds the lane L
 // where the count reaches `need`; then lane l takes bin nb - per L - 1 - l
 // of L's range and a second scan finds the bin.  One barrier publishes the
@@ -130,15 +155,22 @@ __global__ __launch_bounds__(kSelThreads) __attribute__((amdgpu_waves_per_eu(kSh
 void select_kernel(const SelParams p) {
   static_assert(!kShared || I <= 4, "32 keys per lane do not fit 64 VGPRs");
   constexpr bool kAllLoads = !kShared && I <= 4;  // find_digit's bins in one round trip
-  constexpr int K4 = 4 * I;  // keys per lane
+  constexpr int K4 = 4 * I;                       // keys per lane
+  constexpr int kWaveIdsLog2 = I == 1 ? 8 : I == 2 ? 9 : I == 4 ? 10 : 11;
+  static_assert((1 << kWaveIdsLog2) == 256 * I, "a wave owns 256 I ids");
+  using P1 = Pass1<I>;
+  constexpr int kP1Shift = P1::kShift, kHistBins = P1::kBins, kP2Bins = P1::kP2Bins;
+  constexpr int kBPT = P1::kBinsPerThread;  // pass-1 bins per thread: 4 or 8
+  static_assert(kHistBins == kBPT * kSelThreads && kBPT % 4 == 0, "whole int4 reads");
   const int r = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // 64 padding bins past the histogram take the invalid keys of pass 1
-  // (one per lane, so they never contend), which keeps that pass branch-free.
-  __shared__ __attribute__((aligned(16))) int hist[kHistBins + 64];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  __shared__ __attribute__((aligned(16))) int hist[kHistBins];
   __shared__ int s_pick[3];
-  __shared__ int s_cnt[2][kSelWaves];  // [taken outright | eq][wave]
-  __shared__ __attribute__((aligned(16))) uint32_t s_ckey[kCandCap + 4];
+  __shared__ int s_tot[kSelWaves];      // pass 1: keys per wave's bin range
+  __shared__ int s_cnt[2][kSelWaves];   // [taken outright | eq][wave]
+  __shared__ int s_fill;                // candidate-list entries handed out
+  __shared__ __attribute__((aligned(16))) uint32_t s_ckey[kCandCap + kRankPad];
 
   int n = p.lengths ? p.lengths[r] : p.S;
   n = n < 0 ? 0 : (n > p.S ? p.S : n);
@@ -150,6 +182,8 @@ void select_kernel(const SelParams p) {
   const int need0 = want < pool ? want : pool;  // pool keys to take
   int32_t* o = p.out + (int64_t)r * p.ors;
   const int id0 = wave * (256 * I) + 4 * lane;  // id of key[4 i + c] = id0 + 256 i + c
+  // 256-id groups holding candidates: group i of wave w is [256 (w I + i), +256)
+  const int nlive = (n + 255) >> 8;
 
   // 1. keys of the pool (0 elsewhere)
   const float* srow = p.scores + (int64_t)r * p.srs;
@@ -157,12 +191,14 @@ void select_kernel(const SelParams p) {
   // 16-byte aligned and n is a multiple of 4); 4-byte loads otherwise.  The
   // choice is per row, so each path issues all its loads back to back.
   const bool vec = ((uintptr_t)srow & 15u) == 0 && (n & 3) == 0;
+  // Ids at or past n read as the bit pattern 0xFFFFFFFF, whose key is 0.
+  const float kNoKey = __uint_as_float(0xFFFFFFFFu);
   float sc[K4];
   if (vec) {
 #pragma unroll
     for (int i = 0; i < I; ++i) {
       const int j = id0 + 256 * i;
-      float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
+      float4 f = make_float4(kNoKey, kNoKey, kNoKey, kNoKey);
       if (j < n) f = *reinterpret_cast<const float4*>(srow + j);
       sc[4 * i + 0] = f.x;
       sc[4 * i + 1] = f.y;
@@ -175,7 +211,7 @@ void select_kernel(const SelParams p) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const int j = id0 + 256 * i + c;
-        sc[4 * i + c] = j < n ? srow[j] : 0.f;
+        sc[4 * i + c] = j < n ? srow[j] : kNoKey;
       }
   }
   // The histogram is cleared while the scores are in flight: the barrier
@@ -184,71 +220,128 @@ void select_kernel(const SelParams p) {
   const bool take_all = need0 == pool;
   const bool radix = !take_all && need0 > 0;
   if (radix) {
-    for (int b = tid; b < kHistBins; b += kSelThreads) hist[b] = 0;
+#pragma unroll
+    for (int q = 0; q < kBPT / 4; ++q)
+      reinterpret_cast<int4*>(hist)[tid + q * kSelThreads] = make_int4(0, 0, 0, 0);
+    if (tid == 0) s_fill = 0;
     __asm__ __volatile__("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   }
+  // The current region's key is cleared by the one wave that holds it.
   uint32_t key[K4];
 #pragma unroll
-  for (int i = 0; i < I; ++i)
+  for (int k = 0; k < K4; ++k) key[k] = order_key(sc[k]);
+  if (forced && (curx >> kWaveIdsLog2) == wave) {
+    const int d = curx - id0;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int j = id0 + 256 * i + c;
-      key[4 * i + c] = (j < n && j != curx) ? order_key(sc[4 * i + c]) : 0u;
-    }
+    for (int k = 0; k < K4; ++k) key[k] = d == 256 * (k >> 2) + (k & 3) ? 0u : key[k];
+  }
 
   // 2. threshold: every pool key > T is taken, plus need_eq keys == T
   uint32_t T = 0;
   int need_eq = 0, eq_total = 0;
   if (radix) {
-    // pass 1 (bits 31..20) over the registers (histogram cleared above)
+    // Pass 1 (bits 31..kP1Shift) over the live groups' keys.  Key 0 (not a
+    // candidate) lands in bin 0, which only NaN scores share, so the
+    // search below never reaches bin 0 on finite scores.
 #pragma unroll
-    for (int k = 0; k < K4; ++k)
-      atomicAdd(&hist[key[k] != 0u ? (int)(key[k] >> 20) : kHistBins + lane], 1);
+    for (int i = 0; i < I; ++i)
+      if (wave * I + i < nlive)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) atomicAdd(&hist[key[4 * i + c] >> kP1Shift], 1);
     __syncthreads();
-    int above;
-    const int d1 = find_digit<kHistBins, kAllLoads>(hist, need0, s_pick, wave, lane, above);
-    int need = need0 - above;
-    uint32_t prefix = (uint32_t)d1 << 20, pmask = 0xFFF00000u;
-    const int inbin = hist[d1];
+    // Digit search by all threads: thread t holds bins kBPT (1023 - t) ..
+    // + kBPT - 1, so wave 0 holds the top bins.  Per-wave totals, one
+    // barrier, then the wave whose range reaches need0 finds the lane and the
+    // bin.
+    int hb[kBPT];  // this thread's bins, ascending
+    {
+      const int4* hist4 = reinterpret_cast<const int4*>(hist);
+#pragma unroll
+      for (int q = 0; q < kBPT / 4; ++q) {
+        const int4 v = hist4[(kBPT / 4) * (kSelThreads - 1 - tid) + q];
+        hb[4 * q + 0] = v.x;
+        hb[4 * q + 1] = v.y;
+        hb[4 * q + 2] = v.z;
+        hb[4 * q + 3] = v.w;
+      }
+    }
+    int local = 0;
+#pragma unroll
+    for (int q = 0; q < kBPT; ++q) local += hb[q];
+    int wtot;
+    const int excl = wave_exclusive_scan(local, wtot);
+    if (lane == 0) s_tot[wave] = wtot;
+    __syncthreads();
+    {
+      const int wx = wave_inclusive_scan(lane < kSelWaves ? s_tot[lane] : 0);
+      // the histogram holds 256 nlive >= pool >= need0 keys: W exists
+      const int W = (int)__builtin_ctzll(__ballot(lane < kSelWaves && wx >= need0));
+      if (wave == W) {
+        const int wbase = W > 0 ? __builtin_amdgcn_readlane(wx, W - 1) : 0;
+        const int c0 = wbase + excl;
+        if (c0 < need0 && need0 <= c0 + local) {  // exactly one lane
+          // its bins from the top: j steps down to the first where the count
+          // reaches need0
+          int c = c0, j = 0;
+#pragma unroll
+          for (int q = 0; q < kBPT - 1; ++q)
+            if (j == q && need0 > c + hb[kBPT - 1 - q]) {
+              c += hb[kBPT - 1 - q];
+              j = q + 1;
+            }
+          int cnt = hb[kBPT - 1];
+#pragma unroll
+          for (int q = 1; q < kBPT; ++q) cnt = j == q ? hb[kBPT - 1 - q] : cnt;
+          s_pick[0] = kBPT * (kSelThreads - 1 - tid) + kBPT - 1 - j;
+          s_pick[1] = c;
+          s_pick[2] = cnt;
+        }
+      }
+    }
+    __syncthreads();
+    const int d1 = s_pick[0];
+    int need = need0 - s_pick[1];
+    const int inbin = s_pick[2];
+    uint32_t prefix = (uint32_t)d1 << kP1Shift, pmask = ~((1u << kP1Shift) - 1u);
     const bool listed = inbin <= kCandCap;
     const bool ranked = inbin <= kRankCap;
+    // ranking: a group of P lanes per listed key (P a power of two, at most a
+    // wave, inbin * P <= kSelThreads), each lane over 16-byte pieces part,
+    // part + P, ... of the list, four at a time
+    int P = 1;
+    while (P < 64 && inbin * P * 2 <= kSelThreads) P *= 2;
+    const int pieces = (inbin + 3) >> 2;
     if (listed) {
-      // The keys of bin d1 (typically a few percent) go to an LDS list; the
-      // other two passes run over it.  Per-wave counts, one barrier, then
-      // each wave writes at its offset.
-      uint32_t cbits = 0;
+      // The keys of bin d1 (typically a few percent) go to an LDS list.  Each
+      // wave takes its slots from a shared counter (list order is free).
+      int cnt = 0;
 #pragma unroll
-      for (int k = 0; k < K4; ++k)
-        cbits |= (key[k] != 0u && (key[k] >> 20) == (uint32_t)d1 ? 1u : 0u) << k;
+      for (int i = 0; i < I; ++i)
+        if (wave * I + i < nlive)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) cnt += (key[4 * i + c] - prefix) < (1u << kP1Shift) ? 1 : 0;
       int cw;
-      int off = wave_exclusive_scan(__popc(cbits), cw);
-      if (lane == 0) s_cnt[0][wave] = cw;
-      __syncthreads();
-      int before, all;
-      wave_counts(s_cnt[0], wave, lane, before, all);
-      off += before;
-      while (cbits) {  // a lane has ~0.1-1 candidates: order within the list is free
-        const int k = __builtin_ctz(cbits);
-        cbits &= cbits - 1u;
-        uint32_t kk = 0;
+      int off = wave_exclusive_scan(cnt, cw);
+      if (cw > 0) {
+        int base = 0;
+        if (lane == 0) base = atomicAdd(&s_fill, cw);
+        off += __builtin_amdgcn_readlane(base, 0);
 #pragma unroll
-        for (int q = 0; q < K4; ++q) kk = q == k ? key[q] : kk;
-        s_ckey[off++] = kk;
+        for (int i = 0; i < I; ++i)
+          if (wave * I + i < nlive)
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+              if ((key[4 * i + c] - prefix) < (1u << kP1Shift)) s_ckey[off++] = key[4 * i + c];
       }
       // Key 0 (never a candidate: neither greater nor equal) pads the list
-      // to whole 16-byte reads.
-      if (ranked && tid < 3) s_ckey[inbin + tid] = 0u;
+      // to every piece the unrolled ranking reads.
+      if (ranked && tid < 4 * (pieces + 3 * P) - inbin) s_ckey[inbin + tid] = 0u;
     }
     __syncthreads();
     if (ranked) {
       // T is the need-th largest listed key: the one with fewer than `need`
-      // keys above it and at least `need` at or above it.  A group of P
-      // consecutive lanes (P a power of two, inbin * P <= kSelThreads, at
-      // most a wave) ranks one listed key, each lane over every P-th 16-byte
-      // piece of the list, and the group sums its counts.  Every group
+      // keys above it and at least `need` at or above it.  Every group
       // holding a key equal to T writes the same three values.
-      int P = 1;
-      while (P < 64 && inbin * P * 2 <= kSelThreads) P *= 2;
       const int ci = tid / P, part = tid & (P - 1);
       int gt = 0, eq = 0;
       uint32_t kt = 0;
@@ -256,10 +349,15 @@ void select_kernel(const SelParams p) {
         kt = s_ckey[ci];
         const uint4* l4 = reinterpret_cast<const uint4*>(s_ckey);
 #pragma unroll 1
-        for (int e = part; e < (inbin + 3) >> 2; e += P) {
-          const uint4 v = l4[e];
-          gt += (v.x > kt) + (v.y > kt) + (v.z > kt) + (v.w > kt);
-          eq += (v.x == kt) + (v.y == kt) + (v.z == kt) + (v.w == kt);
+        for (int e = part; e < pieces; e += 4 * P) {
+          uint4 v[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) v[u] = l4[e + u * P];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            gt += (v[u].x > kt) + (v[u].y > kt) + (v[u].z > kt) + (v[u].w > kt);
+            eq += (v[u].x == kt) + (v[u].y == kt) + (v[u].z == kt) + (v[u].w == kt);
+          }
         }
       }
       for (int o = 1; o < P; o <<= 1) {
@@ -279,7 +377,7 @@ void select_kernel(const SelParams p) {
 #pragma unroll
       for (int pass = 1; pass < 3; ++pass) {
         const int shift = pass == 1 ? 8 : 0;
-        const int nb = pass == 2 ? 256 : kHistBins;
+        const int nb = pass == 2 ? 256 : kP2Bins;
         const uint32_t dmask = (uint32_t)nb - 1u;
         for (int b = tid; b < nb; b += kSelThreads) hist[b] = 0;
         __syncthreads();
@@ -290,14 +388,19 @@ void select_kernel(const SelParams p) {
           }
         } else {
 #pragma unroll
-          for (int k = 0; k < K4; ++k)
-            if (key[k] != 0u && (key[k] & pmask) == prefix)
-              atomicAdd(&hist[(key[k] >> shift) & dmask], 1);
+          for (int i = 0; i < I; ++i)
+            if (wave * I + i < nlive)
+#pragma unroll
+              for (int c = 0; c < 4; ++c) {
+                const uint32_t k = key[4 * i + c];
+                if ((k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & dmask], 1);
+              }
         }
         __syncthreads();
+        int above;
         const int d = pass == 2 ? find_digit<256, kAllLoads>(hist, need, s_pick, wave, lane, above)
-                                : find_digit<kHistBins, kAllLoads>(hist, need, s_pick, wave, lane,
-                                                                  above);
+                                : find_digit<kP2Bins, kAllLoads>(hist, need, s_pick, wave, lane,
+                                                                above);
         need -= above;
         prefix |= (uint32_t)d << shift;
         pmask |= dmask << shift;
@@ -309,59 +412,91 @@ void select_kernel(const SelParams p) {
   }
   // Without ties at T (all keys == T taken) the selection is key >= T.
   const bool ties = radix && eq_total > need_eq;
-  const uint64_t t_take = (uint64_t)T + (ties ? 1u : 0u);  // taken outright: key >= t_take
 
-  // 3. compaction in id order.  gtf: taken outright (key >= t_take, every
-  // pool key when all are taken, or the forced region); eq (ties only):
-  // key == T, the first need_eq of which in id order are taken.
-  auto gtf_of = [&](int k, int id) -> bool {
-    return (key[k] != 0u && (take_all || (radix && (uint64_t)key[k] >= t_take))) || id == curx;
-  };
-  auto eq_of = [&](int k) -> bool { return ties && key[k] == T; };
-  // Bit k of tbits: key k is taken outright; of ebits (ties only): key == T.
+  // 3. compaction in id order
+  if (!ties) {
+    // Selected: key >= t_sel.  Key 0 marks a non-candidate, so t_sel >= 1;
+    // the current region's key becomes the largest key, which every t_sel
+    // takes (with nothing else to take, t_sel is that key alone).
+    const uint32_t t_sel = take_all ? 1u : !radix ? 0xFFFFFFFFu : (T > 1u ? T : 1u);
+    if (forced && (curx >> kWaveIdsLog2) == wave) {
+      const int d = curx - id0;
+#pragma unroll
+      for (int k = 0; k < K4; ++k) key[k] = d == 256 * (k >> 2) + (k & 3) ? 0xFFFFFFFFu : key[k];
+    }
+    // Per-lane counts of each live group, two groups per 32-bit word (a
+    // group's total over the wave is at most 256), one wave scan per word.
+    constexpr int W2 = (I + 1) / 2;
+    int pre[W2], tot[W2];
+    int g_wave = 0;
+#pragma unroll
+    for (int h = 0; h < W2; ++h) {
+      int v = 0;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int i = 2 * h + s;
+        if (i < I && wave * I + i < nlive) {
+          int c4 = 0;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) c4 += key[4 * i + c] >= t_sel ? 1 : 0;
+          v += c4 << (16 * s);
+        }
+      }
+      pre[h] = wave_exclusive_scan(v, tot[h]);
+      g_wave += (tot[h] & 0xFFFF) + ((uint32_t)tot[h] >> 16);
+    }
+    if (lane == 0) s_cnt[0][wave] = g_wave;
+    __syncthreads();
+    int g_prev, g_all;
+    wave_counts(s_cnt[0], wave, lane, g_prev, g_all);
+    int run = g_prev;  // output slot of this wave's first selection
+#pragma unroll
+    for (int i = 0; i < I; ++i) {
+      if (wave * I + i >= nlive) break;
+      const int h = i >> 1, s = 16 * (i & 1);
+      const int gtot = (int)(((uint32_t)tot[h] >> s) & 0xFFFFu);
+      if (gtot > 0) {
+        int slot = run + (int)(((uint32_t)pre[h] >> s) & 0xFFFFu);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          if (key[4 * i + c] >= t_sel) {
+            if (slot < p.topk) o[slot] = id0 + 256 * i + c;
+            ++slot;
+          }
+        }
+      }
+      run += gtot;
+    }
+    for (int s = g_all + tid; s < p.topk; s += kSelThreads) o[s] = -1;
+    return;
+  }
+
+  // Ties at T: keys > T and the current region are taken outright; of the
+  // keys == T, the first need_eq in id order.
+  auto gtf_of = [&](int k, int id) -> bool { return key[k] > T || id == curx; };
+  auto eq_of = [&](int k) -> bool { return key[k] == T && T != 0u; };
   uint32_t tbits = 0, ebits = 0;
 #pragma unroll
   for (int i = 0; i < I; ++i)
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       tbits |= (gtf_of(4 * i + c, id0 + 256 * i + c) ? 1u : 0u) << (4 * i + c);
-      if (ties) ebits |= (eq_of(4 * i + c) ? 1u : 0u) << (4 * i + c);
+      ebits |= (eq_of(4 * i + c) ? 1u : 0u) << (4 * i + c);
     }
   const int g_wave = wave_sum(__popc(tbits));
-  const int e_wave = ties ? wave_sum(__popc(ebits)) : 0;
+  const int e_wave = wave_sum(__popc(ebits));
   if (lane == 0) {
     s_cnt[0][wave] = g_wave;
     s_cnt[1][wave] = e_wave;
   }
   __syncthreads();
-  int g_prev, g_all, e_prev = 0, e_all = 0;
+  int g_prev, g_all, e_prev, e_all;
   wave_counts(s_cnt[0], wave, lane, g_prev, g_all);
-  if (ties) wave_counts(s_cnt[1], wave, lane, e_prev, e_all);
-  if (!ties) need_eq = 0;
+  wave_counts(s_cnt[1], wave, lane, e_prev, e_all);
   // output slot of the wave's first selection; eq keys still to take there
   int run = g_prev + min(need_eq, e_prev);
   int eq_left = need_eq - e_prev;
-  if (!ties) {
-    if (g_wave > 0) {
-#pragma unroll
-      for (int i = 0; i < I; ++i) {
-        // In id order a 256-id group is lane-major: lane l holds ids 4l .. 4l+3.
-        const uint32_t nib = (tbits >> (4 * i)) & 15u;
-        if (__ballot(nib != 0u) == 0) continue;
-        const int c4 = __popc(nib);
-        const uint64_t b0 = __ballot(c4 & 1), b1 = __ballot(c4 & 2), b2 = __ballot(c4 & 4);
-        int slot = run + mbcnt(b0) + 2 * mbcnt(b1) + 4 * mbcnt(b2);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          if ((nib >> c) & 1u) {
-            if (slot < p.topk) o[slot] = id0 + 256 * i + c;
-            ++slot;
-          }
-        }
-        run += __popcll(b0) + 2 * __popcll(b1) + 4 * __popcll(b2);
-      }
-    }
-  } else if (g_wave + (eq_left > 0 ? e_wave : 0) > 0) {
+  if (g_wave + (eq_left > 0 ? e_wave : 0) > 0) {
 #pragma unroll
     for (int i = 0; i < I; ++i) {
       bool gt[4], eq[4];

@@ -83,8 +83,8 @@ def test_two_workgroups_per_cu(S, dist):
 
 
 def _bin_case(seed, rows, S, m, tied):
-    """Rows whose threshold falls in one bin of the 12-bit first pass holding
-    exactly m keys: 100 keys in [4, 4.5), m keys in [1, 1.125) (distinct, or
+    """Rows whose threshold falls in one bin of the first pass (12 or 13 bits) holding
+    exactly m keys: 100 keys in [4, 4.5), m keys in [1, 1.0625) (distinct, or
     drawn from m // 8 + 1 values when tied), the rest negative; positions
     shuffled per row."""
     g = torch.Generator().manual_seed(seed)
@@ -93,9 +93,9 @@ def _bin_case(seed, rows, S, m, tied):
         hi = 4.0 + 0.5 * torch.rand(100, generator=g)
         if tied:
             nv = m // 8 + 1
-            mid = 1.0 + (0.12 / nv) * torch.randint(0, nv, (m,), generator=g).float()
+            mid = 1.0 + (0.06 / nv) * torch.randint(0, nv, (m,), generator=g).float()
         else:
-            mid = 1.0 + 0.12 * torch.rand(m, generator=g)
+            mid = 1.0 + 0.06 * torch.rand(m, generator=g)
         lo = -1.0 - torch.rand(S - 100 - m, generator=g)
         row = torch.cat([hi, mid, lo])
         out[r] = row[torch.randperm(S, generator=g)]
@@ -109,7 +109,8 @@ def test_threshold_bin_sizes(m, tied):
     # radix passes over its LDS list up to 4096, and over the registers
     # beyond: every path, with the threshold at the bin's first, middle and
     # last key.
-    for rows, S in ((8, 8192), (260, 4400 if m <= 4096 else 8192)):
+    # 12-bit first pass (8192 and 4400 columns) and 13-bit (12000 columns)
+    for rows, S in ((8, 8192), (8, 12000), (260, 4400 if m <= 4096 else 8192), (260, 12000)):
         if rows == 260 and m not in (1, 1024, 1025, 4096, 4097):
             continue
         s = _bin_case(m + 31 * tied + rows, rows, S, m, tied)
