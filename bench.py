@@ -672,7 +672,56 @@ def probe_lib():
     lib.sda_probe_args_size.restype = ctypes.c_size_t
     if lib.sda_probe_args_size() != ctypes.sizeof(ProbeArgs):
         raise RuntimeError("sda_probe_args size mismatch")
+    lib.sda_probe_valu.restype = ctypes.c_int
+    lib.sda_probe_valu.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                   ctypes.c_void_p, ctypes.c_void_p]
     return lib
+
+
+# include/sda_probe.h: kind -> (name, instructions per wave per round)
+VALU_KINDS = {0: ("v_fma_f32", 64), 1: ("v_xor_b32 + v_add_u32", 128),
+              2: ("v_lshrrev_b32 + v_lshl_or_b32", 128)}
+
+
+def run_valu(args, dev) -> int:
+    """SIMD cycles per wave64 VALU instruction of each probe kind: 8 workgroups of
+    4 waves per CU (8 waves per SIMD), `iters` rounds each, timed with HIP
+    events on the launch stream; cycles assume the 2.4 GHz peak clock, and the
+    ratio to the FMA figure is clock-free."""
+    import torch
+    plib = probe_lib()
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    groups, iters = 8 * cus, 2000
+    sink = torch.empty(groups * 256, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    handle = ctypes.c_void_p(stream.cuda_stream)
+    res = {}
+    for kind, (name, per_round) in VALU_KINDS.items():
+        def call():
+            rc = plib.sda_probe_valu(kind, groups, iters, ctypes.c_void_p(sink.data_ptr()), handle)
+            if rc != 0:
+                raise RuntimeError("sda_probe_valu returned %d" % rc)
+        call()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        reps = max(1, min(args.steps, 10))
+        e0.record(stream)
+        for _ in range(reps):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        instr_per_simd = groups * 4 * iters * per_round / (4 * cus)
+        res[name] = {"ms_per_call": round(ms, 4),
+                     "simd_cycles_per_instr_at_2p4GHz": round(ms * 1e-3 * 2.4e9 / instr_per_simd, 3)}
+    fma = res["v_fma_f32"]["simd_cycles_per_instr_at_2p4GHz"]
+    for name in res:
+        res[name]["relative_to_fma"] = round(res[name]["simd_cycles_per_instr_at_2p4GHz"] / fma, 3)
+    print(json.dumps({"metric": "VALU issue cost per wave64 instruction", "cus": cus,
+                      "workgroups": groups, "waves_per_simd": 8, "iters": iters,
+                      "kinds": res}), flush=True)
+    return 0
 
 
 def probe_blocks(w, cache_strides, positions, regions, active, block_table) -> tuple:
@@ -829,6 +878,9 @@ def main() -> int:
     ap.add_argument("--balanced-groups", type=int, default=0, metavar="N",
                     help="--gather-ceiling: deal all blocks evenly to N workgroups instead "
                          "of one per row")
+    ap.add_argument("--valu-rate", action="store_true",
+                    help="time the VALU issue-rate probe (SIMD cycles per wave64 instruction "
+                         "of a few kinds; one JSON line)")
     ap.add_argument("--pack", type=int, default=0,
                     help="with --swa: query tokens per workgroup (0: the library's plan)")
     ap.add_argument("--sets", type=int, default=4, help="rotating input sets")
@@ -878,6 +930,8 @@ def main() -> int:
         return 0
     if args.gather_ceiling:
         return run_gather(args, dev)
+    if args.valu_rate:
+        return run_valu(args, dev)
     if args.swa:
         return run_swa(args, dev)
     if args.select:

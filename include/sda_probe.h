@@ -1,7 +1,8 @@
 /*
- * sda_probe.h - gather-ceiling probe for MI355X (gfx950).  C ABI of
- * libsda_probe.so, a measurement library beside libsda.so (bench.py
- * --gather-ceiling uses it; the decode path never does).
+ * sda_probe.h - gather-ceiling and VALU issue-rate probes for MI355X
+ * (gfx950).  C ABI of libsda_probe.so, a measurement library beside libsda.so
+ * (bench.py --gather-ceiling and --valu-rate use it; the decode path never
+ * does).
  *
  * The probe moves a list of token blocks from HBM into LDS through the split
  * kernel's own chunk loop (the same 12 LDS-DMAs per chunk of 16 bf16 or 32
@@ -57,6 +58,25 @@ typedef struct sda_probe_args {
 } sda_probe_args;
 
 int sda_probe_gather(const sda_probe_args *args, hipStream_t stream);
+
+/*
+ * VALU issue-rate probe: `workgroups` workgroups of 256 threads, each wave
+ * running `iters` rounds of 8 steps over 8 independent register chains of
+ * one instruction kind.  Per wave that is 64 * iters instructions
+ * (SDA_PROBE_VALU_FMA: v_fma_f32) or 128 * iters (the two-instruction kinds:
+ * v_xor_b32 + v_add_u32 with scalar and literal operands, v_lshrrev_b32 +
+ * v_lshl_or_b32).  Timed over a full chip of resident waves, it gives the
+ * SIMD cycles one wave64 instruction of that kind holds, which counter-based
+ * VALU estimates need.  sink: int32 [workgroups * 256], one word per thread.
+ * Returns SDA_ERR_INVALID for a bad argument or kind, SDA_ERR_LAUNCH if the
+ * launch fails.
+ */
+#define SDA_PROBE_VALU_FMA 0
+#define SDA_PROBE_VALU_XOR_ADD 1
+#define SDA_PROBE_VALU_SHIFTS 2
+
+int sda_probe_valu(int32_t kind, int32_t workgroups, int32_t iters, int32_t *sink,
+                   hipStream_t stream);
 
 /* sizeof(sda_probe_args), for bindings that mirror the struct. */
 size_t sda_probe_args_size(void);

@@ -8,6 +8,9 @@
 // bases, and anything else uses per-lane 64-bit addresses, as in the split
 // kernel.  Rows past the end of a workgroup's list load its first token row
 // (the split kernel's masked rows load a visible row of their region).
+// The library also holds a VALU issue-rate probe (sda_probe_valu): waves of
+// independent instructions of one kind, timed to give the SIMD cycles a
+// wave64 instruction of that kind occupies.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -19,6 +22,7 @@ namespace sda {
 namespace {
 
 constexpr int kProbeStages = 2;
+constexpr int kValuThreads = 256;
 
 struct ProbeParams {
   const uint8_t* base;
@@ -138,8 +142,60 @@ void launch_dtype(const ProbeParams& p, unsigned groups, int cus, hipStream_t st
     launch_gather<kFp8, kProbeGeneral>(p, groups, cus, stream);
 }
 
+// VALU issue-rate probe: each wave runs `iters` rounds of 64 independent
+// chains' worth of one instruction kind (8 register chains, 8 steps each), so
+// issue, not latency, bounds it once a few waves share a SIMD.
+template <int kKind>
+__global__ __launch_bounds__(kValuThreads) void valu_kernel(int32_t* sink, int iters, float a) {
+  float v[8];
+  uint32_t u[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    v[q] = a + (float)threadIdx.x * 0.001f + (float)q;
+    u[q] = threadIdx.x * 7u + (uint32_t)q;
+  }
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        if (kKind == SDA_PROBE_VALU_FMA) v[q] = __builtin_fmaf(v[q], a, 0.5f);
+        if (kKind == SDA_PROBE_VALU_XOR_ADD) u[q] = (u[q] ^ (uint32_t)it) + 0x9E3779B9u;
+        if (kKind == SDA_PROBE_VALU_SHIFTS) u[q] = (u[q] >> 3) | (u[q] << 5);
+      }
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) s += v[q] + (float)u[q];
+  sink[(int64_t)blockIdx.x * kValuThreads + threadIdx.x] = __float_as_int(s);
+}
+
 }  // namespace
 }  // namespace sda
+
+extern "C" int sda_probe_valu(int32_t kind, int32_t workgroups, int32_t iters, int32_t* sink,
+                              hipStream_t stream) {
+  if (workgroups < 0 || iters < 0 || (workgroups > 0 && !sink)) return SDA_ERR_INVALID;
+  if (workgroups == 0) return SDA_OK;
+  const dim3 grid((unsigned)workgroups), block(sda::kValuThreads);
+  switch (kind) {
+    case SDA_PROBE_VALU_FMA:
+      hipLaunchKernelGGL(sda::valu_kernel<SDA_PROBE_VALU_FMA>, grid, block, 0, stream, sink, iters,
+                         0.999f);
+      break;
+    case SDA_PROBE_VALU_XOR_ADD:
+      hipLaunchKernelGGL(sda::valu_kernel<SDA_PROBE_VALU_XOR_ADD>, grid, block, 0, stream, sink,
+                         iters, 0.999f);
+      break;
+    case SDA_PROBE_VALU_SHIFTS:
+      hipLaunchKernelGGL(sda::valu_kernel<SDA_PROBE_VALU_SHIFTS>, grid, block, 0, stream, sink,
+                         iters, 0.999f);
+      break;
+    default:
+      return SDA_ERR_INVALID;
+  }
+  return hipGetLastError() == hipSuccess ? SDA_OK : SDA_ERR_LAUNCH;
+}
 
 extern "C" size_t sda_probe_args_size(void) { return sizeof(sda_probe_args); }
 

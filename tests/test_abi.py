@@ -367,7 +367,24 @@ def test_probe_library_exports_its_header():
     import ctypes
     from sparse_paged_decode_02_amd import build as sda_build
     names = _declared_functions("sda_probe.h")
-    assert names == ["sda_probe_args_size", "sda_probe_gather"]
+    assert names == ["sda_probe_args_size", "sda_probe_gather", "sda_probe_valu"]
     lib = ctypes.CDLL(sda_build.PROBE_LIB)
     for n in names:
         assert hasattr(lib, n), n
+
+
+def test_valu_probe_validates_before_launching():
+    # Every call here is rejected, or has nothing to launch, before any HIP call.
+    import ctypes
+    from sparse_paged_decode_02_amd import build as sda_build
+    lib = ctypes.CDLL(sda_build.PROBE_LIB)
+    lib.sda_probe_valu.restype = ctypes.c_int
+    lib.sda_probe_valu.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                   ctypes.c_void_p, ctypes.c_void_p]
+    dummy = ctypes.c_void_p(16)  # never dereferenced: each call returns first
+    assert lib.sda_probe_valu(0, 0, 100, None, None) == B.SDA_OK
+    assert lib.sda_probe_valu(0, 1, 100, None, None) == B.SDA_ERR_INVALID
+    assert lib.sda_probe_valu(0, -1, 100, dummy, None) == B.SDA_ERR_INVALID
+    assert lib.sda_probe_valu(0, 1, -1, dummy, None) == B.SDA_ERR_INVALID
+    assert lib.sda_probe_valu(3, 1, 100, dummy, None) == B.SDA_ERR_INVALID
+    assert lib.sda_probe_valu(-1, 1, 100, dummy, None) == B.SDA_ERR_INVALID
