@@ -1224,7 +1224,7 @@ __global__ __launch_bounds__(64) void combine_kernel(const Params p) {
 // starts late stretches the tail of the launch.  Two small kernels rank the
 // rows by visible tokens (0 for an inactive row) and write them heaviest
 // first within each block of 1024 rows:
-//  * bin_kernel: one wave per 16 rows, spread over the chip; writes each
+//  * bin_kernel: one wave per row, spread over the chip; writes each
 //    row's bin, 0 (heaviest) .. kOrderBins - 1, of width
 //    (R * region tokens + 1) / kOrderBins;
 //  * order_kernel: one 1024-thread workgroup per block of 1024 rows; a stable
@@ -1237,64 +1237,39 @@ __global__ __launch_bounds__(64) void combine_kernel(const Params p) {
 constexpr int kOrderBlock = 1024;
 constexpr int kOrderWaves = kOrderBlock / 64;
 constexpr int kOrderBins = 32;
-constexpr int kOrderBatch = 16;  // rows per wave of the bin kernel
 constexpr int kOrderMaxRounds = 4;  // order grids of up to 4x the resident workgroups
 static_assert(kOrderBins * kOrderWaves <= kOrderBlock, "one scan entry per thread");
 
+template <int kLoads>
 __global__ __launch_bounds__(256) void bin_kernel(Params p, int64_t max_tokens, int32_t* bins) {
   const int lane = threadIdx.x & 63;
-  // Wave w ranks kOrderBatch rows from rbase; lane i < kOrderBatch ends up
-  // with the tokens of row rbase + i.
-  const int rbase = (blockIdx.x * 4 + (threadIdx.x >> 6)) * kOrderBatch;
-  const int r = rbase + lane;
-  const bool valid = lane < kOrderBatch && r < p.rows;
-  // Every load below is unconditional, at an index clamped into the arrays
-  // (the launch has rows >= 1), and masked afterwards: the flag, the
-  // position and all region ids then share one round trip, where loads
-  // under branches had been waited for one by one.
-  const int rc = min(r, p.rows - 1);
-  const int act_raw = p.active[rc];
-  const int pos_raw = p.positions[rc];
+  // One wave per row: lane l holds slots l, l + 64, ... (kLoads >= R / 64
+  // of them) of the row's region ids, all requested at once with the flag
+  // and the position (one round trip), at indices clamped into the row and
+  // masked afterwards.
+  const int r = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
+  if (r >= p.rows) return;
+  const int act = p.active[r];
+  const int pos_raw = p.positions[r];
+  const int32_t* row = p.regions + (int64_t)r * p.rrs;
+  int ids[kLoads];
+#pragma unroll
+  for (int k = 0; k < kLoads; ++k) ids[k] = row[min(64 * k + lane, p.R - 1)];
+  // Region id i is visible in part or whole iff 0 <= i <= pq, wholly iff
+  // 0 <= i < pf; the one partial region shows pos % rt + 1 tokens.
+  const int pos = act ? pos_raw : -1;
+  const int pq = pos >= 0 ? pos / p.rt : -1;
+  const int pf = pos >= 0 ? (pos + 1) / p.rt : 0;
+  const int part = pos >= 0 ? pos - pq * p.rt + 1 : 0;
   int64_t tokens = 0;
-  int pq = -1, pf = 0, part = 0;
-  for (int c = 0; c < p.R; c += 64) {
-    // One coalesced load per row (lane l reads slot c + l), all issued
-    // before the first is used.
-    const bool in_r = c + lane < p.R;
-    const int32_t* col = p.regions + min(c + lane, p.R - 1);
-    int ids[kOrderBatch];
 #pragma unroll
-    for (int i = 0; i < kOrderBatch; ++i)
-      ids[i] = col[(int64_t)min(rbase + i, p.rows - 1) * p.rrs];
-#pragma unroll
-    for (int i = 0; i < kOrderBatch; ++i)
-      if (!(rbase + i < p.rows && in_r)) ids[i] = -1;
-    if (c == 0) {
-      // Region id i of this lane's row is visible in part or whole iff
-      // 0 <= i <= pq, wholly iff 0 <= i < pf; the one partial region shows
-      // pos % rt + 1 tokens.  (Formed once the first ids are requested.)
-      int pos = pos_raw;
-      __asm__ __volatile__("" : "+v"(pos));  // keeps the use below the loads
-      pos = valid ? pos : -1;
-      pq = pos >= 0 ? pos / p.rt : -1;
-      pf = pos >= 0 ? (pos + 1) / p.rt : 0;
-      part = pos >= 0 ? pos - pq * p.rt + 1 : 0;
-    }
-    // Row rbase + i: rt tokens per region that ends at or before its
-    // position, pos % rt + 1 per copy of the region that holds it.
-#pragma unroll
-    for (int i = 0; i < kOrderBatch; ++i) {
-      const int qi = __builtin_amdgcn_readlane(pq, i);
-      const int fi = __builtin_amdgcn_readlane(pf, i);
-      const uint64_t ba = __ballot(ids[i] >= 0 && ids[i] <= qi);
-      const uint64_t bf = __ballot(ids[i] >= 0 && ids[i] < fi);
-      if (lane == i) tokens += __popcll(bf) * p.rt + __popcll(ba & ~bf) * part;
-    }
+  for (int k = 0; k < kLoads; ++k) {
+    const int id = 64 * k + lane < p.R ? ids[k] : -1;
+    const uint64_t ba = __ballot(id >= 0 && id <= pq);
+    const uint64_t bf = __ballot(id >= 0 && id < pf);
+    tokens += (int64_t)__popcll(bf) * p.rt + (int64_t)__popcll(ba & ~bf) * part;
   }
-  if (valid) {
-    if (!act_raw) tokens = 0;
-    bins[r] = kOrderBins - 1 - (int)(tokens * kOrderBins / (max_tokens + 1));
-  }
+  if (lane == 0) bins[r] = kOrderBins - 1 - (int)(tokens * kOrderBins / (max_tokens + 1));
 }
 
 __global__ __launch_bounds__(kOrderBlock) void order_kernel(Params p, const int32_t* bins) {
@@ -1362,8 +1337,14 @@ const int32_t* launch_order(const Params& p, hipStream_t stream) {
   // The workspace's order area holds the bins ([rows] after the order).
   int32_t* bins = p.order_ws + p.rows;
   const int64_t max_tokens = (int64_t)p.R * p.rt;
-  const unsigned bin_wgs = (unsigned)((p.rows + 4 * kOrderBatch - 1) / (4 * kOrderBatch));
-  hipLaunchKernelGGL(bin_kernel, dim3(bin_wgs), dim3(256), 0, stream, p, max_tokens, bins);
+  const dim3 bin_grid((unsigned)((p.rows + 3) / 4));  // one wave per row
+  static_assert(kMaxRegions <= 64 * 32, "at most 32 region-id loads per lane");
+  if (p.R <= 64 * 8)
+    hipLaunchKernelGGL(bin_kernel<8>, bin_grid, dim3(256), 0, stream, p, max_tokens, bins);
+  else if (p.R <= 64 * 16)
+    hipLaunchKernelGGL(bin_kernel<16>, bin_grid, dim3(256), 0, stream, p, max_tokens, bins);
+  else
+    hipLaunchKernelGGL(bin_kernel<32>, bin_grid, dim3(256), 0, stream, p, max_tokens, bins);
   hipLaunchKernelGGL(order_kernel, dim3((unsigned)((p.rows + kOrderBlock - 1) / kOrderBlock)),
                      dim3(kOrderBlock), 0, stream, p, (const int32_t*)bins);
   return p.order_ws;

@@ -476,6 +476,67 @@ def test_row_order_matches_index_order(kv, splits, strided, requests, R):
     check_inactive_zero(outs[0], inp)
 
 
+def host_bins(regions, positions, active, rt, R):
+    """Each row's bin as the order pass defines it: 31 - tokens * 32 // (R rt + 1),
+    tokens = the visible tokens of its slots (rt for a region wholly at or
+    before the position, pos % rt + 1 for the region holding it, 0 for an
+    inactive row)."""
+    bins = np.empty(len(positions), np.int64)
+    for r, pos in enumerate(positions):
+        tokens = 0
+        if active[r] and pos >= 0:
+            pq, pf = pos // rt, (pos + 1) // rt
+            ids = regions[r][regions[r] >= 0]
+            tokens = rt * int((ids < pf).sum()) + (pos - pq * rt + 1) * int(
+                ((ids >= pf) & (ids <= pq)).sum())
+        bins[r] = 31 - tokens * 32 // (R * rt + 1)
+    return bins
+
+
+@pytest.mark.parametrize("R", [130, 600, 1100])
+def test_row_order_bins_and_permutation(R):
+    # The order pass only permutes rows, so the outputs cannot show a wrong
+    # bin: check the workspace itself.  768 rows (2 to 4 rounds of the
+    # resident grid) with each row's slots shuffled over all R (up to 32
+    # region-id loads per lane of the bin kernel), duplicate and past-position
+    # ids added; the bins must equal the host's, and the order must be the
+    # stable sort of each 1024-row block by bin.
+    w = gen.Workload("row-order-bins", requests=96, query_len=2, groups=4, heads=8, block=16,
+                     pages_per_req=128, R=R, kv="bf16", pos_lo=1024, pos_hi=2046,
+                     live=(8, 120), inactive_frac=0.10, gated=True, splits=1, seed=700 + R)
+    inp = gen.make_inputs(w, device=DEV)
+    rng = np.random.default_rng(R)
+    reg = inp.regions.cpu().numpy()
+    pos = inp.positions.cpu().numpy()
+    rt = w.rt
+    for r in range(w.rows):
+        live = reg[r][reg[r] >= 0]
+        if len(live) and r % 3 == 0:
+            reg[r, len(live)] = live[0]                  # a duplicate
+        if r % 5 == 0:
+            reg[r, -1] = pos[r] // rt + 3                # past the position
+        reg[r] = reg[r][rng.permutation(R)]
+    inp.regions = torch.from_numpy(reg).to(DEV)
+    assert kernels(inp, splits=1) & B.SDA_KERNEL_ORDER
+    ws = torch.empty(B.sda_workspace_bytes(w.rows, w.heads, 1), dtype=torch.uint8, device=DEV)
+    out = torch.empty_like(inp.query)
+    _say("sda_decode row-order bins R=%d rows=%d" % (R, w.rows))
+    B.sda_decode(inp.query, inp.cache, inp.regions, inp.block_table, inp.positions, inp.active,
+                 out, scale=inp.scale, query_len=w.query_len, splits=1, gate=inp.gate,
+                 workspace=ws)
+    torch.cuda.synchronize()
+    words = ws[:8 * w.rows].view(torch.int32).cpu().numpy()
+    order, bins = words[:w.rows], words[w.rows:]
+    want = host_bins(reg, pos, inp.active.cpu().numpy(), rt, R)
+    assert np.array_equal(bins, want), np.nonzero(bins != want)[0][:10]
+    assert len(set(want.tolist())) >= 3    # the rows spread over several bins
+    for b0 in range(0, w.rows, 1024):
+        rows = np.arange(b0, min(w.rows, b0 + 1024))
+        expect = rows[np.argsort(want[rows], kind="stable")]
+        assert np.array_equal(order[rows], expect)
+    check_close(out, oracle_out(inp), what="row-order bins R=%d" % R)
+
+
 def expected_kernels(rows, R, splits, row_order, cus):
     """The schedule sda_decode documents for an aligned output: the
     row-stream kernel for 2 to 8 rows per wave (4 waves per CU) with at most
