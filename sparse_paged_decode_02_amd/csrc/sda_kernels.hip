@@ -1238,7 +1238,7 @@ constexpr int kOrderBlock = 1024;
 constexpr int kOrderWaves = kOrderBlock / 64;
 constexpr int kOrderBins = 32;
 constexpr int kOrderMaxRounds = 4;  // order grids of up to 4x the resident workgroups
-static_assert(kOrderBins * kOrderWaves <= kOrderBlock, "one scan entry per thread");
+static_assert(kOrderBins * kOrderWaves == 8 * 64, "the scan: 8 entries per lane of one wave");
 
 template <int kLoads>
 __global__ __launch_bounds__(256) void bin_kernel(Params p, int64_t max_tokens, int32_t* bins) {
@@ -1274,8 +1274,7 @@ __global__ __launch_bounds__(256) void bin_kernel(Params p, int64_t max_tokens, 
 
 __global__ __launch_bounds__(kOrderBlock) void order_kernel(Params p, const int32_t* bins) {
   // s_cnt[bin][wave]: rows of the wave in the bin, then their first slot.
-  __shared__ int s_cnt[kOrderBins * kOrderWaves];
-  __shared__ int s_wave[kOrderWaves];
+  __shared__ __attribute__((aligned(16))) int s_cnt[kOrderBins * kOrderWaves];
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
   const int r = blockIdx.x * kOrderBlock + t;
@@ -1296,18 +1295,23 @@ __global__ __launch_bounds__(kOrderBlock) void order_kernel(Params p, const int3
   const int rank = __popcll(same & below);
   if (bin >= 0 && rank == 0) s_cnt[bin * kOrderWaves + wave] = __popcll(same);
   __syncthreads();
-  // Exclusive scan of s_cnt in (bin, wave) order: the first slot of each
-  // wave's rows of each bin.
-  const int own = t < kOrderBins * kOrderWaves ? s_cnt[t] : 0;
-  const int v = wave_inclusive_scan(own);
-  if (lane == 63) s_wave[wave] = v;
-  __syncthreads();
+  // Exclusive scan of s_cnt in (bin, wave) order, the first slot of each
+  // wave's rows of each bin, by wave 0 alone: lane l takes the 8 entries
+  // [8 l, 8 l + 8), scans them, and one wave scan adds the lanes before.
   if (wave == 0) {
-    const int w = wave_inclusive_scan(lane < kOrderWaves ? s_wave[lane] : 0);
-    if (lane < kOrderWaves) s_wave[lane] = w;
+    int4* c4 = reinterpret_cast<int4*>(s_cnt) + 2 * lane;
+    const int4 a = c4[0], b = c4[1];
+    const int e[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    int run = 0, ex[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      ex[q] = run;
+      run += e[q];
+    }
+    const int base = wave_inclusive_scan(run) - run;
+    c4[0] = make_int4(base + ex[0], base + ex[1], base + ex[2], base + ex[3]);
+    c4[1] = make_int4(base + ex[4], base + ex[5], base + ex[6], base + ex[7]);
   }
-  __syncthreads();
-  if (t < kOrderBins * kOrderWaves) s_cnt[t] = v - own + (wave ? s_wave[wave - 1] : 0);
   __syncthreads();
   if (bin >= 0) p.order_ws[blockIdx.x * kOrderBlock + s_cnt[bin * kOrderWaves + wave] + rank] = r;
 }
