@@ -18,11 +18,15 @@
 //    [64c + 16g, +16), c = 0..3, of region i's summary (16-byte loads: each
 //    instruction reads 64 contiguous bytes of 16 regions), converts them to
 //    bf16, and for every 16-column tile runs 8 v_mfma_f32_16x16x32_bf16 with
-//    the query columns (the same 64 dims per lane on both sides, so the dim
-//    order inside the MFMA is immaterial).  Products are exact, sums fp32.
-//  * Epilogue per tile: max(0, s_j * dot) * w, summed over a row's heads
-//    with lane shuffles, masked to -inf past the row's last region, stored as
-//    16 bytes per lane.  Regions past the request's last are never read.
+//    the query columns as the A rows and the regions as the B columns (the
+//    same 64 dims per lane on both sides, so the dim order inside the MFMA
+//    is immaterial).  Products are exact, sums fp32.
+//  * Epilogue per tile: a lane holds four consecutive columns (heads) of one
+//    region; max(0, s_j * dot) * w, summed over a row's heads in the lane
+//    and across lanes 16 and 32 apart (permlane swaps), masked to -inf past
+//    the row's last region, stored 4 bytes per lane (16 lanes: 64
+//    contiguous bytes of a row).  Regions past the request's last are never
+//    read.  The kernel is instantiated per head count (1..16).
 // The bytes are the summaries (+ scales) of each request's regions, the
 // queries, and the fp32 score matrix written.
 
@@ -61,24 +65,19 @@ __device__ __forceinline__ void e4m3x16_to_bf16(const u32x4 w, bf16x8& lo, bf16x
   hi = __builtin_bit_cast(bf16x8, u32x4{o[4], o[5], o[6], o[7]});
 }
 
-// x plus the value of another lane, moved by DPP (no LDS traffic).
-template <int kCtrl>
-__device__ __forceinline__ float dpp_fadd(float x) {
-  const int y = __builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, 0xF, 0xF, false);
-  return x + __int_as_float(y);
+// x plus x of the lane kDist (16 or 32) away, in every lane: the permlane
+// swap exchanges the two halves of each 32-lane (or the 64-lane) group
+// between its two operands, so with x in both the two results are x and the
+// partner's x in some order, and their sum is the same in both lanes.
+template <int kDist>
+__device__ __forceinline__ float add_across(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto r = kDist == 16 ? __builtin_amdgcn_permlane16_swap(u, u, false, false)
+                             : __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Sum of x over each aligned group of n lanes (n = 1, 2, 4, 8, 16) inside a
-// row of 16: quad permutes for the first two steps, then the half-row and
-// row mirrors (each pairs every lane with one of the other half).
-__device__ __forceinline__ float group_sum(float x, int n) {
-  if (n >= 2) x = dpp_fadd<0xB1>(x);   // quad_perm [1,0,3,2]
-  if (n >= 4) x = dpp_fadd<0x4E>(x);   // quad_perm [2,3,0,1]
-  if (n >= 8) x = dpp_fadd<0x141>(x);  // row_half_mirror
-  if (n >= 16) x = dpp_fadd<0x140>(x); // row_mirror
-  return x;
-}
-
+template <int kHeads>
 __global__ __launch_bounds__(kLgThreads) void logits_kernel(const LogitsParams p) {
   const int req = blockIdx.x;
   const int chunk = blockIdx.y;
@@ -197,29 +196,36 @@ __global__ __launch_bounds__(kLgThreads) void logits_kernel(const LogitsParams p
   }
   if (nt > 0) {
     // Everything a tile's epilogue needs beyond its accumulators is fixed for
-    // the workgroup or known now: each column's weight and row length (LDS),
-    // and every tile's summary offsets and region scales (from the lanes that
-    // resolved them).  Fetched once here, they keep LDS round trips out of
-    // the tile loop.
-    float wcol[kLgMaxCols / 16];
-    int lcol[kLgMaxCols / 16];
+    // the workgroup or known now: the weights of this lane's columns, the
+    // lengths of the rows it stores (LDS), and every tile's summary offsets
+    // and this lane's region scale (from the lanes that resolved them).
+    // Fetched once here, they keep LDS round trips out of the tile loop.
+    constexpr int kHpl = kHeads < 4 ? kHeads : 4;  // a row's heads within a lane
+    constexpr int kRpl = 4 / kHpl;                  // rows per lane and column tile
+    float wq[kLgMaxCols / 16][4];
+    int lrow[kLgMaxCols / 16][kRpl];
 #pragma unroll
     for (int ct = 0; ct < kLgMaxCols / 16; ++ct) {
-      const int col = 16 * ct + i16;
-      wcol[ct] = col < ncols ? s_w[col] : 0.f;
-      lcol[ct] = col < ncols ? s_len[col >> p.hshift] : 0;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int col = 16 * ct + 4 * g4 + v;
+        wq[ct][v] = col < ncols ? s_w[col] : 0.f;
+      }
+#pragma unroll
+      for (int q = 0; q < kRpl; ++q) {
+        const int col = 16 * ct + 4 * g4 + q * kHpl;
+        lrow[ct][q] = col < ncols ? s_len[col / kHeads] : 0;
+      }
     }
     int64_t toff[4];
-    float tsc[4][4];
+    float tsc[4];
 #pragma unroll
     for (int t = 1; t < 4; ++t) {
       const int j = j_begin + kLgTile * wave + kLgTile * kLgWaves * t + i16;
       toff[t] = __shfl(roff_l, j < j_live ? kLgTile * t + i16 : kLgTile * t);
     }
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) tsc[t][v] = __shfl(scale_l, kLgTile * t + 4 * g4 + v);
+    for (int t = 0; t < 4; ++t) tsc[t] = __shfl(scale_l, kLgTile * t + i16);
     toff[0] = 0;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -233,39 +239,40 @@ __global__ __launch_bounds__(kLgThreads) void logits_kernel(const LogitsParams p
 #pragma unroll
         for (int c = 0; c < 4; ++c) raw[c] = *reinterpret_cast<const u32x4*>(an + 64 * c);
       }
+      const int j = j0 + i16;  // this lane's region
 
 #pragma unroll
       for (int ct = 0; ct < kLgMaxCols / 16; ++ct) {
         if (ct >= ntiles) break;
+        // The query columns are the MFMA's A rows and the regions its B
+        // columns, so a lane ends up with four consecutive columns (heads)
+        // of one region: S[column 16 ct + 4 g4 + v][region j0 + i16].
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         const __bf16* bq = &s_q[ct][lane][0];
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
           const bf16x8 b = *reinterpret_cast<const bf16x8*>(bq + 8 * s);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], b, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b, a[s], acc, 0, 0, 0);
         }
-        // lane holds S[region j0 + 4 g4 + v][column 16 ct + i16]
-        const int col = 16 * ct + i16;
         float x[4];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) x[v] = fmaxf(0.f, tsc[t][v] * acc[v]) * wcol[ct];
-        // sum over the row's heads: `heads` consecutive lanes of the 16-lane group
+        for (int v = 0; v < 4; ++v) x[v] = fmaxf(0.f, tsc[t] * acc[v]) * wq[ct][v];
+        // a row's heads: kHpl in the lane, then the lanes 16 and 32 apart
+        float y[kRpl];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) x[v] = group_sum(x[v], p.heads);
-        if (col < ncols && (col & (p.heads - 1)) == 0) {
-          const int rowi = col >> p.hshift;
-          const int len = lcol[ct];
-          const int jb = j0 + 4 * g4;
-          float* dst = p.out + (int64_t)(r0 + rowi) * p.ors + jb;
-          float y[4];
+        for (int q = 0; q < kRpl; ++q) {
+          y[q] = x[q * kHpl];
 #pragma unroll
-          for (int v = 0; v < 4; ++v) y[v] = jb + v < len ? x[v] : -INFINITY;
-          if (jb + 3 < p.S) {
-            *reinterpret_cast<float4*>(dst) = make_float4(y[0], y[1], y[2], y[3]);
-          } else {
+          for (int v = 1; v < kHpl; ++v) y[q] += x[q * kHpl + v];
+        }
+        if (kHeads >= 8) y[0] = add_across<16>(y[0]);
+        if (kHeads >= 16) y[0] = add_across<32>(y[0]);
+        if (j < p.S && (kHeads < 8 || ((4 * g4) & (kHeads - 1)) == 0)) {
 #pragma unroll
-            for (int v = 0; v < 4; ++v)
-              if (jb + v < p.S) dst[v] = y[v];
+          for (int q = 0; q < kRpl; ++q) {
+            const int col = 16 * ct + 4 * g4 + q * kHpl;
+            if (col < ncols)
+              p.out[(int64_t)(r0 + col / kHeads) * p.ors + j] = j < lrow[ct][q] ? y[q] : -INFINITY;
           }
         }
       }
@@ -277,8 +284,14 @@ __global__ __launch_bounds__(kLgThreads) void logits_kernel(const LogitsParams p
 
 hipError_t launch_logits(const LogitsParams& p, hipStream_t stream) {
   const unsigned chunks = (unsigned)((p.S + kLgChunk - 1) / kLgChunk);
-  hipLaunchKernelGGL(logits_kernel, dim3((unsigned)(p.rows / p.rows_per_req), chunks),
-                     dim3(kLgThreads), 0, stream, p);
+  const dim3 grid((unsigned)(p.rows / p.rows_per_req), chunks);
+  switch (p.heads) {
+    case 1: hipLaunchKernelGGL(logits_kernel<1>, grid, dim3(kLgThreads), 0, stream, p); break;
+    case 2: hipLaunchKernelGGL(logits_kernel<2>, grid, dim3(kLgThreads), 0, stream, p); break;
+    case 4: hipLaunchKernelGGL(logits_kernel<4>, grid, dim3(kLgThreads), 0, stream, p); break;
+    case 8: hipLaunchKernelGGL(logits_kernel<8>, grid, dim3(kLgThreads), 0, stream, p); break;
+    default: hipLaunchKernelGGL(logits_kernel<16>, grid, dim3(kLgThreads), 0, stream, p); break;
+  }
   return hipGetLastError();
 }
 
