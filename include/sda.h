@@ -34,7 +34,7 @@
 extern "C" {
 #endif
 
-#define SDA_ABI_VERSION 7
+#define SDA_ABI_VERSION 8
 #define SDA_HEAD_DIM 192     /* query / key / value head dim (fixed) */
 #define SDA_KV_ROW 384       /* one cache token row: K[0:192] then V[192:384] */
 #define SDA_MAX_HEADS 16     /* GQA-packed query heads per KV group */
@@ -397,8 +397,13 @@ int sda_select_regions(const sda_select_args *args, hipStream_t stream);
  *  weights       fp32 [rows, heads], unit head stride.
  *  summaries     e4m3 [pages, regions_per_page, 256]; 16-byte aligned.
  *  summary_scales fp32 [pages, regions_per_page], unit region stride.
- *  block_table   int32 [requests, cols], unit inner stride; only the columns
- *                of each request's scored regions are read.
+ *  block_table   int32 [requests, cols], unit inner stride.
+ *  table_cols    cols of block_table (>= 0, and <= table_row_stride when
+ *                positive), or 0 if unknown.  Every scored region's column
+ *                lies below cols.  With cols given, a workgroup requests its
+ *                chunk's table entries (columns below cols) together with
+ *                the positions, one dependent round trip fewer; with 0 only
+ *                the columns of each request's scored regions are read.
  *  positions     int32 [rows].
  *  scores        fp32 [rows, S] output; 16-byte aligned, row stride % 4 == 0.
  *  current, topk_lengths  optional int32 [rows] outputs for the selection:
@@ -425,6 +430,7 @@ typedef struct sda_logits_args {
   int64_t scores_row_stride;
   int32_t *current;
   int32_t *topk_lengths;
+  int32_t table_cols;
 } sda_logits_args;
 
 /*

@@ -29,7 +29,7 @@ SDA_KERNEL_ORDER = 1
 SDA_KERNEL_SPLIT = 2
 SDA_KERNEL_ROW_STREAM = 4
 SDA_KERNEL_COMBINE = 8
-ABI_VERSION = 7
+ABI_VERSION = 8
 HEAD_DIM = 192
 
 
@@ -112,6 +112,7 @@ class LogitsArgs(ctypes.Structure):
         ("positions", ctypes.c_void_p),
         ("scores", ctypes.c_void_p), ("scores_row_stride", ctypes.c_int64),
         ("current", ctypes.c_void_p), ("topk_lengths", ctypes.c_void_p),
+        ("table_cols", ctypes.c_int32),
     ]
 
 
@@ -564,9 +565,11 @@ def sda_select_regions_raw(args: SelectArgs, stream_handle=None) -> int:
 
 def make_logits_args(query, weights, summaries, summary_scales, block_table, positions, scores,
                      *, groups, query_len=1, region_tokens=8, current=None,
-                     topk_lengths=None) -> LogitsArgs:
+                     topk_lengths=None, table_cols=None) -> LogitsArgs:
     """Fill ``sda_logits_args`` from tensors.  e4m3 tensors are uint8 (or
-    float8_e4m3fn) storage; their strides become bytes."""
+    float8_e4m3fn) storage; their strides become bytes.  ``table_cols``:
+    block_table's column count (None: its shape; 0: unknown, so only the
+    scored regions' columns are read)."""
     a = LogitsArgs()
     a.rows, a.heads, a.groups, a.query_len = query.shape[0], query.shape[1], int(groups), \
         int(query_len)
@@ -582,6 +585,7 @@ def make_logits_args(query, weights, summaries, summary_scales, block_table, pos
     a.ss_page_stride = summary_scales.stride(0)
     a.block_table = _ptr(block_table)
     a.table_row_stride = block_table.stride(0)
+    a.table_cols = block_table.shape[1] if table_cols is None else int(table_cols)
     a.positions = _ptr(positions)
     a.scores = _ptr(scores)
     a.scores_row_stride = scores.stride(0)
@@ -592,12 +596,12 @@ def make_logits_args(query, weights, summaries, summary_scales, block_table, pos
 
 def sda_indexer_logits(query, weights, summaries, summary_scales, block_table, positions, *,
                        groups, num_regions, query_len=1, region_tokens=8, scores=None,
-                       current=None, topk_lengths=None, stream=None):
+                       current=None, topk_lengths=None, table_cols=None, stream=None):
     """Enqueue ``sda_indexer_logits``; returns the fp32 [rows, num_regions] scores.
 
     Names follow ``decode_logits`` on the page "vllm.models.step5.nvidia.
     flashinfer_sparse" (query, weights, the per-page region summaries with
-    their scales, table, positions)."""
+    their scales, table, positions).  ``table_cols``: as in make_logits_args."""
     e4 = (torch.uint8, torch.float8_e4m3fn)
     if query.dtype not in e4 or query.dim() != 3 or query.shape[2] != 256 or query.stride(2) != 1:
         raise SdaError(SDA_ERR_INVALID, "query must be e4m3 [rows, heads, 256]")
@@ -632,7 +636,7 @@ def sda_indexer_logits(query, weights, summaries, summary_scales, block_table, p
                  topk_lengths=topk_lengths)
     a = make_logits_args(query, weights, summaries, summary_scales, block_table, positions,
                          scores, groups=groups, query_len=query_len, region_tokens=region_tokens,
-                         current=current, topk_lengths=topk_lengths)
+                         current=current, topk_lengths=topk_lengths, table_cols=table_cols)
     if stream is None:
         stream = torch.cuda.current_stream(query.device)
     handle = ctypes.c_void_p(stream.cuda_stream)

@@ -385,7 +385,8 @@ int sda_indexer_logits(const sda_logits_args* a, hipStream_t stream) {
   if (!a) return SDA_ERR_INVALID;
   if (a->rows < 0 || a->heads < 1 || a->heads > SDA_MAX_HEADS || (a->heads & (a->heads - 1)) ||
       a->groups < 1 || a->query_len < 1 || a->regions_per_page < 1 || a->num_regions < 0 ||
-      a->region_tokens < 1)
+      a->region_tokens < 1 || a->table_cols < 0 ||
+      (a->table_cols > 0 && a->table_row_stride < a->table_cols))
     return SDA_ERR_INVALID;
   const int64_t rpr = (int64_t)a->groups * a->query_len;
   if (a->rows % rpr) return SDA_ERR_INVALID;
@@ -417,6 +418,7 @@ int sda_indexer_logits(const sda_logits_args* a, hipStream_t stream) {
   p.scps = a->ss_page_stride;
   p.table = a->block_table;
   p.trs = a->table_row_stride;
+  p.tcols = a->table_cols;
   p.positions = a->positions;
   p.out = a->scores;
   p.ors = a->scores_row_stride;

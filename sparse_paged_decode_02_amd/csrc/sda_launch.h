@@ -98,6 +98,9 @@ struct LogitsParams {
   int32_t* current;           // [rows] or null
   int32_t* lengths;           // [rows] or null
   int32_t rows, heads, hshift, rows_per_req, rpb, S, rt;
+  // Last, so that the fields above keep their kernel-argument offsets (the
+  // setup's scalar loads of them batch as they did before this field).
+  int32_t tcols;              // table columns (0: unknown, read scored columns only)
 };
 
 hipError_t launch_logits(const LogitsParams& p, hipStream_t stream);

@@ -77,7 +77,8 @@ __device__ __forceinline__ float add_across(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int kHeads>
+// kEarly: the table's column count is known (p.tcols > 0).
+template <int kHeads, bool kEarly>
 __global__ __launch_bounds__(kLgThreads) void logits_kernel(const LogitsParams p) {
   const int req = blockIdx.x;
   const int chunk = blockIdx.y;
@@ -110,6 +111,24 @@ __global__ __launch_bounds__(kLgThreads) void logits_kernel(const LogitsParams p
   float wv = 0.f;
   if (tid < ncols) wv = p.w[(int64_t)(r0 + (tid >> p.hshift)) * p.wrs + (tid & (p.heads - 1))];
 
+  // With the table's column count known, each lane requests the block-table
+  // entry of one region of its wave's tiles now, beside the positions (an
+  // entry past the scored regions is read but not used); otherwise only
+  // once the positions show which regions are scored.
+  const int j_begin = chunk * kLgChunk;
+  const int j_end = min(p.S, j_begin + kLgChunk);
+  // This wave's tiles start at j_begin + 16 wave + 64 t (t = 0..3).  Lane l
+  // resolves region j_begin + 16 wave + 64 (l >> 4) + (l & 15): its summary
+  // row offset and scale, shared with the MFMA lanes by shuffles, so the
+  // tile loop issues summary loads only.
+  const int jl = j_begin + kLgTile * wave + kLgTile * kLgWaves * (lane >> 4) + (lane & 15);
+  int pg_raw = 0;
+  if (kEarly) {
+    // regions whose column lies in the table: below tcols * rpb
+    const int j_tab = (int)min((int64_t)j_end, (int64_t)p.tcols * p.rpb);
+    if (jl < j_tab) pg_raw = p.table[(int64_t)req * p.trs + jl / p.rpb];
+  }
+
   // Region count of each row (lane t < rpr: row t) and the request's maximum
   // (every wave reduces it itself).
   int lenv = 0, cur = -1;
@@ -125,17 +144,11 @@ __global__ __launch_bounds__(kLgThreads) void logits_kernel(const LogitsParams p
   // covers them, rather than behind the block-table loads below.
   __asm__ __volatile__("" : "+v"(wv), "+v"(qraw[0]), "+v"(qraw[1]), "+v"(qraw[2]), "+v"(qraw[3]));
 
-  const int j_begin = chunk * kLgChunk;
-  const int j_end = min(p.S, j_begin + kLgChunk);
   const int j_live = min(j_end, max_len);
-  // This wave's tiles start at j_begin + 16 wave + 64 t (t = 0..3).  Lane l
-  // resolves region j_begin + 16 wave + 64 (l >> 4) + (l & 15): its summary
-  // row offset and scale, shared with the MFMA lanes by shuffles, so the
-  // tile loop issues summary loads only.
-  const int jl = j_begin + kLgTile * wave + kLgTile * kLgWaves * (lane >> 4) + (lane & 15);
-  int64_t pg = 0;
-  if (jl < j_live) pg = p.table[(int64_t)req * p.trs + jl / p.rpb];
-  // The query conversion below overlaps the block-table round trip.
+  if (!kEarly && jl < j_live) pg_raw = p.table[(int64_t)req * p.trs + jl / p.rpb];
+  const int64_t pg = jl < j_live ? pg_raw : 0;
+  // The query conversion below overlaps the block-table round trip when the
+  // entries are requested only now.
   // Query columns converted to bf16 in the lane order of the MFMA B
   // operand: entry (tile, lane) holds column 16 tile + (lane & 15), dims
   // [64 c + 16 (lane >> 4), +16) for c = 0..3, the dims its A lanes hold.
@@ -280,18 +293,37 @@ __global__ __launch_bounds__(kLgThreads) void logits_kernel(const LogitsParams p
   }
 }
 
+template <bool kEarly>
+void launch_heads(const LogitsParams& p, dim3 grid, hipStream_t stream) {
+  const dim3 block(kLgThreads);
+  switch (p.heads) {
+    case 1:
+      hipLaunchKernelGGL((logits_kernel<1, kEarly>), grid, block, 0, stream, p);
+      break;
+    case 2:
+      hipLaunchKernelGGL((logits_kernel<2, kEarly>), grid, block, 0, stream, p);
+      break;
+    case 4:
+      hipLaunchKernelGGL((logits_kernel<4, kEarly>), grid, block, 0, stream, p);
+      break;
+    case 8:
+      hipLaunchKernelGGL((logits_kernel<8, kEarly>), grid, block, 0, stream, p);
+      break;
+    default:  // 16 (the call validates a power of two <= 16)
+      hipLaunchKernelGGL((logits_kernel<16, kEarly>), grid, block, 0, stream, p);
+      break;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_logits(const LogitsParams& p, hipStream_t stream) {
   const unsigned chunks = (unsigned)((p.S + kLgChunk - 1) / kLgChunk);
   const dim3 grid((unsigned)(p.rows / p.rows_per_req), chunks);
-  switch (p.heads) {
-    case 1: hipLaunchKernelGGL(logits_kernel<1>, grid, dim3(kLgThreads), 0, stream, p); break;
-    case 2: hipLaunchKernelGGL(logits_kernel<2>, grid, dim3(kLgThreads), 0, stream, p); break;
-    case 4: hipLaunchKernelGGL(logits_kernel<4>, grid, dim3(kLgThreads), 0, stream, p); break;
-    case 8: hipLaunchKernelGGL(logits_kernel<8>, grid, dim3(kLgThreads), 0, stream, p); break;
-    default: hipLaunchKernelGGL(logits_kernel<16>, grid, dim3(kLgThreads), 0, stream, p); break;
-  }
+  if (p.tcols > 0)
+    launch_heads<true>(p, grid, stream);
+  else
+    launch_heads<false>(p, grid, stream);
   return hipGetLastError();
 }
 

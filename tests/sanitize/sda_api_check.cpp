@@ -372,11 +372,18 @@ static void select_and_logits_cases() {
     a.ss_page_stride = a.regions_per_page;
     a.block_table = (const int32_t*)dev(size_t(4) << 30);
     a.table_row_stride = 512;
+    a.table_cols = (int)pick(-1, 600);
     a.positions = (const int32_t*)dev(size_t(5) << 30);
     a.scores = (float*)dev(size_t(6) << 30);
     a.scores_row_stride = a.num_regions + (int64_t)pick(0, 3);
+    g_last_logits = sda::LogitsParams{};
     const int rc = sda_indexer_logits(&a, nullptr);
     CHECK(valid_status(rc), "logits status %d", rc);
+    if (a.table_cols < 0 || a.table_cols > a.table_row_stride)
+      CHECK(rc == SDA_ERR_INVALID, "table_cols %d accepted", a.table_cols);
+    if (rc == SDA_OK && g_last_logits.table)
+      CHECK(g_last_logits.tcols == a.table_cols, "table_cols %d passed as %d", a.table_cols,
+            g_last_logits.tcols);
   }
 }
 

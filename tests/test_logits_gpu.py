@@ -29,7 +29,7 @@ def _say(msg):
     sys.stderr.flush()
 
 
-def run(inp, scores=None, query=None, label=""):
+def run(inp, scores=None, query=None, label="", table=None, table_cols=None):
     w = inp.w
     rows = w.rows
     cur = torch.full((rows,), -7, dtype=torch.int32, device=DEV)
@@ -37,10 +37,11 @@ def run(inp, scores=None, query=None, label=""):
     _say("sda_indexer_logits %s rows=%d heads=%d G=%d qlen=%d rpb=%d S=%d" % (
         label or w.name, rows, w.heads, w.groups, w.query_len, w.rpb, w.num_regions))
     out = B.sda_indexer_logits(inp.query if query is None else query, inp.weights, inp.summaries,
-                               inp.scales, inp.block_table, inp.positions, groups=w.groups,
+                               inp.scales, inp.block_table if table is None else table,
+                               inp.positions, groups=w.groups,
                                num_regions=w.num_regions, query_len=w.query_len,
                                region_tokens=w.region_tokens, scores=scores, current=cur,
-                               topk_lengths=lens)
+                               topk_lengths=lens, table_cols=table_cols)
     torch.cuda.synchronize()
     return out, cur, lens
 
@@ -193,3 +194,32 @@ def test_chain_logits_select_decode():
     ref = oracle.decode(hp, threads=16)
     err = np.abs(out.float().cpu().numpy() - ref)
     assert err.max() <= 1.5e-2 and err.mean() <= 1e-3
+
+
+@pytest.mark.parametrize("heads,groups,qlen", [(8, 4, 1), (8, 4, 2), (16, 2, 1)])
+def test_table_cols_given_or_not(heads, groups, qlen):
+    # With the table's column count a workgroup requests its table entries
+    # beside the positions; with 0 only after them.  The same entries are
+    # used either way: the scores must agree bit for bit.
+    w = case(60 + heads + groups + qlen, requests=5, heads=heads, groups=groups, query_len=qlen,
+             block=64, pages_per_req=48, pos_lo=-1, pos_hi=48 * 64 - qlen)
+    inp = gen.make_logits_inputs(w, device=DEV)
+    early, cur_e, lens_e = run(inp, label="table cols given")
+    late, cur_l, lens_l = run(inp, label="table cols 0", table_cols=0)
+    assert torch.equal(early.view(torch.int32), late.view(torch.int32))
+    assert torch.equal(cur_e, cur_l) and torch.equal(lens_e, lens_l)
+    check(inp, early, cur_e, lens_e, what="table cols h%d g%d q%d" % (heads, groups, qlen))
+
+
+def test_table_narrower_than_the_score_columns():
+    # A table with only the columns the scored regions need (21 of the 40
+    # pages that the 320 score columns span): entries past them are never
+    # requested, early or late.
+    w = case(71, requests=4, heads=8, groups=4, block=64, pages_per_req=40, pos_lo=600,
+             pos_hi=21 * 64 - 1)
+    inp = gen.make_logits_inputs(w, device=DEV)
+    narrow = inp.block_table[:, :21].contiguous()
+    for cols in (None, 0):
+        got, cur, lens = run(inp, label="narrow table cols=%s" % cols, table=narrow,
+                             table_cols=cols)
+        check(inp, got, cur, lens, what="narrow table cols=%s" % cols)
