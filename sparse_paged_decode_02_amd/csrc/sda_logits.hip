@@ -94,22 +94,27 @@ __global__ __launch_bounds__(kLgThreads) void logits_kernel(const LogitsParams p
   const int ntiles = (ncols + 15) / 16;
 
   // Loads that depend on nothing else go first: the positions, the query
-  // columns (entry = thread: column tile tid >> 6, lane tid & 63) and the
-  // head weights.
+  // columns (entry = thread: column tile tid >> 6, lane tid & 63), the head
+  // weights and (below) the block-table entries.  Each is issued by every
+  // lane at an index clamped into range and masked afterwards: with no branch
+  // around them they all go out in one round trip, behind one batch of
+  // kernel-argument loads.
   static_assert(kLgThreads == (kLgMaxCols / 16) * 64, "one query entry per thread");
   const int qt = tid >> 6, ql = tid & 63;
   const int qcol = 16 * qt + (ql & 15);
-  u32x4 qraw[4] = {};
-  if (qt < ntiles && qcol < ncols) {
-    const int row = r0 + (qcol >> p.hshift);
-    const int h = qcol & (p.heads - 1);
+  const bool qvalid = qt < ntiles && qcol < ncols;
+  u32x4 qraw[4];
+  {
+    const int qc = qvalid ? qcol : 0;
+    const int row = r0 + (qc >> p.hshift);
+    const int h = qc & (p.heads - 1);
     const uint8_t* src = p.q + (int64_t)row * p.qrs + (int64_t)h * p.qhs + 16 * (ql >> 4);
 #pragma unroll
     for (int c = 0; c < 4; ++c) qraw[c] = *reinterpret_cast<const u32x4*>(src + 64 * c);
   }
   static_assert(kLgMaxCols <= kLgThreads, "one weight per thread");
-  float wv = 0.f;
-  if (tid < ncols) wv = p.w[(int64_t)(r0 + (tid >> p.hshift)) * p.wrs + (tid & (p.heads - 1))];
+  const int wc = tid < ncols ? tid : 0;
+  float wv = p.w[(int64_t)(r0 + (wc >> p.hshift)) * p.wrs + (wc & (p.heads - 1))];
 
   // With the table's column count known, each lane requests the block-table
   // entry of one region of its wave's tiles now, beside the positions (an
@@ -124,16 +129,16 @@ __global__ __launch_bounds__(kLgThreads) void logits_kernel(const LogitsParams p
   const int jl = j_begin + kLgTile * wave + kLgTile * kLgWaves * (lane >> 4) + (lane & 15);
   int pg_raw = 0;
   if (kEarly) {
-    // regions whose column lies in the table: below tcols * rpb
+    // regions whose column lies in the table (below tcols * rpb >= 1)
     const int j_tab = (int)min((int64_t)j_end, (int64_t)p.tcols * p.rpb);
-    if (jl < j_tab) pg_raw = p.table[(int64_t)req * p.trs + jl / p.rpb];
+    pg_raw = p.table[(int64_t)req * p.trs + min(jl, j_tab - 1) / p.rpb];
   }
 
   // Region count of each row (lane t < rpr: row t) and the request's maximum
   // (every wave reduces it itself).
+  const int pos = p.positions[r0 + (lane < rpr ? lane : 0)];
   int lenv = 0, cur = -1;
   if (lane < rpr) {
-    const int pos = p.positions[r0 + lane];
     cur = pos < 0 ? -1 : pos / p.rt;
     lenv = cur + 1 < p.S ? cur + 1 : p.S;
     if (wave == 0) s_len[lane] = lenv;
@@ -143,6 +148,8 @@ __global__ __launch_bounds__(kLgThreads) void logits_kernel(const LogitsParams p
   // have landed: consume them here, where the wait for the positions
   // covers them, rather than behind the block-table loads below.
   __asm__ __volatile__("" : "+v"(wv), "+v"(qraw[0]), "+v"(qraw[1]), "+v"(qraw[2]), "+v"(qraw[3]));
+  if (!qvalid) qraw[0] = qraw[1] = qraw[2] = qraw[3] = u32x4{0u, 0u, 0u, 0u};  // absent columns
+  if (tid >= ncols) wv = 0.f;
 
   const int j_live = min(j_end, max_len);
   if (!kEarly && jl < j_live) pg_raw = p.table[(int64_t)req * p.trs + jl / p.rpb];
