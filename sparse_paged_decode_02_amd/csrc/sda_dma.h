@@ -118,6 +118,67 @@ __device__ __forceinline__ void dma_chunk_sbase2(const uint8_t* base_a, const ui
                        : "memory");
 }
 
+// Four-region chunk (FP8, 8-token regions).  K DMA j covers token rows
+// (64j + lane) / 12: DMAs 0, 2, 3 and 5 lie inside regions 0, 1, 2 and 3 and
+// take that region's uniform base; DMAs 1 and 4 cover rows 5..10 and 21..26,
+// whose lanes 0..31 read region 0 / 2 and lanes 32..63 region 1 / 3, so they
+// take per-lane 64-bit addresses.  V DMA j covers the same rows.  The K/V
+// order and LDS placement are SDA_CHUNK_ASM_KV's.
+#define SDA_CHUNK_ASM_QUAD(suf)                                                               \
+  "s_mov_b32 %[sv], m0\n\t"                                                                   \
+  "s_mov_b32 m0, %[st]\n\t" SDA_LDDMA("k0", "%[b0]", suf) SDA_M0("0x1800")                    \
+      SDA_LDDMA("v0", "%[b0]", suf) SDA_M0("0x400") SDA_LDDMA("k1", "off", suf)                \
+          SDA_M0("0x1c00") SDA_LDDMA("v1", "off", suf) SDA_M0("0x800")                         \
+              SDA_LDDMA("k2", "%[b1]", suf) SDA_M0("0x2000") SDA_LDDMA("v2", "%[b1]", suf)     \
+                  SDA_M0("0xc00") SDA_LDDMA("k3", "%[b2]", suf) SDA_M0("0x2400")               \
+                      SDA_LDDMA("v3", "%[b2]", suf) SDA_M0("0x1000")                           \
+                          SDA_LDDMA("k4", "off", suf) SDA_M0("0x2800")                         \
+                              SDA_LDDMA("v4", "off", suf) SDA_M0("0x1400")                     \
+                                  SDA_LDDMA("k5", "%[b3]", suf) SDA_M0("0x2c00")               \
+                                      SDA_LDDMA("v5", "%[b3]", suf) "s_mov_b32 m0, %[sv]"
+
+// Token row of K DMA j, lane l, in an FP8 chunk (12 pieces per row).
+constexpr int fp8_dma_row(int j, int l) { return (64 * j + l) / Cfg<true>::kPieces; }
+// The region (of four 8-row regions) that every lane of DMA j reads, or -1
+// when the DMA's lanes span two regions.
+constexpr int quad_region(int j) {
+  int q = fp8_dma_row(j, 0) / 8;
+  for (int l = 1; l < 64; ++l)
+    if (fp8_dma_row(j, l) / 8 != q) return -1;
+  return q;
+}
+// DMA j spans regions q and q + 1, split exactly at lane 32.
+constexpr bool quad_split_at_32(int j) {
+  for (int l = 0; l < 64; ++l)
+    if (fp8_dma_row(j, l) / 8 != fp8_dma_row(j, 0) / 8 + (l >= 32 ? 1 : 0)) return false;
+  return true;
+}
+static_assert(quad_region(0) == (0 + 1) / 2 && quad_region(2) == (2 + 1) / 2 &&
+                  quad_region(3) == (3 + 1) / 2 && quad_region(5) == (5 + 1) / 2,
+              "SDA_CHUNK_ASM_QUAD: DMAs 0, 2, 3, 5 each inside one region");
+static_assert(quad_split_at_32(1) && fp8_dma_row(1, 0) / 8 == 0 && quad_split_at_32(4) &&
+                  fp8_dma_row(4, 0) / 8 == 2,
+              "SDA_CHUNK_ASM_QUAD: DMAs 1 and 4 split at lane 32");
+
+// ko/vo: 32-bit lane offsets of DMAs 0, 2, 3, 5 from their region's base;
+// k1/v1, k4/v4: the lane's 64-bit addresses for DMAs 1 and 4.
+__device__ __forceinline__ void dma_chunk_quad(const uint8_t* b0, const uint8_t* b1,
+                                               const uint8_t* b2, const uint8_t* b3,
+                                               uint32_t stage, const uint32_t (&ko)[6],
+                                               const uint32_t (&vo)[6], const uint8_t* k1,
+                                               const uint8_t* v1, const uint8_t* k4,
+                                               const uint8_t* v4) {
+  uint32_t saved;
+  __asm__ __volatile__(SDA_CHUNK_ASM_QUAD(" nt")
+                       : [sv] "=&s"(saved)
+                       : [st] "s"(stage), [b0] "s"(b0), [b1] "s"(b1), [b2] "s"(b2),
+                         [b3] "s"(b3), [k0] "v"(ko[0]), [k1] "v"(k1), [k2] "v"(ko[2]),
+                         [k3] "v"(ko[3]), [k4] "v"(k4), [k5] "v"(ko[5]), [v0] "v"(vo[0]),
+                         [v1] "v"(v1), [v2] "v"(vo[2]), [v3] "v"(vo[3]), [v4] "v"(v4),
+                         [v5] "v"(vo[5])
+                       : "memory");
+}
+
 // dma_chunk_sbase: one uniform 64-bit base (SGPRs) plus 32-bit per-lane
 // byte offsets (chunks inside one region or one page).
 template <bool kFp8>

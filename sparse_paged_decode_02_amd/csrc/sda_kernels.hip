@@ -91,6 +91,7 @@ enum Addr : int {
   kUniform = 1,  // region list; every chunk lies inside one region
   kWindow = 2,   // a contiguous sliding window of tokens, 16-token chunks
   kPair = 3,     // region list of 8-token regions, bf16: a chunk is two regions
+  kQuad = 4,     // region list of 8-token regions, FP8: a chunk is four regions
 };
 
 
@@ -203,6 +204,54 @@ __device__ __forceinline__ uint32_t issue_chunk(const Params& p, int c, int nreg
       vo[j] = roff + ld.voff[j];
     }
     dma_chunk_sbase2(base0, base1, st, ko, vo);
+  } else if (kAddr == kQuad) {
+    // 8-token regions (FP8): chunk c is list entries 4c .. 4c + 3, token rows
+    // 8q .. 8q + 7 of the chunk from entry 4c + q.  Rows past an entry's
+    // visible count load its token 0, and entries past the list load token 0
+    // of entry 4c (visible, finite, weight 0).  DMAs 0, 2, 3, 5 take one
+    // region's uniform base; DMAs 1 and 4 straddle two regions at lane 32
+    // (SDA_CHUNK_ASM_QUAD) and take per-lane 64-bit addresses.
+    static_assert(kFp8 || kAddr != kQuad, "quad chunks are FP8");
+    const int i16 = lane & 15;
+    const int k0 = 4 * c;
+    // Entry k0 + q's uniform base and visible count (named values, not arrays:
+    // an array of pointers here was kept in scratch memory).
+    auto entry_base = [&](int q) {
+      return uniform_ptr(p.cache + s_base[k0 + q < nreg ? k0 + q : k0] * C::kEsz);
+    };
+    auto entry_n = [&](int q) {
+      return k0 + q < nreg ? __builtin_amdgcn_readfirstlane(s_n[k0 + q]) : 0;
+    };
+    const uint8_t* const b0 = entry_base(0);
+    const uint8_t* const b1 = entry_base(1);
+    const uint8_t* const b2 = entry_base(2);
+    const uint8_t* const b3 = entry_base(3);
+    const int n0 = entry_n(0), n1 = entry_n(1), n2 = entry_n(2), n3 = entry_n(3);
+    // slot 16t + i16 is row i16 & 7 of entry 2t + (i16 >> 3)
+    const int r7 = i16 & 7;
+    vbits = (r7 < (i16 < 8 ? n0 : n1) ? 1u : 0u) | (r7 < (i16 < 8 ? n2 : n3) ? 2u : 0u);
+    auto roff = [&](int j, int n) {
+      const int r8 = ld.row[j] & 7;
+      return r8 < n ? (uint32_t)r8 * cts_bytes : 0u;
+    };
+    uint32_t ko[6], vo[6];
+    // DMAs 0, 2, 3, 5: entries 0, 1, 2, 3 (quad_region)
+    const uint32_t o0 = roff(0, n0), o2 = roff(2, n1), o3 = roff(3, n2), o5 = roff(5, n3);
+    ko[0] = o0 + ld.koff[0];
+    vo[0] = o0 + ld.voff[0];
+    ko[2] = o2 + ld.koff[2];
+    vo[2] = o2 + ld.voff[2];
+    ko[3] = o3 + ld.koff[3];
+    vo[3] = o3 + ld.voff[3];
+    ko[5] = o5 + ld.koff[5];
+    vo[5] = o5 + ld.voff[5];
+    ko[1] = vo[1] = ko[4] = vo[4] = 0;  // unused: DMAs 1 and 4 take 64-bit addresses
+    // DMAs 1 and 4: lanes 0..31 read entry 0 / 2, lanes 32..63 entry 1 / 3
+    const bool hi = lane >= 32;
+    const uint8_t* const l1 = (hi ? b1 : b0) + roff(1, hi ? n1 : n0);
+    const uint8_t* const l4 = (hi ? b3 : b2) + roff(4, hi ? n3 : n2);
+    dma_chunk_quad(b0, b1, b2, b3, st, ko, vo, l1 + ld.koff[1], l1 + ld.voff[1],
+                   l4 + ld.koff[4], l4 + ld.voff[4]);
   } else if (kAddr == kUniform) {
     const int i16 = lane & 15;
     // The chunk lies inside one region: uniform base, 32-bit lane offsets.
@@ -1343,7 +1392,13 @@ const int32_t* launch_order(const Params& p, hipStream_t stream) {
   const int64_t max_tokens = (int64_t)p.R * p.rt;
   const dim3 bin_grid((unsigned)((p.rows + 3) / 4));  // one wave per row
   static_assert(kMaxRegions <= 64 * 32, "at most 32 region-id loads per lane");
-  if (p.R <= 64 * 8)
+  if (p.R <= 64)
+    hipLaunchKernelGGL(bin_kernel<1>, bin_grid, dim3(256), 0, stream, p, max_tokens, bins);
+  else if (p.R <= 64 * 2)
+    hipLaunchKernelGGL(bin_kernel<2>, bin_grid, dim3(256), 0, stream, p, max_tokens, bins);
+  else if (p.R <= 64 * 4)
+    hipLaunchKernelGGL(bin_kernel<4>, bin_grid, dim3(256), 0, stream, p, max_tokens, bins);
+  else if (p.R <= 64 * 8)
     hipLaunchKernelGGL(bin_kernel<8>, bin_grid, dim3(256), 0, stream, p, max_tokens, bins);
   else if (p.R <= 64 * 16)
     hipLaunchKernelGGL(bin_kernel<16>, bin_grid, dim3(256), 0, stream, p, max_tokens, bins);
@@ -1370,8 +1425,8 @@ void launch_region_list(const Params& p, hipStream_t stream) {
   const unsigned wgs = (unsigned)p.rows;
   if (p.rt % Cfg<kFp8>::kTok == 0)
     launch_split<kFp8, kFused, kUniform>(p, wgs, stream);
-  else if (!kFp8 && p.rt == 8)
-    launch_split<kFp8, kFused, kFp8 ? kGeneral : kPair>(p, wgs, stream);
+  else if (p.rt == 8)
+    launch_split<kFp8, kFused, kFp8 ? kQuad : kPair>(p, wgs, stream);
   else
     launch_split<kFp8, kFused, kGeneral>(p, wgs, stream);
 }
@@ -1400,8 +1455,8 @@ template <bool kFp8>
 void launch_row_stream(const Params& p, hipStream_t stream) {
   if (p.rt % Cfg<kFp8>::kTok == 0)
     launch_row_stream_addr<kFp8, kUniform>(p, stream);
-  else if (!kFp8 && p.rt == 8)
-    launch_row_stream_addr<kFp8, kFp8 ? kGeneral : kPair>(p, stream);
+  else if (p.rt == 8)
+    launch_row_stream_addr<kFp8, kFp8 ? kQuad : kPair>(p, stream);
   else
     launch_row_stream_addr<kFp8, kGeneral>(p, stream);
 }

@@ -4,9 +4,9 @@
 // the workgroup's concatenated token rows goes to wave c % waves, its 12
 // LDS-DMAs are issued while the previous chunk is read back, and the wait is
 // the split kernel's vmcnt.  Chunks inside one block take a scalar base plus
-// 32-bit lane offsets, bf16 blocks of 8 tokens pair up under two scalar
-// bases, and anything else uses per-lane 64-bit addresses, as in the split
-// kernel.  Rows past the end of a workgroup's list load its first token row
+// 32-bit lane offsets, blocks of 8 tokens pair up (bf16) or go four to a
+// chunk (FP8) under scalar bases, and anything else uses per-lane 64-bit
+// addresses, as in the split kernel.  Rows past the end of a workgroup's list load its first token row
 // (the split kernel's masked rows load a visible row of their region).
 // The library also holds a VALU issue-rate probe (sda_probe_valu): waves of
 // independent instructions of one kind, timed to give the SIMD cycles a
@@ -33,7 +33,7 @@ struct ProbeParams {
   int32_t tpb;  // token rows per block
 };
 
-enum ProbeAddr : int { kProbeGeneral = 0, kProbeUniform = 1, kProbePair = 3 };
+enum ProbeAddr : int { kProbeGeneral = 0, kProbeUniform = 1, kProbePair = 3, kProbeQuad = 4 };
 
 template <bool kFp8, int kAddr, int kWaves>
 __global__ __launch_bounds__(64 * kWaves) void gather_kernel(const ProbeParams p) {
@@ -83,6 +83,25 @@ __global__ __launch_bounds__(64 * kWaves) void gather_kernel(const ProbeParams p
         vo[j] = roff + ld.voff[j];
       }
       dma_chunk_sbase2(base0, base1, st, ko, vo);
+    } else if (kAddr == kProbeQuad) {
+      // FP8 blocks of 8 tokens, four to a chunk (the split kernel's
+      // SDA_CHUNK_ASM_QUAD); blocks past the list load block 4c again.
+      const int k0 = slot0 / 8;
+      auto blk = [&](int q) { return uniform_ptr(p.base + s_off[k0 + q < nb ? k0 + q : k0]); };
+      const uint8_t* const q0 = blk(0);
+      const uint8_t* const q1 = blk(1);
+      const uint8_t* const q2 = blk(2);
+      const uint8_t* const q3 = blk(3);
+#pragma unroll
+      for (int j = 0; j < 6; ++j) {
+        const uint32_t roff = (uint32_t)(ld.row[j] & 7) * ts;
+        ko[j] = roff + ld.koff[j];
+        vo[j] = roff + ld.voff[j];
+      }
+      const bool hi = lane >= 32;
+      const uint8_t* const l1 = hi ? q1 : q0;
+      const uint8_t* const l4 = hi ? q3 : q2;
+      dma_chunk_quad(q0, q1, q2, q3, st, ko, vo, l1 + ko[1], l1 + vo[1], l4 + ko[4], l4 + vo[4]);
     } else {
       const uint8_t* ka[6];
       const uint8_t* va[6];
@@ -136,8 +155,8 @@ template <bool kFp8>
 void launch_dtype(const ProbeParams& p, unsigned groups, int cus, hipStream_t stream) {
   if (p.tpb % Cfg<kFp8>::kTok == 0)
     launch_gather<kFp8, kProbeUniform>(p, groups, cus, stream);
-  else if (!kFp8 && p.tpb == 8)
-    launch_gather<kFp8, kFp8 ? kProbeGeneral : kProbePair>(p, groups, cus, stream);
+  else if (p.tpb == 8)
+    launch_gather<kFp8, kFp8 ? kProbeQuad : kProbePair>(p, groups, cus, stream);
   else
     launch_gather<kFp8, kProbeGeneral>(p, groups, cus, stream);
 }

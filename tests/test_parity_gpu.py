@@ -493,13 +493,13 @@ def host_bins(regions, positions, active, rt, R):
     return bins
 
 
-@pytest.mark.parametrize("R", [130, 600, 1100])
+@pytest.mark.parametrize("R", [64, 100, 130, 300, 600, 1100])
 def test_row_order_bins_and_permutation(R):
     # The order pass only permutes rows, so the outputs cannot show a wrong
     # bin: check the workspace itself.  768 rows (2 to 4 rounds of the
-    # resident grid) with each row's slots shuffled over all R (up to 32
-    # region-id loads per lane of the bin kernel), duplicate and past-position
-    # ids added; the bins must equal the host's, and the order must be the
+    # resident grid) with each row's slots shuffled over all R (1, 2, 4, 8, 16
+    # and 32 region-id loads per lane of the bin kernel), duplicate and
+    # past-position ids added; the bins must equal the host's, and the order must be the
     # stable sort of each 1024-row block by bin.
     w = gen.Workload("row-order-bins", requests=96, query_len=2, groups=4, heads=8, block=16,
                      pages_per_req=128, R=R, kv="bf16", pos_lo=1024, pos_hi=2046,
@@ -511,7 +511,7 @@ def test_row_order_bins_and_permutation(R):
     rt = w.rt
     for r in range(w.rows):
         live = reg[r][reg[r] >= 0]
-        if len(live) and r % 3 == 0:
+        if 0 < len(live) < R and r % 3 == 0:
             reg[r, len(live)] = live[0]                  # a duplicate
         if r % 5 == 0:
             reg[r, -1] = pos[r] // rt + 3                # past the position
