@@ -20,8 +20,10 @@
 //    row instead resolves the pages of its contiguous token window.
 //  * Addressing: a chunk's 12 DMAs take their rows from per-lane 64-bit
 //    addresses when a chunk may straddle regions, from one scalar base when
-//    every chunk lies inside one region (or one window page), and from two
-//    scalar bases when bf16 regions of 8 tokens pair up into a chunk.
+//    every chunk lies inside one region (or one window page), from two
+//    scalar bases when bf16 regions of 8 tokens pair up into a chunk, and
+//    from four (two DMAs per chunk with per-lane addresses) when FP8 regions
+//    of 8 tokens go four to a chunk.
 //  * Main loop: every wave runs its own 2-stage pipeline over chunks of token
 //    slots (16 tokens for a bf16 cache, 32 for FP8: 6 KiB of K and 6 KiB of
 //    V either way).  A chunk is 12 LDS-DMAs (global_load_lds_dwordx4) into a
