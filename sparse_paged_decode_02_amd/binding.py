@@ -34,9 +34,12 @@ HEAD_DIM = 192
 
 
 class SdaError(RuntimeError):
-    def __init__(self, status: int, message: str):
-        super().__init__("sda_decode failed (%d): %s" % (status, message))
+    """A library call's sda_status, with the call it came from (argument
+    checks shared by several calls name none)."""
+    def __init__(self, status: int, message: str, call: str = ""):
+        super().__init__("%s failed (%d): %s" % (call or "sda call", status, message))
         self.status = status
+        self.call = call
 
 
 class DecodeArgs(ctypes.Structure):
@@ -350,7 +353,7 @@ def sda_decode(query, cache, regions, block_table, positions, active, output, *,
                                   gate, region_tokens, workspace, row_order, stream)
     rc = lib().sda_decode(ctypes.byref(a), handle)
     if rc != SDA_OK:
-        raise SdaError(rc, status_string(rc))
+        raise SdaError(rc, status_string(rc), call="sda_decode")
 
 
 def sda_decode_kernels(query, cache, regions, block_table, positions, active, output, *, scale,
@@ -364,7 +367,7 @@ def sda_decode_kernels(query, cache, regions, block_table, positions, active, ou
                                   gate, region_tokens, workspace, row_order, stream)
     rc, bits = sda_decode_kernels_raw(a, handle)
     if rc != SDA_OK:
-        raise SdaError(rc, status_string(rc))
+        raise SdaError(rc, status_string(rc), call="sda_decode_kernels")
     return bits
 
 
@@ -389,7 +392,7 @@ def sda_decode_static(query, cache, regions, block_table, positions, active, out
         stream = torch.cuda.current_stream(query.device)
     rc = lib().sda_decode_static(ctypes.byref(a), ctypes.c_void_p(stream.cuda_stream))
     if rc != SDA_OK:
-        raise SdaError(rc, status_string(rc))
+        raise SdaError(rc, status_string(rc), call="sda_decode_static")
 
 
 def sda_decode_static_raw(args: DecodeArgs, stream_handle=None) -> int:
@@ -507,7 +510,7 @@ def sda_swa_decode(query, cache, block_table, seq_lens, output, *, scale, window
     handle = ctypes.c_void_p(stream.cuda_stream)
     rc = lib().sda_swa_decode(ctypes.byref(a), handle)
     if rc != SDA_OK:
-        raise SdaError(rc, status_string(rc))
+        raise SdaError(rc, status_string(rc), call="sda_swa_decode")
 
 
 def sda_swa_decode_raw(args: SwaArgs, stream_handle=None) -> int:
@@ -536,17 +539,20 @@ def sda_select_regions(scores, current, topk, *, topk_lengths=None, out=None,
     nvidia.flashinfer_sparse" (``sort=False``)."""
     if scores.dtype != torch.float32 or scores.dim() != 2 or (
             scores.shape[1] > 1 and scores.stride(1) != 1):
-        raise SdaError(SDA_ERR_INVALID, "scores must be float32 [rows, regions], unit inner stride")
+        raise SdaError(SDA_ERR_INVALID, "scores must be float32 [rows, regions], unit inner stride",
+                       call="sda_select_regions")
     rows = scores.shape[0]
     for t, name in ((current, "current"), (topk_lengths, "topk_lengths")):
         if t is not None and (t.dtype != torch.int32 or not t.is_contiguous() or
                               t.numel() != rows):
-            raise SdaError(SDA_ERR_INVALID, "%s must be contiguous int32 [rows]" % name)
+            raise SdaError(SDA_ERR_INVALID, "%s must be contiguous int32 [rows]" % name,
+                           call="sda_select_regions")
     if out is None:
         out = torch.empty((rows, int(topk)), dtype=torch.int32, device=scores.device)
     if out.dtype != torch.int32 or out.dim() != 2 or out.shape != (rows, int(topk)) or (
             topk > 1 and out.stride(1) != 1):
-        raise SdaError(SDA_ERR_INVALID, "out must be int32 [rows, topk], unit inner stride")
+        raise SdaError(SDA_ERR_INVALID, "out must be int32 [rows, topk], unit inner stride",
+                       call="sda_select_regions")
     check_device(scores, current=current, topk_lengths=topk_lengths, out=out)
     a = make_select_args(scores, current, topk, out, topk_lengths)
     if stream is None:
@@ -554,7 +560,7 @@ def sda_select_regions(scores, current, topk, *, topk_lengths=None, out=None,
     handle = ctypes.c_void_p(stream.cuda_stream)
     rc = lib().sda_select_regions(ctypes.byref(a), handle)
     if rc != SDA_OK:
-        raise SdaError(rc, status_string(rc))
+        raise SdaError(rc, status_string(rc), call="sda_select_regions")
     return out
 
 
@@ -604,26 +610,32 @@ def sda_indexer_logits(query, weights, summaries, summary_scales, block_table, p
     their scales, table, positions).  ``table_cols``: as in make_logits_args."""
     e4 = (torch.uint8, torch.float8_e4m3fn)
     if query.dtype not in e4 or query.dim() != 3 or query.shape[2] != 256 or query.stride(2) != 1:
-        raise SdaError(SDA_ERR_INVALID, "query must be e4m3 [rows, heads, 256]")
+        raise SdaError(SDA_ERR_INVALID, "query must be e4m3 [rows, heads, 256]",
+                       call="sda_indexer_logits")
     if summaries.dtype not in e4 or summaries.dim() != 3 or summaries.shape[2] != 256 or \
             summaries.stride(2) != 1:
-        raise SdaError(SDA_ERR_INVALID, "summaries must be e4m3 [pages, regions_per_page, 256]")
+        raise SdaError(SDA_ERR_INVALID, "summaries must be e4m3 [pages, regions_per_page, 256]",
+                       call="sda_indexer_logits")
     if weights.dtype != torch.float32 or weights.shape != query.shape[:2] or (
             weights.shape[1] > 1 and weights.stride(1) != 1):
-        raise SdaError(SDA_ERR_INVALID, "weights must be float32 [rows, heads]")
+        raise SdaError(SDA_ERR_INVALID, "weights must be float32 [rows, heads]",
+                       call="sda_indexer_logits")
     if summary_scales.dtype != torch.float32 or summary_scales.shape != summaries.shape[:2] or (
             summary_scales.shape[1] > 1 and summary_scales.stride(1) != 1):
-        raise SdaError(SDA_ERR_INVALID, "summary_scales must be float32 [pages, regions_per_page]")
+        raise SdaError(SDA_ERR_INVALID, "summary_scales must be float32 [pages, regions_per_page]",
+                       call="sda_indexer_logits")
     for t, name in ((block_table, "block_table"),):
         if t.dtype != torch.int32 or t.dim() != 2 or t.stride(1) != 1:
-            raise SdaError(SDA_ERR_INVALID, "%s must be int32 2-D, unit inner stride" % name)
+            raise SdaError(SDA_ERR_INVALID, "%s must be int32 2-D, unit inner stride" % name,
+                           call="sda_indexer_logits")
     rows = query.shape[0]
     check_table_rows(block_table, rows, int(groups) * int(query_len))
     for t, name in ((positions, "positions"), (current, "current"),
                     (topk_lengths, "topk_lengths")):
         if t is not None and (t.dtype != torch.int32 or not t.is_contiguous() or
                               t.numel() != rows):
-            raise SdaError(SDA_ERR_INVALID, "%s must be contiguous int32 [rows]" % name)
+            raise SdaError(SDA_ERR_INVALID, "%s must be contiguous int32 [rows]" % name,
+                           call="sda_indexer_logits")
     if scores is None:
         scores = torch.empty((rows, int(num_regions)), dtype=torch.float32, device=query.device)
     if scores.dtype != torch.float32 or scores.dim() != 2 or \
@@ -642,7 +654,7 @@ def sda_indexer_logits(query, weights, summaries, summary_scales, block_table, p
     handle = ctypes.c_void_p(stream.cuda_stream)
     rc = lib().sda_indexer_logits(ctypes.byref(a), handle)
     if rc != SDA_OK:
-        raise SdaError(rc, status_string(rc))
+        raise SdaError(rc, status_string(rc), call="sda_indexer_logits")
     return scores
 
 

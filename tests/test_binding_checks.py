@@ -123,6 +123,21 @@ def test_logits_refuses_mismatched_scores(shape, dtype):
     assert e.value.status == B.SDA_ERR_INVALID and "scores" in str(e.value)
 
 
+def test_errors_name_their_call():
+    # A wrapper's own argument checks name the call that refused them.
+    with pytest.raises(B.SdaError) as e:
+        B.sda_select_regions(torch.zeros((4, 16), dtype=torch.float64),
+                             torch.zeros(4, dtype=torch.int32), 4)
+    assert e.value.call == "sda_select_regions"
+    assert str(e.value).startswith("sda_select_regions failed (%d)" % B.SDA_ERR_INVALID)
+    with pytest.raises(B.SdaError) as e:
+        B.sda_indexer_logits(torch.zeros((4, 8, 256), dtype=torch.float32), torch.zeros((4, 8)),
+                             torch.zeros((8, 8, 256), dtype=torch.uint8), torch.zeros((8, 8)),
+                             torch.zeros((2, 4), dtype=torch.int32),
+                             torch.zeros(4, dtype=torch.int32), groups=2, num_regions=64)
+    assert str(e.value).startswith("sda_indexer_logits failed")
+
+
 # --- every tensor the library dereferences must be on the query's GPU --------
 def test_decode_refuses_host_tensors():
     # Well-formed shapes on the host: refused before the C call (a host
