@@ -405,7 +405,9 @@ int sda_select_regions(const sda_select_args *args, hipStream_t stream);
  *                the positions, one dependent round trip fewer; with 0 only
  *                the columns of each request's scored regions are read.
  *  positions     int32 [rows].
- *  scores        fp32 [rows, S] output; 16-byte aligned, row stride % 4 == 0.
+ *  scores        fp32 [rows, S] output, 4-byte aligned (else INVALID); the row
+ *                stride (in floats, any value) must keep rows apart, which is
+ *                not checked.
  *  current, topk_lengths  optional int32 [rows] outputs for the selection:
  *                positions / region_tokens (-1 for a negative position) and
  *                the scored region count min(current + 1, S).

@@ -642,7 +642,8 @@ def sda_indexer_logits(query, weights, summaries, summary_scales, block_table, p
             tuple(scores.shape) != (rows, int(num_regions)) or \
             (scores.shape[1] > 1 and scores.stride(1) != 1):
         raise SdaError(SDA_ERR_INVALID,
-                       "scores must be float32 [rows, num_regions], unit inner stride")
+                       "scores must be float32 [rows, num_regions], unit inner stride",
+                       call="sda_indexer_logits")
     check_device(query, weights=weights, summaries=summaries, summary_scales=summary_scales,
                  block_table=block_table, positions=positions, scores=scores, current=current,
                  topk_lengths=topk_lengths)

@@ -397,13 +397,12 @@ int sda_indexer_logits(const sda_logits_args* a, hipStream_t stream) {
   if (!a->query || !a->weights || !a->summaries || !a->summary_scales || !a->block_table ||
       !a->positions || !a->scores)
     return SDA_ERR_INVALID;
-  // 16-byte query / summary loads and score stores
+  // 16-byte query / summary loads (the scores are stored 4 bytes at a time)
   if (!aligned(a->query, 16) || a->q_row_stride % 16 || a->q_head_stride % 16 ||
-      !aligned(a->summaries, 16) || a->s_page_stride % 16 || a->s_region_stride % 16 ||
-      !aligned(a->scores, 16) || a->scores_row_stride % 4)
+      !aligned(a->summaries, 16) || a->s_page_stride % 16 || a->s_region_stride % 16)
     return SDA_ERR_UNSUPPORTED;
-  if (!aligned(a->weights, 4) || !aligned(a->summary_scales, 4) || !aligned(a->current, 4) ||
-      !aligned(a->topk_lengths, 4))
+  if (!aligned(a->weights, 4) || !aligned(a->summary_scales, 4) || !aligned(a->scores, 4) ||
+      !aligned(a->current, 4) || !aligned(a->topk_lengths, 4))
     return SDA_ERR_INVALID;
   sda::LogitsParams p{};
   p.q = static_cast<const uint8_t*>(a->query);

@@ -339,11 +339,11 @@ LOGITS_INVALID = [dict(heads=0), dict(heads=3), dict(heads=32), dict(groups=0), 
                   dict(rows=6), dict(rows=-4), dict(query=None), dict(weights=None),
                   dict(summaries=None), dict(summary_scales=None), dict(block_table=None),
                   dict(positions=None), dict(scores=None), dict(weights=0x200002),
-                  dict(current=0x800001), dict(table_cols=-1), dict(table_cols=513)]
+                  dict(current=0x800001), dict(table_cols=-1), dict(table_cols=513),
+                  dict(scores=0x700002)]
 LOGITS_UNSUPPORTED = [dict(heads=16, query_len=2), dict(query=0x100008),
                       dict(q_head_stride=264), dict(s_region_stride=260),
-                      dict(summaries=0x300004), dict(scores=0x700004),
-                      dict(scores_row_stride=4098), dict(rows=16777216 * 4, groups=4),
+                      dict(summaries=0x300004), dict(rows=16777216 * 4, groups=4),
                       dict(num_regions=65535 * 256 + 1, scores_row_stride=65535 * 256 + 4)]
 
 

@@ -118,6 +118,23 @@ def test_ragged_columns_and_strided_views():
     assert (buf[:, S:] == 7.0).all()
 
 
+def test_scores_rows_of_any_stride():
+    # Score rows are stored 4 bytes at a time: S = 594 (not a multiple of 4)
+    # in a contiguous buffer, and the same in a view one float into a wider
+    # buffer (rows 4-byte but not 16-byte aligned).
+    w = case(17, requests=2, groups=2, heads=2, query_len=2, block=16, pages_per_req=297,
+             pos_lo=459, pos_hi=297 * 16 - 2)
+    inp = gen.make_logits_inputs(w, device=DEV)
+    S = w.num_regions
+    assert S % 4 == 2
+    got, cur, lens = run(inp, scores=torch.empty((w.rows, S), device=DEV))
+    check(inp, got, cur, lens, what="stride S")
+    buf = torch.full((w.rows, S + 3), 7.0, device=DEV)
+    got, cur, lens = run(inp, scores=buf[:, 1:S + 1])
+    check(inp, got, cur, lens, what="stride S + 3, offset 1")
+    assert (buf[:, 0] == 7.0).all() and (buf[:, S + 1:] == 7.0).all()
+
+
 @pytest.mark.parametrize("requests,qlen", [(256, 1), (257, 1), (300, 2)])
 def test_many_requests(requests, qlen):
     # Grids of 256 to 300 requests of 80 regions (a partial 256-region chunk
