@@ -469,6 +469,93 @@ def run_select(args, dev) -> int:
     return 0
 
 
+def run_chain(args, dev) -> int:
+    """One DSA decode step on the bf16-gated decode batch (64 requests x G 4,
+    16 heads, bf16 cache of 64-token pages, positions U[4096, 32767]) at the
+    pages' 8-token regions: indexer logits (8 e4m3 heads) over every region of
+    each row's request, top-512 selection with the current region forced,
+    then the sparse decode over the selected regions (~4K tokens per row).
+    Each stage is timed alone on its own inputs, then the three back to back
+    (the selection reads the logits' scores, the decode the selection's
+    regions).  One input set: the stages hand their outputs on."""
+    import torch
+    from sparse_paged_decode_02_amd import binding as B
+    from sparse_paged_decode_02_amd import inputs as gen
+
+    topk = 512
+    w = gen.Workload("dsa-chain", requests=64, query_len=1, groups=4, heads=16, block=64,
+                     pages_per_req=512, R=topk, kv="bf16", pos_lo=4096, pos_hi=32767,
+                     inactive_frac=0.0, gated=True, splits=1, region_tokens=8,
+                     seed=gen.workload_seed(31))
+    lw = gen.LogitsWorkload("dsa-chain-logits", requests=w.requests, query_len=w.query_len,
+                            groups=w.groups, heads=8, block=w.block,
+                            pages_per_req=w.pages_per_req, pos_lo=w.pos_lo, pos_hi=w.pos_hi,
+                            region_tokens=8, seed=gen.workload_seed(32))
+    desc = ("dsa-chain: %d rows = %d req x G %d; logits %d e4m3 heads x 256 over %d regions "
+            "of 8 tokens; top-%d selection; sparse decode %d heads x 192, bf16 cache, block %d, "
+            "gated" % (w.rows, w.requests, w.groups, lw.heads, lw.num_regions, topk, w.heads,
+                       w.block))
+    print("[bench] drawing %s" % desc, file=sys.stderr, flush=True)
+    dec = gen.make_inputs(w, device=dev, splits=1)
+    li = gen.make_logits_inputs(lw, device=dev)
+    S = lw.num_regions
+    scores = torch.empty((w.rows, S), dtype=torch.float32, device=dev)
+    cur = torch.empty(w.rows, dtype=torch.int32, device=dev)
+    lens = torch.empty(w.rows, dtype=torch.int32, device=dev)
+    regions = torch.empty((w.rows, topk), dtype=torch.int32, device=dev)
+    out = torch.empty_like(dec.query)
+    stream = torch.cuda.current_stream(dev)
+    handle = ctypes.c_void_p(stream.cuda_stream)
+    la = B.make_logits_args(li.query, li.weights, li.summaries, li.scales, dec.block_table,
+                            dec.positions, scores, groups=w.groups, query_len=w.query_len,
+                            region_tokens=8, current=cur, topk_lengths=lens)
+    sa = B.make_select_args(scores, cur, topk, regions, lens)
+    da = B.make_args(dec.query, dec.cache, regions, dec.block_table, dec.positions, dec.active,
+                     out, scale=dec.scale, query_len=w.query_len, splits=1, gate=dec.gate,
+                     region_tokens=8)
+
+    def check(rc):
+        if rc != B.SDA_OK:
+            raise B.SdaError(rc, B.status_string(rc))
+
+    stages = {
+        "logits": lambda i: check(B.sda_indexer_logits_raw(la, handle)),
+        "selection": lambda i: check(B.sda_select_regions_raw(sa, handle)),
+        "decode": lambda i: check(B.sda_decode_raw(da, handle)),
+    }
+
+    def chain(i):
+        for fn in stages.values():
+            fn(i)
+
+    chain(0)  # the selection's regions feed the decode timed alone
+    torch.cuda.synchronize()
+    res = {}
+    for name, fn in list(stages.items()) + [("chain", chain)]:
+        wall, avg_ms, launch_ms = time_calls(fn, args.steps, args.warmup, stream,
+                                             args.settle_ms)
+        res[name] = {"us_per_call": round(wall / args.steps * 1e6, 2),
+                     "hip_event_us": round(avg_ms * 1e3, 2),
+                     "median_us": round(float(np.median(launch_ms)) * 1e3, 2)}
+    pos = dec.positions.cpu().numpy()
+    sel = regions.cpu().numpy()
+    dbytes, tokens = algorithmic_bytes(w, pos, sel, dec.active.cpu().numpy())
+    res["decode"]["bytes_per_call"] = int(dbytes)
+    res["decode"]["GB/s"] = round(dbytes / (res["decode"]["us_per_call"] * 1e-6) / 1e9, 1)
+    res["decode"]["visible_tokens_per_row"] = round(tokens / w.rows, 1)
+    lbytes = logits_algorithmic_bytes(lw, pos)
+    res["logits"]["bytes_per_call"] = int(lbytes)
+    res["logits"]["GB/s"] = round(lbytes / (res["logits"]["us_per_call"] * 1e-6) / 1e9, 1)
+    chain_us = res["chain"]["us_per_call"]
+    rec = {"metric": "DSA decode step (indexer logits -> top-512 selection -> sparse decode)",
+           "value": round(w.rows / (chain_us * 1e-6), 1), "unit": "rows/s",
+           "higher_is_better": True, "us_per_step": chain_us, "steps": args.steps,
+           "warmup": args.warmup, "data": "synthetic", "stages": res,
+           "config": {"workload": desc, "rows": w.rows, "seed": w.seed}}
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def load_traffic(workload_name: str, splits: int, kernel: str = "split_kernel"):
     """Counter-derived HBM bytes per launch from the committed profile summary,
     or None unless it was measured on the current kernel source and split count."""
@@ -869,6 +956,10 @@ def main() -> int:
     ap.add_argument("--logits", default="", metavar="NAME",
                     help="measure the decode indexer logits on workload NAME (logits-decode, "
                          "logits-mtp) instead")
+    ap.add_argument("--chain", action="store_true",
+                    help="time one DSA decode step (indexer logits -> top-512 selection -> "
+                         "sparse decode at 8-token regions), each stage alone and the three "
+                         "back to back")
     ap.add_argument("--gather-ceiling", type=int, default=0, metavar="K",
                     help="time the gather probe on workload K's region blocks beside the "
                          "split kernel on the same inputs (one JSON line)")
@@ -938,6 +1029,8 @@ def main() -> int:
         return run_select(args, dev)
     if args.logits:
         return run_logits(args, dev)
+    if args.chain:
+        return run_chain(args, dev)
     headline = measure_sparse(args, dev, args.config, with_cpu=not args.no_cpu_baseline)
     others = parse_also(args)
     if others:
