@@ -477,7 +477,8 @@ def run_chain(args, dev) -> int:
     then the sparse decode over the selected regions (~4K tokens per row).
     Each stage is timed alone on its own inputs, then the three back to back
     (the selection reads the logits' scores, the decode the selection's
-    regions).  One input set: the stages hand their outputs on."""
+    regions), then the three as one replayed HIP graph.  One input set: the
+    stages hand their outputs on."""
     import torch
     from sparse_paged_decode_02_amd import binding as B
     from sparse_paged_decode_02_amd import inputs as gen
@@ -537,6 +538,27 @@ def run_chain(args, dev) -> int:
         res[name] = {"us_per_call": round(wall / args.steps * 1e6, 2),
                      "hip_event_us": round(avg_ms * 1e3, 2),
                      "median_us": round(float(np.median(launch_ms)) * 1e3, 2)}
+    # The same step captured once in a HIP graph and replayed (the library
+    # calls allocate nothing and record no memset, so they capture as they
+    # are); the replays must reproduce the eager outputs bit for bit.
+    torch.cuda.synchronize()
+    eager_regions, eager_out = regions.clone(), out.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        h = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+        check(B.sda_indexer_logits_raw(la, h))
+        check(B.sda_select_regions_raw(sa, h))
+        check(B.sda_decode_raw(da, h))
+    wall, avg_ms, launch_ms = time_calls(lambda i: graph.replay(), args.steps, args.warmup,
+                                         stream, args.settle_ms)
+    torch.cuda.synchronize()
+    res["chain_graph"] = {"us_per_call": round(wall / args.steps * 1e6, 2),
+                          "hip_event_us": round(avg_ms * 1e3, 2),
+                          "median_us": round(float(np.median(launch_ms)) * 1e3, 2),
+                          "matches_eager": bool(torch.equal(regions, eager_regions) and
+                                                torch.equal(out.view(torch.int16),
+                                                            eager_out.view(torch.int16)))}
+    del graph
     pos = dec.positions.cpu().numpy()
     sel = regions.cpu().numpy()
     dbytes, tokens = algorithmic_bytes(w, pos, sel, dec.active.cpu().numpy())
