@@ -105,17 +105,36 @@ static_assert(kStageBytes == 0x1800, "SDA_CHUNK_ASM_KV: V slices start 6 KiB int
       SDA_LDDMA("v4", addrb, suf) SDA_NEXT SDA_LDDMA("v5", addrb, suf)                         \
   "s_mov_b32 m0, %[sv]"
 
+// Two-region FP8 chunk (16-token regions): K and V DMAs 0..2 cover token
+// rows 0..15 and DMAs 3..5 rows 16..31, each half from its own uniform base,
+// in SDA_CHUNK_ASM_KV's K/V order and LDS placement.
+#define SDA_CHUNK_ASM_KV2(addra, addrb, suf)                                                   \
+  "s_mov_b32 %[sv], m0\n\t"                                                                   \
+  "s_mov_b32 m0, %[st]\n\t" SDA_LDDMA("k0", addra, suf) SDA_M0("0x1800")                      \
+      SDA_LDDMA("v0", addra, suf) SDA_M0("0x400") SDA_LDDMA("k1", addra, suf) SDA_M0("0x1c00")  \
+      SDA_LDDMA("v1", addra, suf) SDA_M0("0x800") SDA_LDDMA("k2", addra, suf) SDA_M0("0x2000")  \
+      SDA_LDDMA("v2", addra, suf) SDA_M0("0xc00") SDA_LDDMA("k3", addrb, suf) SDA_M0("0x2400")  \
+      SDA_LDDMA("v3", addrb, suf) SDA_M0("0x1000") SDA_LDDMA("k4", addrb, suf) SDA_M0("0x2800") \
+      SDA_LDDMA("v4", addrb, suf) SDA_M0("0x1400") SDA_LDDMA("k5", addrb, suf) SDA_M0("0x2c00") \
+      SDA_LDDMA("v5", addrb, suf) "s_mov_b32 m0, %[sv]"
+
+// Two uniform bases: DMAs 0..2 from base_a, 3..5 from base_b (K and V).
+template <bool kFp8>
 __device__ __forceinline__ void dma_chunk_sbase2(const uint8_t* base_a, const uint8_t* base_b,
                                                  uint32_t stage, const uint32_t (&ko)[6],
                                                  const uint32_t (&vo)[6]) {
   uint32_t saved;
-  __asm__ __volatile__(SDA_CHUNK_ASM2("%[b]", "%[b2]", " nt")
-                       : [sv] "=&s"(saved)
-                       : [st] "s"(stage), [b] "s"(base_a), [b2] "s"(base_b), [k0] "v"(ko[0]),
-                         [k1] "v"(ko[1]), [k2] "v"(ko[2]), [k3] "v"(ko[3]), [k4] "v"(ko[4]),
-                         [k5] "v"(ko[5]), [v0] "v"(vo[0]), [v1] "v"(vo[1]), [v2] "v"(vo[2]),
-                         [v3] "v"(vo[3]), [v4] "v"(vo[4]), [v5] "v"(vo[5])
-                       : "memory");
+#define SDA_SBASE2_OPERANDS                                                                     \
+  : [sv] "=&s"(saved)                                                                           \
+  : [st] "s"(stage), [b] "s"(base_a), [b2] "s"(base_b), [k0] "v"(ko[0]), [k1] "v"(ko[1]),      \
+    [k2] "v"(ko[2]), [k3] "v"(ko[3]), [k4] "v"(ko[4]), [k5] "v"(ko[5]), [v0] "v"(vo[0]),        \
+    [v1] "v"(vo[1]), [v2] "v"(vo[2]), [v3] "v"(vo[3]), [v4] "v"(vo[4]), [v5] "v"(vo[5])         \
+  : "memory"
+  if constexpr (kFp8)
+    __asm__ __volatile__(SDA_CHUNK_ASM_KV2("%[b]", "%[b2]", " nt") SDA_SBASE2_OPERANDS);
+  else
+    __asm__ __volatile__(SDA_CHUNK_ASM2("%[b]", "%[b2]", " nt") SDA_SBASE2_OPERANDS);
+#undef SDA_SBASE2_OPERANDS
 }
 
 // Four-region chunk (FP8, 8-token regions).  K DMA j covers token rows
@@ -159,6 +178,11 @@ static_assert(quad_region(0) == (0 + 1) / 2 && quad_region(2) == (2 + 1) / 2 &&
 static_assert(quad_split_at_32(1) && fp8_dma_row(1, 0) / 8 == 0 && quad_split_at_32(4) &&
                   fp8_dma_row(4, 0) / 8 == 2,
               "SDA_CHUNK_ASM_QUAD: DMAs 1 and 4 split at lane 32");
+
+// SDA_CHUNK_ASM_KV2: DMAs 0..2 inside rows 0..15, DMAs 3..5 inside rows 16..31.
+static_assert(fp8_dma_row(0, 0) == 0 && fp8_dma_row(2, 63) == 15 && fp8_dma_row(3, 0) == 16 &&
+                  fp8_dma_row(5, 63) == 31,
+              "SDA_CHUNK_ASM_KV2: DMAs 0..2 and 3..5 each inside one 16-row half");
 
 // ko/vo: 32-bit lane offsets of DMAs 0, 2, 3, 5 from their region's base;
 // k1/v1, k4/v4: the lane's 64-bit addresses for DMAs 1 and 4.

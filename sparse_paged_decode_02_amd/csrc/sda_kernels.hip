@@ -21,9 +21,9 @@
 //  * Addressing: a chunk's 12 DMAs take their rows from per-lane 64-bit
 //    addresses when a chunk may straddle regions, from one scalar base when
 //    every chunk lies inside one region (or one window page), from two
-//    scalar bases when bf16 regions of 8 tokens pair up into a chunk, and
-//    from four (two DMAs per chunk with per-lane addresses) when FP8 regions
-//    of 8 tokens go four to a chunk.
+//    scalar bases when regions of half a chunk (8 bf16 or 16 FP8 tokens)
+//    pair up into a chunk, and from four (two DMAs per chunk with per-lane
+//    addresses) when FP8 regions of 8 tokens go four to a chunk.
 //  * Main loop: every wave runs its own 2-stage pipeline over chunks of token
 //    slots (16 tokens for a bf16 cache, 32 for FP8: 6 KiB of K and 6 KiB of
 //    V either way).  A chunk is 12 LDS-DMAs (global_load_lds_dwordx4) into a
@@ -92,7 +92,7 @@ enum Addr : int {
   kGeneral = 0,  // region list; a chunk may span regions (per-lane 64-bit addresses)
   kUniform = 1,  // region list; every chunk lies inside one region
   kWindow = 2,   // a contiguous sliding window of tokens, 16-token chunks
-  kPair = 3,     // region list of 8-token regions, bf16: a chunk is two regions
+  kPair = 3,     // region list of half-chunk regions (8 tokens bf16, 16 FP8): two per chunk
   kQuad = 4,     // region list of 8-token regions, FP8: a chunk is four regions
 };
 
@@ -181,11 +181,11 @@ __device__ __forceinline__ uint32_t issue_chunk(const Params& p, int c, int nreg
     }
     dma_chunk_sbase<kFp8>(base, st, ko, vo);
   } else if (kAddr == kPair) {
-    // 8-token regions (bf16): chunk c is regions 2c and 2c+1 of the list,
-    // each with a uniform base.  Rows past a region's visible count, and the
-    // second half when the list has no region 2c+1, load token 0 of region
-    // 2c (visible, finite, weight 0).
-    static_assert(!kFp8 || kAddr != kPair, "pair chunks are bf16");
+    // Regions of half a chunk (8 tokens bf16, 16 tokens FP8): chunk c is
+    // regions 2c and 2c+1 of the list, each with a uniform base.  Rows past a
+    // region's visible count, and the second half when the list has no
+    // region 2c+1, load token 0 of region 2c (visible, finite, weight 0).
+    constexpr int kHalf = C::kTok / 2;
     const int i16 = lane & 15;
     const int k0 = 2 * c;
     const bool has1 = k0 + 1 < nreg;
@@ -195,17 +195,22 @@ __device__ __forceinline__ uint32_t issue_chunk(const Params& p, int c, int nreg
     const int64_t rb1 = has1 ? s_base[k0 + 1] : rb0;
     const uint8_t* base0 = uniform_ptr(p.cache + rb0 * C::kEsz);
     const uint8_t* base1 = uniform_ptr(p.cache + rb1 * C::kEsz);
-    vbits = (i16 < 8 ? i16 < n0 : i16 - 8 < n1) ? 1u : 0u;
+    // S^T slot 16t + i16: region t (FP8), region i16 >> 3 (bf16)
+    if (kFp8)
+      vbits = (i16 < n0 ? 1u : 0u) | (i16 < n1 ? 2u : 0u);
+    else
+      vbits = (i16 < 8 ? i16 < n0 : i16 - 8 < n1) ? 1u : 0u;
     uint32_t ko[6], vo[6];
 #pragma unroll
     for (int j = 0; j < 6; ++j) {
-      const int r8 = ld.row[j] & 7;  // rows 0..7 for j < 3, 8..15 for j >= 3
+      // token row within its region: DMAs 0..2 read region 2c, 3..5 region 2c+1
+      const int rr = ld.row[j] & (kHalf - 1);
       const int nn = j < 3 ? n0 : n1;
-      const uint32_t roff = r8 < nn ? (uint32_t)r8 * cts_bytes : 0u;
+      const uint32_t roff = rr < nn ? (uint32_t)rr * cts_bytes : 0u;
       ko[j] = roff + ld.koff[j];
       vo[j] = roff + ld.voff[j];
     }
-    dma_chunk_sbase2(base0, base1, st, ko, vo);
+    dma_chunk_sbase2<kFp8>(base0, base1, st, ko, vo);
   } else if (kAddr == kQuad) {
     // 8-token regions (FP8): chunk c is list entries 4c .. 4c + 3, token rows
     // 8q .. 8q + 7 of the chunk from entry 4c + q.  Rows past an entry's
@@ -1427,8 +1432,10 @@ void launch_region_list(const Params& p, hipStream_t stream) {
   const unsigned wgs = (unsigned)p.rows;
   if (p.rt % Cfg<kFp8>::kTok == 0)
     launch_split<kFp8, kFused, kUniform>(p, wgs, stream);
-  else if (p.rt == 8)
-    launch_split<kFp8, kFused, kFp8 ? kQuad : kPair>(p, wgs, stream);
+  else if (2 * p.rt == Cfg<kFp8>::kTok)
+    launch_split<kFp8, kFused, kPair>(p, wgs, stream);
+  else if (kFp8 && p.rt == 8)
+    launch_split<kFp8, kFused, kFp8 ? kQuad : kGeneral>(p, wgs, stream);
   else
     launch_split<kFp8, kFused, kGeneral>(p, wgs, stream);
 }
@@ -1457,8 +1464,10 @@ template <bool kFp8>
 void launch_row_stream(const Params& p, hipStream_t stream) {
   if (p.rt % Cfg<kFp8>::kTok == 0)
     launch_row_stream_addr<kFp8, kUniform>(p, stream);
-  else if (p.rt == 8)
-    launch_row_stream_addr<kFp8, kFp8 ? kQuad : kPair>(p, stream);
+  else if (2 * p.rt == Cfg<kFp8>::kTok)
+    launch_row_stream_addr<kFp8, kPair>(p, stream);
+  else if (kFp8 && p.rt == 8)
+    launch_row_stream_addr<kFp8, kFp8 ? kQuad : kGeneral>(p, stream);
   else
     launch_row_stream_addr<kFp8, kGeneral>(p, stream);
 }

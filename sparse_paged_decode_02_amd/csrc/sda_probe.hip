@@ -4,9 +4,9 @@
 // the workgroup's concatenated token rows goes to wave c % waves, its 12
 // LDS-DMAs are issued while the previous chunk is read back, and the wait is
 // the split kernel's vmcnt.  Chunks inside one block take a scalar base plus
-// 32-bit lane offsets, blocks of 8 tokens pair up (bf16) or go four to a
-// chunk (FP8) under scalar bases, and anything else uses per-lane 64-bit
-// addresses, as in the split kernel.  Rows past the end of a workgroup's list load its first token row
+// 32-bit lane offsets, blocks of half a chunk pair up (8 bf16 or 16 FP8
+// tokens) and FP8 blocks of 8 tokens go four to a chunk under scalar bases,
+// and anything else uses per-lane 64-bit addresses, as in the split kernel.  Rows past the end of a workgroup's list load its first token row
 // (the split kernel's masked rows load a visible row of their region).
 // The library also holds a VALU issue-rate probe (sda_probe_valu): waves of
 // independent instructions of one kind, timed to give the SIMD cycles a
@@ -72,17 +72,19 @@ __global__ __launch_bounds__(64 * kWaves) void gather_kernel(const ProbeParams p
       }
       dma_chunk_sbase<kFp8>(base, st, ko, vo);
     } else if (kAddr == kProbePair) {
-      const int k0 = slot0 / 8;
+      // blocks of half a chunk (8 bf16 or 16 FP8 tokens), two to a chunk
+      constexpr int kHalf = C::kTok / 2;
+      const int k0 = slot0 / kHalf;
       const bool has1 = k0 + 1 < nb;
       const uint8_t* base0 = uniform_ptr(p.base + s_off[k0]);
       const uint8_t* base1 = uniform_ptr(p.base + s_off[has1 ? k0 + 1 : k0]);
 #pragma unroll
       for (int j = 0; j < 6; ++j) {
-        const uint32_t roff = (uint32_t)(ld.row[j] & 7) * ts;
+        const uint32_t roff = (uint32_t)(ld.row[j] & (kHalf - 1)) * ts;
         ko[j] = roff + ld.koff[j];
         vo[j] = roff + ld.voff[j];
       }
-      dma_chunk_sbase2(base0, base1, st, ko, vo);
+      dma_chunk_sbase2<kFp8>(base0, base1, st, ko, vo);
     } else if (kAddr == kProbeQuad) {
       // FP8 blocks of 8 tokens, four to a chunk (the split kernel's
       // SDA_CHUNK_ASM_QUAD); blocks past the list load block 4c again.
@@ -155,8 +157,10 @@ template <bool kFp8>
 void launch_dtype(const ProbeParams& p, unsigned groups, int cus, hipStream_t stream) {
   if (p.tpb % Cfg<kFp8>::kTok == 0)
     launch_gather<kFp8, kProbeUniform>(p, groups, cus, stream);
-  else if (p.tpb == 8)
-    launch_gather<kFp8, kFp8 ? kProbeQuad : kProbePair>(p, groups, cus, stream);
+  else if (2 * p.tpb == Cfg<kFp8>::kTok)
+    launch_gather<kFp8, kProbePair>(p, groups, cus, stream);
+  else if (kFp8 && p.tpb == 8)
+    launch_gather<kFp8, kFp8 ? kProbeQuad : kProbeGeneral>(p, groups, cus, stream);
   else
     launch_gather<kFp8, kProbeGeneral>(p, groups, cus, stream);
 }
