@@ -148,17 +148,19 @@ def test_sub_page_regions(kv, rt):
         check_close(out, oracle_out(inp), what="rt=%d splits=%d" % (rt, s))
 
 
+@pytest.mark.parametrize("rt", [8, 16])
 @pytest.mark.parametrize("seed", range(12))
-def test_random_eight_token_regions(seed):
-    """Random shapes at the pages' 8-token regions: FP8 takes four regions per
-    32-token chunk and bf16 two per 16-token chunk, under scalar bases.  Pages
-    of 8 to 64 tokens, 1 to 16 heads, 1 to 4 groups, one or two query tokens,
-    region lists of 1 to 700 slots (short lists, several splits, the deferred
-    list and the row-stream kernel), and list lengths that leave a chunk with
-    one to four regions."""
-    rng = np.random.default_rng(5100 + seed)
+def test_random_small_regions(seed, rt):
+    """Random shapes at the pages' 8-token regions and at 16: FP8 takes four
+    8-token or two 16-token regions per 32-token chunk, bf16 two 8-token
+    regions per 16-token chunk, under scalar bases.  Pages of 16 to 64 tokens
+    (8 too at 8-token regions), 1 to 16 heads, 1 to 4 groups, one or two query
+    tokens, region lists of 1 to 700 slots (short lists, several splits, the
+    deferred list and the row-stream kernel), and list lengths that leave a
+    chunk with one to four regions."""
+    rng = np.random.default_rng(5100 + seed + 1000 * (rt != 8))
     kv = "bf16" if seed % 3 == 0 else "fp8"
-    block = int(rng.choice([8, 16, 32, 64]))
+    block = int(rng.choice([8, 16, 32, 64] if rt == 8 else [16, 32, 64]))
     G, ql = int(rng.integers(1, 5)), int(rng.integers(1, 3))
     heads = int(rng.choice([1, 3, 8, 16]))
     big = seed % 4 == 3  # a batch the row-stream kernel takes
@@ -169,15 +171,15 @@ def test_random_eight_token_regions(seed):
         R = int(rng.integers(2, min(64, 256 // per_wave) + 1))
     else:
         requests, R = int(rng.integers(1, 40)), int(rng.integers(1, 700))
-    ppr = int(rng.integers(R * 8 // block + 2, R * 8 // block + 40))
+    ppr = int(rng.integers(R * rt // block + 2, R * rt // block + 40))
     pos_hi = ppr * block - ql  # the last query token stays inside the table
     splits = 1 if big else int(rng.choice([1, 2, 3, 8]))
-    w = gen.Workload("rand8-%d" % seed, requests=requests, query_len=ql, groups=G, heads=heads,
+    w = gen.Workload("rand%d-%d" % (rt, seed), requests=requests, query_len=ql, groups=G, heads=heads,
                      block=block, pages_per_req=ppr, R=R, kv=kv,
                      pos_lo=int(rng.integers(0, pos_hi)), pos_hi=pos_hi,
                      live=(1, R) if rng.random() < 0.5 else None, inactive_frac=0.05,
-                     gated=bool(rng.random() < 0.5), splits=splits, region_tokens=8,
-                     seed=9100 + seed)
+                     gated=bool(rng.random() < 0.5), splits=splits, region_tokens=rt,
+                     seed=9100 + seed + 1000 * (rt != 8))
     inp = gen.make_inputs(w, device=DEV, splits=splits)
     if big:
         assert kernels(inp, splits=1) == B.SDA_KERNEL_ROW_STREAM
@@ -186,8 +188,8 @@ def test_random_eight_token_regions(seed):
     if w.rows > 600:
         rows = np.sort(np.random.default_rng(seed).choice(w.rows, 300, replace=False))
     check_close(out, oracle_out(inp, rows=rows), rows=rows,
-                what="rand8 seed %d %s rows %d R %d block %d splits %d" % (
-                    seed, kv, w.rows, R, block, splits))
+                what="rand rt %d seed %d %s rows %d R %d block %d splits %d" % (
+                    rt, seed, kv, w.rows, R, block, splits))
 
 
 @pytest.mark.parametrize("kv,rt", [("bf16", 0), ("bf16", 24), ("fp8", 0), ("fp8", 24)])
