@@ -183,8 +183,9 @@ __device__ __forceinline__ uint32_t issue_chunk(const Params& p, int c, int nreg
   } else if (kAddr == kPair) {
     // Regions of half a chunk (8 tokens bf16, 16 tokens FP8): chunk c is
     // regions 2c and 2c+1 of the list, each with a uniform base.  Rows past a
-    // region's visible count, and the second half when the list has no
-    // region 2c+1, load token 0 of region 2c (visible, finite, weight 0).
+    // region's visible count load that region's token 0, and the second half
+    // when the list has no region 2c+1 loads token 0 of region 2c (visible,
+    // finite, weight 0).
     constexpr int kHalf = C::kTok / 2;
     const int i16 = lane & 15;
     const int k0 = 2 * c;
